@@ -1,0 +1,188 @@
+"""fp64 CPU oracle for the speculative-decoding hot path (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP
+library and its Python binding never import it, and it imports nothing from
+them: the two implementations share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, no fused multiply-add);
+this module only marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_c_long_p = ctypes.POINTER(ctypes.c_long)
+
+
+def build() -> str:
+    """Compile oracle.c with gcc into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        vp, lg, i, f = ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_float
+        L.oracle_qmv.argtypes = [i, vp, vp, vp, vp, lg, lg, lg, lg, lg, lg, vp, vp]
+        L.oracle_qmv.restype = i
+        L.oracle_qmv_points.argtypes = [i, vp, vp, vp, vp, lg, lg, lg, lg, vp, vp,
+                                        lg, vp, vp]
+        L.oracle_qmv_points.restype = i
+        L.oracle_probs.argtypes = [vp, lg, f, i, f, vp]
+        L.oracle_probs.restype = i
+        L.oracle_sample.argtypes = [vp, lg, f, i, f, f]
+        L.oracle_sample.restype = lg
+        L.oracle_sample_rows.argtypes = [vp, lg, lg, f, i, f, vp, vp]
+        L.oracle_sample_rows.restype = i
+        L.oracle_accept.argtypes = [vp, vp, vp, vp, lg, lg, lg, f, i, f, vp, vp, vp,
+                                    vp, vp]
+        L.oracle_accept.restype = i
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_double.restype = ctypes.c_double
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def half_to_double(h: int) -> float:
+    return lib().oracle_half_to_double(h)
+
+
+def bf16_to_double(b: int) -> float:
+    return lib().oracle_bf16_to_double(b)
+
+
+def qmv(bits: int, w: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+        x: np.ndarray, group: int, rows: tuple[int, int] | None = None,
+        with_abs: bool = False):
+    """y[m][n] for n in ``rows`` (default all), fp64 [M][n1-n0].
+
+    ``w``: uint32 [N][K/8] (bits=4) or uint8 [N][K] (bits=8); ``scales`` and
+    ``biases``: fp16 bit patterns as uint16 [N][K/G]; ``x``: bf16 bit patterns
+    as uint16 [M][K].  With ``with_abs`` also returns sum_k |x * w| per output.
+    """
+    M, K = x.shape
+    N = w.shape[0]
+    n0, n1 = rows if rows is not None else (0, N)
+    y = np.empty((M, n1 - n0), np.float64)
+    a = np.empty_like(y) if with_abs else None
+    rc = lib().oracle_qmv(bits, _ptr(w), _ptr(scales), _ptr(biases), _ptr(x),
+                          M, N, K, group, n0, n1, _ptr(y), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"oracle_qmv rejected its arguments (rc={rc})")
+    return (y, a) if with_abs else y
+
+
+def qmv_points(bits: int, w: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+               x: np.ndarray, group: int, m_idx, n_idx):
+    """Selected outputs y[m_idx[i]][n_idx[i]] and their sum_k |x * w|."""
+    M, K = x.shape
+    N = w.shape[0]
+    mi = np.ascontiguousarray(m_idx, dtype=np.int64)
+    ni = np.ascontiguousarray(n_idx, dtype=np.int64)
+    y = np.empty(mi.shape[0], np.float64)
+    a = np.empty_like(y)
+    rc = lib().oracle_qmv_points(bits, _ptr(w), _ptr(scales), _ptr(biases),
+                                 _ptr(x), M, N, K, group, _ptr(mi), _ptr(ni),
+                                 mi.shape[0], _ptr(y), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"oracle_qmv_points rejected its arguments (rc={rc})")
+    return y, a
+
+
+def probs(z: np.ndarray, temperature: float, top_k: int = 0,
+          top_p: float = 1.0) -> np.ndarray | None:
+    """Filtered sampling distribution of one fp32 row (fp64), None if invalid."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    out = np.empty(z.shape[0], np.float64)
+    rc = lib().oracle_probs(_ptr(z), z.shape[0], temperature, top_k, top_p, _ptr(out))
+    if rc == -1:
+        return None
+    if rc != 0:
+        raise MemoryError("oracle_probs failed")
+    return out
+
+
+def probs_rows(z: np.ndarray, temperature: float, top_k: int = 0,
+               top_p: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    """Row-wise probs of z [R][V]; returns (probs [R][V], valid [R] bool)."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    R, V = z.shape
+    out = np.zeros((R, V), np.float64)
+    valid = np.zeros(R, bool)
+    for r in range(R):
+        p = probs(z[r], temperature, top_k, top_p)
+        if p is not None:
+            out[r] = p
+            valid[r] = True
+    return out, valid
+
+
+def sample(z: np.ndarray, temperature: float, top_k: int, top_p: float,
+           u: float) -> int:
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    return int(lib().oracle_sample(_ptr(z), z.shape[0], temperature, top_k, top_p, u))
+
+
+def sample_rows(z: np.ndarray, temperature: float, top_k: int, top_p: float,
+                u: np.ndarray) -> np.ndarray:
+    """One token per row of z [R][V] with uniforms u [R] (int32 [R])."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    R, V = z.shape
+    tok = np.empty(R, np.int32)
+    lib().oracle_sample_rows(_ptr(z), R, V, temperature, top_k, top_p, _ptr(u), _ptr(tok))
+    return tok
+
+
+def accept(target_logits: np.ndarray, draft_logits: np.ndarray | None,
+           draft_tokens: np.ndarray | None, uniforms: np.ndarray,
+           temperature: float, top_k: int = 0, top_p: float = 1.0) -> dict:
+    """Acceptance for B sequences; target [B][D+1][V], draft [B][D][V]."""
+    tl = np.ascontiguousarray(target_logits, dtype=np.float32)
+    B, D1, V = tl.shape
+    D = D1 - 1
+    dl = None if D == 0 else np.ascontiguousarray(draft_logits, dtype=np.float32)
+    dt = None if D == 0 else np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    assert u.shape == (B, D + 1)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    pd = np.empty((B, max(D, 1)), np.float64)
+    qd = np.empty((B, max(D, 1)), np.float64)
+    row = np.empty(B, np.int32)
+    rc = lib().oracle_accept(_ptr(tl), _ptr(dl), _ptr(dt), _ptr(u), B, D, V,
+                             temperature, top_k, top_p, _ptr(acc), _ptr(nxt),
+                             _ptr(pd), _ptr(qd), _ptr(row))
+    if rc != 0:
+        raise ValueError(f"oracle_accept failed (rc={rc})")
+    return {"accepted_len": acc, "next_token": nxt, "p_draft": pd[:, :D],
+            "q_draft": qd[:, :D], "draw_row": row}

@@ -1,0 +1,432 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the speculative-decoding hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * source, header, table or constant with the HIP library, and the HIP
+ * library never calls it.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *   qmv       y[m][n] = sum_k x[m][k] * (s[n][k/G] * q[n][k] + b[n][k/G])
+ *             Affine group-quantized weights ("4-bit MLX", "affine-quantized
+ *             target"): mlxcel manual page "MTP and DFlash", section on the
+ *             draft block width; MTPLX announcement (molayo1419.me), section
+ *             "Layer 0: MLX Runtime" (small-M quantized matrix-vector kernel).
+ *             Plain definition: dequantize every weight, then an fp64 dot
+ *             product summed sequentially in k order.
+ *
+ *   probs     The sampling distribution at temperature T with top-k and
+ *             top-p: MTPLX announcement, "QWEN 3.6 27B @ 63 TPS" (T 0.6,
+ *             top_p 0.95, top_k 20; exact temperature sampling, not greedy).
+ *             Greedy when T <= 0 or top_k == 1: mlxcel manual, DFlash-family
+ *             drafter table (LFM2 DSpark row: sampling means T > 0 and
+ *             top_k != 1).
+ *
+ *   accept    Probability-ratio (Leviathan-Chen) acceptance per position in
+ *             fp32, residual (p - q)+ on the first rejection, bonus token
+ *             when every draft is accepted: MTPLX announcement, "Layer 2:
+ *             Speculative cycle (the hot loop)"; the same in the Japanese
+ *             re-post (ai-navigate-news), "Layer 2".  D accepted drafts give
+ *             D + 1 tokens and a full rejection still gives one:
+ *             savepearlharbor.com llama.cpp MTP article, section on how
+ *             speculative decoding works.
+ *
+ * Readings taken where the pages are silent are listed in the repository's
+ * design notes; each is restated at the function that takes it.
+ *
+ * Build: gcc -O2 -fPIC -shared -ffp-contract=off oracle.c -o liboracle.so -lm
+ * (no fused multiply-add, no fast-math: every operation is a plain IEEE op).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats, decoded from their IEEE definitions.                 */
+/* ------------------------------------------------------------------ */
+
+/* IEEE 754 binary16 bit pattern -> double (exact). */
+static double half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25); /* (1024 + f) * 2^(e - 15 - 10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 bit pattern -> double: bf16 is the upper half of a binary32. */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_half_to_double(uint16_t h) { return half_to_double(h); }
+double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+
+/* ------------------------------------------------------------------ */
+/* qmv                                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Quantized code of weight (n, k).
+ * W4: uint32 words, row-major [N][K/8]; element k sits in bits 4*(k%8)..+3
+ *     of word k/8 (little-endian nibble order within the word).
+ * W8: one byte per element, row-major [N][K]. */
+static unsigned code_at(int bits, const void *w, long K, long n, long k)
+{
+    if (bits == 4) {
+        const uint32_t *w4 = (const uint32_t *)w;
+        uint32_t word = w4[n * (K / 8) + k / 8];
+        return (word >> (4 * (k % 8))) & 0xFu;
+    }
+    return ((const uint8_t *)w)[n * K + k];
+}
+
+/* One output: y[m][n] = sum_k xhat[m][k] * what[n][k], sequential in k,
+ * with what = s * q + b decoded exactly in fp64 (s, b are fp16; q <= 255 so
+ * s * q + b is exact in a double).  Also returns sum_k |xhat * what|, the
+ * magnitude the tolerance of a near-zero output is scaled by. */
+static double qmv_one(int bits, const void *w, const uint16_t *scales,
+                      const uint16_t *biases, const uint16_t *x, long K, long G,
+                      long m, long n, double *abs_sum)
+{
+    long ng = K / G;
+    double acc = 0.0, mag = 0.0;
+    for (long k = 0; k < K; ++k) {
+        double s = half_to_double(scales[n * ng + k / G]);
+        double b = half_to_double(biases[n * ng + k / G]);
+        double q = (double)code_at(bits, w, K, n, k);
+        double what = s * q + b;
+        double xh = bf16_to_double(x[m * K + k]);
+        acc += xh * what;
+        mag += fabs(xh * what);
+    }
+    if (abs_sum)
+        *abs_sum = mag;
+    return acc;
+}
+
+/* Returns 0, or -1 on an argument error (nothing written). */
+static int qmv_args_ok(int bits, long M, long N, long K, long G)
+{
+    if (bits != 4 && bits != 8)
+        return 0;
+    if (M < 0 || N < 0 || K < 0 || G <= 0 || K % G != 0)
+        return 0;
+    if (bits == 4 && K % 8 != 0)
+        return 0;
+    return 1;
+}
+
+/* Rows n0..n1-1 of all M outputs: y[m][n - n0], y laid out [M][n1 - n0].
+ * abs_sum (nullable) gets sum_k |xhat * what| with the same layout. */
+int oracle_qmv(int bits, const void *w, const uint16_t *scales,
+               const uint16_t *biases, const uint16_t *x, long M, long N,
+               long K, long G, long n0, long n1, double *y, double *abs_sum)
+{
+    if (!qmv_args_ok(bits, M, N, K, G) || n0 < 0 || n1 > N || n0 > n1)
+        return -1;
+    long w_out = n1 - n0;
+    for (long m = 0; m < M; ++m)
+        for (long n = n0; n < n1; ++n) {
+            double mag;
+            y[m * w_out + (n - n0)] =
+                qmv_one(bits, w, scales, biases, x, K, G, m, n, &mag);
+            if (abs_sum)
+                abs_sum[m * w_out + (n - n0)] = mag;
+        }
+    return 0;
+}
+
+/* Selected outputs (m_idx[i], n_idx[i]) one by one, for sampled checks of
+ * shapes too large to compute whole. */
+int oracle_qmv_points(int bits, const void *w, const uint16_t *scales,
+                      const uint16_t *biases, const uint16_t *x, long M,
+                      long N, long K, long G, const long *m_idx,
+                      const long *n_idx, long count, double *y,
+                      double *abs_sum)
+{
+    if (!qmv_args_ok(bits, M, N, K, G))
+        return -1;
+    for (long i = 0; i < count; ++i) {
+        if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N)
+            return -1;
+    }
+    for (long i = 0; i < count; ++i) {
+        double mag;
+        y[i] = qmv_one(bits, w, scales, biases, x, K, G, m_idx[i], n_idx[i],
+                       &mag);
+        if (abs_sum)
+            abs_sum[i] = mag;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sampling distribution                                                */
+/* ------------------------------------------------------------------ */
+
+/* Rank order used by both filters: logit descending, then index ascending.
+ * Softmax is monotone in the logit, so this is the probability order with a
+ * fixed tie-break (lower index first). */
+static const float *g_rank_z; /* qsort has no context argument */
+static int rank_cmp(const void *pa, const void *pb)
+{
+    long a = *(const long *)pa, b = *(const long *)pb;
+    float za = g_rank_z[a], zb = g_rank_z[b];
+    if (za > zb)
+        return -1;
+    if (za < zb)
+        return 1;
+    return (a < b) ? -1 : (a > b);
+}
+
+/* A row is usable when it has no NaN, no +inf and at least one finite
+ * logit (-inf entries are allowed and get probability zero). */
+static int row_valid(const float *z, long V)
+{
+    int finite = 0;
+    for (long i = 0; i < V; ++i) {
+        if (isnan(z[i]) || (isinf(z[i]) && z[i] > 0))
+            return 0;
+        if (isfinite(z[i]))
+            finite = 1;
+    }
+    return finite;
+}
+
+/* Filtered sampling distribution of one logits row, in fp64.
+ *   1. Greedy when !(T > 0) or top_k == 1: one-hot at the first maximum.
+ *   2. pi = exp((z - max z) / T) / sum, with T taken at its fp32 value.
+ *   3. top-k when 1 <= top_k < V: keep the top_k tokens in rank order,
+ *      renormalize.
+ *   4. top-p when top_p < 1: over the kept tokens in rank order, keep the
+ *      shortest prefix whose mass reaches top_p (at least one token),
+ *      renormalize.
+ * The order temperature -> top-k -> top-p is a reading: the pages name the
+ * three settings together but never their order.
+ * Returns 0, or -1 for an invalid row (out untouched). */
+int oracle_probs(const float *z, long V, float T, int top_k, float top_p,
+                 double *out)
+{
+    if (V < 1 || !row_valid(z, V))
+        return -1;
+    long amax = 0;
+    for (long i = 1; i < V; ++i)
+        if (z[i] > z[amax])
+            amax = i;
+    if (!(T > 0.0f) || top_k == 1) {
+        for (long i = 0; i < V; ++i)
+            out[i] = 0.0;
+        out[amax] = 1.0;
+        return 0;
+    }
+
+    double t = (double)T, zmax = (double)z[amax], sum = 0.0;
+    for (long i = 0; i < V; ++i) {
+        out[i] = exp(((double)z[i] - zmax) / t);
+        sum += out[i];
+    }
+    for (long i = 0; i < V; ++i)
+        out[i] /= sum;
+
+    int use_k = (top_k >= 1 && (long)top_k < V);
+    int use_p = (top_p < 1.0f);
+    if (!use_k && !use_p)
+        return 0;
+
+    long *order = (long *)malloc(sizeof(long) * (size_t)V);
+    if (!order)
+        return -2;
+    for (long i = 0; i < V; ++i)
+        order[i] = i;
+    g_rank_z = z;
+    qsort(order, (size_t)V, sizeof(long), rank_cmp);
+
+    long kept = V;
+    if (use_k) {
+        kept = top_k;
+        double s = 0.0;
+        for (long j = 0; j < kept; ++j)
+            s += out[order[j]];
+        for (long j = kept; j < V; ++j)
+            out[order[j]] = 0.0;
+        for (long j = 0; j < kept; ++j)
+            out[order[j]] /= s;
+    }
+    if (use_p) {
+        double cum = 0.0, tp = (double)top_p;
+        long cut = kept;
+        for (long j = 0; j < kept; ++j) {
+            cum += out[order[j]];
+            if (cum >= tp) {
+                cut = j + 1;
+                break;
+            }
+        }
+        double s = 0.0;
+        for (long j = 0; j < cut; ++j)
+            s += out[order[j]];
+        for (long j = cut; j < kept; ++j)
+            out[order[j]] = 0.0;
+        for (long j = 0; j < cut; ++j)
+            out[order[j]] /= s;
+    }
+    free(order);
+    return 0;
+}
+
+/* Inverse CDF in vocabulary order: c_x = sum_{y <= x} w_y (fp64), and the
+ * draw is the first x with c_x > u * c_{V-1}.  The strict comparison means a
+ * zero-weight token is never drawn.  Returns -1 if the weights sum to zero. */
+static long inv_cdf(const double *wts, long V, float u)
+{
+    double total = 0.0;
+    for (long x = 0; x < V; ++x)
+        total += wts[x];
+    if (!(total > 0.0))
+        return -1;
+    double target = (double)u * total, c = 0.0;
+    long last_pos = -1;
+    for (long x = 0; x < V; ++x) {
+        c += wts[x];
+        if (wts[x] > 0.0)
+            last_pos = x;
+        if (c > target)
+            return x;
+    }
+    return last_pos; /* unreachable for u < 1; guards rounding at the end */
+}
+
+/* One token drawn from the filtered distribution of a row with uniform u. */
+long oracle_sample(const float *z, long V, float T, int top_k, float top_p,
+                   float u)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!p)
+        return -2;
+    long tok = -1;
+    if (oracle_probs(z, V, T, top_k, top_p, p) == 0)
+        tok = inv_cdf(p, V, u);
+    free(p);
+    return tok;
+}
+
+/* Many rows at once: tokens[r] drawn from row r with uniform u[r]. */
+int oracle_sample_rows(const float *z, long R, long V, float T, int top_k,
+                       float top_p, const float *u, int32_t *tokens)
+{
+    for (long r = 0; r < R; ++r)
+        tokens[r] = (int32_t)oracle_sample(z + r * V, V, T, top_k, top_p, u[r]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Acceptance                                                           */
+/* ------------------------------------------------------------------ */
+
+/* Verification of one block of B sequences.
+ *
+ * Per sequence b, with P_i = probs(target row i) for i = 0..D and
+ * Q_i = probs(draft row i) for i = 0..D-1:
+ *   for i = 0..D-1:
+ *       a_i = P_i(d_i) / Q_i(d_i), both rounded to fp32 and divided in fp32
+ *             (the pages decide each position in fp32); a_i = 0 when
+ *             P_i(d_i) = 0, +inf when only Q_i(d_i) = 0;
+ *       accept d_i iff u_i < a_i (fp32 compare), i.e. with probability
+ *             min(1, P_i(d_i) / Q_i(d_i));
+ *       on the first rejection: r = max(0, P_i - Q_i) (fp64; r = P_i if it
+ *             sums to zero), next = InvCDF(r, u_D), accepted = i, stop;
+ *   if all D are accepted: next = InvCDF(P_D, u_D), accepted = D (bonus).
+ * The emitted tokens are d_0..d_{accepted-1} followed by next.
+ *
+ * Uniform layout (a reading): u[b][0..D-1] are the D tests, u[b][D] is the
+ * single final draw.  Any row that is invalid, or a draft token outside
+ * [0, V), makes the whole sequence invalid: accepted = next = -1.
+ *
+ * p_draft / q_draft (nullable) receive P_i(d_i), Q_i(d_i) in fp64 for every
+ * i (NaN for an invalid sequence).  draw_row (nullable) receives, per
+ * sequence, the position whose distribution the final draw used (i for a
+ * residual at i, D for the bonus, -1 if invalid). */
+int oracle_accept(const float *target_logits, const float *draft_logits,
+                  const int32_t *draft_tokens, const float *uniforms, long B,
+                  long D, long V, float T, int top_k, float top_p,
+                  int32_t *accepted_len, int32_t *next_token, double *p_draft,
+                  double *q_draft, int32_t *draw_row)
+{
+    if (B < 0 || D < 0 || V < 1)
+        return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)((D + 1) * V));
+    double *Q = (double *)malloc(sizeof(double) * (size_t)((D > 0 ? D : 1) * V));
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!P || !Q || !r) {
+        free(P); free(Q); free(r);
+        return -2;
+    }
+    for (long b = 0; b < B; ++b) {
+        const float *tl = target_logits + b * (D + 1) * V;
+        const float *dl = draft_logits ? draft_logits + b * D * V : NULL;
+        const int32_t *dt = draft_tokens ? draft_tokens + b * D : NULL;
+        const float *u = uniforms + b * (D + 1);
+        int ok = 1;
+        for (long i = 0; i <= D && ok; ++i)
+            ok = (oracle_probs(tl + i * V, V, T, top_k, top_p, P + i * V) == 0);
+        for (long i = 0; i < D && ok; ++i)
+            ok = (oracle_probs(dl + i * V, V, T, top_k, top_p, Q + i * V) == 0);
+        for (long i = 0; i < D && ok; ++i)
+            ok = (dt[i] >= 0 && dt[i] < V);
+        if (!ok) {
+            accepted_len[b] = next_token[b] = -1;
+            if (draw_row)
+                draw_row[b] = -1;
+            for (long i = 0; i < D; ++i) {
+                if (p_draft) p_draft[b * D + i] = NAN;
+                if (q_draft) q_draft[b * D + i] = NAN;
+            }
+            continue;
+        }
+        for (long i = 0; i < D; ++i) {
+            if (p_draft) p_draft[b * D + i] = P[i * V + dt[i]];
+            if (q_draft) q_draft[b * D + i] = Q[i * V + dt[i]];
+        }
+        long i;
+        for (i = 0; i < D; ++i) {
+            float pf = (float)P[i * V + dt[i]];
+            float qf = (float)Q[i * V + dt[i]];
+            float a = (pf == 0.0f) ? 0.0f : pf / qf;
+            if (!(u[i] < a))
+                break;
+        }
+        long tok;
+        if (i < D) {
+            double tot = 0.0;
+            for (long x = 0; x < V; ++x) {
+                double d = P[i * V + x] - Q[i * V + x];
+                r[x] = d > 0.0 ? d : 0.0;
+                tot += r[x];
+            }
+            if (!(tot > 0.0))
+                memcpy(r, P + i * V, sizeof(double) * (size_t)V);
+            tok = inv_cdf(r, V, u[D]);
+        } else {
+            tok = inv_cdf(P + D * V, V, u[D]);
+        }
+        accepted_len[b] = (int32_t)i;
+        next_token[b] = (int32_t)tok;
+        if (draw_row)
+            draw_row[b] = (int32_t)i;
+    }
+    free(P); free(Q); free(r);
+    return 0;
+}

@@ -1,0 +1,40 @@
+"""Bandwidth roofline bookkeeping for the verify qmv and the acceptance step.
+
+Decoding is memory bound: the bound on tokens per second is the memory
+bandwidth divided by the bytes of parameters every token has to stream
+(savepearlharbor.com article on MTP in llama.cpp, section on the theoretical
+maximum of token generation, with its RTX 4060 Ti worked example).  The same
+bookkeeping gives a kernel's achieved fraction of HBM peak: algorithmic bytes
+per launch divided by the launch's duration, over the published peak.
+"""
+from __future__ import annotations
+
+#: MI355X published HBM3E peak, bytes/s.
+HBM_PEAK_BYTES_PER_S = 8.0e12
+
+
+def decode_bound_tokens_per_s(bandwidth_bytes_per_s: float, weight_bytes: float) -> float:
+    """Upper bound on decode tokens/s when every token streams all weights once."""
+    return bandwidth_bytes_per_s / weight_bytes
+
+
+def qmv_bytes(bits: int, M: int, N: int, K: int, group: int = 64) -> int:
+    """Bytes one qmv must move: packed weights, fp16 scales and biases, bf16
+    activations in, fp32 outputs out."""
+    return N * K * bits // 8 + N * (K // group) * 4 + M * K * 2 + M * N * 4
+
+
+def qmv_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def accept_bytes(B: int, D: int, V: int) -> int:
+    """Bytes the acceptance must move: every fp32 logit once (D + 1 target and
+    D draft rows per sequence), the draft tokens, D + 1 uniforms, two int32
+    outputs per sequence."""
+    return B * (2 * D + 1) * V * 4 + B * D * 4 + B * (D + 1) * 4 + B * 8
+
+
+def fraction_of_peak(nbytes: float, seconds: float,
+                     peak: float = HBM_PEAK_BYTES_PER_S) -> float:
+    return nbytes / seconds / peak
