@@ -1,0 +1,178 @@
+/*
+ * spec.h -- C ABI of the MI355X (gfx950) speculative-decoding hot path.
+ *
+ * Two parts, as described by the MTPLX announcement (molayo1419.me) and its
+ * Japanese re-post (ai-navigate-news):
+ *
+ *  1. The target model's verify pass over M = D + 1 positions (one per draft
+ *     token plus the bonus position), whose linear layers are small-M
+ *     group-quantized matrix-vector products ("Layer 0: MLX Runtime": the
+ *     stock quantized matrix-vector kernel stalls at M = 3..6; the verify
+ *     block over D + 1 positions is laid out in the savepearlharbor.com
+ *     llama.cpp MTP article, section on how speculative decoding works).
+ *  2. The probability-ratio (Leviathan-Chen) acceptance in fp32 per
+ *     position, with residual (p - q)+ resampling on the first rejection and
+ *     a bonus token when every draft is accepted ("Layer 2: Speculative
+ *     cycle (the hot loop)").
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are device memory owned by the caller; the library
+ *    never allocates, frees or retains them.  Layouts are row-major and
+ *    contiguous.
+ *  - Calls are asynchronous and stream ordered on `stream` (NULL = the
+ *    default stream).  The library keeps no mutable global state; calls on
+ *    different streams may run concurrently as long as they do not share a
+ *    workspace.
+ *  - Arguments are validated on the host first.  On failure the call returns
+ *    SPEC_ERR_INVALID / SPEC_ERR_UNSUPPORTED / SPEC_ERR_WORKSPACE and
+ *    enqueues nothing.  SPEC_ERR_DEVICE means a HIP call failed.
+ *  - Workspaces: the caller allocates `*_workspace_size(...)` bytes of device
+ *    memory, 256-byte aligned, and fills it with zeros once before its first
+ *    use.  Every call leaves the workspace's counters at zero again, so a
+ *    workspace can be reused by any later call of the same entry point whose
+ *    size query is not larger.  Calls sharing one workspace must be ordered
+ *    on one stream.
+ */
+#ifndef SPEC_H
+#define SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+    SPEC_OK = 0,
+    SPEC_ERR_INVALID = 1,     /* NULL pointer where one is required, size out of range */
+    SPEC_ERR_UNSUPPORTED = 2, /* well formed but not implemented (group size, M > 8, alignment) */
+    SPEC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than its size query */
+    SPEC_ERR_DEVICE = 4       /* a HIP runtime call failed */
+} spec_status;
+
+/* Static, NUL-terminated name of a status code ("SPEC_OK", ...). */
+const char *spec_status_str(spec_status s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int spec_version(void);
+
+/* ------------------------------------------------------------------ */
+/* Verify qmv: y = x * W^T with affine group-quantized W.               */
+/* ------------------------------------------------------------------ */
+/*
+ * Computes y[m][n] = sum_k x[m][k] * (s[n][k/G] * q[n][k] + b[n][k/G]) for
+ * m < M, n < N: every weight of the target's linear layer is streamed once
+ * and serves all M = D + 1 verify rows (affine group quantization as in the
+ * mlxcel manual's "MTP and DFlash" page, draft block width section; MTPLX
+ * "Layer 0: MLX Runtime").
+ *
+ *  w       W4: uint32 [N][K/8]; element k of row n is bits 4*(k%8)..4*(k%8)+3
+ *          of word k/8 (unsigned code 0..15).  16-byte aligned.
+ *          W8: uint8 [N][K]; one unsigned code 0..255 per byte.  16-byte aligned.
+ *  scales  fp16 bit patterns [N][K/G]  (s)
+ *  biases  fp16 bit patterns [N][K/G]  (b)
+ *  x       bf16 bit patterns [M][K], 16-byte aligned
+ *  y       fp32 [M][N], written (never read)
+ *  M       1..8 rows (0 is a no-op)
+ *  N       >= 0 output features
+ *  K       >= 0 input features, K % G == 0
+ *  G       group size; 64 is supported (SPEC_ERR_UNSUPPORTED otherwise)
+ *  workspace / workspace_bytes
+ *          device scratch of at least spec_qmv_workspace_size(M, N, K, G)
+ *          bytes (may be NULL when that size is 0).
+ *
+ * Results are deterministic, and row m of an M-row call is bitwise equal to
+ * the one-row call on x[m] (the reduction order does not depend on M).
+ */
+size_t spec_qmv_workspace_size(int M, int N, int K, int G);
+
+spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales,
+                        const uint16_t *biases, const uint16_t *x, float *y,
+                        int M, int N, int K, int G, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales,
+                        const uint16_t *biases, const uint16_t *x, float *y,
+                        int M, int N, int K, int G, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Sampling distribution                                                */
+/* ------------------------------------------------------------------ */
+/*
+ * The filtered sampling distribution of a logits row (MTPLX "QWEN 3.6 27B @
+ * 63 TPS": exact temperature sampling with top_p and top_k, not greedy-only;
+ * greedy when T <= 0 or top_k == 1 as in the mlxcel manual's DFlash-family
+ * drafter table):
+ *   greedy            one-hot at the first maximum logit;
+ *   otherwise         pi = softmax((z - max z) / T), then
+ *   top-k             if 1 <= top_k < V: keep the top_k logits (ties to the
+ *                     lower index), renormalize;
+ *   top-p             if top_p < 1: keep the shortest prefix, in the same rank
+ *                     order, whose mass reaches top_p (at least one token),
+ *                     renormalize.
+ * top_p < 1 requires 1 <= min(top_k, V) <= 256 (SPEC_ERR_UNSUPPORTED otherwise).
+ * temperature must be finite (SPEC_ERR_INVALID otherwise).
+ * A row holding NaN or +inf, or no finite logit, is invalid: its outputs are
+ * NaN (probs) or -1 (tokens).
+ */
+size_t spec_sample_workspace_size(int R, int V, int top_k);
+
+/* probs [R][V] fp32 = the distribution of each logits row [R][V]. */
+spec_status spec_sample_probs(const float *logits, int R, int V,
+                              float temperature, int top_k, float top_p,
+                              float *probs, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* tokens [R] int32 = inverse-CDF draw (vocabulary order, first token whose
+ * cumulative mass exceeds u * total) from each row with uniforms [R] in [0, 1). */
+spec_status spec_sample_tokens(const float *logits, int R, int V,
+                               float temperature, int top_k, float top_p,
+                               const float *uniforms, int32_t *tokens,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Verification: ratio acceptance, residual resampling, bonus token     */
+/* ------------------------------------------------------------------ */
+/*
+ * For each of B sequences with D drafts (MTPLX "Layer 2: Speculative cycle";
+ * savepearlharbor.com article, how verification works):
+ *   P_i = distribution of target row i (i = 0..D), Q_i = of draft row i
+ *   (i < D), both with the same temperature / top_k / top_p;
+ *   for i = 0..D-1: a_i = P_i(d_i) / Q_i(d_i) in fp32; accept d_i iff
+ *   u_i < a_i; at the first rejection draw the next token from
+ *   max(0, P_i - Q_i) with u_D (from P_i if that residual is all zero);
+ *   if all D are accepted draw the bonus token from P_D with u_D.
+ * The sequence emits draft_tokens[b][0..accepted_len-1] then next_token.
+ *
+ *  target_logits  fp32 [B][D+1][V]
+ *  draft_logits   fp32 [B][D][V] (may be NULL when D == 0)
+ *  draft_tokens   int32 [B][D]   (may be NULL when D == 0)
+ *  uniforms       fp32 [B][D+1] in [0, 1): tests u_0..u_{D-1}, final draw u_D
+ *  B >= 0, 0 <= D <= 15, 2 <= V < 2^24
+ *  accepted_len   int32 [B] out: 0..D
+ *  next_token     int32 [B] out
+ *  p_draft, q_draft  fp32 [B][D] out, nullable: P_i(d_i) and Q_i(d_i)
+ * A sequence with an invalid row or a draft token outside [0, V) gets
+ * accepted_len = next_token = -1 (and NaN in p_draft / q_draft); other
+ * sequences are unaffected.
+ */
+size_t spec_verify_accept_workspace(int B, int D, int V, int top_k);
+
+spec_status spec_verify_accept(const float *target_logits,
+                               const float *draft_logits,
+                               const int32_t *draft_tokens,
+                               const float *uniforms, int B, int D, int V,
+                               float temperature, int top_k, float top_p,
+                               int32_t *accepted_len, int32_t *next_token,
+                               float *p_draft, float *q_draft, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_H */

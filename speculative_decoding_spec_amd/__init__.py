@@ -1,0 +1,268 @@
+"""Python binding of libspec, the MI355X (gfx950) speculative-decoding hot path.
+
+Argument marshalling only: every function hands device pointers, sizes and
+torch's current HIP stream to the C ABI declared in ``include/spec.h`` and
+raises :class:`SpecError` on a non-OK status.  All arithmetic runs in the HIP
+kernels; there is no CPU fallback, and calling any function without the
+built library (``libspec.so`` next to this file) raises immediately.
+
+Names follow the C ABI:
+
+    spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv
+    spec_verify_accept               ratio acceptance + residual / bonus draw
+    spec_sample_probs                filtered sampling distribution
+    spec_sample_tokens               inverse-CDF draw from that distribution
+    spec_*_workspace_size            workspace queries
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspec.so")
+
+STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID", 2: "SPEC_ERR_UNSUPPORTED",
+          3: "SPEC_ERR_WORKSPACE", 4: "SPEC_ERR_DEVICE"}
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.status_name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{fn} returned {self.status_name}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is missing: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` "
+                "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.spec_status_str.argtypes = [i]
+        L.spec_status_str.restype = ctypes.c_char_p
+        L.spec_version.restype = i
+        L.spec_qmv_workspace_size.argtypes = [i, i, i, i]
+        L.spec_qmv_workspace_size.restype = sz
+        for name in ("spec_qmv_w4", "spec_qmv_w8"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
+            fn.restype = i
+        L.spec_verify_accept_workspace.argtypes = [i, i, i, i]
+        L.spec_verify_accept_workspace.restype = sz
+        L.spec_verify_accept.argtypes = [vp, vp, vp, vp, i, i, i, f, i, f, vp, vp,
+                                         vp, vp, vp, sz, vp]
+        L.spec_verify_accept.restype = i
+        L.spec_sample_workspace_size.argtypes = [i, i, i]
+        L.spec_sample_workspace_size.restype = sz
+        L.spec_sample_probs.argtypes = [vp, i, i, f, i, f, vp, vp, sz, vp]
+        L.spec_sample_probs.restype = i
+        L.spec_sample_tokens.argtypes = [vp, i, i, f, i, f, vp, vp, vp, sz, vp]
+        L.spec_sample_tokens.restype = i
+        _lib = L
+        return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SpecError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, dtype, name, device=None):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+# ---- workspaces: zero-filled device buffers cached per (device, purpose) ----
+_ws_cache: dict = {}
+
+
+def get_workspace(nbytes: int, device, key: str = "default"):
+    """A zero-filled, 256-byte aligned device buffer of at least nbytes.
+
+    The library leaves its counters at zero after every call, so one buffer
+    serves every later call on the same stream."""
+    import torch
+    if nbytes == 0:
+        return None
+    slot = (str(device), key)
+    buf = _ws_cache.get(slot)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        assert buf.data_ptr() % 256 == 0
+        _ws_cache[slot] = buf
+    return buf
+
+
+def spec_qmv_workspace_size(M: int, N: int, K: int, G: int = 64) -> int:
+    return int(lib().spec_qmv_workspace_size(M, N, K, G))
+
+
+def _qmv(name, bits, w, scales, biases, x, y, G, ws):
+    import torch
+    dev = x.device
+    _require(x, torch.bfloat16, "x", dev)
+    M, K = x.shape
+    wdt = torch.int32 if bits == 4 else torch.uint8
+    _require(w, wdt, "w", dev)
+    N = w.shape[0]
+    per_row = K // 8 if bits == 4 else K
+    if w.dim() != 2 or w.shape[1] != per_row:
+        raise ValueError(f"w must be [{N}][{per_row}] for K={K}")
+    _require(scales, torch.float16, "scales", dev)
+    _require(biases, torch.float16, "biases", dev)
+    if G <= 0 or K % G:
+        raise ValueError("K must be a multiple of G")
+    if tuple(scales.shape) != (N, K // G) or tuple(biases.shape) != (N, K // G):
+        raise ValueError(f"scales / biases must be [{N}][{K // G}]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _require(y, torch.float32, "y", dev)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [{M}][{N}]")
+    need = spec_qmv_workspace_size(M, N, K, G)
+    if ws is None:
+        ws = get_workspace(need, dev, "qmv")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = getattr(lib(), name)(_ptr(w), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y),
+                              M, N, K, G, _ptr(ws), nbytes, _stream(dev))
+    _check(name, st)
+    return y
+
+
+def spec_qmv_w4(w, scales, biases, x, y=None, G: int = 64, workspace=None):
+    """y[M][N] fp32 = x[M][K] (bf16) times the dequantized W4 matrix.
+
+    w: int32 [N][K/8] packed nibbles (element k at bits 4*(k%8) of word k/8);
+    scales, biases: fp16 [N][K/G]."""
+    return _qmv("spec_qmv_w4", 4, w, scales, biases, x, y, G, workspace)
+
+
+def spec_qmv_w8(w, scales, biases, x, y=None, G: int = 64, workspace=None):
+    """As spec_qmv_w4 with w: uint8 [N][K] codes."""
+    return _qmv("spec_qmv_w8", 8, w, scales, biases, x, y, G, workspace)
+
+
+def spec_verify_accept_workspace(B: int, D: int, V: int, top_k: int) -> int:
+    return int(lib().spec_verify_accept_workspace(B, D, V, top_k))
+
+
+def spec_verify_accept(target_logits, draft_logits, draft_tokens, uniforms,
+                       temperature: float, top_k: int = 0, top_p: float = 1.0,
+                       with_probs: bool = False, out=None, workspace=None):
+    """Acceptance for B sequences.  target_logits fp32 [B][D+1][V],
+    draft_logits fp32 [B][D][V], draft_tokens int32 [B][D], uniforms fp32
+    [B][D+1].  Returns (accepted_len, next_token) int32 [B], plus
+    (p_draft, q_draft) fp32 [B][D] when with_probs."""
+    import torch
+    dev = target_logits.device
+    _require(target_logits, torch.float32, "target_logits", dev)
+    B, D1, V = target_logits.shape
+    D = D1 - 1
+    if D > 0:
+        _require(draft_logits, torch.float32, "draft_logits", dev)
+        _require(draft_tokens, torch.int32, "draft_tokens", dev)
+        if tuple(draft_logits.shape) != (B, D, V) or tuple(draft_tokens.shape) != (B, D):
+            raise ValueError("draft_logits must be [B][D][V] and draft_tokens [B][D]")
+    _require(uniforms, torch.float32, "uniforms", dev)
+    if tuple(uniforms.shape) != (B, D + 1):
+        raise ValueError("uniforms must be [B][D+1]")
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        pd = torch.empty((B, D), dtype=torch.float32, device=dev) if with_probs else None
+        qd = torch.empty((B, D), dtype=torch.float32, device=dev) if with_probs else None
+    else:
+        acc, nxt, pd, qd = out
+    need = spec_verify_accept_workspace(B, D, V, top_k)
+    if workspace is None:
+        workspace = get_workspace(need, dev, "accept")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_verify_accept(
+        _ptr(target_logits), _ptr(draft_logits if D > 0 else None),
+        _ptr(draft_tokens if D > 0 else None), _ptr(uniforms), B, D, V,
+        float(temperature), int(top_k), float(top_p), _ptr(acc), _ptr(nxt),
+        _ptr(pd), _ptr(qd), _ptr(workspace), nbytes, _stream(dev))
+    _check("spec_verify_accept", st)
+    return (acc, nxt, pd, qd) if with_probs else (acc, nxt)
+
+
+def spec_sample_workspace_size(R: int, V: int, top_k: int) -> int:
+    return int(lib().spec_sample_workspace_size(R, V, top_k))
+
+
+def spec_sample_probs(logits, temperature: float, top_k: int = 0,
+                      top_p: float = 1.0, probs=None, workspace=None):
+    """probs fp32 [R][V] = filtered distribution of each row of logits [R][V]."""
+    import torch
+    dev = logits.device
+    _require(logits, torch.float32, "logits", dev)
+    R, V = logits.shape
+    if probs is None:
+        probs = torch.empty((R, V), dtype=torch.float32, device=dev)
+    _require(probs, torch.float32, "probs", dev)
+    need = spec_sample_workspace_size(R, V, top_k)
+    if workspace is None:
+        workspace = get_workspace(need, dev, "sample")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_sample_probs(_ptr(logits), R, V, float(temperature), int(top_k),
+                                 float(top_p), _ptr(probs), _ptr(workspace), nbytes,
+                                 _stream(dev))
+    _check("spec_sample_probs", st)
+    return probs
+
+
+def spec_sample_tokens(logits, uniforms, temperature: float, top_k: int = 0,
+                       top_p: float = 1.0, tokens=None, workspace=None):
+    """tokens int32 [R]: one inverse-CDF draw per row of logits [R][V]."""
+    import torch
+    dev = logits.device
+    _require(logits, torch.float32, "logits", dev)
+    R, V = logits.shape
+    _require(uniforms, torch.float32, "uniforms", dev)
+    if uniforms.numel() != R:
+        raise ValueError("uniforms must hold one value per row")
+    if tokens is None:
+        tokens = torch.empty(R, dtype=torch.int32, device=dev)
+    need = spec_sample_workspace_size(R, V, top_k)
+    if workspace is None:
+        workspace = get_workspace(need, dev, "sample")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_sample_tokens(_ptr(logits), R, V, float(temperature), int(top_k),
+                                  float(top_p), _ptr(uniforms), _ptr(tokens),
+                                  _ptr(workspace), nbytes, _stream(dev))
+    _check("spec_sample_tokens", st)
+    return tokens

@@ -1,0 +1,217 @@
+// C ABI of libspec: host-side validation, then kernel launches.  Every
+// argument check runs before anything is enqueued.  Declarations and the
+// meaning of every argument: include/spec.h.
+#include "../../include/spec.h"
+#include "spec_internal.h"
+
+#include <cmath>
+
+namespace {
+
+constexpr int kMaxM = 8;
+constexpr int kMaxD = 15;
+constexpr int kMaxCand = 256;
+constexpr int kMaxV = (1 << 24) - 1;
+constexpr size_t kMaxRows = (size_t)1 << 23;  // grid x of 256-thread workgroups
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+spec_status qmv_common(int bits, const void *w, const uint16_t *scales,
+                       const uint16_t *biases, const uint16_t *x, float *y,
+                       int M, int N, int K, int G, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || G <= 0)
+        return SPEC_ERR_INVALID;
+    if (K % G != 0)
+        return SPEC_ERR_INVALID;
+    if (G != 64)
+        return SPEC_ERR_UNSUPPORTED;
+    if (M > kMaxM)
+        return SPEC_ERR_UNSUPPORTED;
+    if ((size_t)N * (size_t)(K / 8) > (size_t)1 << 40)
+        return SPEC_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return SPEC_OK;
+    if (!y || (K > 0 && (!w || !scales || !biases || !x)))
+        return SPEC_ERR_INVALID;
+    if (K > 0 && (!aligned16(w) || !aligned16(x)))
+        return SPEC_ERR_UNSUPPORTED;
+    if (!aligned4(y))
+        return SPEC_ERR_INVALID;
+    const spec::QmvPlan plan = spec::qmv_plan(N, K);
+    const size_t need = K > 0 ? spec::qmv_workspace_bytes(plan, M, N) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return SPEC_ERR_WORKSPACE;
+    if (spec::launch_qmv(bits, w, scales, biases, x, y, M, N, K, plan, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+// Shared checks of the sampling settings.
+spec_status check_sampling(int V, float temperature, int top_k, float top_p) {
+    if (V < 2 || V > kMaxV)
+        return V < 2 ? SPEC_ERR_INVALID : SPEC_ERR_UNSUPPORTED;
+    if (!std::isfinite(temperature) || std::isnan(top_p))
+        return SPEC_ERR_INVALID;
+    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
+    if (sp.candidates && sp.k_eff > kMaxCand)
+        return SPEC_ERR_UNSUPPORTED;
+    return SPEC_OK;
+}
+
+bool ws_ok(const void *ws, size_t have, size_t need) {
+    return need == 0 || (ws && have >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0);
+}
+
+} // namespace
+
+extern "C" {
+
+const char *spec_status_str(spec_status s) {
+    switch (s) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID: return "SPEC_ERR_INVALID";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
+    case SPEC_ERR_DEVICE: return "SPEC_ERR_DEVICE";
+    }
+    return "SPEC_ERR_UNKNOWN";
+}
+
+int spec_version(void) { return 100; }
+
+size_t spec_qmv_workspace_size(int M, int N, int K, int G) {
+    if (M <= 0 || N <= 0 || K <= 0 || G != 64 || K % G != 0 || M > kMaxM)
+        return 0;
+    return spec::qmv_workspace_bytes(spec::qmv_plan(N, K), M, N);
+}
+
+spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales,
+                        const uint16_t *biases, const uint16_t *x, float *y,
+                        int M, int N, int K, int G, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    return qmv_common(4, w, scales, biases, x, y, M, N, K, G, workspace,
+                      workspace_bytes, stream);
+}
+
+spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales,
+                        const uint16_t *biases, const uint16_t *x, float *y,
+                        int M, int N, int K, int G, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    return qmv_common(8, w, scales, biases, x, y, M, N, K, G, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t spec_verify_accept_workspace(int B, int D, int V, int top_k) {
+    if (B <= 0 || D < 0 || D > kMaxD || V < 2 || V > kMaxV)
+        return 0;
+    // Size for the larger of the two modes, so any temperature / top_p works.
+    const int k = (top_k >= 1 && top_k < V) ? top_k : 1;
+    const int kc = std::min(std::max(k, 1), kMaxCand);
+    const spec::AcceptPlan a = spec::accept_plan(B, D, V, kc, true);
+    const spec::AcceptPlan f = spec::accept_plan(B, D, V, 0, false);
+    const int kv = std::min(V, kMaxCand);  // top_p over a small full vocabulary
+    const spec::AcceptPlan v = spec::accept_plan(B, D, V, kv, true);
+    return std::max(a.ws_bytes, std::max(f.ws_bytes, V <= kMaxCand ? v.ws_bytes : 0));
+}
+
+spec_status spec_verify_accept(const float *target_logits,
+                               const float *draft_logits,
+                               const int32_t *draft_tokens,
+                               const float *uniforms, int B, int D, int V,
+                               float temperature, int top_k, float top_p,
+                               int32_t *accepted_len, int32_t *next_token,
+                               float *p_draft, float *q_draft, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || D < 0)
+        return SPEC_ERR_INVALID;
+    if (D > kMaxD)
+        return SPEC_ERR_UNSUPPORTED;
+    const spec_status s = check_sampling(V, temperature, top_k, top_p);
+    if (s != SPEC_OK)
+        return s;
+    if (B == 0)
+        return SPEC_OK;
+    if (!target_logits || !uniforms || !accepted_len || !next_token)
+        return SPEC_ERR_INVALID;
+    if (D > 0 && (!draft_logits || !draft_tokens))
+        return SPEC_ERR_INVALID;
+    if (!aligned4(target_logits) || (D > 0 && !aligned4(draft_logits)))
+        return SPEC_ERR_INVALID;
+    if (((V & 3) == 0) && (!aligned16(target_logits) || (D > 0 && !aligned16(draft_logits))))
+        return SPEC_ERR_UNSUPPORTED;
+    if ((size_t)B * (2 * D + 1) > kMaxRows)
+        return SPEC_ERR_UNSUPPORTED;
+    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
+    const spec::AcceptPlan plan = spec::accept_plan(B, D, V, sp.k_eff, sp.candidates);
+    if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes))
+        return SPEC_ERR_WORKSPACE;
+    if (spec::launch_accept(target_logits, draft_logits, draft_tokens, uniforms,
+                            plan, sp, accepted_len, next_token, p_draft,
+                            q_draft, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+size_t spec_sample_workspace_size(int R, int V, int top_k) {
+    return spec_verify_accept_workspace(R, 0, V, top_k);
+}
+
+spec_status spec_sample_probs(const float *logits, int R, int V,
+                              float temperature, int top_k, float top_p,
+                              float *probs, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    if (R < 0)
+        return SPEC_ERR_INVALID;
+    const spec_status s = check_sampling(V, temperature, top_k, top_p);
+    if (s != SPEC_OK)
+        return s;
+    if (R == 0)
+        return SPEC_OK;
+    if ((size_t)R > kMaxRows)
+        return SPEC_ERR_UNSUPPORTED;
+    if (!logits || !probs || !aligned4(logits) || !aligned4(probs))
+        return SPEC_ERR_INVALID;
+    if (((V & 3) == 0) && !aligned16(logits))
+        return SPEC_ERR_UNSUPPORTED;
+    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
+    const spec::AcceptPlan plan = spec::accept_plan(R, 0, V, sp.k_eff, sp.candidates);
+    if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes))
+        return SPEC_ERR_WORKSPACE;
+    if (spec::launch_probs(logits, plan, sp, probs, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_sample_tokens(const float *logits, int R, int V,
+                               float temperature, int top_k, float top_p,
+                               const float *uniforms, int32_t *tokens,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (R < 0)
+        return SPEC_ERR_INVALID;
+    const spec_status s = check_sampling(V, temperature, top_k, top_p);
+    if (s != SPEC_OK)
+        return s;
+    if (R == 0)
+        return SPEC_OK;
+    if ((size_t)R > kMaxRows)
+        return SPEC_ERR_UNSUPPORTED;
+    if (!logits || !uniforms || !tokens || !aligned4(logits))
+        return SPEC_ERR_INVALID;
+    if (((V & 3) == 0) && !aligned16(logits))
+        return SPEC_ERR_UNSUPPORTED;
+    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
+    const spec::AcceptPlan plan = spec::accept_plan(R, 0, V, sp.k_eff, sp.candidates);
+    if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes))
+        return SPEC_ERR_WORKSPACE;
+    // D = 0: every sequence is one target row and takes the bonus draw.
+    if (spec::launch_accept(logits, nullptr, nullptr, uniforms, plan, sp,
+                            nullptr, tokens, nullptr, nullptr, workspace,
+                            stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+} // extern "C"

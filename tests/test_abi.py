@@ -1,0 +1,127 @@
+"""The C ABI: the library loads, exports every function include/spec.h
+declares, and rejects bad arguments on the host before touching a GPU.
+
+Validation runs before any HIP call, so these checks need no device: the
+pointers below are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_spec_amd as spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = ctypes.c_void_p(0x10000)      # fake, 256-byte aligned device address
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)    # 4-byte aligned, not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return spec.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"libspec.so does not export {n}"
+    out = os.popen(f"nm -D --defined-only {spec.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_status_strings(L):
+    assert L.spec_status_str(0) == b"SPEC_OK"
+    assert L.spec_status_str(3) == b"SPEC_ERR_WORKSPACE"
+    assert L.spec_version() >= 100
+
+
+def qmv(L, fn="spec_qmv_w4", w=P, s=P, b=P, x=P, y=P, M=4, N=64, K=128, G=64,
+        ws=None, nbytes=0):
+    return getattr(L, fn)(w, s, b, x, y, M, N, K, G, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("fn", ["spec_qmv_w4", "spec_qmv_w8"])
+def test_qmv_validation(L, fn):
+    assert qmv(L, fn, M=-1) == INVALID
+    assert qmv(L, fn, K=100) == INVALID            # K % G != 0
+    assert qmv(L, fn, G=32, K=128) == UNSUPPORTED
+    assert qmv(L, fn, M=9) == UNSUPPORTED
+    assert qmv(L, fn, w=None) == INVALID
+    assert qmv(L, fn, x=None) == INVALID
+    assert qmv(L, fn, y=None) == INVALID
+    assert qmv(L, fn, w=MIS) == UNSUPPORTED
+    assert qmv(L, fn, x=MIS) == UNSUPPORTED
+    assert qmv(L, fn, M=0) == OK                   # no-op, nothing enqueued
+    assert qmv(L, fn, N=0) == OK
+
+
+def test_qmv_workspace_rules(L):
+    M, N, K = 8, 1024, 5120                        # small N: K is split
+    need = L.spec_qmv_workspace_size(M, N, K, 64)
+    assert need > 0
+    assert qmv(L, M=M, N=N, K=K, ws=None, nbytes=0) == WORKSPACE
+    assert qmv(L, M=M, N=N, K=K, ws=P2, nbytes=need - 1) == WORKSPACE
+    assert qmv(L, M=M, N=N, K=K, ws=ctypes.c_void_p(0x20010), nbytes=need) == WORKSPACE
+    assert L.spec_qmv_workspace_size(8, 151936, 64, 64) == 0  # one step: no split
+
+
+def accept(L, t=P, d=P, tok=P, u=P, B=2, D=3, V=1024, T=0.6, k=0, p=1.0,
+           acc=P, nxt=P, ws=None, nbytes=None):
+    if nbytes is None:
+        nbytes = L.spec_verify_accept_workspace(B, D, V, k)
+        ws = ws or P2
+    return L.spec_verify_accept(t, d, tok, u, B, D, V, ctypes.c_float(T), k,
+                                ctypes.c_float(p), acc, nxt, None, None, ws,
+                                nbytes, None)
+
+
+def test_accept_validation(L):
+    assert accept(L, B=-1) == INVALID
+    assert accept(L, D=16) == UNSUPPORTED
+    assert accept(L, V=1) == INVALID
+    assert accept(L, T=float("nan")) == INVALID
+    assert accept(L, T=float("inf")) == INVALID
+    assert accept(L, p=float("nan")) == INVALID
+    assert accept(L, k=0, p=0.9) == UNSUPPORTED    # top-p over 1024 tokens
+    assert accept(L, k=300, p=1.0) == UNSUPPORTED  # top-k above 256
+    assert accept(L, t=None) == INVALID
+    assert accept(L, d=None) == INVALID
+    assert accept(L, tok=None) == INVALID
+    assert accept(L, u=None) == INVALID
+    assert accept(L, acc=None) == INVALID
+    assert accept(L, t=MIS) == UNSUPPORTED         # V % 4 == 0 needs 16 B rows
+    assert accept(L, ws=None, nbytes=0) == WORKSPACE
+    assert accept(L, B=0) == OK
+    need = L.spec_verify_accept_workspace(4, 5, 151936, 20)
+    assert accept(L, B=4, D=5, V=151936, k=20, p=0.95, ws=P2, nbytes=need - 1) == WORKSPACE
+    # D = 0 needs no draft arrays
+    assert accept(L, d=None, tok=None, D=0, B=0) == OK
+
+
+def test_sample_validation(L):
+    f = ctypes.c_float
+    need = L.spec_sample_workspace_size(4, 1000, 20)
+    assert L.spec_sample_probs(P, 4, 1000, f(0.6), 20, f(0.9), P, None, 0, None) == WORKSPACE
+    assert L.spec_sample_probs(None, 4, 1000, f(0.6), 20, f(0.9), P, P2, need, None) == INVALID
+    assert L.spec_sample_probs(P, 4, 1, f(0.6), 20, f(0.9), P, P2, need, None) == INVALID
+    assert L.spec_sample_tokens(P, 4, 1000, f(0.6), 0, f(0.5), P, P, P2, need, None) == UNSUPPORTED
+    assert L.spec_sample_tokens(P, 0, 1000, f(0.6), 20, f(0.9), P, P, P2, need, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(spec, "_lib", None)
+    monkeypatch.setattr(spec, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        spec.lib()

@@ -1,0 +1,242 @@
+"""GPU parity of sampling and verification against the fp64 oracle, through
+the C ABI, plus the rule's invariants re-run on the GPU.
+
+Workloads: B=1 D=3 V=32768 T=0.6 (draft logits N(0, 2), target = draft +
+N(0, 0.5)); the batched stress B=256 D=5 V=151936 T=0.6 with residual and
+bonus draws; the LM-head case D=5 V=151936 T=0.6 top_k=20 top_p=0.95 whose
+target logits are the oracle's W4 head output; greedy and small shapes."""
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_spec_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def T_(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gpu_accept(t, d, toks, u, T, k, p, dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    D = t.shape[1] - 1
+    acc, nxt, pd, qd = spec.spec_verify_accept(
+        T_(t, dev), T_(d, dev) if D else None, T_(toks, dev) if D else None,
+        T_(u, dev), T, k, p, with_probs=True)
+    torch.cuda.synchronize()
+    return {"accepted_len": acc.cpu().numpy(), "next_token": nxt.cpu().numpy(),
+            "p_draft": pd.cpu().numpy().astype(np.float64),
+            "q_draft": qd.cpu().numpy().astype(np.float64)}
+
+
+def draft_tokens(d, T, k, p, cfg):
+    B, D, V = d.shape
+    ud = synth.uniforms(cfg, synth.U_DRAFT, B * D)
+    return oracle.sample_rows(d.reshape(B * D, V), T, k, p, ud).reshape(B, D)
+
+
+def check(t, d, toks, u, T, k, p, dev, max_tie_frac=0.01):
+    got = gpu_accept(t, d, toks, u, T, k, p, dev)
+    ref = parity.oracle_accept_threaded(t, d, toks, u, T, k, p)
+    res = parity.compare_accept(got, ref, t, d, toks, u, T, k, p)
+    B = t.shape[0]
+    print(f"B={B} D={t.shape[1]-1} V={t.shape[2]} T={T} k={k} p={p}: exact={res['exact']} "
+          f"ties={res['ties']} bad={len(res['bad'])} prob_err={res['prob_err']:.2e} "
+          f"accepted_mean={ref['accepted_len'].mean():.3f}", flush=True)
+    assert not res["bad"], res["bad"][:5]
+    assert res["prob_err"] <= 1e-5
+    assert res["ties"] <= max(1, int(max_tie_frac * B))
+    return got, ref
+
+
+# --------------------------------------------------------------- probs ----
+@pytest.mark.parametrize("R,V,T,k,p", [
+    (7, 32768, 0.6, 0, 1.0),        # unfiltered, 1024-multiple vocab
+    (5, 151936, 0.6, 20, 0.95),     # LM-head settings
+    (3, 151936, 0.6, 256, 0.5),     # widest candidate set
+    (4, 1000, 1.0, 0, 1.0),         # vocab not a multiple of 4 blocks
+    (4, 999, 0.8, 10, 1.0),         # odd vocab, scalar loads
+    (3, 200, 0.7, 0, 0.9),          # top-p over a small full vocabulary
+    (4, 5000, 0.0, 0, 1.0),         # greedy (T = 0)
+    (4, 5000, 0.9, 1, 1.0),         # greedy (k = 1)
+])
+def test_sample_probs(dev, R, V, T, k, p):
+    import speculative_decoding_spec_amd as spec
+    z = synth.rng(70 + V, synth.DRAFT).normal(0, 2, size=(R, V)).astype(np.float32)
+    got = spec.spec_sample_probs(T_(z, dev), T, k, p).cpu().numpy()
+    for r in range(R):
+        ref = oracle.probs(z[r], T, k, p)
+        if parity.top_p_tie(z[r], T, k, p):
+            continue
+        assert np.abs(got[r] - ref).max() <= 1e-5, r
+        assert np.array_equal(got[r] > 0, ref > 0), r
+
+
+def test_sample_probs_ties_and_invalid_rows(dev):
+    import speculative_decoding_spec_amd as spec
+    V = 4096
+    z = np.zeros((4, V), np.float32)
+    z[0, [5, 9, 700]] = 3.0                 # tied maxima: top-k keeps lower index
+    z[1, :] = -np.inf
+    z[1, 17] = 0.0                          # one finite logit
+    z[2, 33] = np.nan                       # invalid
+    z[3, :] = -np.inf                       # invalid (no finite logit)
+    for k in (2, 0):
+        got = spec.spec_sample_probs(T_(z, dev), 0.6, k, 1.0).cpu().numpy()
+        for r in (0, 1):
+            assert np.abs(got[r] - oracle.probs(z[r], 0.6, k, 1.0)).max() <= 1e-5
+        assert np.all(np.isnan(got[2])) and np.all(np.isnan(got[3]))
+
+
+@pytest.mark.parametrize("V,T,k,p", [(32768, 0.6, 0, 1.0), (151936, 0.6, 20, 0.95), (999, 1.0, 0, 1.0)])
+def test_sample_tokens(dev, V, T, k, p):
+    import speculative_decoding_spec_amd as spec
+    R = 512
+    z = synth.rng(80 + V, synth.DRAFT).normal(0, 2, size=(R, V)).astype(np.float32)
+    u = synth.uniforms(80 + V, synth.U_ACCEPT, R)
+    got = spec.spec_sample_tokens(T_(z, dev), T_(u, dev), T, k, p).cpu().numpy()
+    ref = oracle.sample_rows(z, T, k, p, u)
+    ties = 0
+    for r in np.nonzero(got != ref)[0]:
+        w = oracle.probs(z[r], T, k, p)
+        assert parity.top_p_tie(z[r], T, k, p) or parity.draw_tie(w, u[r], int(got[r]), int(ref[r])), r
+        ties += 1
+    assert ties <= 5
+
+
+# -------------------------------------------------------------- accept ----
+def test_single_sequence_depth3_vocab32k(dev):
+    t, d = synth.logits_pair(0, 1, 3, 32768)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 0)
+    u = synth.uniforms(0, synth.U_ACCEPT, (1, 4))
+    check(t, d, toks, u, 0.6, 0, 1.0, dev)
+
+
+def test_batched_depth3_vocab32k(dev):
+    B, D, V = 256, 3, 32768
+    t, d = synth.logits_pair(100, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 100)
+    u = synth.uniforms(100, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 0.6, 0, 1.0, dev)
+
+
+def test_batched_stress_depth5_vocab152k(dev):
+    B, D, V = 256, 5, 151936
+    t, d = synth.logits_pair(4, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 4)
+    u = synth.uniforms(4, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    L = ref["accepted_len"]
+    assert (L < D).sum() > 0 and (L == D).sum() > 0   # both residual and bonus draws ran
+
+
+def test_lm_head_logits_top_k_top_p(dev):
+    # Target logits = the oracle's W4 LM head (5120 -> 151936) on M = 6 rows;
+    # draft logits = target - N(0, 0.5).
+    N, K, M = 151936, 5120, 6
+    w, s, b = synth.qweights(2, 4, N, K, 64)
+    x = synth.activations(2, M, K)
+    y, _ = parity.oracle_qmv_threaded(4, w, s, b, x, 64)
+    t = y.astype(np.float32)[None]                       # [1][6][V]
+    noise = synth.rng(2, synth.NOISE).normal(0, 0.5, size=(1, M - 1, N)).astype(np.float32)
+    d = (t[:, :M - 1] - noise).astype(np.float32)
+    toks = draft_tokens(d, 0.6, 20, 0.95, 2)
+    u = synth.uniforms(2, synth.U_ACCEPT, (1, M))
+    check(t, d, toks, u, 0.6, 20, 0.95, dev)
+
+
+@pytest.mark.parametrize("k,p", [(20, 0.95), (5, 1.0), (0, 1.0)])
+def test_batched_filters_small_vocab(dev, k, p):
+    B, D, V = 300, 4, 3000
+    t, d = synth.logits_pair(200 + k, B, D, V)
+    toks = draft_tokens(d, 0.8, k, p, 200 + k)
+    u = synth.uniforms(200 + k, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 0.8, k, p, dev)
+
+
+def test_identical_distributions_accept_all(dev):
+    B, D, V = 64, 5, 32768
+    t, _ = synth.logits_pair(300, B, D, V)
+    d = np.ascontiguousarray(t[:, :D])
+    toks = draft_tokens(d, 0.6, 0, 1.0, 300)
+    u = synth.uniforms(300, synth.U_ACCEPT, (B, D + 1))
+    got = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert np.all(got["accepted_len"] == D)
+
+
+def test_greedy_is_sample_and_match(dev):
+    B, D, V = 128, 5, 4096
+    rng = np.random.default_rng(31)
+    t = rng.normal(0, 3, size=(B, D + 1, V)).astype(np.float32)
+    d = t[:, :D].copy()
+    flip = rng.random((B, D)) < 0.3
+    d[flip] = rng.normal(0, 3, size=(int(flip.sum()), V)).astype(np.float32)
+    toks = np.argmax(d, axis=2).astype(np.int32)
+    u = synth.uniforms(31, synth.U_ACCEPT, (B, D + 1))
+    for k, T in [(1, 0.6), (0, 0.0)]:
+        got = gpu_accept(t, d, toks, u, T, k, 1.0, dev)
+        tgt = np.argmax(t, axis=2)
+        for b in range(B):
+            L = int(got["accepted_len"][b])
+            ref_L = next((i for i in range(D) if tgt[b, i] != toks[b, i]), D)
+            assert L == ref_L
+            assert got["next_token"][b] == tgt[b, L]
+
+
+def test_emitted_tokens_follow_the_target_chi_square(dev):
+    # 10^6 sequences of vocab 8 on the GPU; drafts drawn from Q by the oracle.
+    B, D, V = 1_000_000, 3, 8
+    t1, d1 = synth.logits_pair(41, 1, D, V)
+    P = np.stack([oracle.probs(t1[0, i], 0.6) for i in range(D + 1)])
+    t = np.ascontiguousarray(np.broadcast_to(t1, (B, D + 1, V)))
+    d = np.ascontiguousarray(np.broadcast_to(d1, (B, D, V)))
+    toks = draft_tokens(d, 0.6, 0, 1.0, 41)
+    u = synth.uniforms(41, synth.U_ACCEPT, (B, D + 1))
+    got = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    L, nxt = got["accepted_len"], got["next_token"]
+    for i in range(D + 1):
+        reach = L >= i
+        tok_i = np.where(L[reach] > i, toks[reach, min(i, D - 1)], nxt[reach])
+        obs = np.bincount(tok_i, minlength=V)
+        exp = P[i] * reach.sum()
+        chi2 = float(((obs - exp) ** 2 / exp).sum())
+        assert chi2 < 24.32, (i, chi2)
+
+
+def test_invalid_sequences(dev):
+    B, D, V = 6, 2, 4096
+    t, d = synth.logits_pair(500, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 500)
+    t[1, 2, 5] = np.nan
+    toks[2, 1] = V
+    toks[3, 0] = -1
+    d[4, 0, :] = -np.inf
+    t[5, 0, 9] = np.inf
+    u = synth.uniforms(500, synth.U_ACCEPT, (B, D + 1))
+    got = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    ref = oracle.accept(t, d, toks, u, 0.6)
+    assert got["accepted_len"].tolist() == ref["accepted_len"].tolist()
+    assert got["next_token"][1:].tolist() == [-1] * 5
+    assert got["next_token"][0] == ref["next_token"][0]
+
+
+def test_determinism(dev):
+    B, D, V = 64, 5, 151936
+    t, d = synth.logits_pair(600, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 600)
+    u = synth.uniforms(600, synth.U_ACCEPT, (B, D + 1))
+    a = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    b = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
