@@ -179,17 +179,22 @@ int oracle_qmv_points(int bits, const void *w, const uint16_t *scales,
 
 /* Rank order used by both filters: logit descending, then index ascending.
  * Softmax is monotone in the logit, so this is the probability order with a
- * fixed tie-break (lower index first). */
-static const float *g_rank_z; /* qsort has no context argument */
+ * fixed tie-break (lower index first).  Records carry their own logit, so
+ * sorting needs no shared state and the oracle is safe to call from several
+ * threads at once. */
+typedef struct {
+    float z;
+    long idx;
+} ranked;
+
 static int rank_cmp(const void *pa, const void *pb)
 {
-    long a = *(const long *)pa, b = *(const long *)pb;
-    float za = g_rank_z[a], zb = g_rank_z[b];
-    if (za > zb)
+    const ranked *a = (const ranked *)pa, *b = (const ranked *)pb;
+    if (a->z > b->z)
         return -1;
-    if (za < zb)
+    if (a->z < b->z)
         return 1;
-    return (a < b) ? -1 : (a > b);
+    return (a->idx < b->idx) ? -1 : (a->idx > b->idx);
 }
 
 /* A row is usable when it has no NaN, no +inf and at least one finite
@@ -246,13 +251,21 @@ int oracle_probs(const float *z, long V, float T, int top_k, float top_p,
     if (!use_k && !use_p)
         return 0;
 
+    ranked *rec = (ranked *)malloc(sizeof(ranked) * (size_t)V);
     long *order = (long *)malloc(sizeof(long) * (size_t)V);
-    if (!order)
+    if (!rec || !order) {
+        free(rec);
+        free(order);
         return -2;
+    }
+    for (long i = 0; i < V; ++i) {
+        rec[i].z = z[i];
+        rec[i].idx = i;
+    }
+    qsort(rec, (size_t)V, sizeof(ranked), rank_cmp);
     for (long i = 0; i < V; ++i)
-        order[i] = i;
-    g_rank_z = z;
-    qsort(order, (size_t)V, sizeof(long), rank_cmp);
+        order[i] = rec[i].idx;
+    free(rec);
 
     long kept = V;
     if (use_k) {

@@ -46,6 +46,21 @@ constexpr int kTargetBlocks = 1024;
 
 constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
 
+// The workspace starts with two fixed counter areas (rows, then sequences)
+// that no plan uses for anything else, so calls of any shape can share one
+// workspace: every call leaves its counters at zero.  Row statistics are
+// launched in batches of at most kRowSlots rows when a row spans several
+// chunks; sequences only use counters when the batch is small.
+constexpr int kRowSlots = 131072;
+constexpr int kSeqSlots = 131072;
+constexpr size_t kCounterBytes = (size_t)(kRowSlots + kSeqSlots) * sizeof(unsigned);
+
+// Release: make this workgroup's earlier global writes visible device-wide
+// before the counter increment.  Acquire: after observing the last
+// increment, see every other workgroup's writes.
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 struct RowFinal {
     float m;      // max logit
     float inv;    // 1 / normalizer (full vocabulary, or of the kept candidates)
@@ -305,9 +320,9 @@ struct StatsShared {
 };
 
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(
-    Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
+    Rows rows, int row0, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
     __shared__ StatsShared sh;
-    const int r = blockIdx.x;
+    const int r = row0 + blockIdx.x;
     const int c = blockIdx.y;
     const int V = rows.V;
     const float *z = rows.row(r);
@@ -408,16 +423,20 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
     }
 
     // ---- the last chunk of this row merges all chunks in chunk order ----
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&ws.row_cnt[r], 1u);
-        sh.last = (prev == (unsigned)(chunks - 1));
+    if (chunks > 1) {
+        release_agent();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned prev = atomicAdd(&ws.row_cnt[blockIdx.x], 1u);
+            sh.last = (prev == (unsigned)(chunks - 1));
+        }
+        __syncthreads();
+        if (!sh.last)
+            return;
+        acquire_agent();
+    } else {
+        __syncthreads();
     }
-    __syncthreads();
-    if (!sh.last)
-        return;
-    __threadfence();
 
     int rbad = 0, rfin = 0;
     for (int cc = 0; cc < chunks; ++cc) {
@@ -435,7 +454,8 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
                 merge_ms(m, S, st.m, st.S, scale);
             }
             ws.row_final[r] = RowFinal{m, 1.0f / S, 0, flags};
-            atomicExch(&ws.row_cnt[r], 0u);
+            if (chunks > 1)
+                atomicExch(&ws.row_cnt[blockIdx.x], 0u);
         }
         return;
     }
@@ -479,7 +499,8 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
             S_kept = cum;
         }
         ws.row_final[r] = RowFinal{m, 1.0f / S_kept, kept, flags};
-        atomicExch(&ws.row_cnt[r], 0u);
+        if (chunks > 1)
+            atomicExch(&ws.row_cnt[blockIdx.x], 0u);
     }
     uint64_t *rk = ws.row_keys + (size_t)r * k;
     for (int i = threadIdx.x; i < k; i += kThreads)
@@ -661,16 +682,20 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     if (threadIdx.x == 0)
         ws.seq_sums[(size_t)b * chunks3 + c] = make_float2(residual ? wr : wp, wp);
 
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&ws.seq_cnt[b], 1u);
-        sh.last = (prev == (unsigned)(chunks3 - 1));
+    if (chunks3 > 1) {
+        release_agent();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned prev = atomicAdd(&ws.seq_cnt[b], 1u);
+            sh.last = (prev == (unsigned)(chunks3 - 1));
+        }
+        __syncthreads();
+        if (!sh.last)
+            return;
+        acquire_agent();
+    } else {
+        __syncthreads();
     }
-    __syncthreads();
-    if (!sh.last)
-        return;
-    __threadfence();
 
     // ---- last chunk: locate the target mass, then scan one chunk ----
     __shared__ int s_chunk;
@@ -712,7 +737,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         s_before = before;
         s_target = target;
         s_use_p = use_p;
-        atomicExch(&ws.seq_cnt[b], 0u);
+        if (chunks3 > 1)
+            atomicExch(&ws.seq_cnt[b], 0u);
     }
     __syncthreads();
     const int cs = s_chunk;
@@ -801,6 +827,22 @@ __global__ __launch_bounds__(kThreads) void probs_kernel(
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
+                            const SamplingParams &sp, const Ws &w, hipStream_t stream) {
+    // One launch when rows finish without counters; otherwise batches of at
+    // most kRowSlots rows, each batch reusing the same counter slots.
+    const int batch = plan.chunks > 1 ? kRowSlots : plan.rows;
+    for (int r0 = 0; r0 < plan.rows; r0 += batch) {
+        const int n = std::min(batch, plan.rows - r0);
+        row_stats_kernel<<<dim3(n, plan.chunks), kThreads, 0, stream>>>(
+            rows, r0, plan.chunks, plan.chunk_len, sp, w);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 Ws carve(const AcceptPlan &p, void *base) {
     unsigned char *b = reinterpret_cast<unsigned char *>(base);
     Ws w;
@@ -856,14 +898,16 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
     } else {
         int C3 = (kTargetBlocks + std::max(B, 1) - 1) / std::max(B, 1);
         C3 = std::max(1, std::min(C3, std::min(64, (V + 2047) / 2048)));
+        if (B > kSeqSlots)
+            C3 = 1;
         int len = (V + C3 - 1) / C3;
         p.chunk3_len = ((len + 1023) / 1024) * 1024;
         p.chunks3 = std::max(1, (V + p.chunk3_len - 1) / p.chunk3_len);
     }
     const int k = candidates ? k_eff : 0;
     size_t off = 0;
-    p.off_row_cnt = off;     off += align256((size_t)p.rows * sizeof(unsigned));
-    p.off_seq_cnt = off;     off += align256((size_t)B * sizeof(unsigned));
+    p.off_row_cnt = off;     off += (size_t)kRowSlots * sizeof(unsigned);
+    p.off_seq_cnt = off;     off += (size_t)kSeqSlots * sizeof(unsigned);
     p.off_chunk_stats = off; off += align256((size_t)p.rows * p.chunks * sizeof(ChunkStat));
     p.off_chunk_keys = off;  off += align256((size_t)p.rows * p.chunks * k * sizeof(uint64_t));
     p.off_row_final = off;   off += align256((size_t)p.rows * sizeof(RowFinal));
@@ -883,9 +927,7 @@ hipError_t launch_accept(const float *target, const float *draft,
         return hipSuccess;
     Rows rows{target, draft, plan.D, plan.V};
     Ws w = carve(plan, ws);
-    row_stats_kernel<<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
-        rows, plan.chunks, plan.chunk_len, sp, w);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_row_stats(rows, plan, sp, w, stream);
     if (e != hipSuccess)
         return e;
     accept_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
@@ -901,9 +943,7 @@ hipError_t launch_probs(const float *logits, const AcceptPlan &plan,
         return hipSuccess;
     Rows rows{logits, nullptr, 0, plan.V};
     Ws w = carve(plan, ws);
-    row_stats_kernel<<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
-        rows, plan.chunks, plan.chunk_len, sp, w);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_row_stats(rows, plan, sp, w, stream);
     if (e != hipSuccess)
         return e;
     const int pc = (plan.V + 4095) / 4096;

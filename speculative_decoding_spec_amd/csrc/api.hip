@@ -29,7 +29,7 @@ spec_status qmv_common(int bits, const void *w, const uint16_t *scales,
         return SPEC_ERR_UNSUPPORTED;
     if (M > kMaxM)
         return SPEC_ERR_UNSUPPORTED;
-    if ((size_t)N * (size_t)(K / 8) > (size_t)1 << 40)
+    if (N > spec::qmv_max_rows())
         return SPEC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0)
         return SPEC_OK;

@@ -45,6 +45,10 @@ constexpr int kFragBytesPerPair = 4 * 32 * 16;  // 4 MFMA steps x 32 lane slots 
 constexpr int kSumBytesPerPair = 2 * 8 * 4;     // 2 groups x 8 rows x fp32
 constexpr int kMinPairsPerSplit = 2;
 constexpr int kTargetBlocks = 512;
+// The workspace starts with a fixed counter area, one counter per 64-row
+// block, that no plan ever uses for anything else: calls of any shape can
+// then share one workspace, because every call leaves its counters at zero.
+constexpr size_t kCounterBytes = 256 * 1024;   // 65536 blocks: N <= 4194304
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
         return;
 
     // ---- K splits: the last workgroup of this row block sums them in order ----
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev = atomicAdd(&counters[blk], 1u);
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     for (int e = threadIdx.x; e < M * kRowsPerBlock; e += kThreads) {
         const int m = e / kRowsPerBlock;
         const int nn = blk * kRowsPerBlock + e % kRowsPerBlock;
@@ -301,9 +305,10 @@ QmvPlan qmv_plan(int N, int K) {
 size_t qmv_workspace_bytes(const QmvPlan &p, int M, int N) {
     if (p.splits <= 1 || M <= 0 || N <= 0)
         return 0;
-    return align256((size_t)p.n_blocks * sizeof(unsigned)) +
-           align256((size_t)p.splits * M * N * sizeof(float));
+    return kCounterBytes + align256((size_t)p.splits * M * N * sizeof(float));
 }
+
+int qmv_max_rows() { return (int)(kCounterBytes / sizeof(unsigned)) * kRowsPerBlock; }
 
 hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
                       const uint16_t *biases, const uint16_t *x, float *y,
@@ -321,9 +326,7 @@ hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
     float *partial = nullptr;
     if (plan.splits > 1) {
         counters = reinterpret_cast<unsigned *>(ws);
-        partial = reinterpret_cast<float *>(
-            reinterpret_cast<unsigned char *>(ws) +
-            align256((size_t)plan.n_blocks * sizeof(unsigned)));
+        partial = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(ws) + kCounterBytes);
     }
     dim3 grid(plan.n_blocks, plan.splits);
     if (bits == 4)

@@ -22,6 +22,7 @@ struct QmvPlan {
 
 QmvPlan qmv_plan(int N, int K);
 size_t qmv_workspace_bytes(const QmvPlan &p, int M, int N);
+int qmv_max_rows();  // largest N a workspace's counter area supports
 hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
                       const uint16_t *biases, const uint16_t *x, float *y,
                       int M, int N, int K, const QmvPlan &plan, void *ws,

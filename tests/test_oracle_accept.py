@@ -304,3 +304,16 @@ def test_zero_weight_tokens_are_never_drawn():
     out = oracle.accept(t, d, np.array([[2]], np.int32),
                         np.array([[0.99, 0.0]], np.float32), 1.0)
     assert out["accepted_len"][0] == 0 and out["next_token"][0] == 1
+
+
+def test_oracle_is_thread_safe():
+    # The tests call the oracle from host threads; filtered rows must rank
+    # the same whether or not other rows are being ranked concurrently.
+    from concurrent.futures import ThreadPoolExecutor
+    z = synth.rng(90, synth.DRAFT).normal(0, 2, size=(64, 3000)).astype(np.float32)
+    serial = [oracle.probs(z[r], 0.8, 20, 0.95) for r in range(64)]
+    with ThreadPoolExecutor(8) as ex:
+        for _ in range(3):
+            par = list(ex.map(lambda r: oracle.probs(z[r], 0.8, 20, 0.95), range(64)))
+            for a, b in zip(serial, par):
+                assert np.array_equal(a, b)
