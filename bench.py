@@ -43,19 +43,27 @@ def parse():
 
 
 def build_inputs(dev):
+    """Packed W4 weights (packing is a load-time step, outside the timing)."""
     import torch
+    import speculative_decoding_spec_amd as spec
     from speculative_decoding_spec_amd import synth
+
+    def packed(N, K, seed):
+        w, s, b = synth.torch_qweights(4, N, K, GROUP, seed, dev)
+        return spec.spec_pack_w4(w, s, b, G=GROUP)
+
     blocks = []
     for i, M in enumerate(MS):
-        gate = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1000 + 10 * i, dev)
-        up = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1001 + 10 * i, dev)
-        down = synth.torch_qweights(4, HIDDEN, FFN, GROUP, 1002 + 10 * i, dev)
+        gate = packed(FFN, HIDDEN, 1000 + 10 * i)
+        up = packed(FFN, HIDDEN, 1001 + 10 * i)
+        down = packed(HIDDEN, FFN, 1002 + 10 * i)
         x = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
         h = synth.torch_activations(M, FFN, 1004 + 10 * i, dev)
         yg = torch.empty((M, FFN), dtype=torch.float32, device=dev)
         yu = torch.empty((M, FFN), dtype=torch.float32, device=dev)
         yd = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
         blocks.append(dict(M=M, gate=gate, up=up, down=down, x=x, h=h, yg=yg, yu=yu, yd=yd))
+    torch.cuda.synchronize()
     return blocks
 
 
@@ -77,10 +85,9 @@ def build_accept(dev):
 
 def run_qmv(b):
     import speculative_decoding_spec_amd as spec
-    g, u, d = b["gate"], b["up"], b["down"]
-    spec.spec_qmv_w4(g[0], g[1], g[2], b["x"], y=b["yg"])
-    spec.spec_qmv_w4(u[0], u[1], u[2], b["x"], y=b["yu"])
-    spec.spec_qmv_w4(d[0], d[1], d[2], b["h"], y=b["yd"])
+    spec.spec_qmv_w4(b["gate"], b["x"], y=b["yg"])
+    spec.spec_qmv_w4(b["up"], b["x"], y=b["yu"])
+    spec.spec_qmv_w4(b["down"], b["h"], y=b["yd"])
 
 
 def run_accept(a):

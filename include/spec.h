@@ -68,35 +68,50 @@ int spec_version(void);
  * mlxcel manual's "MTP and DFlash" page, draft block width section; MTPLX
  * "Layer 0: MLX Runtime").
  *
+ * Weights are given once in the interchange layout below and packed by
+ * spec_pack_w4 / spec_pack_w8 into the layout the kernel streams (tiles of
+ * 16 rows x 128 k, each read by one wave as 1 KB contiguous; scale and bias
+ * interleaved).  Packing is a one-time, load-time step; spec_qmv_* read only
+ * the packed buffers.
+ *
+ * Interchange layout (inputs of spec_pack_*):
  *  w       W4: uint32 [N][K/8]; element k of row n is bits 4*(k%8)..4*(k%8)+3
  *          of word k/8 (unsigned code 0..15).  16-byte aligned.
  *          W8: uint8 [N][K]; one unsigned code 0..255 per byte.  16-byte aligned.
  *  scales  fp16 bit patterns [N][K/G]  (s)
  *  biases  fp16 bit patterns [N][K/G]  (b)
+ *  N >= 0, K >= 0 with K % G == 0, G == 64 (SPEC_ERR_UNSUPPORTED otherwise).
+ *
+ * Packed buffers (outputs of spec_pack_*, device memory owned by the caller):
+ *  w_packed   spec_qmv_packed_weight_bytes(bits, N, K, G) bytes, 16-byte aligned
+ *  sb_packed  spec_qmv_packed_sb_bytes(N, K, G) bytes, 4-byte aligned
+ *
+ * spec_qmv_*:
  *  x       bf16 bit patterns [M][K], 16-byte aligned
  *  y       fp32 [M][N], written (never read)
- *  M       1..8 rows (0 is a no-op)
- *  N       >= 0 output features
- *  K       >= 0 input features, K % G == 0
- *  G       group size; 64 is supported (SPEC_ERR_UNSUPPORTED otherwise)
- *  workspace / workspace_bytes
- *          device scratch of at least spec_qmv_workspace_size(M, N, K, G)
- *          bytes (may be NULL when that size is 0).
+ *  M       1..8 rows (0 is a no-op); N, K, G as given to spec_pack_*.
  *
  * Results are deterministic, and row m of an M-row call is bitwise equal to
  * the one-row call on x[m] (the reduction order does not depend on M).
  */
-size_t spec_qmv_workspace_size(int M, int N, int K, int G);
+size_t spec_qmv_packed_weight_bytes(int bits, int N, int K, int G);
+size_t spec_qmv_packed_sb_bytes(int N, int K, int G);
 
-spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales,
-                        const uint16_t *biases, const uint16_t *x, float *y,
-                        int M, int N, int K, int G, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+spec_status spec_pack_w4(const uint32_t *w, const uint16_t *scales,
+                         const uint16_t *biases, int N, int K, int G,
+                         void *w_packed, void *sb_packed, hipStream_t stream);
 
-spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales,
-                        const uint16_t *biases, const uint16_t *x, float *y,
-                        int M, int N, int K, int G, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+spec_status spec_pack_w8(const uint8_t *w, const uint16_t *scales,
+                         const uint16_t *biases, int N, int K, int G,
+                         void *w_packed, void *sb_packed, hipStream_t stream);
+
+spec_status spec_qmv_w4(const void *w_packed, const void *sb_packed,
+                        const uint16_t *x, float *y, int M, int N, int K,
+                        int G, hipStream_t stream);
+
+spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
+                        const uint16_t *x, float *y, int M, int N, int K,
+                        int G, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* Sampling distribution                                                */

@@ -8,6 +8,7 @@ built library (``libspec.so`` next to this file) raises immediately.
 
 Names follow the C ABI:
 
+    spec_pack_w4 / spec_pack_w8      one-time repack of quantized weights
     spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv
     spec_verify_accept               ratio acceptance + residual / bonus draw
     spec_sample_probs                filtered sampling distribution
@@ -56,11 +57,17 @@ def lib() -> ctypes.CDLL:
         L.spec_status_str.argtypes = [i]
         L.spec_status_str.restype = ctypes.c_char_p
         L.spec_version.restype = i
-        L.spec_qmv_workspace_size.argtypes = [i, i, i, i]
-        L.spec_qmv_workspace_size.restype = sz
+        L.spec_qmv_packed_weight_bytes.argtypes = [i, i, i, i]
+        L.spec_qmv_packed_weight_bytes.restype = sz
+        L.spec_qmv_packed_sb_bytes.argtypes = [i, i, i]
+        L.spec_qmv_packed_sb_bytes.restype = sz
+        for name in ("spec_pack_w4", "spec_pack_w8"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
+            fn.restype = i
         for name in ("spec_qmv_w4", "spec_qmv_w8"):
             fn = getattr(L, name)
-            fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
+            fn.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
             fn.restype = i
         L.spec_verify_accept_workspace.argtypes = [i, i, i, i]
         L.spec_verify_accept_workspace.restype = sz
@@ -127,53 +134,85 @@ def get_workspace(nbytes: int, device, key: str = "default"):
     return buf
 
 
-def spec_qmv_workspace_size(M: int, N: int, K: int, G: int = 64) -> int:
-    return int(lib().spec_qmv_workspace_size(M, N, K, G))
+class PackedWeights:
+    """Quantized weights in the layout the qmv kernels stream (see
+    include/spec.h): produced once by spec_pack_w4 / spec_pack_w8."""
+
+    def __init__(self, bits, N, K, G, w, sb):
+        self.bits, self.N, self.K, self.G, self.w, self.sb = bits, N, K, G, w, sb
 
 
-def _qmv(name, bits, w, scales, biases, x, y, G, ws):
+def spec_qmv_packed_weight_bytes(bits: int, N: int, K: int, G: int = 64) -> int:
+    return int(lib().spec_qmv_packed_weight_bytes(bits, N, K, G))
+
+
+def spec_qmv_packed_sb_bytes(N: int, K: int, G: int = 64) -> int:
+    return int(lib().spec_qmv_packed_sb_bytes(N, K, G))
+
+
+def _pack(name, bits, w, scales, biases, G):
     import torch
-    dev = x.device
-    _require(x, torch.bfloat16, "x", dev)
-    M, K = x.shape
+    dev = w.device
     wdt = torch.int32 if bits == 4 else torch.uint8
     _require(w, wdt, "w", dev)
     N = w.shape[0]
-    per_row = K // 8 if bits == 4 else K
-    if w.dim() != 2 or w.shape[1] != per_row:
-        raise ValueError(f"w must be [{N}][{per_row}] for K={K}")
+    K = w.shape[1] * 8 if bits == 4 else w.shape[1]
     _require(scales, torch.float16, "scales", dev)
     _require(biases, torch.float16, "biases", dev)
     if G <= 0 or K % G:
         raise ValueError("K must be a multiple of G")
     if tuple(scales.shape) != (N, K // G) or tuple(biases.shape) != (N, K // G):
         raise ValueError(f"scales / biases must be [{N}][{K // G}]")
+    wb = spec_qmv_packed_weight_bytes(bits, N, K, G)
+    sbb = spec_qmv_packed_sb_bytes(N, K, G)
+    wp = torch.empty(max(wb, 16), dtype=torch.uint8, device=dev)
+    sbp = torch.empty(max(sbb, 16), dtype=torch.uint8, device=dev)
+    st = getattr(lib(), name)(_ptr(w), _ptr(scales), _ptr(biases), N, K, G,
+                              _ptr(wp), _ptr(sbp), _stream(dev))
+    _check(name, st)
+    return PackedWeights(bits, N, K, G, wp, sbp)
+
+
+def spec_pack_w4(w, scales, biases, G: int = 64) -> PackedWeights:
+    """Pack W4 weights: w int32 [N][K/8] (element k at bits 4*(k%8) of word
+    k/8), scales / biases fp16 [N][K/G]."""
+    return _pack("spec_pack_w4", 4, w, scales, biases, G)
+
+
+def spec_pack_w8(w, scales, biases, G: int = 64) -> PackedWeights:
+    """Pack W8 weights: w uint8 [N][K], scales / biases fp16 [N][K/G]."""
+    return _pack("spec_pack_w8", 8, w, scales, biases, G)
+
+
+def _qmv(name, bits, packed, x, y):
+    import torch
+    dev = x.device
+    if packed.bits != bits:
+        raise ValueError(f"{name} needs W{bits} packed weights, got W{packed.bits}")
+    _require(x, torch.bfloat16, "x", dev)
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has K={K}, weights have K={packed.K}")
+    N = packed.N
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     _require(y, torch.float32, "y", dev)
     if tuple(y.shape) != (M, N):
         raise ValueError(f"y must be [{M}][{N}]")
-    need = spec_qmv_workspace_size(M, N, K, G)
-    if ws is None:
-        ws = get_workspace(need, dev, "qmv")
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = getattr(lib(), name)(_ptr(w), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y),
-                              M, N, K, G, _ptr(ws), nbytes, _stream(dev))
+    st = getattr(lib(), name)(_ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(y),
+                              M, N, K, packed.G, _stream(dev))
     _check(name, st)
     return y
 
 
-def spec_qmv_w4(w, scales, biases, x, y=None, G: int = 64, workspace=None):
-    """y[M][N] fp32 = x[M][K] (bf16) times the dequantized W4 matrix.
-
-    w: int32 [N][K/8] packed nibbles (element k at bits 4*(k%8) of word k/8);
-    scales, biases: fp16 [N][K/G]."""
-    return _qmv("spec_qmv_w4", 4, w, scales, biases, x, y, G, workspace)
+def spec_qmv_w4(packed: PackedWeights, x, y=None):
+    """y[M][N] fp32 = x[M][K] (bf16) times the dequantized W4 matrix."""
+    return _qmv("spec_qmv_w4", 4, packed, x, y)
 
 
-def spec_qmv_w8(w, scales, biases, x, y=None, G: int = 64, workspace=None):
-    """As spec_qmv_w4 with w: uint8 [N][K] codes."""
-    return _qmv("spec_qmv_w8", 8, w, scales, biases, x, y, G, workspace)
+def spec_qmv_w8(packed: PackedWeights, x, y=None):
+    """As spec_qmv_w4 for W8 packed weights."""
+    return _qmv("spec_qmv_w8", 8, packed, x, y)
 
 
 def spec_verify_accept_workspace(B: int, D: int, V: int, top_k: int) -> int:

@@ -53,7 +53,6 @@ constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
 // chunks; sequences only use counters when the batch is small.
 constexpr int kRowSlots = 131072;
 constexpr int kSeqSlots = 131072;
-constexpr size_t kCounterBytes = (size_t)(kRowSlots + kSeqSlots) * sizeof(unsigned);
 
 // Release: make this workgroup's earlier global writes visible device-wide
 // before the counter increment.  Acquire: after observing the last
@@ -338,14 +337,18 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
         if (vec) {
             const float4 *z4 = reinterpret_cast<const float4 *>(z);
             for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 16) {
+                // Branch-free: clamp each load into the chunk and mask the
+                // lanes past its end to -inf (which adds nothing below).
                 float v[16];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int e = base + u * kThreads * 4;
-                    float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                    if (e < hi)
-                        t = z4[e >> 2];
-                    v[4 * u + 0] = t.x; v[4 * u + 1] = t.y; v[4 * u + 2] = t.z; v[4 * u + 3] = t.w;
+                    const float4 t = z4[min(e, hi - 4) >> 2];
+                    const bool in = e < hi;
+                    v[4 * u + 0] = in ? t.x : -INFINITY;
+                    v[4 * u + 1] = in ? t.y : -INFINITY;
+                    v[4 * u + 2] = in ? t.z : -INFINITY;
+                    v[4 * u + 3] = in ? t.w : -INFINITY;
                 }
                 float bm = m;
 #pragma unroll
@@ -669,12 +672,44 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     const int lo = c * chunk3_len;
     const int hi = min(V, lo + chunk3_len);
     float wr = 0.0f, wp = 0.0f;
-    for (int x = lo + threadIdx.x; x < hi; x += kThreads) {
-        const float p = weight(zt[x], ft.m, scale) * ft.inv;
-        wp += p;
-        if (residual) {
-            const float q = weight(zd[x], fd.m, scale) * fd.inv;
-            wr += fmaxf(p - q, 0.0f);
+    if ((V & 3) == 0) {
+        // float4 loads, clamped into the chunk; lanes past its end add 0
+        const float4 *zt4 = reinterpret_cast<const float4 *>(zt);
+        const float4 *zd4 = residual ? reinterpret_cast<const float4 *>(zd) : zt4;
+        for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 8) {
+            float4 a[2], q4[2];
+            bool in[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = base + u * kThreads * 4;
+                in[u] = e < hi;
+                const int ec = min(e, hi - 4) >> 2;
+                a[u] = zt4[ec];
+                q4[u] = zd4[ec];
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float tv[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+                const float dv[4] = {q4[u].x, q4[u].y, q4[u].z, q4[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float p = in[u] ? weight(tv[q], ft.m, scale) * ft.inv : 0.0f;
+                    wp += p;
+                    if (residual) {
+                        const float qq = weight(dv[q], fd.m, scale) * fd.inv;
+                        wr += in[u] ? fmaxf(p - qq, 0.0f) : 0.0f;
+                    }
+                }
+            }
+        }
+    } else {
+        for (int x = lo + threadIdx.x; x < hi; x += kThreads) {
+            const float p = weight(zt[x], ft.m, scale) * ft.inv;
+            wp += p;
+            if (residual) {
+                const float q = weight(zd[x], fd.m, scale) * fd.inv;
+                wr += fmaxf(p - q, 0.0f);
+            }
         }
     }
     wr = block_sum(wr, sh.fsh);

@@ -17,33 +17,53 @@ constexpr size_t kMaxRows = (size_t)1 << 23;  // grid x of 256-thread workgroups
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-spec_status qmv_common(int bits, const void *w, const uint16_t *scales,
-                       const uint16_t *biases, const uint16_t *x, float *y,
-                       int M, int N, int K, int G, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-    if (M < 0 || N < 0 || K < 0 || G <= 0)
-        return SPEC_ERR_INVALID;
-    if (K % G != 0)
+spec_status qmv_shape_ok(int N, int K, int G) {
+    if (N < 0 || K < 0 || G <= 0 || K % G != 0)
         return SPEC_ERR_INVALID;
     if (G != 64)
         return SPEC_ERR_UNSUPPORTED;
-    if (M > kMaxM)
+    // 32-bit byte offsets inside one 16-row tile and inside x
+    if ((size_t)K * 2 > ((size_t)1 << 30) || N > (1 << 28))
         return SPEC_ERR_UNSUPPORTED;
-    if (N > spec::qmv_max_rows())
+    return SPEC_OK;
+}
+
+spec_status pack_common(int bits, const void *w, const uint16_t *scales,
+                        const uint16_t *biases, int N, int K, int G,
+                        void *w_packed, void *sb_packed, hipStream_t stream) {
+    const spec_status s = qmv_shape_ok(N, K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (N == 0 || K == 0)
+        return SPEC_OK;
+    if (!w || !scales || !biases || !w_packed || !sb_packed)
+        return SPEC_ERR_INVALID;
+    if (!aligned16(w) || !aligned16(w_packed) || !aligned4(sb_packed))
+        return SPEC_ERR_UNSUPPORTED;
+    if (spec::launch_pack(bits, w, scales, biases, N, K, w_packed, sb_packed, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status qmv_common(int bits, const void *w_packed, const void *sb_packed,
+                       const uint16_t *x, float *y, int M, int N, int K, int G,
+                       hipStream_t stream) {
+    if (M < 0)
+        return SPEC_ERR_INVALID;
+    const spec_status s = qmv_shape_ok(N, K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (M > kMaxM)
         return SPEC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0)
         return SPEC_OK;
-    if (!y || (K > 0 && (!w || !scales || !biases || !x)))
+    if (!y || (K > 0 && (!w_packed || !sb_packed || !x)))
         return SPEC_ERR_INVALID;
-    if (K > 0 && (!aligned16(w) || !aligned16(x)))
+    if (K > 0 && (!aligned16(w_packed) || !aligned16(x) || !aligned4(sb_packed)))
         return SPEC_ERR_UNSUPPORTED;
     if (!aligned4(y))
         return SPEC_ERR_INVALID;
-    const spec::QmvPlan plan = spec::qmv_plan(N, K);
-    const size_t need = K > 0 ? spec::qmv_workspace_bytes(plan, M, N) : 0;
-    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
-        return SPEC_ERR_WORKSPACE;
-    if (spec::launch_qmv(bits, w, scales, biases, x, y, M, N, K, plan, workspace, stream) != hipSuccess)
+    if (spec::launch_qmv(bits, w_packed, sb_packed, x, y, M, N, K, stream) != hipSuccess)
         return SPEC_ERR_DEVICE;
     return SPEC_OK;
 }
@@ -81,26 +101,42 @@ const char *spec_status_str(spec_status s) {
 
 int spec_version(void) { return 100; }
 
-size_t spec_qmv_workspace_size(int M, int N, int K, int G) {
-    if (M <= 0 || N <= 0 || K <= 0 || G != 64 || K % G != 0 || M > kMaxM)
+size_t spec_qmv_packed_weight_bytes(int bits, int N, int K, int G) {
+    if ((bits != 4 && bits != 8) || qmv_shape_ok(N, K, G) != SPEC_OK)
         return 0;
-    return spec::qmv_workspace_bytes(spec::qmv_plan(N, K), M, N);
+    return spec::qmv_packed_bytes(bits, N, K);
 }
 
-spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales,
-                        const uint16_t *biases, const uint16_t *x, float *y,
-                        int M, int N, int K, int G, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
-    return qmv_common(4, w, scales, biases, x, y, M, N, K, G, workspace,
-                      workspace_bytes, stream);
+size_t spec_qmv_packed_sb_bytes(int N, int K, int G) {
+    if (qmv_shape_ok(N, K, G) != SPEC_OK)
+        return 0;
+    return spec::qmv_packed_sb_bytes(N, K);
 }
 
-spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales,
-                        const uint16_t *biases, const uint16_t *x, float *y,
-                        int M, int N, int K, int G, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
-    return qmv_common(8, w, scales, biases, x, y, M, N, K, G, workspace,
-                      workspace_bytes, stream);
+spec_status spec_pack_w4(const uint32_t *w, const uint16_t *scales,
+                         const uint16_t *biases, int N, int K, int G,
+                         void *w_packed, void *sb_packed, hipStream_t stream) {
+    if (K % 8 != 0)
+        return SPEC_ERR_INVALID;
+    return pack_common(4, w, scales, biases, N, K, G, w_packed, sb_packed, stream);
+}
+
+spec_status spec_pack_w8(const uint8_t *w, const uint16_t *scales,
+                         const uint16_t *biases, int N, int K, int G,
+                         void *w_packed, void *sb_packed, hipStream_t stream) {
+    return pack_common(8, w, scales, biases, N, K, G, w_packed, sb_packed, stream);
+}
+
+spec_status spec_qmv_w4(const void *w_packed, const void *sb_packed,
+                        const uint16_t *x, float *y, int M, int N, int K, int G,
+                        hipStream_t stream) {
+    return qmv_common(4, w_packed, sb_packed, x, y, M, N, K, G, stream);
+}
+
+spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
+                        const uint16_t *x, float *y, int M, int N, int K, int G,
+                        hipStream_t stream) {
+    return qmv_common(8, w_packed, sb_packed, x, y, M, N, K, G, stream);
 }
 
 size_t spec_verify_accept_workspace(int B, int D, int V, int top_k) {

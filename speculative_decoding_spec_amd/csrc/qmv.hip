@@ -8,27 +8,30 @@
 // by streaming every weight once, and extra rows ride on the same fetch).
 //
 // Design (one pass over the weights, every fetched weight feeds all M rows):
-//  * A workgroup of 4 waves owns 64 weight rows (16 per wave) and one K
-//    split.  It stages its slice of x in LDS once, already permuted into the
-//    per-lane MFMA operand order, together with per-group sums of x.
-//  * Each lane streams 16 bytes of packed codes per 128-wide K step ("pair"
-//    of two 64-groups): W4 = 32 nibbles, W8 = 2 x 16 bytes.  Four lanes
-//    cover 64 (W4) or 128 (W8) contiguous bytes of one row.
+//  * A workgroup owns one 16-row tile of W (the MFMA's 16 columns) and its
+//    4 or 8 waves split K, wave w taking every 4th/8th 128-wide step ("pair"
+//    of two 64-groups).  Nothing crosses workgroups: no fences, no
+//    workspace, and even N = 5120 launches 320 workgroups of 8 waves.
+//  * Each lane streams 16 bytes of packed codes per pair (W4: 32 nibbles;
+//    W8: two 16-byte loads); four lanes cover 64 (W4) or 128 (W8) contiguous
+//    bytes of one row.  Loads are branch-free (indices clamp into range) and
+//    double buffered in batches, so a whole batch stays in flight.
 //  * Codes become bf16 in registers with no conversion instruction for W4:
 //    OR-ing a nibble q into the mantissa of 128.0 (0x4300) gives 128 + q
 //    exactly; the 128 offset is removed with the group sum of x.  W8 codes
 //    convert with the byte-to-float instructions (exact below 256).
 //  * v_mfma_f32_16x16x32_bf16 does the multiply-accumulate: B = 16 weight
-//    rows x 32 k, A = the x rows.  The two groups of a pair are kept apart
-//    by feeding group 0 through A rows 0..7 and group 1 through A rows
-//    8..15 (each zero on the other group's k slots), so M <= 8 rows use the
-//    whole 16-row tile and every output of the MFMA belongs to exactly one
-//    group.  The per-group affine terms are then applied in fp32:
+//    rows x 32 k, A = the x rows, read straight from global memory (x is a
+//    few hundred KB at most and stays in L2).  The two groups of a pair are
+//    kept apart by feeding group 0 through A rows 0..7 and group 1 through
+//    A rows 8..15 (each zero on the other group's k slots), so M <= 8 rows
+//    use the whole 16-row tile and every MFMA output belongs to one group.
+//    A second MFMA against a ones operand yields the group sums of x in the
+//    same lane layout.  The per-group affine terms are applied in fp32:
 //        acc += s * C + (b - 128 s) * sum_x            (W4)
 //        acc += s * C + b * sum_x                      (W8)
-//  * The two group halves meet with one cross-lane add; K splits (when N is
-//    too small to fill the GPU) meet in a fixed order in the workgroup that
-//    arrives last, so the result is deterministic and independent of M.
+//  * The two group halves and the waves meet in LDS in a fixed order, so
+//    results are deterministic and row m never depends on M.
 #include "spec_internal.h"
 
 namespace spec {
@@ -38,45 +41,31 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;          // 4 waves of 64
-constexpr int kRowsPerBlock = 64;      // 16 rows per wave
-constexpr int kMaxPairsPerSplit = 20;  // LDS budget: 20 x 2112 B = 42 KB
-constexpr int kFragBytesPerPair = 4 * 32 * 16;  // 4 MFMA steps x 32 lane slots x 16 B
-constexpr int kSumBytesPerPair = 2 * 8 * 4;     // 2 groups x 8 rows x fp32
-constexpr int kMinPairsPerSplit = 2;
-constexpr int kTargetBlocks = 512;
-// The workspace starts with a fixed counter area, one counter per 64-row
-// block, that no plan ever uses for anything else: calls of any shape can
-// then share one workspace, because every call leaves its counters at zero.
-constexpr size_t kCounterBytes = 256 * 1024;   // 65536 blocks: N <= 4194304
+// Raw (unformatted, stride 0) buffer resource flags for gfx9-family parts,
+// and a byte offset beyond any x buffer: loads there return zeros.
+constexpr int kBufferFlags = 0x00020000;
+constexpr unsigned kOutOfRange = 0x40000000u;
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-__device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-// 8 bf16 of x in k order (x0|x1, x2|x3, x4|x5, x6|x7) -> the order the W4
-// unpack produces on the B side: (x0|x4, x1|x5, x2|x6, x3|x7).
-__device__ __forceinline__ u32x4 permute_for_w4(u32x4 v) {
-    u32x4 o;
-    o.x = (v.x & 0xFFFFu) | (v.z << 16);
-    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-    o.z = (v.y & 0xFFFFu) | (v.w << 16);
-    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    return o;
-}
-
-// One 32-bit word of 8 nibbles -> 8 bf16 values 128 + q, in the order
-// (q0, q4, q1, q5, q2, q6, q3, q7).
+// One 32-bit word of 8 nibbles q0..q7 (q_i at bits 4i) -> 8 bf16 values
+// 128 + q_i in k order.  The even and odd nibbles are first separated into
+// bytes (lo = q0 q2 q4 q6, hi = q1 q3 q5 q7), interleaved into k order
+// (q0 q1 q2 q3 / q4 q5 q6 q7), and each byte is then paired with the byte
+// 0x43: bf16 0x43qq = 128 + q exactly (128 has 7 mantissa bits of ulp 1).
 __device__ __forceinline__ bf16x8 unpack_w4(unsigned d) {
-    const unsigned mask = 0x000F000Fu, magic = 0x43004300u;
+    const unsigned lo = d & 0x0F0F0F0Fu;
+    const unsigned hi = (d >> 4) & 0x0F0F0F0Fu;
+    const unsigned q03 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // q0 q1 q2 q3
+    const unsigned q47 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // q4 q5 q6 q7
+    const unsigned c43 = 0x43434343u;
     u32x4 o;
-    o.x = (d & mask) | magic;
-    o.y = ((d >> 4) & mask) | magic;
-    o.z = ((d >> 8) & mask) | magic;
-    o.w = ((d >> 12) & mask) | magic;
+    o.x = __builtin_amdgcn_perm(c43, q03, 0x04010400u);   // 0x43 q1 0x43 q0
+    o.y = __builtin_amdgcn_perm(c43, q03, 0x04030402u);
+    o.z = __builtin_amdgcn_perm(c43, q47, 0x04010400u);
+    o.w = __builtin_amdgcn_perm(c43, q47, 0x04030402u);
     return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -95,180 +84,202 @@ __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-template <int BITS>
-__global__ __launch_bounds__(kThreads) void qmv_kernel(
-    const void *__restrict__ w, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x,
-    float *__restrict__ y, int M, int N, int K, int pairs_per_split,
-    int splits, float *__restrict__ partial, unsigned *__restrict__ counters) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    u32x4 *xf = reinterpret_cast<u32x4 *>(lds);
-    float *xs = reinterpret_cast<float *>(lds + (size_t)pairs_per_split * kFragBytesPerPair);
-    __shared__ int s_last;
+// ---------------------------------------------------------------------------
+// Packed layout (written once by pack_kernel, read by qmv_kernel).
+//
+// W is cut into tiles of 16 rows x 128 k (one "pair" of 64-groups).  Tile
+// (t, p) -- rows 16t..16t+15, k = 128p..128p+127 -- is stored contiguously at
+// tile index t * n_pairs + p, as 64 lane slots of 16 bytes (W4) or two
+// 1 KB halves of 64 x 16 bytes (W8).  Lane slot l = 16 j + r holds row
+// 16t + r, k = 128p + 64 (j >> 1) + 32 (j & 1) + [0, 32): exactly the bytes
+// the MFMA B operand of lane l needs, in the original code order.  A wave
+// therefore reads 1 KB per load instruction and streams a contiguous region.
+// Scales and biases become one 32-bit word per (row, group): fp16 scale in
+// the low half, fp16 bias in the high half, stored as [t][g][r] with the group
+// count padded to 2 * n_pairs.  Rows past N and groups past K/64 are zero, so
+// they contribute exactly nothing.
+// ---------------------------------------------------------------------------
 
-    const int blk = blockIdx.x;
-    const int split = blockIdx.y;
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_kernel(
+    const void *__restrict__ w, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ biases, u32x4 *__restrict__ wp,
+    uint32_t *__restrict__ sbp, int N, int K) {
     const int ng = K >> 6;
     const int n_pairs = (ng + 1) >> 1;
-    const int p_begin = split * pairs_per_split;
-    const int P = min(pairs_per_split, n_pairs - p_begin);
-
-    // ---- stage x: one item = (pair p, half h, row m), 64 values of x ----
-    for (int item = threadIdx.x; item < P * 16; item += kThreads) {
-        const int p = item >> 4, h = (item >> 3) & 1, m = item & 7;
-        if (m >= M)
-            continue;
-        const int g = 2 * (p_begin + p) + h;
-        u32x4 frag[8];
-        float sum = 0.0f;
-        if (g < ng) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)m * K + (size_t)g * 64);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const u32x4 v = src[q];
-                sum += bf16_lo(v.x); sum += bf16_hi(v.x);
-                sum += bf16_lo(v.y); sum += bf16_hi(v.y);
-                sum += bf16_lo(v.z); sum += bf16_hi(v.z);
-                sum += bf16_lo(v.w); sum += bf16_hi(v.w);
-                frag[q] = (BITS == 4) ? permute_for_w4(v) : v;
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                frag[q] = u32x4{0u, 0u, 0u, 0u};
+    const int ngp = 2 * n_pairs;
+    const int n_tiles = (N + 15) >> 4;
+    constexpr int L = BITS / 4;   // 16-byte slots per lane and tile
+    const size_t slots = (size_t)n_tiles * n_pairs * 64 * L;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < slots;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(i & 63);
+        const size_t rest = i >> 6;
+        const int v = (int)(rest % L);            // which 1 KB half (W8)
+        const size_t tp = rest / L;               // t * n_pairs + p
+        const int p = (int)(tp % n_pairs);
+        const int t = (int)(tp / n_pairs);
+        const int r = lane & 15, j = lane >> 4;
+        const int n = 16 * t + r;
+        const int k = 128 * p + 64 * (j >> 1) + 32 * (j & 1) + 16 * v;  // first k of the 16 bytes
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (n < N && k < K) {
+            if (BITS == 4)
+                val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 5];
+            else
+                val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 4];
         }
-        // 8-value block q = 4 * sub + t feeds MFMA step t of lane slot
-        // (half h, sub, row m).
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            xf[(p * 4 + (q & 3)) * 32 + 16 * h + 8 * (q >> 2) + m] = frag[q];
-        xs[(p * 2 + h) * 8 + m] = sum;
+        wp[i] = val;
     }
-    __syncthreads();
+    const size_t sb_count = (size_t)n_tiles * ngp * 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < sb_count;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i & 15);
+        const size_t tg = i >> 4;
+        const int g = (int)(tg % ngp);
+        const int t = (int)(tg / ngp);
+        const int n = 16 * t + r;
+        uint32_t val = 0;
+        if (n < N && g < ng)
+            val = (uint32_t)scales[(size_t)n * ng + g] | ((uint32_t)biases[(size_t)n * ng + g] << 16);
+        sbp[i] = val;
+    }
+}
 
-    // ---- lane roles ----
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
+    const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
+    const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
+    __shared__ f32x4 red[WAVES][64];
+
+    constexpr int L = BITS / 4;              // 1 KB loads per pair and wave
+    const int ng = K >> 6;                   // groups per row
+    const int n_pairs = (ng + 1) >> 1;       // 128-wide K steps
+    const int ngp = 2 * n_pairs;
+    const int t = blockIdx.x;                // 16-row tile
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane >> 4;   // k-slot group of the A/B operands, row group of C
     const int r = lane & 15;   // A row / B and C column
     const int h = j >> 1;      // which group of the pair this lane's k slots hold
     const int sub = j & 1;     // which 32-k half of that group
-    const int n = blk * kRowsPerBlock + wave * 16 + r;
-    const bool n_ok = n < N;
-    // A row r carries x row (r & 7) for half (r >> 3); it is non-zero only on
-    // the k slots of that half.
+    const int n = t * 16 + r;
+
+    // This wave's contiguous share of the tile's pairs.
+    const int ppw = (n_pairs + WAVES - 1) / WAVES;
+    const int p_lo = min(n_pairs, wave * ppw);
+    const int p_hi = min(n_pairs, p_lo + ppw);
+
+    // Buffer resources: all lane-dependent offsets are fixed, the per-pair
+    // offsets are wave-uniform (scalar registers).
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(wp + (size_t)t * n_pairs * 64 * L), (short)0, n_pairs * 1024 * L, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t sbres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(sbp + (size_t)t * ngp * 16), (short)0, ngp * 64, kBufferFlags);
+    // A row r carries x row (r & 7) for half (r >> 3) and is non-zero only on
+    // that half's k slots.  Lanes outside that pattern, or with a row >= M,
+    // start past the end of x, where buffer loads return zeros.
     const bool a_act = (h == (r >> 3)) && ((r & 7) < M);
-    const int a_slot = 16 * h + 8 * sub + (r & 7);
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, M * K * 2, kBufferFlags);
+    const unsigned xoff = a_act ? (unsigned)(((r & 7) * K + 64 * h + 32 * sub) * 2) : kOutOfRange;
+    const unsigned woff = (unsigned)lane * 16u;
+    const unsigned sboff = (unsigned)(h * 16 + r) * 4u;
 
-    const uint16_t *srow = scales + (size_t)(n_ok ? n : 0) * ng;
-    const uint16_t *brow = biases + (size_t)(n_ok ? n : 0) * ng;
-    const u32x4 *wrow;
-    if (BITS == 4)
-        wrow = reinterpret_cast<const u32x4 *>(w) + (size_t)(n_ok ? n : 0) * (K >> 5) + 2 * h + sub;
-    else
-        wrow = reinterpret_cast<const u32x4 *>(w) + (size_t)(n_ok ? n : 0) * (K >> 4) + 4 * h + 2 * sub;
-
-    const f32x4 *xs4 = reinterpret_cast<const f32x4 *>(xs);
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int U = (BITS == 4) ? 8 : 4;   // pairs in flight per lane
-    constexpr int W = BITS / 4;              // 16-byte loads per pair per lane
-    for (int p0 = 0; p0 < P; p0 += U) {
-        u32x4 raw[U][W];
-        uint16_t s16[U], b16[U];
+    constexpr int U = 4;   // pairs per batch
+    struct Batch {
+        u32x4 raw[U][L];
+        uint32_t sb[U];
+    };
+    auto load_w = [&](Batch &bt, int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int p = p0 + u;
-            const int g = 2 * (p_begin + p) + h;
-            if (n_ok && p < P && g < ng) {
+            const int p = min(p0 + u, n_pairs - 1);
 #pragma unroll
-                for (int v = 0; v < W; ++v)
-                    raw[u][v] = wrow[(size_t)(p_begin + p) * (4 * W) + v];
-                s16[u] = srow[g];
-                b16[u] = brow[g];
-            } else {
-#pragma unroll
-                for (int v = 0; v < W; ++v)
-                    raw[u][v] = u32x4{0u, 0u, 0u, 0u};
-                s16[u] = 0;
-                b16[u] = 0;
-            }
+            for (int v = 0; v < L; ++v)
+                bt.raw[u][v] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, (p * L + v) * 1024, 0));
+            bt.sb[u] = __builtin_amdgcn_raw_buffer_load_b32(sbres, sboff, p * 128, 0);
         }
+    };
+    auto load_x = [&](u32x4 (&a)[U][4], int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int p = p0 + u;
-            if (p >= P)
+            const int p = min(p0 + u, n_pairs - 1);
+            // the odd last group of a row has no partner: its half reads zeros
+            const unsigned off = (2 * p + h < ng) ? xoff : kOutOfRange;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                a[u][s4] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + s4 * 16u, p * 256, 0));
+        }
+    };
+    auto compute = [&](const Batch &bt, const u32x4 (&a)[U][4], int p0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (p0 + u >= p_hi)
                 break;
             f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 cx = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x8 a = a_act ? __builtin_bit_cast(bf16x8, xf[(p * 4 + t) * 32 + a_slot]) : zero8;
-                bf16x8 b;
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a[u][s4]);
+                bf16x8 bv;
                 if (BITS == 4) {
-                    b = unpack_w4(raw[u][0][t]);
+                    bv = unpack_w4(bt.raw[u][0][s4]);
                 } else {
-                    const u32x4 &lo = raw[u][(t * 2) >> 2];
-                    b = unpack_w8(lo[(t * 2) & 3], lo[(t * 2 + 1) & 3]);
+                    const u32x4 &lo = bt.raw[u][s4 >> 1];
+                    bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
                 }
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+                cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, cx, 0, 0, 0);
             }
-            // C row 4*j + i is x row m = 4*sub + i of half h.
-            const f32x4 xsum = xs4[(p * 2 + h) * 2 + sub];
-            const float s = half_bits_to_float(s16[u]);
-            const float b = half_bits_to_float(b16[u]);
-            const float bb = (BITS == 4) ? fmaf(-128.0f, s, b) : b;
+            // C row 4*j + i is x row m = 4*sub + i of half h; cx holds the
+            // same rows' sums of x over the group.
+            const float s = half_bits_to_float((uint16_t)(bt.sb[u] & 0xFFFFu));
+            const float bias = half_bits_to_float((uint16_t)(bt.sb[u] >> 16));
+            const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[i] = fmaf(s, c[i], acc[i]);
-                acc[i] = fmaf(bb, xsum[i], acc[i]);
+                acc[i] = fmaf(bb, cx[i], acc[i]);
             }
         }
+    };
+
+    // Vector-memory loads complete in issue order, so each batch's x
+    // operands (L2 hits) are requested before the next batch of weights
+    // (HBM): consuming them never waits for the weights still in flight.
+    Batch cur, nxt;
+    u32x4 a[U][4];
+    if (p_lo < p_hi)
+        load_w(cur, p_lo);
+    for (int p0 = p_lo; p0 < p_hi; p0 += U) {
+        load_x(a, p0);
+        if (p0 + U < p_hi)
+            load_w(nxt, p0 + U);
+        compute(cur, a, p0);
+        cur = nxt;
     }
 
-    // Lanes l and l ^ 32 hold the same (m, n) for the two groups of each pair.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc[i] += __shfl_xor(acc[i], 32);
-
-    if (lane < 32 && n_ok) {
+    // Fixed-order reduction: the two groups of a pair (lanes l, l ^ 32), then
+    // the waves in index order.  Neither depends on M.
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && lane < 32 && n < N) {
+        f32x4 tot = red[0][lane] + red[0][lane + 32];
+        for (int ww = 1; ww < WAVES; ++ww)
+            tot += red[ww][lane] + red[ww][lane + 32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * sub + i;
-            if (m < M) {
-                if (splits == 1)
-                    y[(size_t)m * N + n] = acc[i];
-                else
-                    partial[((size_t)split * M + m) * N + n] = acc[i];
-            }
+            if (m < M)
+                y[(size_t)m * N + n] = tot[i];
         }
     }
-    if (splits == 1)
-        return;
-
-    // ---- K splits: the last workgroup of this row block sums them in order ----
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&counters[blk], 1u);
-        s_last = (prev == (unsigned)(splits - 1));
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int e = threadIdx.x; e < M * kRowsPerBlock; e += kThreads) {
-        const int m = e / kRowsPerBlock;
-        const int nn = blk * kRowsPerBlock + e % kRowsPerBlock;
-        if (nn >= N)
-            continue;
-        float v = __builtin_nontemporal_load(&partial[(size_t)m * N + nn]);
-        for (int sp = 1; sp < splits; ++sp)
-            v += __builtin_nontemporal_load(&partial[((size_t)sp * M + m) * N + nn]);
-        y[(size_t)m * N + nn] = v;
-    }
-    if (threadIdx.x == 0)
-        atomicExch(&counters[blk], 0u);
 }
 
 __global__ void fill_zero_kernel(float *__restrict__ y, size_t count) {
@@ -277,42 +288,46 @@ __global__ void fill_zero_kernel(float *__restrict__ y, size_t count) {
         y[i] = 0.0f;
 }
 
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
 } // namespace
 
 QmvPlan qmv_plan(int N, int K) {
     QmvPlan p{};
-    p.n_blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int ng = K / 64;
-    p.n_pairs = (ng + 1) / 2;
-    int S = 1;
-    if (p.n_pairs > 0 && p.n_blocks > 0) {
-        while (p.n_blocks * S < kTargetBlocks &&
-               (p.n_pairs + 2 * S - 1) / (2 * S) >= kMinPairsPerSplit)
-            S *= 2;
-        S = std::max(S, (p.n_pairs + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
-        p.pairs_per_split = (p.n_pairs + S - 1) / S;
-        S = (p.n_pairs + p.pairs_per_split - 1) / p.pairs_per_split;
-    } else {
-        p.pairs_per_split = 0;
-    }
-    p.splits = S;
-    p.lds_bytes = (size_t)p.pairs_per_split * (kFragBytesPerPair + kSumBytesPerPair);
+    p.n_tiles = (N + 15) / 16;
+    p.n_pairs = (K / 64 + 1) / 2;
+    // Long rows are split over 8 waves, short ones over 4, so that even
+    // N = 5120 gives >= 2560 waves; the split depends on K only, never on M.
+    p.waves = K >= 8192 ? 8 : 4;
     return p;
 }
 
-size_t qmv_workspace_bytes(const QmvPlan &p, int M, int N) {
-    if (p.splits <= 1 || M <= 0 || N <= 0)
-        return 0;
-    return kCounterBytes + align256((size_t)p.splits * M * N * sizeof(float));
+size_t qmv_packed_bytes(int bits, int N, int K) {
+    const QmvPlan p = qmv_plan(N, K);
+    return (size_t)p.n_tiles * p.n_pairs * 64 * 16 * (bits / 4);
 }
 
-int qmv_max_rows() { return (int)(kCounterBytes / sizeof(unsigned)) * kRowsPerBlock; }
+size_t qmv_packed_sb_bytes(int N, int K) {
+    const QmvPlan p = qmv_plan(N, K);
+    return (size_t)p.n_tiles * (2 * p.n_pairs) * 16 * 4;
+}
 
-hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
-                      const uint16_t *biases, const uint16_t *x, float *y,
-                      int M, int N, int K, const QmvPlan &plan, void *ws,
+hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
+                       const uint16_t *biases, int N, int K, void *w_packed,
+                       void *sb_packed, hipStream_t stream) {
+    if (N == 0 || K == 0)
+        return hipSuccess;
+    const size_t slots = qmv_packed_bytes(bits, N, K) / 16;
+    const int blocks = (int)std::min<size_t>((slots + 255) / 256, 65536);
+    if (bits == 4)
+        pack_kernel<4><<<blocks, 256, 0, stream>>>(w, scales, biases, (u32x4 *)w_packed,
+                                                   (uint32_t *)sb_packed, N, K);
+    else
+        pack_kernel<8><<<blocks, 256, 0, stream>>>(w, scales, biases, (u32x4 *)w_packed,
+                                                   (uint32_t *)sb_packed, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
+                      const uint16_t *x, float *y, int M, int N, int K,
                       hipStream_t stream) {
     if (M == 0 || N == 0)
         return hipSuccess;
@@ -322,21 +337,21 @@ hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
         fill_zero_kernel<<<blocks, 256, 0, stream>>>(y, count);
         return hipGetLastError();
     }
-    unsigned *counters = nullptr;
-    float *partial = nullptr;
-    if (plan.splits > 1) {
-        counters = reinterpret_cast<unsigned *>(ws);
-        partial = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(ws) + kCounterBytes);
+    const QmvPlan plan = qmv_plan(N, K);
+    const u32x4 *wp = (const u32x4 *)w_packed;
+    const uint32_t *sbp = (const uint32_t *)sb_packed;
+    const dim3 grid(plan.n_tiles);
+    if (bits == 4) {
+        if (plan.waves == 8)
+            qmv_kernel<4, 8><<<grid, 512, 0, stream>>>(wp, sbp, x, y, M, N, K);
+        else
+            qmv_kernel<4, 4><<<grid, 256, 0, stream>>>(wp, sbp, x, y, M, N, K);
+    } else {
+        if (plan.waves == 8)
+            qmv_kernel<8, 8><<<grid, 512, 0, stream>>>(wp, sbp, x, y, M, N, K);
+        else
+            qmv_kernel<8, 4><<<grid, 256, 0, stream>>>(wp, sbp, x, y, M, N, K);
     }
-    dim3 grid(plan.n_blocks, plan.splits);
-    if (bits == 4)
-        qmv_kernel<4><<<grid, kThreads, plan.lds_bytes, stream>>>(
-            w, scales, biases, x, y, M, N, K, plan.pairs_per_split, plan.splits,
-            partial, counters);
-    else
-        qmv_kernel<8><<<grid, kThreads, plan.lds_bytes, stream>>>(
-            w, scales, biases, x, y, M, N, K, plan.pairs_per_split, plan.splits,
-            partial, counters);
     return hipGetLastError();
 }
 

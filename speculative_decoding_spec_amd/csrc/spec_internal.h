@@ -9,23 +9,23 @@
 namespace spec {
 
 // ---------------------------------------------------------------- qmv ----
-// Work decomposition of one qmv call.  It depends on (N, K) only, never on
-// M, so row m of an M-row call reduces in exactly the same order as a
-// one-row call.
+// Work decomposition of one qmv call: one workgroup per 16 weight rows, its
+// waves splitting K.  It depends on (N, K) only, never on M, so row m of an
+// M-row call reduces in exactly the same order as a one-row call.
 struct QmvPlan {
-    int n_blocks;        // 64-row blocks along N (one workgroup column each)
-    int n_pairs;         // 128-wide K steps ("pairs" of two 64-groups)
-    int splits;          // K splits across workgroups (1 = no partials)
-    int pairs_per_split; // K steps per split
-    size_t lds_bytes;    // dynamic LDS per workgroup
+    int n_tiles;   // 16-row tiles = workgroups
+    int n_pairs;   // 128-wide K steps (pairs of 64-groups)
+    int waves;     // waves per workgroup (K split inside the workgroup)
 };
 
 QmvPlan qmv_plan(int N, int K);
-size_t qmv_workspace_bytes(const QmvPlan &p, int M, int N);
-int qmv_max_rows();  // largest N a workspace's counter area supports
-hipError_t launch_qmv(int bits, const void *w, const uint16_t *scales,
-                      const uint16_t *biases, const uint16_t *x, float *y,
-                      int M, int N, int K, const QmvPlan &plan, void *ws,
+size_t qmv_packed_bytes(int bits, int N, int K);
+size_t qmv_packed_sb_bytes(int N, int K);
+hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
+                       const uint16_t *biases, int N, int K, void *w_packed,
+                       void *sb_packed, hipStream_t stream);
+hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
+                      const uint16_t *x, float *y, int M, int N, int K,
                       hipStream_t stream);
 
 // ------------------------------------------------------------ sampling ----

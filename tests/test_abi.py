@@ -47,9 +47,12 @@ def test_status_strings(L):
     assert L.spec_version() >= 100
 
 
-def qmv(L, fn="spec_qmv_w4", w=P, s=P, b=P, x=P, y=P, M=4, N=64, K=128, G=64,
-        ws=None, nbytes=0):
-    return getattr(L, fn)(w, s, b, x, y, M, N, K, G, ws, nbytes, None)
+def qmv(L, fn="spec_qmv_w4", w=P, sb=P, x=P, y=P, M=4, N=64, K=128, G=64):
+    return getattr(L, fn)(w, sb, x, y, M, N, K, G, None)
+
+
+def pack(L, fn="spec_pack_w4", w=P, s=P, b=P, N=64, K=128, G=64, wp=P, sbp=P2):
+    return getattr(L, fn)(w, s, b, N, K, G, wp, sbp, None)
 
 
 @pytest.mark.parametrize("fn", ["spec_qmv_w4", "spec_qmv_w8"])
@@ -59,6 +62,7 @@ def test_qmv_validation(L, fn):
     assert qmv(L, fn, G=32, K=128) == UNSUPPORTED
     assert qmv(L, fn, M=9) == UNSUPPORTED
     assert qmv(L, fn, w=None) == INVALID
+    assert qmv(L, fn, sb=None) == INVALID
     assert qmv(L, fn, x=None) == INVALID
     assert qmv(L, fn, y=None) == INVALID
     assert qmv(L, fn, w=MIS) == UNSUPPORTED
@@ -67,14 +71,26 @@ def test_qmv_validation(L, fn):
     assert qmv(L, fn, N=0) == OK
 
 
-def test_qmv_workspace_rules(L):
-    M, N, K = 8, 1024, 5120                        # small N: K is split
-    need = L.spec_qmv_workspace_size(M, N, K, 64)
-    assert need > 0
-    assert qmv(L, M=M, N=N, K=K, ws=None, nbytes=0) == WORKSPACE
-    assert qmv(L, M=M, N=N, K=K, ws=P2, nbytes=need - 1) == WORKSPACE
-    assert qmv(L, M=M, N=N, K=K, ws=ctypes.c_void_p(0x20010), nbytes=need) == WORKSPACE
-    assert L.spec_qmv_workspace_size(8, 151936, 64, 64) == 0  # one step: no split
+@pytest.mark.parametrize("fn", ["spec_pack_w4", "spec_pack_w8"])
+def test_pack_validation(L, fn):
+    assert pack(L, fn, N=-1) == INVALID
+    assert pack(L, fn, K=96) == INVALID            # K % G != 0
+    assert pack(L, fn, G=128, K=256) == UNSUPPORTED
+    assert pack(L, fn, w=None) == INVALID
+    assert pack(L, fn, s=None) == INVALID
+    assert pack(L, fn, wp=None) == INVALID
+    assert pack(L, fn, w=MIS) == UNSUPPORTED
+    assert pack(L, fn, N=0) == OK
+
+
+def test_packed_sizes(L):
+    # 16-row tiles x 128-wide K steps of 1 KB (W4) / 2 KB (W8); one 32-bit
+    # scale/bias word per row and (padded) group.
+    assert L.spec_qmv_packed_weight_bytes(4, 5120, 17408, 64) == 320 * 136 * 1024
+    assert L.spec_qmv_packed_weight_bytes(8, 151936, 5120, 64) == 9496 * 40 * 2048
+    assert L.spec_qmv_packed_weight_bytes(4, 100, 192, 64) == 7 * 2 * 1024   # ragged N, odd groups
+    assert L.spec_qmv_packed_sb_bytes(100, 192, 64) == 7 * 4 * 16 * 4
+    assert L.spec_qmv_packed_weight_bytes(4, 64, 100, 64) == 0           # invalid shape
 
 
 def accept(L, t=P, d=P, tok=P, u=P, B=2, D=3, V=1024, T=0.6, k=0, p=1.0,

@@ -27,8 +27,9 @@ def dev():
 def run(bits, w, s, b, x, dev, G=64):
     import speculative_decoding_spec_amd as spec
     wt, st, bt = parity.dev_qweights(w, s, b, dev)
+    pack = spec.spec_pack_w4 if bits == 4 else spec.spec_pack_w8
     fn = spec.spec_qmv_w4 if bits == 4 else spec.spec_qmv_w8
-    y = fn(wt, st, bt, parity.dev_x(x, dev), G=G)
+    y = fn(pack(wt, st, bt, G=G), parity.dev_x(x, dev))
     return y.cpu().numpy()
 
 
@@ -93,17 +94,17 @@ def test_degenerate_shapes(dev):
     import torch
     import speculative_decoding_spec_amd as spec
     # K = 0: every output is an empty sum.
-    w = torch.zeros((16, 0), dtype=torch.int32, device=dev)
-    s = torch.zeros((16, 0), dtype=torch.float16, device=dev)
-    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=dev)
+    pk = spec.spec_pack_w4(torch.zeros((16, 0), dtype=torch.int32, device=dev),
+                           torch.zeros((16, 0), dtype=torch.float16, device=dev),
+                           torch.zeros((16, 0), dtype=torch.float16, device=dev))
     y = torch.full((3, 16), 7.0, device=dev)
-    spec.spec_qmv_w4(w, s, s, x, y=y)
+    spec.spec_qmv_w4(pk, torch.zeros((3, 0), dtype=torch.bfloat16, device=dev), y=y)
     assert torch.all(y == 0)
-    # M = 0 and N = 0 are no-ops.
-    spec.spec_qmv_w4(torch.zeros((16, 8), dtype=torch.int32, device=dev),
-                     torch.zeros((16, 1), dtype=torch.float16, device=dev),
-                     torch.zeros((16, 1), dtype=torch.float16, device=dev),
-                     torch.zeros((0, 64), dtype=torch.bfloat16, device=dev))
+    # M = 0 is a no-op.
+    pk = spec.spec_pack_w4(torch.zeros((16, 8), dtype=torch.int32, device=dev),
+                           torch.zeros((16, 1), dtype=torch.float16, device=dev),
+                           torch.zeros((16, 1), dtype=torch.float16, device=dev))
+    spec.spec_qmv_w4(pk, torch.zeros((0, 64), dtype=torch.bfloat16, device=dev))
     torch.cuda.synchronize()
 
 
