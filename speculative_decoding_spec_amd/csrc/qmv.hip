@@ -146,36 +146,44 @@ __global__ __launch_bounds__(256) void pack_kernel(
     }
 }
 
-template <int BITS, int WAVES>
+template <int BITS, int WAVES, int T>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
     const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
-    __shared__ f32x4 red[WAVES][64];
+    __shared__ f32x4 red[WAVES][T][64];
 
-    constexpr int L = BITS / 4;              // 1 KB loads per pair and wave
+    constexpr int L = BITS / 4;              // 1 KB loads per pair, tile and wave
     const int ng = K >> 6;                   // groups per row
     const int n_pairs = (ng + 1) >> 1;       // 128-wide K steps
     const int ngp = 2 * n_pairs;
-    const int t = blockIdx.x;                // 16-row tile
+    const int n_tiles = (N + 15) >> 4;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane >> 4;   // k-slot group of the A/B operands, row group of C
     const int r = lane & 15;   // A row / B and C column
     const int h = j >> 1;      // which group of the pair this lane's k slots hold
     const int sub = j & 1;     // which 32-k half of that group
-    const int n = t * 16 + r;
 
-    // This wave's contiguous share of the tile's pairs.
+    // This wave's contiguous share of the pairs, for each of the T tiles.
     const int ppw = (n_pairs + WAVES - 1) / WAVES;
     const int p_lo = min(n_pairs, wave * ppw);
     const int p_hi = min(n_pairs, p_lo + ppw);
 
-    // Buffer resources: all lane-dependent offsets are fixed, the per-pair
-    // offsets are wave-uniform (scalar registers).
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(wp + (size_t)t * n_pairs * 64 * L), (short)0, n_pairs * 1024 * L, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t sbres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(sbp + (size_t)t * ngp * 16), (short)0, ngp * 64, kBufferFlags);
+    // Buffer resources: lane-dependent offsets are fixed, per-pair offsets
+    // are wave-uniform (scalar registers).  A tile past the last one gets an
+    // empty resource, so its loads return zeros.
+    __amdgpu_buffer_rsrc_t wres[T], sbres[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+        const int t = blockIdx.x * T + tt;
+        const bool there = t < n_tiles;
+        wres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(wp + (size_t)min(t, n_tiles - 1) * n_pairs * 64 * L), (short)0,
+            there ? n_pairs * 1024 * L : 0, kBufferFlags);
+        sbres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(sbp + (size_t)min(t, n_tiles - 1) * ngp * 16), (short)0,
+            there ? ngp * 64 : 0, kBufferFlags);
+    }
     // A row r carries x row (r & 7) for half (r >> 3) and is non-zero only on
     // that half's k slots.  Lanes outside that pattern, or with a row >= M,
     // start past the end of x, where buffer loads return zeros.
@@ -187,22 +195,28 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const unsigned sboff = (unsigned)(h * 16 + r) * 4u;
 
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+        acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int U = 4;   // pairs per batch
+    constexpr int U = (T == 1) ? 4 : (T == 2 ? 2 : 1);   // pairs per batch
     struct Batch {
-        u32x4 raw[U][L];
-        uint32_t sb[U];
+        u32x4 raw[U][T][L];
+        uint32_t sb[U][T];
     };
     auto load_w = [&](Batch &bt, int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int p = min(p0 + u, n_pairs - 1);
 #pragma unroll
-            for (int v = 0; v < L; ++v)
-                bt.raw[u][v] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, (p * L + v) * 1024, 0));
-            bt.sb[u] = __builtin_amdgcn_raw_buffer_load_b32(sbres, sboff, p * 128, 0);
+            for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+                for (int v = 0; v < L; ++v)
+                    bt.raw[u][tt][v] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[tt], woff, (p * L + v) * 1024, 0));
+                bt.sb[u][tt] = __builtin_amdgcn_raw_buffer_load_b32(sbres[tt], sboff, p * 128, 0);
+            }
         }
     };
     auto load_x = [&](u32x4 (&a)[U][4], int p0) {
@@ -222,30 +236,39 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         for (int u = 0; u < U; ++u) {
             if (p0 + u >= p_hi)
                 break;
-            f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 c[T];
             f32x4 cx = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt)
+                c[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 const bf16x8 av = __builtin_bit_cast(bf16x8, a[u][s4]);
-                bf16x8 bv;
-                if (BITS == 4) {
-                    bv = unpack_w4(bt.raw[u][0][s4]);
-                } else {
-                    const u32x4 &lo = bt.raw[u][s4 >> 1];
-                    bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
-                }
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
                 cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, cx, 0, 0, 0);
+#pragma unroll
+                for (int tt = 0; tt < T; ++tt) {
+                    bf16x8 bv;
+                    if (BITS == 4) {
+                        bv = unpack_w4(bt.raw[u][tt][0][s4]);
+                    } else {
+                        const u32x4 &lo = bt.raw[u][tt][s4 >> 1];
+                        bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
+                    }
+                    c[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c[tt], 0, 0, 0);
+                }
             }
             // C row 4*j + i is x row m = 4*sub + i of half h; cx holds the
             // same rows' sums of x over the group.
-            const float s = half_bits_to_float((uint16_t)(bt.sb[u] & 0xFFFFu));
-            const float bias = half_bits_to_float((uint16_t)(bt.sb[u] >> 16));
-            const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] = fmaf(s, c[i], acc[i]);
-                acc[i] = fmaf(bb, cx[i], acc[i]);
+            for (int tt = 0; tt < T; ++tt) {
+                const float s = half_bits_to_float((uint16_t)(bt.sb[u][tt] & 0xFFFFu));
+                const float bias = half_bits_to_float((uint16_t)(bt.sb[u][tt] >> 16));
+                const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[tt][i] = fmaf(s, c[tt][i], acc[tt][i]);
+                    acc[tt][i] = fmaf(bb, cx[i], acc[tt][i]);
+                }
             }
         }
     };
@@ -267,17 +290,25 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
 
     // Fixed-order reduction: the two groups of a pair (lanes l, l ^ 32), then
     // the waves in index order.  Neither depends on M.
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0 && lane < 32 && n < N) {
-        f32x4 tot = red[0][lane] + red[0][lane + 32];
-        for (int ww = 1; ww < WAVES; ++ww)
-            tot += red[ww][lane] + red[ww][lane + 32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * sub + i;
-            if (m < M)
-                y[(size_t)m * N + n] = tot[i];
+    for (int tt = 0; tt < T; ++tt)
+        red[wave][tt][lane] = acc[tt];
+    __syncthreads();
+    if (wave == 0 && lane < 32) {
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            const int n = (blockIdx.x * T + tt) * 16 + r;
+            if (n >= N)
+                continue;
+            f32x4 tot = red[0][tt][lane] + red[0][tt][lane + 32];
+            for (int ww = 1; ww < WAVES; ++ww)
+                tot += red[ww][tt][lane] + red[ww][tt][lane + 32];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * sub + i;
+                if (m < M)
+                    y[(size_t)m * N + n] = tot[i];
+            }
         }
     }
 }
@@ -290,23 +321,35 @@ __global__ void fill_zero_kernel(float *__restrict__ y, size_t count) {
 
 } // namespace
 
-QmvPlan qmv_plan(int N, int K) {
+QmvPlan qmv_plan(int bits, int N, int K) {
     QmvPlan p{};
     p.n_tiles = (N + 15) / 16;
     p.n_pairs = (K / 64 + 1) / 2;
-    // Long rows are split over 8 waves, short ones over 4, so that even
-    // N = 5120 gives >= 2560 waves; the split depends on K only, never on M.
-    p.waves = K >= 8192 ? 8 : 4;
+    // Enough tiles: each wave serves two (or, for very wide matrices, four)
+    // tiles with one x operand, cutting the x traffic by that factor; 4 waves
+    // split K.  (W8 streams twice the bytes per x fragment, so two suffice.)  Few tiles: one tile per workgroup and K
+    // split over 4 or 8 waves, so even N = 5120 gives >= 2560 waves.  The
+    // choice depends on (N, K) only, never on M.
+    if (p.n_tiles >= 4096 && bits == 4) {
+        p.tiles_per_wave = 4;
+        p.waves = 4;
+    } else if (p.n_tiles >= 1024) {
+        p.tiles_per_wave = 2;
+        p.waves = 4;
+    } else {
+        p.tiles_per_wave = 1;
+        p.waves = K >= 8192 ? 8 : 4;
+    }
     return p;
 }
 
 size_t qmv_packed_bytes(int bits, int N, int K) {
-    const QmvPlan p = qmv_plan(N, K);
+    const QmvPlan p = qmv_plan(bits, N, K);
     return (size_t)p.n_tiles * p.n_pairs * 64 * 16 * (bits / 4);
 }
 
 size_t qmv_packed_sb_bytes(int N, int K) {
-    const QmvPlan p = qmv_plan(N, K);
+    const QmvPlan p = qmv_plan(4, N, K);
     return (size_t)p.n_tiles * (2 * p.n_pairs) * 16 * 4;
 }
 
@@ -337,21 +380,32 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
         fill_zero_kernel<<<blocks, 256, 0, stream>>>(y, count);
         return hipGetLastError();
     }
-    const QmvPlan plan = qmv_plan(N, K);
+    const QmvPlan plan = qmv_plan(bits, N, K);
     const u32x4 *wp = (const u32x4 *)w_packed;
     const uint32_t *sbp = (const uint32_t *)sb_packed;
-    const dim3 grid(plan.n_tiles);
+    const dim3 grid((plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave);
+#define SPEC_QMV_LAUNCH(B, W, TT) \
+    qmv_kernel<B, W, TT><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K)
     if (bits == 4) {
-        if (plan.waves == 8)
-            qmv_kernel<4, 8><<<grid, 512, 0, stream>>>(wp, sbp, x, y, M, N, K);
+        if (plan.tiles_per_wave == 4)
+            SPEC_QMV_LAUNCH(4, 4, 4);
+        else if (plan.tiles_per_wave == 2)
+            SPEC_QMV_LAUNCH(4, 4, 2);
+        else if (plan.waves == 8)
+            SPEC_QMV_LAUNCH(4, 8, 1);
         else
-            qmv_kernel<4, 4><<<grid, 256, 0, stream>>>(wp, sbp, x, y, M, N, K);
+            SPEC_QMV_LAUNCH(4, 4, 1);
     } else {
-        if (plan.waves == 8)
-            qmv_kernel<8, 8><<<grid, 512, 0, stream>>>(wp, sbp, x, y, M, N, K);
+        if (plan.tiles_per_wave == 4)
+            SPEC_QMV_LAUNCH(8, 4, 4);
+        else if (plan.tiles_per_wave == 2)
+            SPEC_QMV_LAUNCH(8, 4, 2);
+        else if (plan.waves == 8)
+            SPEC_QMV_LAUNCH(8, 8, 1);
         else
-            qmv_kernel<8, 4><<<grid, 256, 0, stream>>>(wp, sbp, x, y, M, N, K);
+            SPEC_QMV_LAUNCH(8, 4, 1);
     }
+#undef SPEC_QMV_LAUNCH
     return hipGetLastError();
 }
 

@@ -10,15 +10,16 @@ namespace spec {
 
 // ---------------------------------------------------------------- qmv ----
 // Work decomposition of one qmv call: one workgroup per 16 weight rows, its
-// waves splitting K.  It depends on (N, K) only, never on M, so row m of an
+// waves splitting K.  It depends on (bits, N, K) only, never on M, so row m of an
 // M-row call reduces in exactly the same order as a one-row call.
 struct QmvPlan {
     int n_tiles;   // 16-row tiles = workgroups
     int n_pairs;   // 128-wide K steps (pairs of 64-groups)
     int waves;     // waves per workgroup (K split inside the workgroup)
+    int tiles_per_wave;  // tiles each wave serves with one x operand
 };
 
-QmvPlan qmv_plan(int N, int K);
+QmvPlan qmv_plan(int bits, int N, int K);
 size_t qmv_packed_bytes(int bits, int N, int K);
 size_t qmv_packed_sb_bytes(int N, int K);
 hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
