@@ -27,11 +27,12 @@
  *    SPEC_ERR_INVALID / SPEC_ERR_UNSUPPORTED / SPEC_ERR_WORKSPACE and
  *    enqueues nothing.  SPEC_ERR_DEVICE means a HIP call failed.
  *  - Workspaces: the caller allocates `*_workspace_size(...)` bytes of device
- *    memory, 256-byte aligned, and fills it with zeros once before its first
- *    use.  Every call leaves the workspace's counters at zero again, so a
- *    workspace can be reused by any later call of the same entry point whose
- *    size query is not larger.  Calls sharing one workspace must be ordered
- *    on one stream.
+ *    memory, 256-byte aligned.  Its contents need no initialization and
+ *    carry nothing from one call to the next (every call writes what it
+ *    reads), so a workspace can be reused by any later call whose size query
+ *    is not larger.  Calls sharing one workspace must be ordered on one
+ *    stream.  No kernel of the library waits for another workgroup: there
+ *    are no counters, spin waits or device-scope fences.
  */
 #ifndef SPEC_H
 #define SPEC_H

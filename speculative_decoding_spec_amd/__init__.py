@@ -113,22 +113,22 @@ def _require(t, dtype, name, device=None):
     return t
 
 
-# ---- workspaces: zero-filled device buffers cached per (device, purpose) ----
+# ---- workspaces: device buffers cached per (device, purpose) ----
 _ws_cache: dict = {}
 
 
 def get_workspace(nbytes: int, device, key: str = "default"):
-    """A zero-filled, 256-byte aligned device buffer of at least nbytes.
+    """A 256-byte aligned device buffer of at least nbytes.
 
-    The library leaves its counters at zero after every call, so one buffer
-    serves every later call on the same stream."""
+    Workspaces need no initialization and hold nothing between calls, so one
+    buffer serves every later call ordered on the same stream."""
     import torch
     if nbytes == 0:
         return None
     slot = (str(device), key)
     buf = _ws_cache.get(slot)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
         assert buf.data_ptr() % 256 == 0
         _ws_cache[slot] = buf
     return buf

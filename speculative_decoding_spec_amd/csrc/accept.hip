@@ -11,22 +11,25 @@
 // gives one.  Sampling uses the temperature / top-k / top-p settings of the
 // MTPLX benchmark ("QWEN 3.6 27B @ 63 TPS").
 //
-// Kernels:
-//  1. row_stats  -- grid (row, chunk).  One streaming pass over every fp32
+// Kernels (no workgroup ever waits for, or signals, another: each step's
+// results reach the next through the kernel boundary, so there are no
+// fences, counters or spin waits):
+//  1. row_chunk  -- grid (row, chunk).  One streaming pass over every fp32
 //     logit.  Full-vocabulary mode: per-chunk running max and sum of
 //     exp2((z - max) * log2(e)/T).  Candidate mode (top-k active, top-p, or
-//     greedy): the chunk's top-k (logit, index) keys by radix select.  The
-//     workgroup that finishes a row last merges its chunks in chunk order
-//     into the row's final statistics (max, normalizer, kept candidates).
-//  2. accept     -- grid (sequence, chunk).  Every workgroup recomputes the
-//     D ratio tests from the row statistics (a handful of gathers), then
-//     sums the draw distribution (residual at the rejected position, or the
-//     bonus row) over its vocabulary chunk.  The last workgroup of the
-//     sequence turns u_D into a target mass, finds the chunk that holds it
-//     and scans that chunk in vocabulary order: an inverse-CDF draw with no
-//     sort.  In candidate mode one workgroup does the draw over <= 256
-//     candidates.
-//  3. probs      -- dense write of the distributions (spec_sample_probs).
+//     greedy): the chunk's top-k (logit, index) keys by radix select.  A row
+//     that is a single chunk is finalized right here.
+//  2. row_merge  -- grid (row), only when rows span several chunks: merges
+//     the chunks in chunk order into the row's final statistics.
+//  3. draw_sums  -- grid (sequence, chunk), full-vocabulary mode: recomputes
+//     the D ratio tests from the row statistics (a handful of gathers) and
+//     sums the draw distribution -- residual max(0, p - q) at the rejected
+//     position, or the bonus row -- over every 256-token block.
+//  4. draw_final -- grid (sequence): decisions, then the inverse-CDF draw:
+//     scan the block sums for the block holding u * total, re-read that one
+//     block and scan it in vocabulary order.  In candidate mode the draw runs
+//     over the <= 256 kept candidates instead.
+//  5. probs      -- dense write of the distributions (spec_sample_probs).
 //
 // Every reduction runs in a fixed order, so results are deterministic.
 #include "spec_internal.h"
@@ -43,22 +46,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxCand = 256;       // top-k cap in candidate mode
 constexpr int kCandChunk = 4096;    // logits per workgroup in candidate mode
 constexpr int kTargetBlocks = 1024;
+constexpr int kBlock = 256;         // tokens per draw block (64 lanes x 4)
 
 constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
-
-// The workspace starts with two fixed counter areas (rows, then sequences)
-// that no plan uses for anything else, so calls of any shape can share one
-// workspace: every call leaves its counters at zero.  Row statistics are
-// launched in batches of at most kRowSlots rows when a row spans several
-// chunks; sequences only use counters when the batch is small.
-constexpr int kRowSlots = 131072;
-constexpr int kSeqSlots = 131072;
-
-// Release: make this workgroup's earlier global writes visible device-wide
-// before the counter increment.  Acquire: after observing the last
-// increment, see every other workgroup's writes.
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 struct RowFinal {
     float m;      // max logit
@@ -92,13 +82,11 @@ struct Rows {
 };
 
 struct Ws {
-    unsigned *row_cnt;
-    unsigned *seq_cnt;
     ChunkStat *chunk_stats;     // [rows][chunks]
     uint64_t *chunk_keys;       // [rows][chunks][k]  (candidate mode)
     RowFinal *row_final;        // [rows]
     uint64_t *row_keys;         // [rows][k]          (candidate mode)
-    float2 *seq_sums;           // [B][chunks3]  (residual mass, target mass)
+    float2 *block_sums;         // [B][nblocks]  (draw mass, target mass)
 };
 
 // ---------------------------------------------------------------- keys ----
@@ -308,20 +296,49 @@ __device__ void block_sort_desc(uint64_t *keys, int n) {
     }
 }
 
-// ------------------------------------------------------------- kernel 1 ----
+// ------------------------------------------------------- row statistics ----
 struct StatsShared {
     SelectShared sel;
     uint64_t keys[kMaxCand * 2];
     float fsh[kWaves];
     float fsh2[kWaves];
     int ish[kWaves];
-    int last;
 };
 
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(
-    Rows rows, int row0, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
+// Sorted candidates -> the row's final statistics (top-p cut, normalizer).
+// keys[0..got) sorted by rank, in LDS; called by all threads.
+__device__ void finalize_candidates(const uint64_t *keys, int got, int flags,
+                                    const SamplingParams &sp, int r, Ws &ws) {
+    if (threadIdx.x == 0) {
+        const float m = key_logit(keys[0]);
+        float cum = 0.0f;
+        for (int i = 0; i < got; ++i)
+            cum += weight(key_logit(keys[i]), m, sp.scale);
+        const float S_all = cum;
+        int kept = got;
+        float S_kept = S_all;
+        if (sp.use_p) {
+            cum = 0.0f;
+            for (int i = 0; i < got; ++i) {
+                cum += weight(key_logit(keys[i]), m, sp.scale);
+                if (cum / S_all >= sp.top_p) {
+                    kept = i + 1;
+                    break;
+                }
+            }
+            S_kept = (kept == got) ? S_all : cum;
+        }
+        ws.row_final[r] = RowFinal{m, 1.0f / S_kept, kept, flags};
+    }
+    uint64_t *rk = ws.row_keys + (size_t)r * sp.k_eff;
+    for (int i = threadIdx.x; i < sp.k_eff; i += kThreads)
+        rk[i] = (i < got) ? keys[i] : 0;
+}
+
+__global__ __launch_bounds__(kThreads) void row_chunk_kernel(
+    Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
     __shared__ StatsShared sh;
-    const int r = row0 + blockIdx.x;
+    const int r = blockIdx.x;
     const int c = blockIdx.y;
     const int V = rows.V;
     const float *z = rows.row(r);
@@ -333,8 +350,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
     if (!sp.candidates) {
         // ---- running max and normalizer over the chunk ----
         float m = -INFINITY, S = 0.0f;
-        const bool vec = ((V & 3) == 0);
-        if (vec) {
+        if ((V & 3) == 0) {
             const float4 *z4 = reinterpret_cast<const float4 *>(z);
             for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 16) {
                 // Branch-free: clamp each load into the chunk and mask the
@@ -390,57 +406,56 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
             float mm = sh.fsh[0], SS = sh.fsh2[0];
             for (int w = 1; w < kWaves; ++w)
                 merge_ms(mm, SS, sh.fsh[w], sh.fsh2[w], scale);
-            ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{mm, SS, bad, finite};
+            if (chunks == 1)
+                ws.row_final[r] = RowFinal{mm, 1.0f / SS, 0, (bad || !finite) ? kInvalid : 0};
+            else
+                ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{mm, SS, bad, finite};
         }
-    } else {
-        // ---- candidate mode: the chunk's top-k keys ----
-        constexpr int E = kCandChunk / kThreads;  // 16 keys per thread
-        uint64_t mine[E];
-#pragma unroll
-        for (int q = 0; q < E; ++q) {
-            const int e = lo + q * kThreads + threadIdx.x;
-            if (e < hi) {
-                const float v = z[e];
-                bad |= (v != v) | (v == INFINITY);
-                finite |= (v > -INFINITY) & (v < INFINITY);
-                mine[q] = make_key(v, e);
-            } else {
-                mine[q] = 0;  // below every real key; never selected (see n)
-            }
-        }
-        const int n = hi - lo;
-        auto each = [&](auto f) {
-#pragma unroll
-            for (int q = 0; q < E; ++q)
-                if (lo + q * kThreads + (int)threadIdx.x < hi)
-                    f(mine[q]);
-        };
-        const int got = block_select_topk(each, n, sp.k_eff, sh.keys, kMaxCand, sh.sel);
-        uint64_t *dst = ws.chunk_keys + ((size_t)r * chunks + c) * sp.k_eff;
-        for (int i = threadIdx.x; i < sp.k_eff; i += kThreads)
-            dst[i] = (i < got) ? sh.keys[i] : 0;
-        bad = block_or(bad, sh.ish);
-        finite = block_or(finite, sh.ish);
-        if (threadIdx.x == 0)
-            ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{0.0f, 0.0f, bad, finite};
+        return;
     }
 
-    // ---- the last chunk of this row merges all chunks in chunk order ----
-    if (chunks > 1) {
-        release_agent();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const unsigned prev = atomicAdd(&ws.row_cnt[blockIdx.x], 1u);
-            sh.last = (prev == (unsigned)(chunks - 1));
+    // ---- candidate mode: the chunk's top-k keys ----
+    constexpr int E = kCandChunk / kThreads;  // 16 keys per thread
+    uint64_t mine[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+        const int e = lo + q * kThreads + threadIdx.x;
+        if (e < hi) {
+            const float v = z[e];
+            bad |= (v != v) | (v == INFINITY);
+            finite |= (v > -INFINITY) & (v < INFINITY);
+            mine[q] = make_key(v, e);
+        } else {
+            mine[q] = 0;  // below every real key; never visited (see each)
         }
-        __syncthreads();
-        if (!sh.last)
-            return;
-        acquire_agent();
-    } else {
-        __syncthreads();
     }
+    const int n = hi - lo;
+    auto each = [&](auto f) {
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            if (lo + q * kThreads + (int)threadIdx.x < hi)
+                f(mine[q]);
+    };
+    const int got = block_select_topk(each, n, sp.k_eff, sh.keys, kMaxCand, sh.sel);
+    bad = block_or(bad, sh.ish);
+    finite = block_or(finite, sh.ish);
+    if (chunks == 1) {
+        block_sort_desc(sh.keys, got);
+        finalize_candidates(sh.keys, got, (bad || !finite) ? kInvalid : 0, sp, r, ws);
+        return;
+    }
+    uint64_t *dst = ws.chunk_keys + ((size_t)r * chunks + c) * sp.k_eff;
+    for (int i = threadIdx.x; i < sp.k_eff; i += kThreads)
+        dst[i] = (i < got) ? sh.keys[i] : 0;
+    if (threadIdx.x == 0)
+        ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{0.0f, 0.0f, bad, finite};
+}
 
+__global__ __launch_bounds__(kThreads) void row_merge_kernel(
+    Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
+    __shared__ StatsShared sh;
+    const int r = blockIdx.x;
+    const int V = rows.V;
     int rbad = 0, rfin = 0;
     for (int cc = 0; cc < chunks; ++cc) {
         const ChunkStat st = ws.chunk_stats[(size_t)r * chunks + cc];
@@ -448,27 +463,23 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
         rfin |= st.finite;
     }
     const int flags = (rbad || !rfin) ? kInvalid : 0;
-
     if (!sp.candidates) {
         if (threadIdx.x == 0) {
             float m = -INFINITY, S = 0.0f;
             for (int cc = 0; cc < chunks; ++cc) {
                 const ChunkStat st = ws.chunk_stats[(size_t)r * chunks + cc];
-                merge_ms(m, S, st.m, st.S, scale);
+                merge_ms(m, S, st.m, st.S, sp.scale);
             }
             ws.row_final[r] = RowFinal{m, 1.0f / S, 0, flags};
-            if (chunks > 1)
-                atomicExch(&ws.row_cnt[blockIdx.x], 0u);
         }
         return;
     }
-
     const int k = sp.k_eff;
     const uint64_t *ck = ws.chunk_keys + (size_t)r * chunks * k;
     const int total = chunks * k;
     auto each_g = [&](auto f) {
         for (int i = threadIdx.x; i < total; i += kThreads) {
-            const uint64_t key = __builtin_nontemporal_load(&ck[i]);
+            const uint64_t key = ck[i];
             if (key != 0)
                 f(key);
         }
@@ -479,38 +490,10 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
         n_real += min(k, min(V, (cc + 1) * chunk_len) - cc * chunk_len);
     const int got = block_select_topk(each_g, n_real, k, sh.keys, kMaxCand, sh.sel);
     block_sort_desc(sh.keys, got);
-    if (threadIdx.x == 0) {
-        const float m = key_logit(sh.keys[0]);
-        float cum = 0.0f;
-        for (int i = 0; i < got; ++i)
-            cum += weight(key_logit(sh.keys[i]), m, scale);
-        const float S_all = cum;
-        int kept = got;
-        float S_kept = S_all;
-        if (sp.use_p) {
-            cum = 0.0f;
-            for (int i = 0; i < got; ++i) {
-                cum += weight(key_logit(sh.keys[i]), m, scale);
-                if (cum / S_all >= sp.top_p) {
-                    kept = i + 1;
-                    break;
-                }
-            }
-            if (kept == got) {
-                cum = S_all;
-            }
-            S_kept = cum;
-        }
-        ws.row_final[r] = RowFinal{m, 1.0f / S_kept, kept, flags};
-        if (chunks > 1)
-            atomicExch(&ws.row_cnt[blockIdx.x], 0u);
-    }
-    uint64_t *rk = ws.row_keys + (size_t)r * k;
-    for (int i = threadIdx.x; i < k; i += kThreads)
-        rk[i] = (i < got) ? sh.keys[i] : 0;
+    finalize_candidates(sh.keys, got, flags, sp, r, ws);
 }
 
-// ------------------------------------------------------------- kernel 2 ----
+// ---------------------------------------------------------- verification ----
 // Probability of token x under row r's final distribution, given its logit.
 __device__ __forceinline__ float row_prob(const RowFinal &f, const uint64_t *keys,
                                           bool candidates, float scale, float zx, int x) {
@@ -519,21 +502,8 @@ __device__ __forceinline__ float row_prob(const RowFinal &f, const uint64_t *key
     return weight(zx, f.m, scale) * f.inv;
 }
 
-struct AcceptShared {
-    float fsh[kWaves];
-    int ish[kWaves];
-    int last;
-    int seq_L;
-    int seq_ok;
-    float2 sums[64];
-    // candidate draw
-    uint64_t ckey[kMaxCand];   // (index-major key for sorting) index << 32 | float bits of r
-    float cw[kMaxCand];
-    float cp[kMaxCand];
-    int found;
-};
-
-// Decisions of sequence b from the row statistics: returns L (0..D) or -1.
+// Decisions of sequence b from the row statistics: returns L (0..D) or -1
+// for an invalid sequence.  p_out / q_out (nullable) get P_i(d_i), Q_i(d_i).
 __device__ int decide(const Rows &rows, const Ws &ws, const SamplingParams &sp,
                       const int32_t *draft_tokens, const float *uniforms, int b,
                       float *p_out, float *q_out) {
@@ -565,74 +535,160 @@ __device__ int decide(const Rows &rows, const Ws &ws, const SamplingParams &sp,
     return L;
 }
 
-__global__ __launch_bounds__(kThreads) void accept_kernel(
+// The draw distribution of sequence b once L is known: target row L, and
+// for a residual (L < D) the draft row L as well.
+struct DrawRows {
+    bool residual;
+    RowFinal ft, fd;
+    const float *zt, *zd;
+    const uint64_t *kt, *kd;
+};
+
+__device__ DrawRows draw_rows(const Rows &rows, const Ws &ws, const SamplingParams &sp, int b, int L) {
+    DrawRows d;
+    d.residual = L < rows.D;
+    const int tr = rows.target_row(b, L);
+    d.ft = ws.row_final[tr];
+    d.zt = rows.row(tr);
+    d.kt = ws.row_keys + (size_t)tr * sp.k_eff;
+    if (d.residual) {
+        const int dr = rows.draft_row(b, L);
+        d.fd = ws.row_final[dr];
+        d.zd = rows.row(dr);
+        d.kd = ws.row_keys + (size_t)dr * sp.k_eff;
+    } else {
+        d.fd = RowFinal{0.0f, 1.0f, 0, 0};
+        d.zd = d.zt;
+        d.kd = d.kt;
+    }
+    return d;
+}
+
+// Weights of token x: (residual max(0, p - q) or p, and p), full vocabulary.
+__device__ __forceinline__ float2 draw_weight(const DrawRows &d, float scale, float zt, float zd) {
+    const float p = weight(zt, d.ft.m, scale) * d.ft.inv;
+    if (!d.residual)
+        return make_float2(p, p);
+    const float q = weight(zd, d.fd.m, scale) * d.fd.inv;
+    return make_float2(fmaxf(p - q, 0.0f), p);
+}
+
+// Kernel 3: per 256-token block, the sums of the draw weights.
+__global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
-    const float *__restrict__ uniforms, int chunks3, int chunk3_len,
-    int32_t *__restrict__ accepted_len, int32_t *__restrict__ next_token,
-    float *__restrict__ p_draft, float *__restrict__ q_draft, Ws ws) {
-    __shared__ AcceptShared sh;
+    const float *__restrict__ uniforms, int blocks_per_chunk, Ws ws) {
+    __shared__ int s_L;
     const int b = blockIdx.x;
     const int c = blockIdx.y;
+    const int V = rows.V;
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    if (threadIdx.x == 0)
+        s_L = decide(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr);
+    __syncthreads();
+    const int L = s_L;
+    if (L < 0)
+        return;
+    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk_lo = c * blocks_per_chunk;
+    const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
+    float2 *out = ws.block_sums + (size_t)b * nblocks;
+    for (int blk = blk_lo + wave; blk < blk_hi; blk += kWaves) {
+        const int e = blk * kBlock + 4 * lane;   // this lane's 4 tokens
+        float zt4[4], zd4[4];
+        if ((V & 3) == 0) {
+            const float4 t = reinterpret_cast<const float4 *>(d.zt)[min(e, V - 4) >> 2];
+            const float4 q = reinterpret_cast<const float4 *>(d.zd)[min(e, V - 4) >> 2];
+            zt4[0] = t.x; zt4[1] = t.y; zt4[2] = t.z; zt4[3] = t.w;
+            zd4[0] = q.x; zd4[1] = q.y; zd4[2] = q.z; zd4[3] = q.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                zt4[q] = d.zt[min(e + q, V - 1)];
+                zd4[q] = d.zd[min(e + q, V - 1)];
+            }
+        }
+        float wr = 0.0f, wp = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float2 wv = draw_weight(d, sp.scale, zt4[q], zd4[q]);
+            const bool in = e + q < V;
+            wr += in ? wv.x : 0.0f;
+            wp += in ? wv.y : 0.0f;
+        }
+        wr = wave_sum(wr);
+        wp = wave_sum(wp);
+        if (lane == 0)
+            out[blk] = make_float2(wr, wp);
+    }
+}
+
+struct FinalShared {
+    float fsh[kWaves];
+    int ish[kWaves];
+    int found;
+    int L;
+    float before, target;
+    int use_p, blk;
+    // candidate draw
+    uint64_t ckey[kMaxCand];
+    float cw[kMaxCand];
+    float cp[kMaxCand];
+};
+
+// Kernel 4: decisions, then the inverse-CDF draw.
+__global__ __launch_bounds__(kThreads) void draw_final_kernel(
+    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
+    const float *__restrict__ uniforms, int32_t *__restrict__ accepted_len,
+    int32_t *__restrict__ next_token, float *__restrict__ p_draft,
+    float *__restrict__ q_draft, Ws ws) {
+    __shared__ FinalShared sh;
+    const int b = blockIdx.x;
     const int D = rows.D, V = rows.V;
     const float scale = sp.scale;
 
     if (threadIdx.x == 0) {
         float pv[16], qv[16];
         const int L = decide(rows, ws, sp, draft_tokens, uniforms, b, pv, qv);
-        sh.seq_L = L;
-        if (c == 0) {
-            for (int i = 0; i < D; ++i) {
-                if (p_draft) p_draft[(size_t)b * D + i] = (L < 0) ? NAN : pv[i];
-                if (q_draft) q_draft[(size_t)b * D + i] = (L < 0) ? NAN : qv[i];
-            }
-            if (L < 0) {
-                if (accepted_len) accepted_len[b] = -1;
-                next_token[b] = -1;
-            }
+        sh.L = L;
+        for (int i = 0; i < D; ++i) {
+            if (p_draft) p_draft[(size_t)b * D + i] = (L < 0) ? NAN : pv[i];
+            if (q_draft) q_draft[(size_t)b * D + i] = (L < 0) ? NAN : qv[i];
+        }
+        if (L < 0) {
+            if (accepted_len) accepted_len[b] = -1;
+            next_token[b] = -1;
         }
     }
     __syncthreads();
-    const int L = sh.seq_L;
+    const int L = sh.L;
     if (L < 0)
         return;
     const float u = uniforms[(size_t)b * (D + 1) + D];
-    const bool residual = (L < D);
-    const int tr = rows.target_row(b, L);
-    const RowFinal ft = ws.row_final[tr];
-    const float *zt = rows.row(tr);
-    const uint64_t *kt = ws.row_keys + (size_t)tr * sp.k_eff;
-    const int dr = residual ? rows.draft_row(b, L) : 0;
-    const RowFinal fd = residual ? ws.row_final[dr] : RowFinal{0.0f, 1.0f, 0, 0};
-    const float *zd = residual ? rows.row(dr) : nullptr;
-    const uint64_t *kd = residual ? ws.row_keys + (size_t)dr * sp.k_eff : nullptr;
+    const DrawRows d = draw_rows(rows, ws, sp, b, L);
 
     if (sp.candidates) {
-        // ---- draw over the kept candidates of the target row (c == 0 only) ----
-        if (c != 0)
-            return;
-        const int n = ft.n_kept;
+        // ---- draw over the kept candidates of the target row ----
+        const int n = d.ft.n_kept;
         for (int i = threadIdx.x; i < kMaxCand; i += kThreads) {
             if (i < n) {
-                const uint64_t key = kt[i];
+                const uint64_t key = d.kt[i];
                 const int x = key_index(key);
-                const float p = weight(key_logit(key), ft.m, scale) * ft.inv;
+                const float p = weight(key_logit(key), d.ft.m, scale) * d.ft.inv;
                 float w = p;
-                if (residual) {
-                    const float q = row_prob(fd, kd, true, scale, zd[x], x);
+                if (d.residual) {
+                    const float q = row_prob(d.fd, d.kd, true, scale, d.zd[x], x);
                     w = fmaxf(p - q, 0.0f);
                 }
-                // sort key: index ascending -> store index in the high word
-                sh.ckey[i] = ((uint64_t)(uint32_t)x << 32) | (uint32_t)i;
+                // index-major sort key, complemented so a descending sort
+                // yields ascending vocabulary order
+                sh.ckey[i] = ~(((uint64_t)(uint32_t)x << 32) | (uint32_t)i);
                 sh.cw[i] = w;
                 sh.cp[i] = p;
             } else {
-                sh.ckey[i] = ~(uint64_t)0;  // sorts last in ascending order
+                sh.ckey[i] = 0;  // sorts last
             }
         }
-        __syncthreads();
-        // ascending sort by index: sort descending the complemented keys
-        for (int i = threadIdx.x; i < kMaxCand; i += kThreads)
-            sh.ckey[i] = ~sh.ckey[i];
         __syncthreads();
         block_sort_desc(sh.ckey, kMaxCand);
         if (threadIdx.x == 0) {
@@ -668,99 +724,54 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         return;
     }
 
-    // ---- full-vocabulary draw: chunk sums ----
-    const int lo = c * chunk3_len;
-    const int hi = min(V, lo + chunk3_len);
-    float wr = 0.0f, wp = 0.0f;
-    if ((V & 3) == 0) {
-        // float4 loads, clamped into the chunk; lanes past its end add 0
-        const float4 *zt4 = reinterpret_cast<const float4 *>(zt);
-        const float4 *zd4 = residual ? reinterpret_cast<const float4 *>(zd) : zt4;
-        for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 8) {
-            float4 a[2], q4[2];
-            bool in[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int e = base + u * kThreads * 4;
-                in[u] = e < hi;
-                const int ec = min(e, hi - 4) >> 2;
-                a[u] = zt4[ec];
-                q4[u] = zd4[ec];
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const float tv[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
-                const float dv[4] = {q4[u].x, q4[u].y, q4[u].z, q4[u].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float p = in[u] ? weight(tv[q], ft.m, scale) * ft.inv : 0.0f;
-                    wp += p;
-                    if (residual) {
-                        const float qq = weight(dv[q], fd.m, scale) * fd.inv;
-                        wr += in[u] ? fmaxf(p - qq, 0.0f) : 0.0f;
-                    }
-                }
-            }
-        }
-    } else {
-        for (int x = lo + threadIdx.x; x < hi; x += kThreads) {
-            const float p = weight(zt[x], ft.m, scale) * ft.inv;
-            wp += p;
-            if (residual) {
-                const float q = weight(zd[x], fd.m, scale) * fd.inv;
-                wr += fmaxf(p - q, 0.0f);
-            }
-        }
+    // ---- full vocabulary: find the block holding u * total ----
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    const float2 *bs = ws.block_sums + (size_t)b * nblocks;
+    // thread t owns a contiguous run of blocks
+    const int per = (nblocks + kThreads - 1) / kThreads;
+    const int b_lo = min(nblocks, (int)threadIdx.x * per);
+    const int b_hi = min(nblocks, b_lo + per);
+    float my_r = 0.0f, my_p = 0.0f;
+    for (int k = b_lo; k < b_hi; ++k) {
+        const float2 v = bs[k];
+        my_r += v.x;
+        my_p += v.y;
     }
-    wr = block_sum(wr, sh.fsh);
-    wp = block_sum(wp, sh.fsh);
+    float incl_r = block_incl_scan_f(my_r, sh.fsh);
+    __syncthreads();
+    if (threadIdx.x == kThreads - 1)
+        sh.use_p = !(incl_r > 0.0f);
+    __syncthreads();
+    const bool use_p = sh.use_p != 0;
+    float incl = incl_r, mine = my_r;
+    if (use_p) {
+        incl = block_incl_scan_f(my_p, sh.fsh);
+        mine = my_p;
+    }
+    if (threadIdx.x == kThreads - 1)
+        sh.target = u * incl;   // u * total
     if (threadIdx.x == 0)
-        ws.seq_sums[(size_t)b * chunks3 + c] = make_float2(residual ? wr : wp, wp);
-
-    if (chunks3 > 1) {
-        release_agent();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const unsigned prev = atomicAdd(&ws.seq_cnt[b], 1u);
-            sh.last = (prev == (unsigned)(chunks3 - 1));
-        }
-        __syncthreads();
-        if (!sh.last)
-            return;
-        acquire_agent();
-    } else {
-        __syncthreads();
-    }
-
-    // ---- last chunk: locate the target mass, then scan one chunk ----
-    __shared__ int s_chunk;
-    __shared__ float s_before, s_target;
-    __shared__ int s_use_p;
-    if (threadIdx.x == 0) {
-        float tot = 0.0f;
-        for (int cc = 0; cc < chunks3; ++cc)
-            tot += __builtin_nontemporal_load(&ws.seq_sums[(size_t)b * chunks3 + cc].x);
-        int use_p = !(tot > 0.0f);
-        if (use_p) {
-            tot = 0.0f;
-            for (int cc = 0; cc < chunks3; ++cc)
-                tot += __builtin_nontemporal_load(&ws.seq_sums[(size_t)b * chunks3 + cc].y);
-        }
-        const float target = u * tot;
-        float cum = 0.0f, before = 0.0f;
+        sh.found = 0x7FFFFFFF;
+    __syncthreads();
+    const float target = sh.target;
+    const float excl = incl - mine;
+    if (incl > target && excl <= target)
+        atomicMin(&sh.found, (int)threadIdx.x);
+    __syncthreads();
+    if ((int)threadIdx.x == (sh.found == 0x7FFFFFFF ? -1 : sh.found)) {
+        float cum = excl;
         int pick = -1, last_pos = -1;
-        float last_before = 0.0f;
-        for (int cc = 0; cc < chunks3; ++cc) {
-            const float2 s2 = ws.seq_sums[(size_t)b * chunks3 + cc];
-            const float w = use_p ? s2.y : s2.x;
+        float before = excl, last_before = excl;
+        for (int k = b_lo; k < b_hi; ++k) {
+            const float w = use_p ? bs[k].y : bs[k].x;
             before = cum;
             cum += w;
             if (w > 0.0f) {
-                last_pos = cc;
+                last_pos = k;
                 last_before = before;
             }
             if (cum > target) {
-                pick = cc;
+                pick = k;
                 break;
             }
         }
@@ -768,84 +779,84 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
             pick = last_pos;
             before = last_before;
         }
-        s_chunk = pick;
-        s_before = before;
-        s_target = target;
-        s_use_p = use_p;
-        if (chunks3 > 1)
-            atomicExch(&ws.seq_cnt[b], 0u);
+        sh.blk = pick;
+        sh.before = before;
+    }
+    if (sh.found == 0x7FFFFFFF && threadIdx.x == 0) {
+        // rounding left the target at or past the end: the last block with
+        // positive mass
+        int k = nblocks - 1;
+        while (k > 0 && !((use_p ? bs[k].y : bs[k].x) > 0.0f))
+            --k;
+        sh.blk = k;
+        float before = 0.0f;
+        for (int kk = 0; kk < k; ++kk)
+            before += use_p ? bs[kk].y : bs[kk].x;
+        sh.before = before;
     }
     __syncthreads();
-    const int cs = s_chunk;
-    const bool use_p = s_use_p != 0;
-    const float tgt = s_target - s_before;
-    const int clo = cs * chunk3_len;
-    const int chi = min(V, clo + chunk3_len);
-    const int seg = (chi - clo + kThreads - 1) / kThreads;
-    const int slo = clo + threadIdx.x * seg;
-    const int shi = min(chi, slo + seg);
-    auto wt = [&](int x) -> float {
-        const float p = weight(zt[x], ft.m, scale) * ft.inv;
-        if (!residual || use_p)
-            return p;
-        const float q = weight(zd[x], fd.m, scale) * fd.inv;
-        return fmaxf(p - q, 0.0f);
-    };
-    float mysum = 0.0f;
-    int mylast = -1;
-    for (int x = slo; x < shi; ++x) {
-        const float w = wt(x);
-        mysum += w;
-        if (w > 0.0f)
-            mylast = x;
-    }
-    const float incl = block_incl_scan_f(mysum, sh.fsh);
-    const float excl = incl - mysum;
-    if (threadIdx.x == 0)
-        sh.found = 0x7FFFFFFF;
-    __syncthreads();
-    if (incl > tgt && excl <= tgt)
-        atomicMin(&sh.found, (int)threadIdx.x);
-    __syncthreads();
-    int owner = sh.found;
-    if (owner == 0x7FFFFFFF) {
-        // rounding left the target at or past the chunk end: last positive
-        // token of the chunk
-        __syncthreads();
-        if (threadIdx.x == 0)
-            sh.found = -1;
-        __syncthreads();
-        if (mylast >= 0)
-            atomicMax(&sh.found, (int)threadIdx.x);
-        __syncthreads();
-        owner = sh.found;
-        if ((int)threadIdx.x == owner) {
-            if (accepted_len) accepted_len[b] = L;
-            next_token[b] = mylast;
-        }
+    // ---- scan the chosen block in vocabulary order (one wave) ----
+    if (threadIdx.x >= 64)
         return;
-    }
-    if ((int)threadIdx.x == owner) {
-        float cum = excl;
-        int pick = -1, last_pos = -1;
-        for (int x = slo; x < shi; ++x) {
-            const float w = wt(x);
-            cum += w;
-            if (w > 0.0f)
-                last_pos = x;
-            if (cum > tgt) {
-                pick = x;
-                break;
-            }
+    const int lane = threadIdx.x;
+    const int blk = sh.blk;
+    const int e = blk * kBlock + 4 * lane;
+    float w4[4];
+    int last_local = -1;
+    float lane_sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int x = e + q;
+        float w = 0.0f;
+        if (x < V) {
+            const float2 wv = draw_weight(d, scale, d.zt[x], d.residual ? d.zd[x] : 0.0f);
+            w = use_p ? wv.y : wv.x;
         }
-        if (pick < 0)
-            pick = last_pos;
-        if (accepted_len) accepted_len[b] = L;
-        next_token[b] = pick;
+        w4[q] = w;
+        lane_sum += w;
+        if (w > 0.0f)
+            last_local = x;
+    }
+    // inclusive scan of the lane sums in lane order
+    float incl_l = lane_sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(incl_l, o);
+        if (lane >= o)
+            incl_l += t;
+    }
+    const float tgt = target - sh.before;
+    const float excl_l = incl_l - lane_sum;
+    int pick = -1;
+    {
+        float cum = excl_l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            cum += w4[q];
+            if (pick < 0 && w4[q] > 0.0f && cum > tgt)
+                pick = e + q;
+        }
+    }
+    // first lane (in vocabulary order) whose run crosses the target
+    const unsigned long long hit = __ballot(pick >= 0);
+    const unsigned long long pos = __ballot(last_local >= 0);
+    if (hit) {
+        const int first = __ffsll(hit) - 1;
+        if (lane == first) {
+            if (accepted_len) accepted_len[b] = L;
+            next_token[b] = pick;
+        }
+    } else {
+        // rounding: the target sits at the block end -- last positive token
+        const int lastl = 63 - __clzll(pos);
+        if (lane == lastl) {
+            if (accepted_len) accepted_len[b] = L;
+            next_token[b] = last_local;
+        }
     }
 }
 
-// ------------------------------------------------------------- kernel 3 ----
+// ----------------------------------------------------------------- probs ----
 __global__ __launch_bounds__(kThreads) void probs_kernel(
     Rows rows, SamplingParams sp, int chunk_len, float *__restrict__ probs, Ws ws) {
     const int r = blockIdx.x;
@@ -862,33 +873,26 @@ __global__ __launch_bounds__(kThreads) void probs_kernel(
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
-                            const SamplingParams &sp, const Ws &w, hipStream_t stream) {
-    // One launch when rows finish without counters; otherwise batches of at
-    // most kRowSlots rows, each batch reusing the same counter slots.
-    const int batch = plan.chunks > 1 ? kRowSlots : plan.rows;
-    for (int r0 = 0; r0 < plan.rows; r0 += batch) {
-        const int n = std::min(batch, plan.rows - r0);
-        row_stats_kernel<<<dim3(n, plan.chunks), kThreads, 0, stream>>>(
-            rows, r0, plan.chunks, plan.chunk_len, sp, w);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
-}
-
 Ws carve(const AcceptPlan &p, void *base) {
     unsigned char *b = reinterpret_cast<unsigned char *>(base);
     Ws w;
-    w.row_cnt = reinterpret_cast<unsigned *>(b + p.off_row_cnt);
-    w.seq_cnt = reinterpret_cast<unsigned *>(b + p.off_seq_cnt);
     w.chunk_stats = reinterpret_cast<ChunkStat *>(b + p.off_chunk_stats);
     w.chunk_keys = reinterpret_cast<uint64_t *>(b + p.off_chunk_keys);
     w.row_final = reinterpret_cast<RowFinal *>(b + p.off_row_final);
     w.row_keys = reinterpret_cast<uint64_t *>(b + p.off_row_keys);
-    w.seq_sums = reinterpret_cast<float2 *>(b + p.off_seq_sums);
+    w.block_sums = reinterpret_cast<float2 *>(b + p.off_block_sums);
     return w;
+}
+
+hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
+                            const SamplingParams &sp, const Ws &w, hipStream_t stream) {
+    row_chunk_kernel<<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
+        rows, plan.chunks, plan.chunk_len, sp, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.chunks == 1)
+        return e;
+    row_merge_kernel<<<plan.rows, kThreads, 0, stream>>>(rows, plan.chunks, plan.chunk_len, sp, w);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -927,27 +931,19 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
         p.chunk_len = ((len + 1023) / 1024) * 1024;
     }
     p.chunks = std::max(1, (V + p.chunk_len - 1) / p.chunk_len);
-    if (candidates) {
-        p.chunks3 = 1;
-        p.chunk3_len = V;
-    } else {
-        int C3 = (kTargetBlocks + std::max(B, 1) - 1) / std::max(B, 1);
-        C3 = std::max(1, std::min(C3, std::min(64, (V + 2047) / 2048)));
-        if (B > kSeqSlots)
-            C3 = 1;
-        int len = (V + C3 - 1) / C3;
-        p.chunk3_len = ((len + 1023) / 1024) * 1024;
-        p.chunks3 = std::max(1, (V + p.chunk3_len - 1) / p.chunk3_len);
-    }
+    p.nblocks = (V + kBlock - 1) / kBlock;
+    // draw-sum workgroups: about kTargetBlocks in total, whole 256-token blocks
+    int C3 = (kTargetBlocks + std::max(B, 1) - 1) / std::max(B, 1);
+    C3 = std::max(1, std::min(C3, (p.nblocks + 31) / 32));
+    p.blocks_per_chunk3 = (p.nblocks + C3 - 1) / C3;
+    p.chunks3 = (p.nblocks + p.blocks_per_chunk3 - 1) / p.blocks_per_chunk3;
     const int k = candidates ? k_eff : 0;
     size_t off = 0;
-    p.off_row_cnt = off;     off += (size_t)kRowSlots * sizeof(unsigned);
-    p.off_seq_cnt = off;     off += (size_t)kSeqSlots * sizeof(unsigned);
     p.off_chunk_stats = off; off += align256((size_t)p.rows * p.chunks * sizeof(ChunkStat));
     p.off_chunk_keys = off;  off += align256((size_t)p.rows * p.chunks * k * sizeof(uint64_t));
     p.off_row_final = off;   off += align256((size_t)p.rows * sizeof(RowFinal));
     p.off_row_keys = off;    off += align256((size_t)p.rows * k * sizeof(uint64_t));
-    p.off_seq_sums = off;    off += align256((size_t)B * p.chunks3 * sizeof(float2));
+    p.off_block_sums = off;  off += align256(candidates ? 0 : (size_t)B * p.nblocks * sizeof(float2));
     p.ws_bytes = off;
     return p;
 }
@@ -965,9 +961,15 @@ hipError_t launch_accept(const float *target, const float *draft,
     hipError_t e = launch_row_stats(rows, plan, sp, w, stream);
     if (e != hipSuccess)
         return e;
-    accept_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
-        rows, sp, draft_tokens, uniforms, plan.chunks3, plan.chunk3_len,
-        accepted_len, next_token, p_draft, q_draft, w);
+    if (!sp.candidates) {
+        draw_sums_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
+            rows, sp, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    draw_final_kernel<<<plan.B, kThreads, 0, stream>>>(
+        rows, sp, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
     return hipGetLastError();
 }
 

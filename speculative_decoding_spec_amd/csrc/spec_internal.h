@@ -43,12 +43,12 @@ struct AcceptPlan {
     int rows;        // B * (2D + 1)
     int chunks;      // vocabulary chunks per row in the statistics pass
     int chunk_len;   // elements per chunk
-    int chunks3;     // vocabulary chunks per sequence in the draw pass
-    int chunk3_len;
+    int nblocks;     // 256-token draw blocks per row
+    int chunks3;     // draw-sum workgroups per sequence
+    int blocks_per_chunk3;
     size_t ws_bytes;
     // workspace offsets
-    size_t off_row_cnt, off_seq_cnt, off_chunk_stats, off_chunk_keys,
-        off_row_final, off_row_keys, off_seq_sums;
+    size_t off_chunk_stats, off_chunk_keys, off_row_final, off_row_keys, off_block_sums;
 };
 
 AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates);

@@ -240,3 +240,34 @@ def test_determinism(dev):
     b = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
     for key in a:
         assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("k,p", [(0, 1.0), (20, 0.95)])
+def test_workspace_contents_do_not_matter(dev, k, p):
+    """A workspace full of garbage (all-ones bytes, then another shape's
+    leftovers) gives bitwise the same results as a fresh one."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    B, D, V = 6, 4, 40000
+    t, d = synth.logits_pair(610, B, D, V)
+    toks = draft_tokens(d, 0.7, k, p, 610)
+    u = synth.uniforms(610, synth.U_ACCEPT, (B, D + 1))
+    need = spec.spec_verify_accept_workspace(B, D, V, k)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    args = (T_(t, dev), T_(d, dev), T_(toks, dev), T_(u, dev), 0.7, k, p)
+    first = [a.cpu().numpy() for a in spec.spec_verify_accept(*args, with_probs=True, workspace=ws)]
+    # leave other data behind in the same buffer, then repeat
+    t2, d2 = synth.logits_pair(611, 2, 1, 999)
+    toks2 = draft_tokens(d2, 1.0, 0, 1.0, 611)
+    u2 = synth.uniforms(611, synth.U_ACCEPT, (2, 2))
+    spec.spec_verify_accept(T_(t2, dev), T_(d2, dev), T_(toks2, dev), T_(u2, dev), 1.0,
+                            workspace=ws)
+    again = [a.cpu().numpy() for a in spec.spec_verify_accept(*args, with_probs=True, workspace=ws)]
+    fresh = gpu_accept(t, d, toks, u, 0.7, k, p, dev)
+    for x, y in zip(first, again):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(first[0], fresh["accepted_len"])
+    assert np.array_equal(first[1], fresh["next_token"])
+    ref = parity.oracle_accept_threaded(t, d, toks, u, 0.7, k, p)
+    res = parity.compare_accept(fresh, ref, t, d, toks, u, 0.7, k, p)
+    assert not res["bad"]
