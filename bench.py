@@ -13,10 +13,23 @@ One step = one pass of the whole hot path over resident synthetic inputs:
 Printed: one JSON line.  `value` is the verify qmv throughput in HBM GB/s
 (algorithmic bytes / time of the qmv part of the steps); the acceptance
 throughput (verify positions per second) and per-M figures ride along.
+
+`roofline` covers qmv_kernel, the kernel with the most time per step (24
+launches): algorithmic bytes per launch over the average launch duration,
+the qmv part of the timed steps (HIP events on the launch stream around
+the 24 back-to-back launches) divided by 24.  A second set of timed steps
+with events around every launch splits that time by shape and M.  Its `traffic`
+is the HBM bytes per launch from the committed counter summary under
+profiles/ (FETCH_SIZE + WRITE_SIZE scaled by a plain-copy calibration), and
+null when qmv.hip has changed since those counters were taken.
+
+`--copy-probe` runs only a plain read-once / write-once elementwise kernel
+over 1 GiB (the calibration kernel for those counters) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -29,6 +42,10 @@ HIDDEN, FFN = 5120, 17408
 GROUP = 64
 MS = list(range(1, 9))
 ACC_B, ACC_D, ACC_V, ACC_T = 256, 5, 151936, 0.6
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmv_kernel_w4_mlp_block_hbm_traffic.txt")
+QMV_SOURCE = os.path.join(ROOT, "speculative_decoding_spec_amd", "csrc", "qmv.hip")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -39,7 +56,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     return ap.parse_args()
+
+
+def copy_probe(dev):
+    """A plain elementwise kernel that reads COPY_BYTES once and writes them once."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per qmv launch from the committed counter summary, or None
+    when the summary is missing or belongs to another qmv.hip."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        with open(QMV_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None, "qmv.hip changed since the counters were taken"
+        return float(kv["traffic_bytes_per_launch"]), kv
+    except (OSError, KeyError, ValueError):
+        return None, "no counter summary"
 
 
 def build_inputs(dev):
@@ -83,13 +129,6 @@ def build_accept(dev):
     return dict(t=t, d=d, toks=toks.contiguous(), u=u, acc=acc, nxt=nxt)
 
 
-def run_qmv(b):
-    import speculative_decoding_spec_amd as spec
-    spec.spec_qmv_w4(b["gate"], b["x"], y=b["yg"])
-    spec.spec_qmv_w4(b["up"], b["x"], y=b["yu"])
-    spec.spec_qmv_w4(b["down"], b["h"], y=b["yd"])
-
-
 def run_accept(a):
     import speculative_decoding_spec_amd as spec
     spec.spec_verify_accept(a["t"], a["d"], a["toks"], a["u"], ACC_T,
@@ -97,44 +136,55 @@ def run_accept(a):
 
 
 def cpu_baseline(seconds):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload.
+    """The fp64 oracle, as it stands, on a bounded sample of the step.
 
-    qmv: rows of the gate projection (M = 8, K = 5120) in chunks over the host
-    threads until about `seconds` have passed; acceptance: sequences of the
-    batched workload likewise.  Rates are scaled to GB/s (same algorithmic
-    bytes as the GPU figure) and verify positions per second."""
+    qmv: the step's 24 products (gate, up and down at M = 1..8) with one
+    seeded weight set per shape, rows split over the host threads, stopping
+    once `seconds` have passed; acceptance: the 256-sequence batch, drafts
+    drawn from the draft rows as on the GPU, likewise bounded.  Rates use the
+    GPU figure's algorithmic bytes (GB/s) and verify positions per second."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     import oracle
-    from speculative_decoding_spec_amd import synth
+    from speculative_decoding_spec_amd import roofline, synth
     threads = min(16, os.cpu_count() or 1)
-    M = 8
-    w, s, b = synth.qweights(1, 4, FFN, HIDDEN, GROUP)
-    x = synth.activations(1, M, HIDDEN)
-    chunk = 64
-    done, t0 = 0, time.perf_counter()
+    shapes = {"gate_up": (FFN, HIDDEN), "down": (HIDDEN, FFN)}
+    weights = {k: synth.qweights(1, 4, N, K, GROUP, salt=N) for k, (N, K) in shapes.items()}
+    work = []
+    for M in MS:
+        for name in ("gate_up", "gate_up", "down"):
+            work.append((name, M))
+    chunk = 256
+    done_bytes, products, t0 = 0, 0, time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        while done < FFN and time.perf_counter() - t0 < seconds:
-            spans = [(r, min(FFN, r + chunk)) for r in range(done, min(FFN, done + chunk * threads), chunk)]
+        for name, M in work:
+            if time.perf_counter() - t0 >= seconds:
+                break
+            N, K = shapes[name]
+            w, s, b = weights[name]
+            x = synth.activations(1, M, K, salt=M)
+            spans = [(r, min(N, r + chunk)) for r in range(0, N, chunk)]
             list(ex.map(lambda sp: oracle.qmv(4, w, s, b, x, GROUP, rows=sp), spans))
-            done = spans[-1][1]
+            done_bytes += roofline.qmv_bytes(4, M, N, K, GROUP)
+            products += 1
     dt = time.perf_counter() - t0
-    qbytes = done * (HIDDEN * 4 // 8 + (HIDDEN // GROUP) * 4) + M * HIDDEN * 2 + M * done * 4
-    tl, dl = synth.logits_pair(4, threads, ACC_D, ACC_V)
-    toks = np.zeros((threads, ACC_D), np.int32)
-    u = synth.uniforms(4, synth.U_ACCEPT, (threads, ACC_D + 1))
+    tl, dl = synth.logits_pair(4, ACC_B, ACC_D, ACC_V)
+    ud = synth.uniforms(4, synth.U_DRAFT, ACC_B * ACC_D)
+    toks = oracle.sample_rows(dl.reshape(ACC_B * ACC_D, ACC_V), ACC_T, 0, 1.0, ud).reshape(ACC_B, ACC_D)
+    u = synth.uniforms(4, synth.U_ACCEPT, (ACC_B, ACC_D + 1))
     nseq, t1 = 0, time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         while nseq < ACC_B and time.perf_counter() - t1 < seconds:
+            idx = range(nseq, min(ACC_B, nseq + threads))
             list(ex.map(lambda i: oracle.accept(tl[i:i + 1], dl[i:i + 1], toks[i:i + 1],
-                                                u[i:i + 1], ACC_T), range(threads)))
-            nseq += threads
+                                                u[i:i + 1], ACC_T), idx))
+            nseq = idx[-1] + 1
     at = time.perf_counter() - t1
     return {
-        "value": round(qbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": (f"W4 g64 qmv M=8 K=5120: {done} of the 17408 gate rows "
-                   f"({qbytes / 1e6:.1f} MB algorithmic) in {dt:.1f} s; acceptance: "
-                   f"{nseq} sequences of D=5 V=151936 T=0.6 in {at:.1f} s"),
+        "value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"W4 g64 qmv: {products} of the step's 24 products (gate/up 5120->17408, "
+                   f"down 17408->5120, M=1..8), {done_bytes / 1e6:.0f} MB algorithmic in {dt:.1f} s; "
+                   f"acceptance: {nseq} of 256 sequences (D=5, V=151936, T=0.6) in {at:.2f} s"),
         "accept_positions_per_s": round(nseq * (ACC_D + 1) / at, 1),
         "cpu": platform.processor() or platform.machine(),
     }
@@ -154,6 +204,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(dev)
+        return
     blocks = build_inputs(dev)
     acc = build_accept(dev)
     stream = torch.cuda.current_stream(dev)
@@ -162,60 +215,108 @@ def main():
                          roofline.qmv_bytes(4, b["M"], HIDDEN, FFN) for b in blocks)
     acc_bytes = roofline.accept_bytes(ACC_B, ACC_D, ACC_V)
 
-    def step(events=None):
-        for i, b in enumerate(blocks):
-            if events is not None:
-                events[i][0].record(stream)
-            run_qmv(b)
-            if events is not None:
-                events[i][1].record(stream)
-        if events is not None:
-            events[-1][0].record(stream)
-        run_accept(acc)
-        if events is not None:
-            events[-1][1].record(stream)
+    # Per step: 24 qmv launches (gate, up, down at M = 1..8) and one
+    # acceptance call, all marshalled once so the host stays ahead of the GPU.
+    launches = []
+    for b in blocks:
+        launches.append((spec.bind_qmv(b["gate"], b["x"], b["yg"]), "gate",
+                         roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
+        launches.append((spec.bind_qmv(b["up"], b["x"], b["yu"]), "up",
+                         roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
+        launches.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
+                         roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
+    accept_call = spec.bind_verify_accept(acc["t"], acc["d"], acc["toks"], acc["u"], ACC_T,
+                                          out=(acc["acc"], acc["nxt"], None, None))
+
+    def pair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def step(ev=None, per_launch=False):
+        if ev is not None:
+            ev["q"][0].record(stream)
+        for i, (call, _, _) in enumerate(launches):
+            if per_launch:
+                ev["l"][i][0].record(stream)
+            call()
+            if per_launch:
+                ev["l"][i][1].record(stream)
+        if ev is not None:
+            ev["q"][1].record(stream)
+            ev["a"][0].record(stream)
+        accept_call()
+        if ev is not None:
+            ev["a"][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(len(blocks) + 1)] for _ in range(args.steps)]
+    # Timed steps: events around the qmv part and the acceptance call only.
+    ev = [{"q": pair(), "a": pair()} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    qspan_ms = sum(e["q"][0].elapsed_time(e["q"][1]) for e in ev) / args.steps
+    acc_ms = sum(e["a"][0].elapsed_time(e["a"][1]) for e in ev) / args.steps
+    qmv_gbs = qmv_bytes_step / (qspan_ms * 1e-3) / 1e9
 
-    per_m_ms = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
-                for i in range(len(blocks))]
-    acc_ms = sum(ev[k][-1][0].elapsed_time(ev[k][-1][1]) for k in range(args.steps)) / args.steps
-    qmv_ms = sum(per_m_ms)
-    qmv_gbs = qmv_bytes_step / (qmv_ms * 1e-3) / 1e9
+    # Same steps again with a pair of events around every qmv launch: the
+    # per-launch durations behind the roofline and the per-shape figures.
+    # Each step's 24 launches are queued behind the previous step's
+    # acceptance call, so every start event executes behind GPU work rather
+    # than ahead of a launch the host has yet to issue.
+    evl = [{"q": pair(), "a": pair(), "l": [pair() for _ in launches]} for _ in range(args.steps)]
+    step()   # untimed, not waited for: the queue is already busy at the first event
+    for k in range(args.steps):
+        step(evl[k], per_launch=True)
+    torch.cuda.synchronize()
+    q_ms = [sum(e["l"][i][0].elapsed_time(e["l"][i][1]) for e in evl) / args.steps
+            for i in range(len(launches))]
     per_m = {}
-    for b, ms in zip(blocks, per_m_ms):
-        nb = roofline.qmv_bytes(4, b["M"], FFN, HIDDEN) * 2 + roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)
+    for j, b in enumerate(blocks):
+        ms = sum(q_ms[3 * j:3 * j + 3])
+        nb = sum(l[2] for l in launches[3 * j:3 * j + 3])
         per_m[str(b["M"])] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                               "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
+    per_shape = {}
+    for name in ("gate", "up", "down"):
+        idx = [i for i, l in enumerate(launches) if l[1] == name]
+        ms = sum(q_ms[i] for i in idx) / len(idx)
+        nb = sum(launches[i][2] for i in idx) / len(idx)
+        per_shape[name] = {"us_per_launch": round(ms * 1e3, 2),
+                           "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                           "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
     positions = ACC_B * (ACC_D + 1)
     acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
-    accept = {"positions_per_s": positions / (acc_ms * 1e-3), "us": round(acc_ms * 1e3, 2),
+    accept = {"positions_per_s": round(positions / (acc_ms * 1e-3), 1), "us": round(acc_ms * 1e3, 2),
               "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4),
               "algorithmic_bytes": acc_bytes,
               "mean_accepted": float(acc["acc"].float().mean().item())}
 
-    # Dominant kernel by time: report its roofline.
-    if qmv_ms >= acc_ms:
-        roof = {"kernel": "qmv_kernel<4> (all 24 launches of a step)", "bound": "hbm",
-                "achieved": round(qmv_gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                "frac": round(qmv_gbs / 8000.0, 4), "traffic": None}
-    else:
-        roof = {"kernel": "row_stats_kernel + accept_kernel", "bound": "hbm",
-                "achieved": round(acc_gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                "frac": round(acc_gbs / 8000.0, 4), "traffic": None}
-    other = {"qmv": {"achieved": round(qmv_gbs, 1), "frac": round(qmv_gbs / 8000.0, 4)},
-             "accept": {"achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4)}}
+    # Roofline of qmv_kernel: algorithmic bytes per launch over the average
+    # launch duration, i.e. the qmv part of a step (24 launches queued back to
+    # back, no events between them) divided by 24.  The per-launch events of
+    # the second set add about 2 us of marker time to each launch, so they
+    # only split the time by shape.
+    bytes_per_launch = qmv_bytes_step / len(launches)
+    launch_us = qspan_ms / len(launches) * 1e3
+    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
+    traffic, tinfo = measured_traffic()
+    roof = {"kernel": "qmv_kernel (W4; 24 launches per step: gate, up, down at M=1..8)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+            "frac": round(achieved / 8000.0, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "algorithmic_bytes_per_launch": round(bytes_per_launch),
+            "avg_launch_us": round(launch_us, 2),
+            "traffic_source": (os.path.relpath(TRAFFIC_FILE, ROOT) if traffic is not None else tinfo)}
+    other = {"qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
+                            "per_shape": per_shape},
+             "accept (row_chunk + draw_sums + draw_final)": {
+                 "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
+                 "us_per_call": round(acc_ms * 1e3, 2)}}
 
     out = {
         "metric": METRIC, "value": round(qmv_gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -228,6 +329,7 @@ def main():
                                 "B=256 D=5 V=151936 T=0.6"),
                    "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
         "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
+        "qmv_us_per_step": round(qspan_ms * 1e3, 2),
         "per_M": per_m, "accept": accept, "roofline": roof, "roofline_parts": other,
     }
     if not args.no_cpu_baseline:

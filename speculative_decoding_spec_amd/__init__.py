@@ -14,6 +14,8 @@ Names follow the C ABI:
     spec_sample_probs                filtered sampling distribution
     spec_sample_tokens               inverse-CDF draw from that distribution
     spec_*_workspace_size            workspace queries
+    bind_qmv / bind_verify_accept    the same calls with arguments marshalled
+                                     once, for launch loops
 """
 from __future__ import annotations
 
@@ -215,6 +217,32 @@ def spec_qmv_w8(packed: PackedWeights, x, y=None):
     return _qmv("spec_qmv_w8", 8, packed, x, y)
 
 
+class _Bound:
+    """A C-ABI call with its arguments marshalled once (pointers, sizes and
+    the stream current at bind time).  Calling it re-issues the same call
+    with no Python-side checks: for loops that launch the same shapes over
+    and over.  The tensors it was bound to must stay alive and in place."""
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise SpecError(self.name, st)
+
+
+def bind_qmv(packed: PackedWeights, x, y) -> _Bound:
+    """spec_qmv_w4 / spec_qmv_w8 on fixed tensors, marshalled once.  The
+    first call is checked like spec_qmv_* (it runs through them)."""
+    name = "spec_qmv_w4" if packed.bits == 4 else "spec_qmv_w8"
+    _qmv(name, packed.bits, packed, x, y)
+    M, K = x.shape
+    args = (_ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(y), M, packed.N, K, packed.G,
+            _stream(x.device))
+    return _Bound(name, getattr(lib(), name), args, (packed, x, y))
+
+
 def spec_verify_accept_workspace(B: int, D: int, V: int, top_k: int) -> int:
     return int(lib().spec_verify_accept_workspace(B, D, V, top_k))
 
@@ -257,6 +285,32 @@ def spec_verify_accept(target_logits, draft_logits, draft_tokens, uniforms,
         _ptr(pd), _ptr(qd), _ptr(workspace), nbytes, _stream(dev))
     _check("spec_verify_accept", st)
     return (acc, nxt, pd, qd) if with_probs else (acc, nxt)
+
+
+def bind_verify_accept(target_logits, draft_logits, draft_tokens, uniforms,
+                       temperature: float, top_k: int = 0, top_p: float = 1.0,
+                       out=None) -> _Bound:
+    """spec_verify_accept on fixed tensors, marshalled once (first call
+    checked through spec_verify_accept).  `out` = (accepted_len, next_token,
+    p_draft or None, q_draft or None)."""
+    import torch
+    dev = target_logits.device
+    B, D1, V = target_logits.shape
+    D = D1 - 1
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev), None, None)
+    need = spec_verify_accept_workspace(B, D, V, top_k)
+    ws = torch.empty(max(need, 4096), dtype=torch.uint8, device=dev)
+    spec_verify_accept(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                       top_k, top_p, out=out, workspace=ws)
+    acc, nxt, pd, qd = out
+    args = (_ptr(target_logits), _ptr(draft_logits if D > 0 else None),
+            _ptr(draft_tokens if D > 0 else None), _ptr(uniforms), B, D, V,
+            ctypes.c_float(temperature), int(top_k), ctypes.c_float(top_p), _ptr(acc),
+            _ptr(nxt), _ptr(pd), _ptr(qd), _ptr(ws), ws.numel(), _stream(dev))
+    keep = (target_logits, draft_logits, draft_tokens, uniforms, out, ws)
+    return _Bound("spec_verify_accept", lib().spec_verify_accept, args, keep)
 
 
 def spec_sample_workspace_size(R: int, V: int, top_k: int) -> int:

@@ -271,3 +271,23 @@ def test_workspace_contents_do_not_matter(dev, k, p):
     ref = parity.oracle_accept_threaded(t, d, toks, u, 0.7, k, p)
     res = parity.compare_accept(fresh, ref, t, d, toks, u, 0.7, k, p)
     assert not res["bad"]
+
+
+def test_bound_call_matches_plain_call(dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    B, D, V = 8, 3, 32768
+    t, d = synth.logits_pair(620, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 620)
+    u = synth.uniforms(620, synth.U_ACCEPT, (B, D + 1))
+    acc = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    call = spec.bind_verify_accept(T_(t, dev), T_(d, dev), T_(toks, dev), T_(u, dev), 0.6,
+                                   out=(acc, nxt, None, None))
+    acc.fill_(-7)
+    nxt.fill_(-7)
+    call()
+    torch.cuda.synchronize()
+    ref = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert np.array_equal(acc.cpu().numpy(), ref["accepted_len"])
+    assert np.array_equal(nxt.cpu().numpy(), ref["next_token"])

@@ -122,3 +122,21 @@ def test_row_independence_and_determinism(dev, bits, N, K):
     for M in (3, 5):
         part = run(bits, w, s, b, np.ascontiguousarray(x[:M]), dev)
         assert np.array_equal(part.view(np.uint32), full[:M].view(np.uint32))
+
+
+def test_bound_call_matches_plain_call(dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    w, s, b = synth.qweights(7, 4, 4096, 1024, 64)
+    x = synth.activations(7, 5, 1024)
+    wt, st, bt = parity.dev_qweights(w, s, b, dev)
+    pk = spec.spec_pack_w4(wt, st, bt)
+    xt = parity.dev_x(x, dev)
+    y = torch.empty((5, 4096), dtype=torch.float32, device=dev)
+    call = spec.bind_qmv(pk, xt, y)
+    first = y.clone()
+    y.fill_(float("nan"))
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), first.view(torch.int32))
+    assert torch.equal(spec.spec_qmv_w4(pk, xt).view(torch.int32), y.view(torch.int32))
