@@ -8,26 +8,32 @@
 // by streaming every weight once, and extra rows ride on the same fetch).
 //
 // Design (one pass over the weights, every fetched weight feeds all M rows):
-//  * A workgroup owns one 16-row tile of W (the MFMA's 16 columns) and its
-//    4 or 8 waves split K, wave w taking every 4th/8th 128-wide step ("pair"
-//    of two 64-groups).  Nothing crosses workgroups: no fences, no
-//    workspace, and even N = 5120 launches 320 workgroups of 8 waves.
-//  * Each lane streams 16 bytes of packed codes per pair (W4: 32 nibbles;
-//    W8: two 16-byte loads); four lanes cover 64 (W4) or 128 (W8) contiguous
-//    bytes of one row.  Loads are branch-free (indices clamp into range) and
-//    double buffered in batches, so a whole batch stays in flight.
+//  * A workgroup owns 1, 2 or 4 16-row tiles of W (the MFMA's 16 columns)
+//    and its 4 or 8 waves split K, each wave taking a contiguous run of
+//    128-wide steps ("pairs" of two 64-groups) for all of the workgroup's
+//    tiles.  Nothing crosses workgroups: no fences, no workspace.
+//  * Each lane streams 16 bytes of packed codes per pair and tile (W4: 32
+//    nibbles; W8: two 16-byte loads), so one load instruction moves 1 KB of
+//    contiguous weights.  A wave keeps two stages of loads in flight: the
+//    codes, scale/bias words and x rows of one pair are issued together while
+//    the previous pair is computed.  Edges use out-of-range buffer offsets
+//    (zeros, no memory traffic) instead of branches.
+//  * x is read compactly (the M rows of the pair, 16 bytes per lane) and
+//    staged through a per-wave LDS slot, from which each lane reads its MFMA
+//    operand.  Reading the operand straight from memory would cost four
+//    mostly-empty 16-byte loads per lane and pair, which measured as the
+//    largest single cost of the kernel.
 //  * Codes become bf16 in registers with no conversion instruction for W4:
 //    OR-ing a nibble q into the mantissa of 128.0 (0x4300) gives 128 + q
 //    exactly; the 128 offset is removed with the group sum of x.  W8 codes
 //    convert with the byte-to-float instructions (exact below 256).
 //  * v_mfma_f32_16x16x32_bf16 does the multiply-accumulate: B = 16 weight
-//    rows x 32 k, A = the x rows, read straight from global memory (x is a
-//    few hundred KB at most and stays in L2).  The two groups of a pair are
-//    kept apart by feeding group 0 through A rows 0..7 and group 1 through
-//    A rows 8..15 (each zero on the other group's k slots), so M <= 8 rows
-//    use the whole 16-row tile and every MFMA output belongs to one group.
-//    A second MFMA against a ones operand yields the group sums of x in the
-//    same lane layout.  The per-group affine terms are applied in fp32:
+//    rows x 32 k, A = the x rows.  The two groups of a pair are kept apart by
+//    feeding group 0 through A rows 0..7 and group 1 through A rows 8..15
+//    (each zero on the other group's k slots), so M <= 8 rows use the whole
+//    16-row tile and every MFMA output belongs to one group.  A second MFMA
+//    against a ones operand yields the group sums of x in the same lane
+//    layout.  The per-group affine terms are applied in fp32:
 //        acc += s * C + (b - 128 s) * sum_x            (W4)
 //        acc += s * C + b * sum_x                      (W8)
 //  * The two group halves and the waves meet in LDS in a fixed order, so
@@ -50,23 +56,29 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// One 32-bit word of 8 nibbles q0..q7 (q_i at bits 4i) -> 8 bf16 values
-// 128 + q_i in k order.  The even and odd nibbles are first separated into
-// bytes (lo = q0 q2 q4 q6, hi = q1 q3 q5 q7), interleaved into k order
-// (q0 q1 q2 q3 / q4 q5 q6 q7), and each byte is then paired with the byte
-// 0x43: bf16 0x43qq = 128 + q exactly (128 has 7 mantissa bits of ulp 1).
-__device__ __forceinline__ bf16x8 unpack_w4(unsigned d) {
-    const unsigned lo = d & 0x0F0F0F0Fu;
-    const unsigned hi = (d >> 4) & 0x0F0F0F0Fu;
-    const unsigned q03 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // q0 q1 q2 q3
-    const unsigned q47 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // q4 q5 q6 q7
-    const unsigned c43 = 0x43434343u;
+// One packed 32-bit word of 8 codes -> 8 bf16 values 128 + q in k order.
+// The packing step stores the codes of k-slots 0..7 as
+//     q0 | q2 << 4 | q4 << 8 | q6 << 12 | q1 << 16 | q3 << 20 | q5 << 24 | q7 << 28
+// so each output register (two bf16: k-slot 2i low, 2i + 1 high) is one
+// mask-and-or of the word shifted by 4i: OR-ing a nibble into the mantissa of
+// bf16 128.0 (0x4300) gives 128 + q exactly (128 has 7 mantissa bits of ulp
+// 1).  Seven VALU operations per 8 codes.
+__device__ __forceinline__ bf16x8 unpack_w4(unsigned d, unsigned base) {
+    constexpr unsigned kMask = 0x000F000Fu;
     u32x4 o;
-    o.x = __builtin_amdgcn_perm(c43, q03, 0x04010400u);   // 0x43 q1 0x43 q0
-    o.y = __builtin_amdgcn_perm(c43, q03, 0x04030402u);
-    o.z = __builtin_amdgcn_perm(c43, q47, 0x04010400u);
-    o.w = __builtin_amdgcn_perm(c43, q47, 0x04030402u);
+    o.x = (d & kMask) | base;
+    o.y = ((d >> 4) & kMask) | base;
+    o.z = ((d >> 8) & kMask) | base;
+    o.w = ((d >> 12) & kMask) | base;
     return __builtin_bit_cast(bf16x8, o);
+}
+
+// 0x43004300 (two bf16 128.0) in a vector register: with the mask as the one
+// scalar operand, each (d & mask) | base is a single v_and_or_b32.
+__device__ __forceinline__ unsigned w4_base_vgpr() {
+    unsigned v;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(v));
+    return v;
 }
 
 // Two words of 4 bytes each -> 8 bf16 values q (exact: q < 256 needs 8
@@ -92,12 +104,14 @@ __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
 // tile index t * n_pairs + p, as 64 lane slots of 16 bytes (W4) or two
 // 1 KB halves of 64 x 16 bytes (W8).  Lane slot l = 16 j + r holds row
 // 16t + r, k = 128p + 64 (j >> 1) + 32 (j & 1) + [0, 32): exactly the bytes
-// the MFMA B operand of lane l needs, in the original code order.  A wave
-// therefore reads 1 KB per load instruction and streams a contiguous region.
-// Scales and biases become one 32-bit word per (row, group): fp16 scale in
-// the low half, fp16 bias in the high half, stored as [t][g][r] with the group
-// count padded to 2 * n_pairs.  Rows past N and groups past K/64 are zero, so
-// they contribute exactly nothing.
+// the MFMA B operand of lane l needs; within each 32-bit word (k-slots 0..7)
+// the W4 codes are reordered so that unpacking is one mask per output
+// register (see unpack_w4).  A wave therefore reads 1 KB per load
+// instruction and streams a contiguous region.  Scales and biases become one
+// 32-bit word per (row, group): fp16 scale in the low half, fp16 bias in the
+// high half, stored as [t][p / 2][h * 16 + r][p % 2] for group g = 2p + h, so
+// one 8-byte load gives a lane the words of two pairs.  Rows past N and
+// groups past K/64 are zero, so they contribute exactly nothing.
 // ---------------------------------------------------------------------------
 
 template <int BITS>
@@ -107,7 +121,6 @@ __global__ __launch_bounds__(256) void pack_kernel(
     uint32_t *__restrict__ sbp, int N, int K) {
     const int ng = K >> 6;
     const int n_pairs = (ng + 1) >> 1;
-    const int ngp = 2 * n_pairs;
     const int n_tiles = (N + 15) >> 4;
     constexpr int L = BITS / 4;   // 16-byte slots per lane and tile
     const size_t slots = (size_t)n_tiles * n_pairs * 64 * L;
@@ -124,21 +137,35 @@ __global__ __launch_bounds__(256) void pack_kernel(
         const int k = 128 * p + 64 * (j >> 1) + 32 * (j & 1) + 16 * v;  // first k of the 16 bytes
         u32x4 val = {0u, 0u, 0u, 0u};
         if (n < N && k < K) {
-            if (BITS == 4)
+            if (BITS == 4) {
                 val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 5];
-            else
+                // k-slot e of each word moves to nibble (e & 1) * 4 + (e >> 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    unsigned out = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        out |= ((val[c] >> (4 * e)) & 0xFu) << (16 * (e & 1) + 4 * (e >> 1));
+                    val[c] = out;
+                }
+            } else {
                 val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 4];
+            }
         }
         wp[i] = val;
     }
-    const size_t sb_count = (size_t)n_tiles * ngp * 16;
+    // scale/bias words: [t][p / 2][h * 16 + r][p % 2] for the group g = 2p + h
+    const int npp = (n_pairs + 1) >> 1;
+    const size_t sb_count = (size_t)n_tiles * npp * 64;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < sb_count;
          i += (size_t)gridDim.x * blockDim.x) {
-        const int r = (int)(i & 15);
-        const size_t tg = i >> 4;
-        const int g = (int)(tg % ngp);
-        const int t = (int)(tg / ngp);
-        const int n = 16 * t + r;
+        const int e = (int)(i & 1);
+        const int hr = (int)((i >> 1) & 31);
+        const size_t rest = i >> 6;
+        const int pp = (int)(rest % npp);
+        const int t = (int)(rest / npp);
+        const int n = 16 * t + (hr & 15);
+        const int g = 2 * (2 * pp + e) + (hr >> 4);
         uint32_t val = 0;
         if (n < N && g < ng)
             val = (uint32_t)scales[(size_t)n * ng + g] | ((uint32_t)biases[(size_t)n * ng + g] << 16);
@@ -146,26 +173,38 @@ __global__ __launch_bounds__(256) void pack_kernel(
     }
 }
 
-template <int BITS, int WAVES, int T>
+template <int BITS, int WAVES, int T, int U, int S>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
     const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
-    __shared__ f32x4 red[WAVES][T][64];
+    static_assert(U == 1 || U == 2, "a stage is one or two pairs");
+    constexpr int L = BITS / 4;     // 1 KB loads per pair, tile and wave
+    constexpr int kPitch = 136;     // bf16 per staged x row: 256 B + 16 B against bank conflicts
+    // Each wave stages its x rows in its own slot; the cross-wave reduction
+    // reuses the same memory after the main loop.
+    union Shared {
+        uint16_t xs[WAVES][U][8][kPitch];
+        f32x4 red[WAVES][T][64];
+    };
+    __shared__ __attribute__((aligned(16))) Shared sh;
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[8];
 
-    constexpr int L = BITS / 4;              // 1 KB loads per pair, tile and wave
     const int ng = K >> 6;                   // groups per row
     const int n_pairs = (ng + 1) >> 1;       // 128-wide K steps
-    const int ngp = 2 * n_pairs;
+    const int npp = (n_pairs + 1) >> 1;      // scale/bias blocks of two pairs
     const int n_tiles = (N + 15) >> 4;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // readfirstlane makes the wave index (and all that derives from it)
+    // provably uniform, so buffer offsets stay in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int j = lane >> 4;   // k-slot group of the A/B operands, row group of C
     const int r = lane & 15;   // A row / B and C column
     const int h = j >> 1;      // which group of the pair this lane's k slots hold
     const int sub = j & 1;     // which 32-k half of that group
 
-    // This wave's contiguous share of the pairs, for each of the T tiles.
-    const int ppw = (n_pairs + WAVES - 1) / WAVES;
+    // This wave's contiguous share of the pairs (an even count, so a stage
+    // of two pairs never straddles a scale/bias block).
+    const int ppw = ((n_pairs + WAVES - 1) / WAVES + 1) & ~1;
     const int p_lo = min(n_pairs, wave * ppw);
     const int p_hi = min(n_pairs, p_lo + ppw);
 
@@ -181,57 +220,93 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
             (void *)(wp + (size_t)min(t, n_tiles - 1) * n_pairs * 64 * L), (short)0,
             there ? n_pairs * 1024 * L : 0, kBufferFlags);
         sbres[tt] = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(sbp + (size_t)min(t, n_tiles - 1) * ngp * 16), (short)0,
-            there ? ngp * 64 : 0, kBufferFlags);
+            (void *)(sbp + (size_t)min(t, n_tiles - 1) * npp * 64), (short)0,
+            there ? npp * 256 : 0, kBufferFlags);
     }
-    // A row r carries x row (r & 7) for half (r >> 3) and is non-zero only on
-    // that half's k slots.  Lanes outside that pattern, or with a row >= M,
-    // start past the end of x, where buffer loads return zeros.
-    const bool a_act = (h == (r >> 3)) && ((r & 7) < M);
     const __amdgpu_buffer_rsrc_t xres =
         __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, M * K * 2, kBufferFlags);
-    const unsigned xoff = a_act ? (unsigned)(((r & 7) * K + 64 * h + 32 * sub) * 2) : kOutOfRange;
     const unsigned woff = (unsigned)lane * 16u;
-    const unsigned sboff = (unsigned)(h * 16 + r) * 4u;
+    const unsigned sboff = (unsigned)(h * 16 + r) * 8u;
+    // x is loaded compactly: lane -> row (lane >> 4) + 4 i, 16-byte chunk
+    // (lane & 15) of the pair's 128 k; rows >= M read zeros.
+    const int xrow0 = lane >> 4, xch = lane & 15;
+    // MFMA A operand: row r carries x row (r & 7) for group half (r >> 3)
+    // and is zero on the other half's k slots (and for rows >= M).
+    const bool a_act = (h == (r >> 3)) && ((r & 7) < M);
+    if (threadIdx.x < 8)
+        xzero[threadIdx.x] = 0;
+    __syncthreads();
 
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    const unsigned w4base = w4_base_vgpr();
     f32x4 acc[T];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
         acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int U = (T == 1) ? 4 : (T == 2 ? 2 : 1);   // pairs per batch
-    struct Batch {
+    // A stage is U pairs: the T tiles' codes and scale/bias words, and the
+    // compact x rows, all issued together.  Pairs outside this wave's range
+    // load through an out-of-range offset (zeros, no memory traffic), so no
+    // load sits under a branch and the compiler counts outstanding loads
+    // exactly.
+    struct Stage {
         u32x4 raw[U][T][L];
         uint32_t sb[U][T];
+        u32x4 xc[U][2];
     };
-    auto load_w = [&](Batch &bt, int p0) {
+    auto issue = [&](Stage &st, int p0) {
+        const bool in0 = p0 >= p_lo && p0 < p_hi;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int p = min(p0 + u, n_pairs - 1);
+            const int p = p0 + u;
+            const bool in = p >= p_lo && p < p_hi;
+            const int pc = in ? p : 0;
+            const unsigned wv = in ? woff : kOutOfRange;
 #pragma unroll
-            for (int tt = 0; tt < T; ++tt) {
+            for (int tt = 0; tt < T; ++tt)
 #pragma unroll
                 for (int v = 0; v < L; ++v)
-                    bt.raw[u][tt][v] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[tt], woff, (p * L + v) * 1024, 0));
-                bt.sb[u][tt] = __builtin_amdgcn_raw_buffer_load_b32(sbres[tt], sboff, p * 128, 0);
+                    st.raw[u][tt][v] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[tt], wv, (pc * L + v) * 1024, 0));
+        }
+        // one load gives this lane's scale/bias words of both pairs of a block
+        const int pc0 = in0 ? p0 : 0;
+        const unsigned sv = in0 ? sboff : kOutOfRange;
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            if (U == 2) {
+                const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sbres[tt], sv, (pc0 >> 1) * 256, 0);
+                st.sb[0][tt] = v2[0];
+                st.sb[U - 1][tt] = v2[1];
+            } else {
+                st.sb[0][tt] = __builtin_amdgcn_raw_buffer_load_b32(sbres[tt], sv, (pc0 >> 1) * 256 + (pc0 & 1) * 4, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u;
+            const bool in = p >= p_lo && p < p_hi;
+            const int pc = in ? p : 0;
+            // the odd last group of a row has no partner: its chunks read zeros
+            const bool gin = 2 * pc + (xch >> 3) < ng;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = xrow0 + 4 * i;
+                const unsigned off = (in && gin && row < M) ? (unsigned)((row * K + 8 * xch) * 2) : kOutOfRange;
+                st.xc[u][i] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, pc * 256, 0));
             }
         }
     };
-    auto load_x = [&](u32x4 (&a)[U][4], int p0) {
+    auto compute = [&](const Stage &st, int p0) {
+        // Stage x through this wave's LDS slot, then read the MFMA A
+        // fragments back.  LDS operations of one wave complete in order, so
+        // the slot can be rewritten by the next stage right away.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = min(p0 + u, n_pairs - 1);
-            // the odd last group of a row has no partner: its half reads zeros
-            const unsigned off = (2 * p + h < ng) ? xoff : kOutOfRange;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                a[u][s4] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + s4 * 16u, p * 256, 0));
-        }
-    };
-    auto compute = [&](const Batch &bt, const u32x4 (&a)[U][4], int p0) {
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<u32x4 *>(&sh.xs[wave][u][xrow0 + 4 * i][8 * xch]) = st.xc[u][i];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (p0 + u >= p_hi)
@@ -243,15 +318,16 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
                 c[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a[u][s4]);
+                const uint16_t *src = a_act ? &sh.xs[wave][u][r & 7][64 * h + 32 * sub + 8 * s4] : xzero;
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(src);
                 cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, cx, 0, 0, 0);
 #pragma unroll
                 for (int tt = 0; tt < T; ++tt) {
                     bf16x8 bv;
                     if (BITS == 4) {
-                        bv = unpack_w4(bt.raw[u][tt][0][s4]);
+                        bv = unpack_w4(st.raw[u][tt][0][s4], w4base);
                     } else {
-                        const u32x4 &lo = bt.raw[u][tt][s4 >> 1];
+                        const u32x4 &lo = st.raw[u][tt][s4 >> 1];
                         bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
                     }
                     c[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c[tt], 0, 0, 0);
@@ -261,8 +337,8 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
             // same rows' sums of x over the group.
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
-                const float s = half_bits_to_float((uint16_t)(bt.sb[u][tt] & 0xFFFFu));
-                const float bias = half_bits_to_float((uint16_t)(bt.sb[u][tt] >> 16));
+                const float s = half_bits_to_float((uint16_t)(st.sb[u][tt] & 0xFFFFu));
+                const float bias = half_bits_to_float((uint16_t)(st.sb[u][tt] >> 16));
                 const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -273,26 +349,28 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         }
     };
 
-    // Vector-memory loads complete in issue order, so each batch's x
-    // operands (L2 hits) are requested before the next batch of weights
-    // (HBM): consuming them never waits for the weights still in flight.
-    Batch cur, nxt;
-    u32x4 a[U][4];
-    if (p_lo < p_hi)
-        load_w(cur, p_lo);
-    for (int p0 = p_lo; p0 < p_hi; p0 += U) {
-        load_x(a, p0);
-        if (p0 + U < p_hi)
-            load_w(nxt, p0 + U);
-        compute(cur, a, p0);
-        cur = nxt;
+    // S stages in flight: while one is computed the others are loading.  The
+    // loop starts one round early with nothing to compute, so the loads the
+    // loop header sees are always the previous round's, in issue order, and
+    // each compute waits only for its own stage.
+    Stage st[S];
+    for (int base = p_lo - S * U; base < p_hi; base += S * U) {
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            if (base + q * U >= p_lo)
+                compute(st[q], base + q * U);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(st[q], base + (q + S) * U);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // Fixed-order reduction: the two groups of a pair (lanes l, l ^ 32), then
     // the waves in index order.  Neither depends on M.
+    __syncthreads();   // every wave is done with its x slot
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
-        red[wave][tt][lane] = acc[tt];
+        sh.red[wave][tt][lane] = acc[tt];
     __syncthreads();
     if (wave == 0 && lane < 32) {
 #pragma unroll
@@ -300,9 +378,9 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
             const int n = (blockIdx.x * T + tt) * 16 + r;
             if (n >= N)
                 continue;
-            f32x4 tot = red[0][tt][lane] + red[0][tt][lane + 32];
+            f32x4 tot = sh.red[0][tt][lane] + sh.red[0][tt][lane + 32];
             for (int ww = 1; ww < WAVES; ++ww)
-                tot += red[ww][tt][lane] + red[ww][tt][lane + 32];
+                tot += sh.red[ww][tt][lane] + sh.red[ww][tt][lane + 32];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * sub + i;
@@ -325,20 +403,26 @@ QmvPlan qmv_plan(int bits, int N, int K) {
     QmvPlan p{};
     p.n_tiles = (N + 15) / 16;
     p.n_pairs = (K / 64 + 1) / 2;
-    // Enough tiles: each wave serves two (or, for very wide matrices, four)
-    // tiles with one x operand, cutting the x traffic by that factor; 4 waves
-    // split K.  (W8 streams twice the bytes per x fragment, so two suffice.)  Few tiles: one tile per workgroup and K
-    // split over 4 or 8 waves, so even N = 5120 gives >= 2560 waves.  The
-    // choice depends on (N, K) only, never on M.
-    if (p.n_tiles >= 4096 && bits == 4) {
-        p.tiles_per_wave = 4;
-        p.waves = 4;
+    // Launch shape, from (N, K) only (never M, so row m never depends on M),
+    // chosen by measurement on the verify shapes: enough waves in flight to
+    // cover HBM latency, and as many tiles per wave as that allows, since
+    // the tiles served by one x fragment share its staging and its
+    // group-sum MFMA.
+    //   very tall (LM head, >= 4096 tiles):   4 tiles, 4 waves split K
+    //   tall (MLP gate/up, >= 1024 tiles):    2 tiles, 4 waves (W8: 1 tile, 8 waves)
+    //   long K (MLP down, >= 96 pairs):       2 tiles, 8 waves
+    //   the rest (attention q/k/v/o):         1 tile, 8 waves
+    p.pairs_per_stage = 1;
+    if (p.n_tiles >= 4096) {
+        p.tiles_per_wave = bits == 4 ? 4 : 2;
+        p.waves = bits == 4 ? 4 : 8;
     } else if (p.n_tiles >= 1024) {
-        p.tiles_per_wave = 2;
-        p.waves = 4;
+        p.tiles_per_wave = bits == 4 ? 2 : 1;
+        p.waves = bits == 4 ? 4 : 8;
+    } else if (p.n_pairs >= 96) {
+        p.tiles_per_wave = 2; p.waves = 8;
     } else {
-        p.tiles_per_wave = 1;
-        p.waves = K >= 8192 ? 8 : 4;
+        p.tiles_per_wave = 1; p.waves = 8;
     }
     return p;
 }
@@ -350,7 +434,7 @@ size_t qmv_packed_bytes(int bits, int N, int K) {
 
 size_t qmv_packed_sb_bytes(int N, int K) {
     const QmvPlan p = qmv_plan(4, N, K);
-    return (size_t)p.n_tiles * (2 * p.n_pairs) * 16 * 4;
+    return (size_t)p.n_tiles * ((p.n_pairs + 1) / 2) * 256;
 }
 
 hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
@@ -384,29 +468,19 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
     const u32x4 *wp = (const u32x4 *)w_packed;
     const uint32_t *sbp = (const uint32_t *)sb_packed;
     const dim3 grid((plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave);
-#define SPEC_QMV_LAUNCH(B, W, TT) \
-    qmv_kernel<B, W, TT><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K)
-    if (bits == 4) {
-        if (plan.tiles_per_wave == 4)
-            SPEC_QMV_LAUNCH(4, 4, 4);
-        else if (plan.tiles_per_wave == 2)
-            SPEC_QMV_LAUNCH(4, 4, 2);
-        else if (plan.waves == 8)
-            SPEC_QMV_LAUNCH(4, 8, 1);
-        else
-            SPEC_QMV_LAUNCH(4, 4, 1);
-    } else {
-        if (plan.tiles_per_wave == 4)
-            SPEC_QMV_LAUNCH(8, 4, 4);
-        else if (plan.tiles_per_wave == 2)
-            SPEC_QMV_LAUNCH(8, 4, 2);
-        else if (plan.waves == 8)
-            SPEC_QMV_LAUNCH(8, 8, 1);
-        else
-            SPEC_QMV_LAUNCH(8, 4, 1);
+#define SPEC_QMV_LAUNCH(B, W, TT, UU)                                                       \
+    if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.pairs_per_stage == UU) { \
+        qmv_kernel<B, W, TT, UU, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+        return hipGetLastError();                                                           \
     }
+#define SPEC_QMV_SHAPES(B) \
+    SPEC_QMV_LAUNCH(B, 4, 4, 1) SPEC_QMV_LAUNCH(B, 4, 2, 1) SPEC_QMV_LAUNCH(B, 8, 2, 1) \
+    SPEC_QMV_LAUNCH(B, 8, 1, 1)
+    SPEC_QMV_SHAPES(4)
+    SPEC_QMV_SHAPES(8)
+#undef SPEC_QMV_SHAPES
 #undef SPEC_QMV_LAUNCH
-    return hipGetLastError();
+    return hipErrorInvalidConfiguration;   // no kernel for this plan (unreachable)
 }
 
 } // namespace spec

@@ -13,10 +13,11 @@ namespace spec {
 // waves splitting K.  It depends on (bits, N, K) only, never on M, so row m of an
 // M-row call reduces in exactly the same order as a one-row call.
 struct QmvPlan {
-    int n_tiles;   // 16-row tiles = workgroups
-    int n_pairs;   // 128-wide K steps (pairs of 64-groups)
-    int waves;     // waves per workgroup (K split inside the workgroup)
-    int tiles_per_wave;  // tiles each wave serves with one x operand
+    int n_tiles;          // 16-row tiles
+    int n_pairs;          // 128-wide K steps (pairs of 64-groups)
+    int waves;            // waves per workgroup (K split inside the workgroup)
+    int tiles_per_wave;   // tiles each workgroup (and each of its waves) serves
+    int pairs_per_stage;  // pairs per in-flight load stage (1 or 2)
 };
 
 QmvPlan qmv_plan(int bits, int N, int K);

@@ -85,11 +85,13 @@ def test_pack_validation(L, fn):
 
 def test_packed_sizes(L):
     # 16-row tiles x 128-wide K steps of 1 KB (W4) / 2 KB (W8); one 32-bit
-    # scale/bias word per row and (padded) group.
+    # scale/bias word per row and group, in blocks of two K steps (256 B per
+    # tile and block, the last block padded).
     assert L.spec_qmv_packed_weight_bytes(4, 5120, 17408, 64) == 320 * 136 * 1024
     assert L.spec_qmv_packed_weight_bytes(8, 151936, 5120, 64) == 9496 * 40 * 2048
     assert L.spec_qmv_packed_weight_bytes(4, 100, 192, 64) == 7 * 2 * 1024   # ragged N, odd groups
-    assert L.spec_qmv_packed_sb_bytes(100, 192, 64) == 7 * 4 * 16 * 4
+    assert L.spec_qmv_packed_sb_bytes(100, 192, 64) == 7 * 1 * 256
+    assert L.spec_qmv_packed_sb_bytes(100, 320, 64) == 7 * 2 * 256        # 3 K steps -> 2 blocks
     assert L.spec_qmv_packed_weight_bytes(4, 64, 100, 64) == 0           # invalid shape
 
 
