@@ -502,37 +502,46 @@ __device__ __forceinline__ float row_prob(const RowFinal &f, const uint64_t *key
     return weight(zx, f.m, scale) * f.inv;
 }
 
-// Decisions of sequence b from the row statistics: returns L (0..D) or -1
-// for an invalid sequence.  p_out / q_out (nullable) get P_i(d_i), Q_i(d_i).
-__device__ int decide(const Rows &rows, const Ws &ws, const SamplingParams &sp,
-                      const int32_t *draft_tokens, const float *uniforms, int b,
-                      float *p_out, float *q_out) {
+// Decisions of sequence b from the row statistics, one position per lane
+// of wave 0: returns L (0..D) or -1 for an invalid sequence to every thread
+// of the block (through *sh_L).  When p_out / q_out are given, wave 0 also
+// writes P_i(d_i), Q_i(d_i) for the sequence (NaN if it is invalid).  Called
+// by all threads of the block.
+__device__ int decide_block(const Rows &rows, const Ws &ws, const SamplingParams &sp,
+                            const int32_t *draft_tokens, const float *uniforms, int b,
+                            float *p_out, float *q_out, int *sh_L) {
     const int D = rows.D, V = rows.V;
-    for (int i = 0; i <= D; ++i)
-        if (ws.row_final[rows.target_row(b, i)].flags)
-            return -1;
-    for (int i = 0; i < D; ++i) {
-        if (ws.row_final[rows.draft_row(b, i)].flags)
-            return -1;
-        const int d = draft_tokens[(size_t)b * D + i];
-        if (d < 0 || d >= V)
-            return -1;
+    if (threadIdx.x < 64) {
+        const int i = threadIdx.x;
+        bool bad = false, rej = false;
+        float p = 0.0f, q = 0.0f;
+        if (i <= D)
+            bad = ws.row_final[rows.target_row(b, i)].flags != 0;
+        if (i < D) {
+            const int tr = rows.target_row(b, i), dr = rows.draft_row(b, i);
+            const RowFinal ft = ws.row_final[tr], fd = ws.row_final[dr];
+            const int d = draft_tokens[(size_t)b * D + i];
+            bad = bad || fd.flags != 0 || d < 0 || d >= V;
+            if (!bad) {
+                const float zt = rows.row(tr)[d], zd = rows.row(dr)[d];
+                p = row_prob(ft, ws.row_keys + (size_t)tr * sp.k_eff, sp.candidates, sp.scale, zt, d);
+                q = row_prob(fd, ws.row_keys + (size_t)dr * sp.k_eff, sp.candidates, sp.scale, zd, d);
+                const float a = (p == 0.0f) ? 0.0f : p / q;
+                rej = !(uniforms[(size_t)b * (D + 1) + i] < a);
+            }
+        }
+        const unsigned long long any_bad = __ballot(bad);
+        const unsigned long long rejects = __ballot(rej);
+        const int L = any_bad ? -1 : (rejects ? __ffsll((long long)rejects) - 1 : D);
+        if (i < D) {
+            if (p_out) p_out[(size_t)b * D + i] = (L < 0) ? NAN : p;
+            if (q_out) q_out[(size_t)b * D + i] = (L < 0) ? NAN : q;
+        }
+        if (i == 0)
+            *sh_L = L;
     }
-    int L = D;
-    for (int i = 0; i < D; ++i) {
-        const int d = draft_tokens[(size_t)b * D + i];
-        const int tr = rows.target_row(b, i), dr = rows.draft_row(b, i);
-        const RowFinal ft = ws.row_final[tr], fd = ws.row_final[dr];
-        const float zt = rows.row(tr)[d], zd = rows.row(dr)[d];
-        const float p = row_prob(ft, ws.row_keys + (size_t)tr * sp.k_eff, sp.candidates, sp.scale, zt, d);
-        const float q = row_prob(fd, ws.row_keys + (size_t)dr * sp.k_eff, sp.candidates, sp.scale, zd, d);
-        if (p_out) p_out[i] = p;
-        if (q_out) q_out[i] = q;
-        const float a = (p == 0.0f) ? 0.0f : p / q;
-        if (L == D && !(uniforms[(size_t)b * (D + 1) + i] < a))
-            L = i;
-    }
-    return L;
+    __syncthreads();
+    return *sh_L;
 }
 
 // The draw distribution of sequence b once L is known: target row L, and
@@ -582,10 +591,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const int c = blockIdx.y;
     const int V = rows.V;
     const int nblocks = (V + kBlock - 1) / kBlock;
-    if (threadIdx.x == 0)
-        s_L = decide(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr);
-    __syncthreads();
-    const int L = s_L;
+    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
     if (L < 0)
         return;
     const DrawRows d = draw_rows(rows, ws, sp, b, L);
@@ -647,23 +653,14 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     const int D = rows.D, V = rows.V;
     const float scale = sp.scale;
 
-    if (threadIdx.x == 0) {
-        float pv[16], qv[16];
-        const int L = decide(rows, ws, sp, draft_tokens, uniforms, b, pv, qv);
-        sh.L = L;
-        for (int i = 0; i < D; ++i) {
-            if (p_draft) p_draft[(size_t)b * D + i] = (L < 0) ? NAN : pv[i];
-            if (q_draft) q_draft[(size_t)b * D + i] = (L < 0) ? NAN : qv[i];
-        }
-        if (L < 0) {
+    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    if (L < 0) {
+        if (threadIdx.x == 0) {
             if (accepted_len) accepted_len[b] = -1;
             next_token[b] = -1;
         }
-    }
-    __syncthreads();
-    const int L = sh.L;
-    if (L < 0)
         return;
+    }
     const float u = uniforms[(size_t)b * (D + 1) + D];
     const DrawRows d = draw_rows(rows, ws, sp, b, L);
 
