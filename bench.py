@@ -3,25 +3,35 @@
 One step = one pass of the whole hot path over resident synthetic inputs:
   * verify qmv: the MLP block of a 5120-hidden decoder (gate and up
     5120 -> 17408, down 17408 -> 5120, W4 group 64) at every verify width
-    M = 1..8.  Each M uses its own copy of the weights, so one step streams
-    1.2 GB of distinct weights -- far beyond the 256 MB last-level cache --
-    and nothing is served from cache across steps either.
+    M = 1..8.  Gate and up share their input, so they are packed as one
+    5120 -> 34816 matrix and computed by one launch (its outputs are bitwise
+    those of two separate launches); down is a second launch.  Each M uses
+    its own copy of the weights, so one step streams 1.2 GB of distinct
+    weights -- far beyond the 256 MB last-level cache -- and nothing is
+    served from cache across steps either.
   * verification: probability-ratio acceptance with residual / bonus draws
     for B = 256 sequences of depth D = 5 over a 151936-token vocabulary
     (fp32 logits, T = 0.6), i.e. 1536 verify positions.
+
+Launches go through pre-marshalled calls (`bind_qmv`, `bind_verify_accept`),
+so the host queues them far faster than the GPU runs them.  The same qmv
+work with gate and up as separate launches is timed as well and reported
+under `variants`.  (Replaying the step from a HIP graph measured slower than
+these eager launches on this system -- 359 vs 322 us for the qmv part -- so
+graphs are not used here; the library's calls are capture-safe all the same.)
 
 Printed: one JSON line.  `value` is the verify qmv throughput in HBM GB/s
 (algorithmic bytes / time of the qmv part of the steps); the acceptance
 throughput (verify positions per second) and per-M figures ride along.
 
-`roofline` covers qmv_kernel, the kernel with the most time per step (24
+`roofline` covers qmv_kernel, the kernel with the most time per step (16
 launches): algorithmic bytes per launch over the average launch duration,
-the qmv part of the timed steps (HIP events on the launch stream around
-the 24 back-to-back launches) divided by 24.  A second set of timed steps
-with events around every launch splits that time by shape and M.  Its `traffic`
-is the HBM bytes per launch from the committed counter summary under
-profiles/ (FETCH_SIZE + WRITE_SIZE scaled by a plain-copy calibration), and
-null when qmv.hip has changed since those counters were taken.
+the qmv part of the timed steps (HIP events on the launch stream around the
+16 back-to-back launches) divided by 16.  A second set of timed steps with
+events around every launch splits the time by shape and M.  `traffic` is the HBM bytes per
+launch from the committed counter summary under profiles/ (FETCH_SIZE +
+WRITE_SIZE scaled by a plain-copy calibration), and null when qmv.hip or the
+step's launches have changed since those counters were taken.
 
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
@@ -72,9 +82,10 @@ def copy_probe(dev):
     print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
-def measured_traffic():
+def measured_traffic(bytes_per_launch):
     """HBM bytes per qmv launch from the committed counter summary, or None
-    when the summary is missing or belongs to another qmv.hip."""
+    when the summary is missing, belongs to another qmv.hip, or was taken on
+    another mix of launches (other algorithmic bytes per launch)."""
     try:
         with open(TRAFFIC_FILE) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
@@ -83,32 +94,38 @@ def measured_traffic():
             sha = hashlib.sha256(f.read()).hexdigest()
         if kv.get("source_sha256") != sha:
             return None, "qmv.hip changed since the counters were taken"
+        if int(kv.get("algorithmic_bytes_per_launch", -1)) != round(bytes_per_launch):
+            return None, "the step's launches changed since the counters were taken"
         return float(kv["traffic_bytes_per_launch"]), kv
     except (OSError, KeyError, ValueError):
         return None, "no counter summary"
 
 
 def build_inputs(dev):
-    """Packed W4 weights (packing is a load-time step, outside the timing)."""
+    """Packed W4 weights (packing is a load-time step, outside the timing):
+    per M, the fused gate/up matrix, the down matrix, and gate and up packed
+    separately (for the unfused comparison)."""
     import torch
     import speculative_decoding_spec_amd as spec
     from speculative_decoding_spec_amd import synth
 
-    def packed(N, K, seed):
-        w, s, b = synth.torch_qweights(4, N, K, GROUP, seed, dev)
-        return spec.spec_pack_w4(w, s, b, G=GROUP)
-
     blocks = []
     for i, M in enumerate(MS):
-        gate = packed(FFN, HIDDEN, 1000 + 10 * i)
-        up = packed(FFN, HIDDEN, 1001 + 10 * i)
-        down = packed(HIDDEN, FFN, 1002 + 10 * i)
+        g = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1000 + 10 * i, dev)
+        u = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1001 + 10 * i, dev)
+        d = synth.torch_qweights(4, HIDDEN, FFN, GROUP, 1002 + 10 * i, dev)
+        gate_up = spec.spec_pack_w4(*[torch.cat([a, b]) for a, b in zip(g, u)], G=GROUP)
+        gate, up = spec.spec_pack_w4(*g, G=GROUP), spec.spec_pack_w4(*u, G=GROUP)
+        down = spec.spec_pack_w4(*d, G=GROUP)
+        del g, u, d
         x = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
         h = synth.torch_activations(M, FFN, 1004 + 10 * i, dev)
+        ygu = torch.empty((M, 2 * FFN), dtype=torch.float32, device=dev)
         yg = torch.empty((M, FFN), dtype=torch.float32, device=dev)
         yu = torch.empty((M, FFN), dtype=torch.float32, device=dev)
         yd = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
-        blocks.append(dict(M=M, gate=gate, up=up, down=down, x=x, h=h, yg=yg, yu=yu, yd=yd))
+        blocks.append(dict(M=M, gate_up=gate_up, gate=gate, up=up, down=down, x=x, h=h,
+                           ygu=ygu, yg=yg, yu=yu, yd=yd))
     torch.cuda.synchronize()
     return blocks
 
@@ -211,35 +228,44 @@ def main():
     acc = build_accept(dev)
     stream = torch.cuda.current_stream(dev)
 
-    qmv_bytes_step = sum(roofline.qmv_bytes(4, b["M"], FFN, HIDDEN) * 2 +
-                         roofline.qmv_bytes(4, b["M"], HIDDEN, FFN) for b in blocks)
     acc_bytes = roofline.accept_bytes(ACC_B, ACC_D, ACC_V)
-
-    # Per step: 24 qmv launches (gate, up, down at M = 1..8) and one
-    # acceptance call, all marshalled once so the host stays ahead of the GPU.
-    launches = []
-    for b in blocks:
-        launches.append((spec.bind_qmv(b["gate"], b["x"], b["yg"]), "gate",
-                         roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
-        launches.append((spec.bind_qmv(b["up"], b["x"], b["yu"]), "up",
-                         roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
-        launches.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
-                         roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
-    accept_call = spec.bind_verify_accept(acc["t"], acc["d"], acc["toks"], acc["u"], ACC_T,
-                                          out=(acc["acc"], acc["nxt"], None, None))
 
     def pair():
         return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
-    def step(ev=None, per_launch=False):
+    def fused_launches():
+        """(bound call, shape name, algorithmic bytes) of the 16 launches."""
+        out = []
+        for b in blocks:
+            out.append((spec.bind_qmv(b["gate_up"], b["x"], b["ygu"]), "gate_up",
+                        roofline.qmv_bytes(4, b["M"], 2 * FFN, HIDDEN)))
+            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
+                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
+        return out
+
+    def unfused_launches():
+        out = []
+        for b in blocks:
+            out.append((spec.bind_qmv(b["gate"], b["x"], b["yg"]), "gate",
+                        roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
+            out.append((spec.bind_qmv(b["up"], b["x"], b["yu"]), "up",
+                        roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
+            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
+                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
+        return out
+
+    launches = fused_launches()
+    unfused = unfused_launches()
+    accept_call = spec.bind_verify_accept(acc["t"], acc["d"], acc["toks"], acc["u"], ACC_T,
+                                          out=(acc["acc"], acc["nxt"], None, None))
+    qmv_bytes_step = sum(l[2] for l in launches)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
         if ev is not None:
             ev["q"][0].record(stream)
-        for i, (call, _, _) in enumerate(launches):
-            if per_launch:
-                ev["l"][i][0].record(stream)
+        for call, _, _ in launches:
             call()
-            if per_launch:
-                ev["l"][i][1].record(stream)
         if ev is not None:
             ev["q"][1].record(stream)
             ev["a"][0].record(stream)
@@ -251,7 +277,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed steps: events around the qmv part and the acceptance call only.
+    # Timed steps: events around the qmv part and the acceptance call.
     ev = [{"q": pair(), "a": pair()} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -263,32 +289,50 @@ def main():
     acc_ms = sum(e["a"][0].elapsed_time(e["a"][1]) for e in ev) / args.steps
     qmv_gbs = qmv_bytes_step / (qspan_ms * 1e-3) / 1e9
 
-    # Same steps again with a pair of events around every qmv launch: the
-    # per-launch durations behind the roofline and the per-shape figures.
-    # Each step's 24 launches are queued behind the previous step's
-    # acceptance call, so every start event executes behind GPU work rather
-    # than ahead of a launch the host has yet to issue.
-    evl = [{"q": pair(), "a": pair(), "l": [pair() for _ in launches]} for _ in range(args.steps)]
-    step()   # untimed, not waited for: the queue is already busy at the first event
-    for k in range(args.steps):
-        step(evl[k], per_launch=True)
-    torch.cuda.synchronize()
-    q_ms = [sum(e["l"][i][0].elapsed_time(e["l"][i][1]) for e in evl) / args.steps
-            for i in range(len(launches))]
+    def eager(calls, per_launch):
+        """K eager steps of `calls`: the span of each step and, if asked, the
+        duration of every launch (events around it)."""
+        evs = [(pair(), [pair() for _ in calls]) for _ in range(args.steps)]
+        accept_call()          # untimed: the queue is busy at the first event
+        for span, each in evs:
+            span[0].record(stream)
+            for i, (call, _, _) in enumerate(calls):
+                if per_launch:
+                    each[i][0].record(stream)
+                call()
+                if per_launch:
+                    each[i][1].record(stream)
+            span[1].record(stream)
+            accept_call()
+        torch.cuda.synchronize()
+        span_ms = sum(s[0].elapsed_time(s[1]) for s, _ in evs) / args.steps
+        each_ms = ([sum(e[i][0].elapsed_time(e[i][1]) for _, e in evs) / args.steps
+                    for i in range(len(calls))] if per_launch else None)
+        return span_ms, each_ms
+
+    eager_unfused_ms, _ = eager(unfused, False)
+    _, q_ms = eager(launches, True)
     per_m = {}
     for j, b in enumerate(blocks):
-        ms = sum(q_ms[3 * j:3 * j + 3])
-        nb = sum(l[2] for l in launches[3 * j:3 * j + 3])
+        ms = sum(q_ms[2 * j:2 * j + 2])
+        nb = sum(l[2] for l in launches[2 * j:2 * j + 2])
         per_m[str(b["M"])] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                               "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
     per_shape = {}
-    for name in ("gate", "up", "down"):
+    for name in ("gate_up", "down"):
         idx = [i for i, l in enumerate(launches) if l[1] == name]
         ms = sum(q_ms[i] for i in idx) / len(idx)
         nb = sum(launches[i][2] for i in idx) / len(idx)
         per_shape[name] = {"us_per_launch": round(ms * 1e3, 2),
                            "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                            "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
+    unfused_bytes = sum(l[2] for l in unfused)
+    variants = {
+        "fused gate/up, 16 launches (value)": {"qmv_us_per_step": round(qspan_ms * 1e3, 2),
+                                               "GB/s": round(qmv_gbs, 1)},
+        "separate gate and up, 24 launches": {"qmv_us_per_step": round(eager_unfused_ms * 1e3, 2),
+                                              "GB/s": round(unfused_bytes / (eager_unfused_ms * 1e-3) / 1e9, 1)},
+    }
     positions = ACC_B * (ACC_D + 1)
     acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
     accept = {"positions_per_s": round(positions / (acc_ms * 1e-3), 1), "us": round(acc_ms * 1e3, 2),
@@ -297,15 +341,15 @@ def main():
               "mean_accepted": float(acc["acc"].float().mean().item())}
 
     # Roofline of qmv_kernel: algorithmic bytes per launch over the average
-    # launch duration, i.e. the qmv part of a step (24 launches queued back to
-    # back, no events between them) divided by 24.  The per-launch events of
-    # the second set add about 2 us of marker time to each launch, so they
-    # only split the time by shape.
+    # launch duration, i.e. the qmv part of a step (16 launches back to back,
+    # no events between them) divided by 16.  The per-launch events of the
+    # second set of steps add about 2 us of marker time to each launch, so
+    # they only split the time by shape.
     bytes_per_launch = qmv_bytes_step / len(launches)
     launch_us = qspan_ms / len(launches) * 1e3
     achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
-    traffic, tinfo = measured_traffic()
-    roof = {"kernel": "qmv_kernel (W4; 24 launches per step: gate, up, down at M=1..8)",
+    traffic, tinfo = measured_traffic(bytes_per_launch)
+    roof = {"kernel": "qmv_kernel (W4; 16 launches per step: fused gate/up and down at M=1..8)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
             "frac": round(achieved / 8000.0, 4),
             "traffic": None if traffic is None else round(traffic),
@@ -313,7 +357,7 @@ def main():
             "avg_launch_us": round(launch_us, 2),
             "traffic_source": (os.path.relpath(TRAFFIC_FILE, ROOT) if traffic is not None else tinfo)}
     other = {"qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
-                            "per_shape": per_shape},
+                            "per_shape (per-launch events)": per_shape},
              "accept (row_chunk + draw_sums + draw_final)": {
                  "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
                  "us_per_call": round(acc_ms * 1e3, 2)}}
@@ -324,13 +368,13 @@ def main():
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "w4-bf16xfp32 qmv; fp32 accept",
         "data": "synthetic (seeded, on-device generators)",
-        "config": {"workload": ("verify MLP block W4 g64 (gate/up 5120->17408, down 17408->5120) "
-                                "at M=1..8 on distinct weight copies + batched acceptance "
-                                "B=256 D=5 V=151936 T=0.6"),
+        "config": {"workload": ("verify MLP block W4 g64 (gate/up 5120->17408 packed as one "
+                                "5120->34816 launch, down 17408->5120) at M=1..8 on distinct "
+                                "weight copies + batched acceptance B=256 D=5 V=151936 T=0.6"),
                    "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
         "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
-        "qmv_us_per_step": round(qspan_ms * 1e3, 2),
-        "per_M": per_m, "accept": accept, "roofline": roof, "roofline_parts": other,
+        "qmv_us_per_step": round(qspan_ms * 1e3, 2), "variants": variants,
+        "per_M (per-launch events)": per_m, "accept": accept, "roofline": roof, "roofline_parts": other,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

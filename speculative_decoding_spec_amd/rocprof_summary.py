@@ -6,8 +6,9 @@
         per kernel and counter: dispatches and average value per dispatch
     python -m speculative_decoding_spec_amd.rocprof_summary traffic \
             --fetch DB --write DB --copy-fetch DB --copy-write DB \
-            --copy-bytes N --match S --source FILE
-        HBM bytes per launch of the matching kernels: FETCH_SIZE and
+            --copy-bytes N --match S --source FILE [--mix GRID_X:N ...]
+        HBM bytes per launch of the matching kernels (optionally a weighted
+        mix of launches told apart by grid size): FETCH_SIZE and
         WRITE_SIZE (KiB per dispatch) each scaled by the ratio of known bytes
         to what the same counter reads for a plain copy kernel of N bytes
         (read once, written once); FILE's sha256 records the kernel source
@@ -92,17 +93,36 @@ def counter_rows(db: str, match=None):
     return out
 
 
-def _per_dispatch(db: str, counter: str, match):
-    """{dispatch_id: summed value} of one counter over the matching kernels."""
+def _per_dispatch(db: str, counter: str, match, grid=None):
+    """{dispatch_id: summed value} of one counter over the matching kernels
+    (and, if given, the launches of total grid size `grid` in x)."""
     con = sqlite3.connect(db)
     cols = [r[1] for r in con.execute("pragma table_info(counters_collection)")]
     name_col = "kernel_name" if "kernel_name" in cols else "name"
+    gx = "grid_size_x" if "grid_size_x" in cols else "0"
     d: dict = {}
-    for name, c, v, disp in con.execute(
-            f"select {name_col}, counter_name, value, dispatch_id from counters_collection"):
-        if c == counter and _matches(name, match):
+    for name, c, v, disp, g in con.execute(
+            f"select {name_col}, counter_name, value, dispatch_id, {gx} from counters_collection"):
+        if c == counter and _matches(name, match) and (grid is None or g == grid):
             d[disp] = d.get(disp, 0.0) + v
     return d
+
+
+def _mix_average(db: str, counter: str, match, mix):
+    """Per-launch average of a counter over a launch mix: `mix` maps grid
+    size to launches per step; each grid's dispatches are averaged first."""
+    if not mix:
+        vals = list(_per_dispatch(db, counter, match).values())
+        return sum(vals) / len(vals), len(vals)
+    total, count, seen = 0.0, 0, 0
+    for grid, n in mix.items():
+        vals = list(_per_dispatch(db, counter, match, grid).values())
+        if not vals:
+            raise SystemExit(f"no {counter} dispatches with grid {grid}")
+        total += n * sum(vals) / len(vals)
+        count += n
+        seen += len(vals)
+    return total / count, seen
 
 
 def traffic(a) -> None:
@@ -113,9 +133,12 @@ def traffic(a) -> None:
     copy_fetch_kib, copy_write_kib = max(cf.values()), max(cw.values())
     fetch_factor = a.copy_bytes / (copy_fetch_kib * 1024.0)
     write_factor = a.copy_bytes / (copy_write_kib * 1024.0)
-    f = list(_per_dispatch(a.fetch, "FETCH_SIZE", a.match).values())
-    w = list(_per_dispatch(a.write, "WRITE_SIZE", a.match).values())
-    fk, wk = sum(f) / len(f), sum(w) / len(w)
+    mix = {}
+    for item in a.mix or []:
+        g, n = item.split(":")
+        mix[int(g)] = int(n)
+    fk, nf = _mix_average(a.fetch, "FETCH_SIZE", a.match, mix)
+    wk, nw = _mix_average(a.write, "WRITE_SIZE", a.match, mix)
     with open(a.source, "rb") as fh:
         sha = hashlib.sha256(fh.read()).hexdigest()
     print(f"kernel_match: {' '.join(a.match)}")
@@ -126,8 +149,10 @@ def traffic(a) -> None:
     print(f"copy_write_kib: {copy_write_kib:.1f}")
     print(f"fetch_factor: {fetch_factor:.4f}")
     print(f"write_factor: {write_factor:.4f}")
-    print(f"launches_fetch: {len(f)}")
-    print(f"launches_write: {len(w)}")
+    if mix:
+        print("launch_mix: " + " ".join(f"{g}:{n}" for g, n in mix.items()))
+    print(f"launches_fetch: {nf}")
+    print(f"launches_write: {nw}")
     print(f"fetch_kib_per_launch: {fk:.1f}")
     print(f"write_kib_per_launch: {wk:.1f}")
     print(f"hbm_read_bytes_per_launch: {fk * 1024 * fetch_factor:.0f}")
@@ -146,6 +171,7 @@ def main(argv=None):
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int)
     ap.add_argument("--source")
+    ap.add_argument("--mix", nargs="*", help="GRID_X:LAUNCHES pairs weighting the per-grid averages")
     a = ap.parse_args(argv)
     if a.mode == "traffic":
         traffic(a)

@@ -140,3 +140,21 @@ def test_bound_call_matches_plain_call(dev):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), first.view(torch.int32))
     assert torch.equal(spec.spec_qmv_w4(pk, xt).view(torch.int32), y.view(torch.int32))
+
+
+def test_fused_gate_up_matches_separate_launches(dev):
+    """Packing the gate and up projections as one 5120 -> 34816 matrix (one
+    launch) gives bitwise the outputs of the two separate launches."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    K, N = 5120, 17408
+    gate = synth.qweights(8, 4, N, K, 64, salt=1)
+    up = synth.qweights(8, 4, N, K, 64, salt=2)
+    x = parity.dev_x(synth.activations(8, 6, K), dev)
+    g = spec.spec_pack_w4(*parity.dev_qweights(*gate, dev))
+    u = spec.spec_pack_w4(*parity.dev_qweights(*up, dev))
+    cat = [np.concatenate([a, b], axis=0) for a, b in zip(gate, up)]
+    gu = spec.spec_pack_w4(*parity.dev_qweights(*cat, dev))
+    y = spec.spec_qmv_w4(gu, x)
+    assert torch.equal(y[:, :N].view(torch.int32), spec.spec_qmv_w4(g, x).view(torch.int32))
+    assert torch.equal(y[:, N:].view(torch.int32), spec.spec_qmv_w4(u, x).view(torch.int32))
