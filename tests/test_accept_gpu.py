@@ -291,3 +291,44 @@ def test_bound_call_matches_plain_call(dev):
     ref = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
     assert np.array_equal(acc.cpu().numpy(), ref["accepted_len"])
     assert np.array_equal(nxt.cpu().numpy(), ref["next_token"])
+
+
+# ------------------------------------------------------------ size limits ----
+@pytest.mark.parametrize("V,k,p", [((1 << 24) - 1, 0, 1.0), ((1 << 22) + 3, 256, 0.9)])
+def test_largest_vocabulary(dev, V, k, p):
+    """V = 2^24 - 1, the largest the ABI accepts (odd, so the scalar-load
+    path); the widest candidate set (k = 256) on a 4M vocabulary (the oracle
+    sorts whole rows for top-k, so the largest size would take it minutes)."""
+    B, D = 1, 1
+    t, d = synth.logits_pair(700, B, D, V)
+    toks = draft_tokens(d, 0.6, k, p, 700)
+    u = synth.uniforms(700, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 0.6, k, p, dev)
+
+
+def test_deepest_block(dev):
+    """D = 15 drafts (M = 16 verify positions), the largest depth accepted."""
+    B, D, V = 8, 15, 4096
+    t, d = synth.logits_pair(701, B, D, V)
+    # draft = target exactly for the first positions makes deep acceptance likely
+    d[:, :10] = t[:, :10]
+    toks = draft_tokens(d, 0.6, 0, 1.0, 701)
+    u = synth.uniforms(701, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert ref["accepted_len"].max() >= 10
+
+
+def test_many_sequences_small_vocabulary(dev):
+    B, D, V = 4096, 2, 256
+    t, d = synth.logits_pair(702, B, D, V)
+    toks = draft_tokens(d, 1.0, 0, 1.0, 702)
+    u = synth.uniforms(702, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 1.0, 0, 1.0, dev)
+
+
+def test_two_token_vocabulary(dev):
+    B, D, V = 64, 3, 2
+    t, d = synth.logits_pair(703, B, D, V)
+    toks = draft_tokens(d, 0.8, 0, 1.0, 703)
+    u = synth.uniforms(703, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 0.8, 0, 1.0, dev)

@@ -158,3 +158,9 @@ def test_fused_gate_up_matches_separate_launches(dev):
     y = spec.spec_qmv_w4(gu, x)
     assert torch.equal(y[:, :N].view(torch.int32), spec.spec_qmv_w4(g, x).view(torch.int32))
     assert torch.equal(y[:, N:].view(torch.int32), spec.spec_qmv_w4(u, x).view(torch.int32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_long_k(dev, bits):
+    """K = 131072 (1024 pairs per row, 64-128 per wave) on two ragged tiles."""
+    full_check(bits, 8, 30, 131072, dev, cfg=10, salt=bits)
