@@ -177,7 +177,10 @@ __global__ __launch_bounds__(256) void pack_kernel(
     }
 }
 
-template <int BITS, int WAVES, int T, int U, int S>
+// XH: 16-byte x loads per lane and pair -- 1 when M <= 4 (rows 0..3),
+// 2 when M <= 8.  Rows a launch does not stage are never read (their MFMA
+// operand lanes read zeros), so both variants compute bitwise the same.
+template <int BITS, int WAVES, int T, int U, int S, int XH>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
     const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     struct Stage {
         u32x4 raw[U][T][L];
         uint32_t sb[U][T];
-        u32x4 xc[U][2];
+        u32x4 xc[U][XH];
     };
     auto issue = [&](Stage &st, int p0) {
         const bool in0 = p0 >= p_lo && p0 < p_hi;
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
             // the odd last group of a row has no partner: its chunks read zeros
             const bool gin = 2 * pc + (xch >> 3) < ng;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < XH; ++i) {
                 const int row = xrow0 + 4 * i;
                 const unsigned off = (in && gin && row < M) ? (unsigned)((row * K + 8 * xch) * 2) : kOutOfRange;
                 st.xc[u][i] = __builtin_bit_cast(
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < XH; ++i)
                 *reinterpret_cast<u32x4 *>(&sh.xs[wave][u][xrow0 + 4 * i][8 * xch]) = st.xc[u][i];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -474,7 +477,10 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
     const dim3 grid((plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave);
 #define SPEC_QMV_LAUNCH(B, W, TT, UU)                                                       \
     if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.pairs_per_stage == UU) { \
-        qmv_kernel<B, W, TT, UU, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+        if (M <= 4)                                                                         \
+            qmv_kernel<B, W, TT, UU, 2, 1><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+        else                                                                                \
+            qmv_kernel<B, W, TT, UU, 2, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
         return hipGetLastError();                                                           \
     }
 #define SPEC_QMV_SHAPES(B) \
