@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_accept.argtypes = [vp, vp, vp, vp, lg, lg, lg, f, i, f, vp, vp, vp,
                                     vp, vp]
         L.oracle_accept.restype = i
+        L.oracle_verify_greedy.argtypes = [vp, vp, lg, lg, lg, vp, vp]
+        L.oracle_verify_greedy.restype = i
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -186,3 +188,18 @@ def accept(target_logits: np.ndarray, draft_logits: np.ndarray | None,
         raise ValueError(f"oracle_accept failed (rc={rc})")
     return {"accepted_len": acc, "next_token": nxt, "p_draft": pd[:, :D],
             "q_draft": qd[:, :D], "draw_row": row}
+
+
+def verify_greedy(target_logits: np.ndarray, draft_tokens: np.ndarray | None) -> dict:
+    """Greedy verification (sample-and-match) of B sequences; target
+    [B][D+1][V], draft_tokens [B][D]."""
+    tl = np.ascontiguousarray(target_logits, dtype=np.float32)
+    B, D1, V = tl.shape
+    D = D1 - 1
+    dt = None if D == 0 else np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    rc = lib().oracle_verify_greedy(_ptr(tl), _ptr(dt), B, D, V, _ptr(acc), _ptr(nxt))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_greedy failed (rc={rc})")
+    return {"accepted_len": acc, "next_token": nxt}

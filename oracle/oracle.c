@@ -32,6 +32,13 @@
  *             savepearlharbor.com llama.cpp MTP article, section on how
  *             speculative decoding works.
  *
+ *   greedy    Verification with greedy sampling: keep each draft while it
+ *             equals the target's argmax at its position, emit the target's
+ *             argmax at the first mismatch (or at the bonus position):
+ *             savepearlharbor.com llama.cpp MTP article, how speculative
+ *             decoding works; greedy is T <= 0 or top_k == 1 (mlxcel manual,
+ *             DFlash-family drafter table).
+ *
  * Readings taken where the pages are silent are listed in the repository's
  * design notes; each is restated at the function that takes it.
  *
@@ -441,5 +448,58 @@ int oracle_accept(const float *target_logits, const float *draft_logits,
             draw_row[b] = (int32_t)i;
     }
     free(P); free(Q); free(r);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Greedy verification                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Greedy verification of B sequences: the sample-and-match loop of the
+ * savepearlharbor.com llama.cpp MTP article (how speculative decoding
+ * works), with the greedy sampler of the mlxcel manual's DFlash-family
+ * drafter table (sampling only when T > 0 and top_k != 1).
+ *
+ * Per sequence b, with t_i = the first index of the largest logit of
+ * target row i (i = 0..D):
+ *   for i = 0..D-1: keep d_i while d_i == t_i; at the first mismatch emit
+ *       t_i and stop (accepted = i, next = t_i);
+ *   if all D match: accepted = D, next = t_D.
+ * Only the target rows are read.  A target row that is invalid (NaN, +inf,
+ * or no finite logit, as for sampling) or a draft token outside [0, V) makes
+ * the sequence invalid: accepted = next = -1.  draft_tokens may be NULL when
+ * D == 0. */
+int oracle_verify_greedy(const float *target_logits, const int32_t *draft_tokens,
+                         long B, long D, long V, int32_t *accepted_len,
+                         int32_t *next_token)
+{
+    if (B < 0 || D < 0 || V < 1)
+        return -1;
+    for (long b = 0; b < B; ++b) {
+        const float *tl = target_logits + b * (D + 1) * V;
+        const int32_t *dt = draft_tokens ? draft_tokens + b * D : NULL;
+        int ok = 1;
+        for (long i = 0; i <= D && ok; ++i)
+            ok = row_valid(tl + i * V, V);
+        for (long i = 0; i < D && ok; ++i)
+            ok = (dt[i] >= 0 && dt[i] < V);
+        if (!ok) {
+            accepted_len[b] = next_token[b] = -1;
+            continue;
+        }
+        long i = 0;
+        long t = 0;
+        for (;; ++i) {
+            const float *z = tl + i * V;
+            t = 0;
+            for (long x = 1; x < V; ++x)
+                if (z[x] > z[t])
+                    t = x;
+            if (i == D || dt[i] != t)
+                break;
+        }
+        accepted_len[b] = (int32_t)i;
+        next_token[b] = (int32_t)t;
+    }
     return 0;
 }

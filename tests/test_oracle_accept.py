@@ -317,3 +317,83 @@ def test_oracle_is_thread_safe():
             par = list(ex.map(lambda r: oracle.probs(z[r], 0.8, 20, 0.95), range(64)))
             for a, b in zip(serial, par):
                 assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------ greedy verify ----
+
+def test_verify_greedy_matches_golden_sample_and_match(golden_dir):
+    # The article's worked block: drafts kept while they equal the target's
+    # token, the target's token emitted at the first mismatch or the bonus.
+    g = json.load(open(os.path.join(golden_dir, "verify_block_greedy.json")))
+    V = 32
+    for c in g["cases"]:
+        D = len(c["draft"])
+        t = np.zeros((1, D + 1, V), np.float32)
+        t[0, np.arange(D + 1), c["target_argmax"]] = 5.0
+        out = oracle.verify_greedy(t, np.array([c["draft"]], np.int32))
+        L = int(out["accepted_len"][0])
+        assert c["draft"][:L] + [int(out["next_token"][0])] == c["emitted"]
+
+
+def test_verify_greedy_equals_ratio_rule_at_top_k_one():
+    # Greedy limit of the probability-ratio rule: with one-hot P and Q the
+    # rule accepts exactly the drafts equal to the target argmax and emits
+    # the target argmax, so the two oracle functions must agree whatever
+    # the draft logits and uniforms are.
+    B, D, V = 300, 5, 40
+    rng = np.random.default_rng(31)
+    t, d = synth.logits_pair(31, B, D, V)
+    tok = np.argmax(t[:, :D], axis=2).astype(np.int32)
+    miss = rng.random((B, D)) < 0.25
+    tok[miss] = rng.integers(0, V, size=int(miss.sum()))
+    u = synth.uniforms(31, synth.U_ACCEPT, (B, D + 1))
+    ref = oracle.accept(t, d, tok, u, 0.6, top_k=1)
+    got = oracle.verify_greedy(t, tok)
+    assert np.array_equal(got["accepted_len"], ref["accepted_len"])
+    assert np.array_equal(got["next_token"], ref["next_token"])
+    assert 0 < np.mean(got["accepted_len"] == D) < 1      # both outcomes occur
+
+
+def test_verify_greedy_ties_take_the_lowest_index():
+    z = np.array([[[0.0, 2.0, 1.0, 2.0], [2.0, 2.0, 2.0, 2.0]]], np.float32)
+    out = oracle.verify_greedy(z, np.array([[3]], np.int32))
+    assert (int(out["accepted_len"][0]), int(out["next_token"][0])) == (0, 1)
+    out = oracle.verify_greedy(z, np.array([[1]], np.int32))
+    assert (int(out["accepted_len"][0]), int(out["next_token"][0])) == (1, 0)
+
+
+def test_verify_greedy_matches_numpy_argmax_prefix():
+    # numpy's argmax (first maximum) gives the target tokens; the accepted
+    # length is the length of the common prefix with the drafts.
+    B, D, V = 500, 7, 64
+    rng = np.random.default_rng(32)
+    t = rng.integers(-3, 4, size=(B, D + 1, V)).astype(np.float32)   # many ties
+    am = np.argmax(t, axis=2)
+    tok = am[:, :D].astype(np.int32).copy()
+    cut = rng.integers(0, D + 1, size=B)
+    for b in range(B):
+        if cut[b] < D:
+            tok[b, cut[b]] = (am[b, cut[b]] + 1 + rng.integers(0, V - 1)) % V
+    out = oracle.verify_greedy(t, tok)
+    assert np.array_equal(out["accepted_len"], cut)
+    assert np.array_equal(out["next_token"], am[np.arange(B), cut])
+
+
+def test_verify_greedy_invalid_and_depth_zero():
+    B, D, V = 5, 2, 16
+    t, _ = synth.logits_pair(33, B, D, V)
+    tok = np.argmax(t[:, :D], axis=2).astype(np.int32)
+    t[1, 2, 5] = np.nan            # NaN in the bonus row
+    t[2, 0, 3] = np.inf            # +inf
+    t[3, 1, :] = -np.inf           # no finite logit
+    tok[4, 1] = -1                 # draft token out of range
+    out = oracle.verify_greedy(t, tok)
+    assert out["accepted_len"].tolist() == [D, -1, -1, -1, -1]
+    assert out["next_token"].tolist()[1:] == [-1, -1, -1, -1]
+    z, _ = synth.logits_pair(34, 20, 0, V)
+    out = oracle.verify_greedy(z, None)
+    assert np.all(out["accepted_len"] == 0)
+    assert np.array_equal(out["next_token"], np.argmax(z[:, 0], axis=1))
+    zi = np.full((1, 1, 4), -np.inf, np.float32)
+    zi[0, 0, 2] = -1e30
+    assert int(oracle.verify_greedy(zi, None)["next_token"][0]) == 2   # -inf is never the max
