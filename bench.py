@@ -20,6 +20,11 @@ under `variants`.  (Replaying the step from a HIP graph measured slower than
 these eager launches on this system -- 359 vs 322 us for the qmv part -- so
 graphs are not used here; the library's calls are capture-safe all the same.)
 
+Greedy verification (`bind_verify_greedy`: match the greedy draft's tokens
+against the target's argmax, reading only the target logits) of the same
+block is timed on its own after the steps and reported under
+`accept_greedy`; it is not part of the step.
+
 Printed: one JSON line.  `value` is the verify qmv throughput in HBM GB/s
 (algorithmic bytes / time of the qmv part of the steps); the acceptance
 throughput (verify positions per second) and per-M figures ride along.
@@ -310,6 +315,23 @@ def main():
                     for i in range(len(calls))] if per_launch else None)
         return span_ms, each_ms
 
+    # Greedy verification of the same block (target logits only), drafts
+    # from the greedy draft (argmax of each draft row).
+    g_toks = torch.argmax(acc["d"], dim=2).to(torch.int32).contiguous()
+    g_out = (torch.empty(ACC_B, dtype=torch.int32, device=dev),
+             torch.empty(ACC_B, dtype=torch.int32, device=dev))
+    greedy_call = spec.bind_verify_greedy(acc["t"], g_toks, out=g_out)
+    for _ in range(args.warmup):
+        greedy_call()
+    g_ev = [pair() for _ in range(args.steps)]
+    for e in g_ev:
+        e[0].record(stream)
+        greedy_call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    g_ms = sum(e[0].elapsed_time(e[1]) for e in g_ev) / args.steps
+    g_bytes = roofline.greedy_bytes(ACC_B, ACC_D, ACC_V)
+
     eager_unfused_ms, _ = eager(unfused, False)
     _, q_ms = eager(launches, True)
     per_m = {}
@@ -339,6 +361,12 @@ def main():
               "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4),
               "algorithmic_bytes": acc_bytes,
               "mean_accepted": float(acc["acc"].float().mean().item())}
+
+    greedy = {"positions_per_s": round(positions / (g_ms * 1e-3), 1), "us": round(g_ms * 1e3, 2),
+              "GB/s": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+              "frac": round(g_bytes / (g_ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4),
+              "algorithmic_bytes": g_bytes,
+              "mean_accepted": float(g_out[0].float().mean().item())}
 
     # Roofline of qmv_kernel: algorithmic bytes per launch over the average
     # launch duration, i.e. the qmv part of a step (16 launches back to back,
@@ -374,7 +402,9 @@ def main():
                    "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
         "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
         "qmv_us_per_step": round(qspan_ms * 1e3, 2), "variants": variants,
-        "per_M (per-launch events)": per_m, "accept": accept, "roofline": roof, "roofline_parts": other,
+        "per_M (per-launch events)": per_m, "accept": accept,
+        "accept_greedy (same block, target logits only; not part of the step)": greedy,
+        "roofline": roof, "roofline_parts": other,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -187,6 +187,38 @@ spec_status spec_verify_accept(const float *target_logits,
                                float *p_draft, float *q_draft, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ */
+/* Greedy verification: match the drafts against the target's argmax   */
+/* ------------------------------------------------------------------ */
+/*
+ * The sample-and-match loop with a greedy sampler (savepearlharbor.com
+ * llama.cpp MTP article, how speculative decoding works; greedy means
+ * T <= 0 or top_k == 1, mlxcel manual, DFlash-family drafter table).  For
+ * each of B sequences, with t_i the first index of the largest logit of
+ * target row i (i = 0..D):
+ *   keep d_i while d_i == t_i; at the first mismatch accepted_len = i and
+ *   next_token = t_i; if all D match, accepted_len = D, next_token = t_D.
+ * Only the target logits are read.  For valid draft rows this is exactly
+ * what spec_verify_accept returns with top_k = 1.
+ *
+ *  target_logits  fp32 [B][D+1][V]; 16-byte aligned when V % 4 == 0
+ *  draft_tokens   int32 [B][D] (may be NULL when D == 0)
+ *  B >= 0, 0 <= D <= 15, 2 <= V < 2^24, B * (D + 1) <= 2^23
+ *  accepted_len   int32 [B] out: 0..D
+ *  next_token     int32 [B] out
+ * A sequence with an invalid target row (a NaN, a +inf, or no finite
+ * logit) or a draft token outside [0, V) gets accepted_len = next_token =
+ * -1; other sequences are unaffected.  The workspace holds one 16-byte
+ * record per (row, vocabulary chunk).
+ */
+size_t spec_verify_greedy_workspace(int B, int D, int V);
+
+spec_status spec_verify_greedy(const float *target_logits,
+                               const int32_t *draft_tokens, int B, int D, int V,
+                               int32_t *accepted_len, int32_t *next_token,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,9 +13,10 @@ Names follow the C ABI:
     spec_verify_accept               ratio acceptance + residual / bonus draw
     spec_sample_probs                filtered sampling distribution
     spec_sample_tokens               inverse-CDF draw from that distribution
+    spec_verify_greedy               greedy verification (match the target argmax)
     spec_*_workspace_size            workspace queries
-    bind_qmv / bind_verify_accept    the same calls with arguments marshalled
-                                     once, for launch loops
+    bind_qmv / bind_verify_accept /  the same calls with arguments marshalled
+    bind_verify_greedy               once, for launch loops
 """
 from __future__ import annotations
 
@@ -81,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.spec_sample_probs.argtypes = [vp, i, i, f, i, f, vp, vp, sz, vp]
         L.spec_sample_probs.restype = i
         L.spec_sample_tokens.argtypes = [vp, i, i, f, i, f, vp, vp, vp, sz, vp]
+        L.spec_verify_greedy_workspace.argtypes = [i, i, i]
+        L.spec_verify_greedy_workspace.restype = sz
+        L.spec_verify_greedy.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
+        L.spec_verify_greedy.restype = i
         L.spec_sample_tokens.restype = i
         _lib = L
         return _lib
@@ -359,3 +364,54 @@ def spec_sample_tokens(logits, uniforms, temperature: float, top_k: int = 0,
                                   _ptr(workspace), nbytes, _stream(dev))
     _check("spec_sample_tokens", st)
     return tokens
+
+
+def spec_verify_greedy_workspace(B: int, D: int, V: int) -> int:
+    return int(lib().spec_verify_greedy_workspace(B, D, V))
+
+
+def spec_verify_greedy(target_logits, draft_tokens, out=None, workspace=None):
+    """Greedy verification of B sequences: target_logits fp32 [B][D+1][V],
+    draft_tokens int32 [B][D].  Returns (accepted_len, next_token) int32 [B]."""
+    import torch
+    dev = target_logits.device
+    _require(target_logits, torch.float32, "target_logits", dev)
+    B, D1, V = target_logits.shape
+    D = D1 - 1
+    if D > 0:
+        _require(draft_tokens, torch.int32, "draft_tokens", dev)
+        if tuple(draft_tokens.shape) != (B, D):
+            raise ValueError("draft_tokens must be [B][D]")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    acc, nxt = out
+    need = spec_verify_greedy_workspace(B, D, V)
+    if workspace is None:
+        workspace = get_workspace(need, dev, "greedy")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_verify_greedy(_ptr(target_logits), _ptr(draft_tokens if D > 0 else None),
+                                  B, D, V, _ptr(acc), _ptr(nxt), _ptr(workspace), nbytes,
+                                  _stream(dev))
+    _check("spec_verify_greedy", st)
+    return acc, nxt
+
+
+def bind_verify_greedy(target_logits, draft_tokens, out=None) -> _Bound:
+    """spec_verify_greedy on fixed tensors, marshalled once (first call
+    checked through spec_verify_greedy).  `out` = (accepted_len, next_token)."""
+    import torch
+    dev = target_logits.device
+    B, D1, V = target_logits.shape
+    D = D1 - 1
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    need = spec_verify_greedy_workspace(B, D, V)
+    ws = torch.empty(max(need, 4096), dtype=torch.uint8, device=dev)
+    spec_verify_greedy(target_logits, draft_tokens, out=out, workspace=ws)
+    acc, nxt = out
+    args = (_ptr(target_logits), _ptr(draft_tokens if D > 0 else None), B, D, V,
+            _ptr(acc), _ptr(nxt), _ptr(ws), ws.numel(), _stream(dev))
+    keep = (target_logits, draft_tokens, out, ws)
+    return _Bound("spec_verify_greedy", lib().spec_verify_greedy, args, keep)

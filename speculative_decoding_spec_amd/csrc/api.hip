@@ -250,4 +250,38 @@ spec_status spec_sample_tokens(const float *logits, int R, int V,
     return SPEC_OK;
 }
 
+size_t spec_verify_greedy_workspace(int B, int D, int V) {
+    if (B <= 0 || D < 0 || D > kMaxD || V < 2 || V > kMaxV)
+        return 0;
+    return spec::greedy_plan(B, D, V).ws_bytes;
+}
+
+spec_status spec_verify_greedy(const float *target_logits,
+                               const int32_t *draft_tokens, int B, int D, int V,
+                               int32_t *accepted_len, int32_t *next_token,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (B < 0 || D < 0 || V < 2)
+        return SPEC_ERR_INVALID;
+    if (D > kMaxD || V > kMaxV)
+        return SPEC_ERR_UNSUPPORTED;
+    if (B == 0)
+        return SPEC_OK;
+    if (!target_logits || !accepted_len || !next_token || (D > 0 && !draft_tokens))
+        return SPEC_ERR_INVALID;
+    if (!aligned4(target_logits))
+        return SPEC_ERR_INVALID;
+    if (((V & 3) == 0) && !aligned16(target_logits))
+        return SPEC_ERR_UNSUPPORTED;
+    if ((size_t)B * (D + 1) > kMaxRows)
+        return SPEC_ERR_UNSUPPORTED;
+    const spec::GreedyPlan plan = spec::greedy_plan(B, D, V);
+    if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes))
+        return SPEC_ERR_WORKSPACE;
+    if (spec::launch_greedy(target_logits, draft_tokens, plan, accepted_len,
+                            next_token, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
 } // extern "C"

@@ -69,4 +69,21 @@ hipError_t launch_probs(const float *logits, const AcceptPlan &plan,
                         const SamplingParams &sp, float *probs, void *ws,
                         hipStream_t stream);
 
+// -------------------------------------------------------------- greedy ----
+struct GreedyPlan {
+    int B, D, V;
+    int rows;        // B * (D + 1) target rows
+    int chunks;      // vocabulary chunks per row
+    int chunk_len;   // elements per chunk
+    size_t ws_bytes;
+};
+
+GreedyPlan greedy_plan(int B, int D, int V);
+
+// Enqueue greedy verification: the argmax pass over the target rows, then
+// the per-sequence match.  draft_tokens may be null when D == 0.
+hipError_t launch_greedy(const float *target, const int32_t *draft_tokens,
+                         const GreedyPlan &plan, int32_t *accepted_len,
+                         int32_t *next_token, void *ws, hipStream_t stream);
+
 } // namespace spec

@@ -35,6 +35,13 @@ def accept_bytes(B: int, D: int, V: int) -> int:
     return B * (2 * D + 1) * V * 4 + B * D * 4 + B * (D + 1) * 4 + B * 8
 
 
+def greedy_bytes(B: int, D: int, V: int) -> int:
+    """Bytes greedy verification must move: every fp32 target logit once
+    (D + 1 rows per sequence), the draft tokens, two int32 outputs per
+    sequence.  The draft logits are not needed."""
+    return B * (D + 1) * V * 4 + B * D * 4 + B * 8
+
+
 def fraction_of_peak(nbytes: float, seconds: float,
                      peak: float = HBM_PEAK_BYTES_PER_S) -> float:
     return nbytes / seconds / peak

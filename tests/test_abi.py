@@ -143,3 +143,33 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(spec, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         spec.lib()
+
+
+def greedy(L, t=P, tok=P, B=4, D=3, V=1000, acc=P, nxt=P, ws=None, nbytes=None):
+    if nbytes is None:
+        nbytes = L.spec_verify_greedy_workspace(B, D, V)
+        ws = ws or P2
+    return L.spec_verify_greedy(t, tok, B, D, V, acc, nxt, ws, nbytes, None)
+
+
+def test_greedy_validation(L):
+    assert greedy(L, B=-1) == INVALID
+    assert greedy(L, D=-1) == INVALID
+    assert greedy(L, V=1) == INVALID
+    assert greedy(L, D=16) == UNSUPPORTED
+    assert greedy(L, V=1 << 24) == UNSUPPORTED
+    assert greedy(L, t=None) == INVALID
+    assert greedy(L, tok=None) == INVALID
+    assert greedy(L, acc=None) == INVALID
+    assert greedy(L, nxt=None) == INVALID
+    assert greedy(L, t=MIS) == UNSUPPORTED          # V % 4 == 0 needs 16 B rows
+    assert greedy(L, t=ctypes.c_void_p(0x10002), V=999) == INVALID   # not 4-byte aligned
+    assert greedy(L, ws=None, nbytes=0) == WORKSPACE
+    need = L.spec_verify_greedy_workspace(256, 5, 151936)
+    assert need == 256 * 6 * 16                     # one record per row: one chunk each
+    assert greedy(L, B=256, D=5, V=151936, nbytes=need - 1, ws=P2) == WORKSPACE
+    assert greedy(L, B=0) == OK
+    assert greedy(L, tok=None, D=0, B=0) == OK
+    # a single row splits into chunks of whole 1024-logit multiples
+    assert L.spec_verify_greedy_workspace(1, 0, 151936) == 75 * 16
+    assert L.spec_verify_greedy_workspace(0, 0, 1000) == 0
