@@ -40,6 +40,9 @@ step's launches have changed since those counters were taken.
 
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
+`--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
+weight copies) plus an N sweep that splits a launch's time into a fixed
+cost and an incremental bandwidth, prints one JSON line each, and exits.
 """
 from __future__ import annotations
 
@@ -73,7 +76,87 @@ def parse():
                     help="target CPU time of each oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
+    ap.add_argument("--shapes", action="store_true",
+                    help="only time qmv per layer shape and M (one JSON line each) and exit")
     return ap.parse_args()
+
+
+# Layer shapes of the verify pass (N, K): a 5120-hidden decoder with 48 query
+# and 8 key/value heads of 128, a 17408-wide MLP and a 151936-token head.
+SHAPES = {
+    "gate_up (fused 5120->34816)": (4, 2 * FFN, HIDDEN),
+    "gate or up 5120->17408": (4, FFN, HIDDEN),
+    "down 17408->5120": (4, HIDDEN, FFN),
+    "q 5120->6144": (4, 6144, HIDDEN),
+    "k or v 5120->1024": (4, 1024, HIDDEN),
+    "qkv (fused 5120->8192)": (4, 8192, HIDDEN),
+    "o 6144->5120": (4, HIDDEN, 6144),
+    "lm_head 5120->151936": (4, 151936, HIDDEN),
+    "gate or up W8": (8, FFN, HIDDEN),
+    "down W8": (8, HIDDEN, FFN),
+    "lm_head W8": (8, 151936, HIDDEN),
+}
+# N sweep at K = 5120, M = 1: time per launch against bytes per launch.
+SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
+
+
+def shapes(dev, steps):
+    """Microseconds per launch of qmv at each layer shape and M = 1, 4, 8:
+    back-to-back launches over enough weight copies (at least 1.1 GB) that
+    nothing is served from the 256 MB last-level cache; then a least-squares
+    line through the N sweep, whose slope is the incremental bandwidth and
+    whose intercept the fixed cost of one launch."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+
+    def timed(bits, N, K, Ms):
+        nb1 = roofline.qmv_bytes(bits, 1, N, K)
+        nc = min(400, max(2, -(-int(1.1e9) // nb1)))
+        pk = spec.spec_pack_w4 if bits == 4 else spec.spec_pack_w8
+        copies = [pk(*synth.torch_qweights(bits, N, K, GROUP, 5000 + c, dev), G=GROUP)
+                  for c in range(nc)]
+        res = {}
+        for M in Ms:
+            x = synth.torch_activations(M, K, 5100 + M, dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            calls = [spec.bind_qmv(w, x, y) for w in copies]
+            reps = max(steps * 3, 2 * nc)
+            for i in range(min(nc, 8)):
+                calls[i]()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                calls[i % nc]()
+            e1.record()
+            torch.cuda.synchronize()
+            res[M] = (e0.elapsed_time(e1) * 1e3 / reps, roofline.qmv_bytes(bits, M, N, K), nc)
+        del copies
+        torch.cuda.empty_cache()
+        return res
+
+    for name, (bits, N, K) in SHAPES.items():
+        for M, (us, nb, nc) in timed(bits, N, K, (1, 4, 8)).items():
+            print(json.dumps({"shape": name, "bits": bits, "N": N, "K": K, "M": M,
+                              "us_per_launch": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
+                              "frac": round(nb / us / 1e3 / 8000.0, 4), "weight_copies": nc}),
+                  flush=True)
+    xs, ys = [], []
+    for N in SWEEP_N:
+        us, nb, _ = timed(4, N, HIDDEN, (1,))[1]
+        xs.append(nb)
+        ys.append(us)
+        print(json.dumps({"sweep": "W4 K=5120 M=1", "N": N, "bytes": nb,
+                          "us_per_launch": round(us, 2)}), flush=True)
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+    icpt = my - slope * mx
+    print(json.dumps({"fit": "us = intercept + bytes / rate over the N sweep",
+                      "intercept_us": round(icpt, 2),
+                      "incremental_GB/s": round(1e-3 / slope, 1),
+                      "incremental_frac": round(1e-3 / slope / 8000.0, 4)}), flush=True)
 
 
 def copy_probe(dev):
@@ -228,6 +311,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_probe:
         copy_probe(dev)
+        return
+    if args.shapes:
+        shapes(dev, args.steps)
         return
     blocks = build_inputs(dev)
     acc = build_accept(dev)

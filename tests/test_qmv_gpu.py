@@ -160,6 +160,32 @@ def test_fused_gate_up_matches_separate_launches(dev):
     assert torch.equal(y[:, N:].view(torch.int32), spec.spec_qmv_w4(u, x).view(torch.int32))
 
 
+@pytest.mark.parametrize("M", [3, 6])
+def test_fused_qkv_matches_separate_launches(dev, M):
+    """q (5120 -> 6144), k and v (5120 -> 1024 each) share their input: packed
+    as one 5120 -> 8192 matrix they give bitwise the three separate outputs,
+    which match the oracle on sampled outputs."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    K = 5120
+    parts = [synth.qweights(9, 4, n, K, 64, salt=s) for n, s in ((6144, 1), (1024, 2), (1024, 3))]
+    xa = synth.activations(9, M, K)
+    x = parity.dev_x(xa, dev)
+    cat = [np.concatenate(list(t), axis=0) for t in zip(*parts)]
+    y = spec.spec_qmv_w4(spec.spec_pack_w4(*parity.dev_qweights(*cat, dev)), x)
+    lo = 0
+    for p in parts:
+        n = p[0].shape[0]
+        ys = spec.spec_qmv_w4(spec.spec_pack_w4(*parity.dev_qweights(*p, dev)), x)
+        assert torch.equal(y[:, lo:lo + n].view(torch.int32), ys.view(torch.int32))
+        lo += n
+    rng = np.random.default_rng(M)
+    m_idx, n_idx = rng.integers(0, M, 256), rng.integers(0, 8192, 256)
+    ref, mag = oracle.qmv_points(4, *cat, xa, 64, m_idx, n_idx)
+    nf, _, _ = parity.check_qmv(y.cpu().numpy()[m_idx, n_idx], ref, mag)
+    assert nf == 0
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_long_k(dev, bits):
     """K = 131072 (1024 pairs per row, 64-128 per wave) on two ragged tiles."""
