@@ -101,7 +101,7 @@ SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
 
 
 def shapes(dev, steps):
-    """Microseconds per launch of qmv at each layer shape and M = 1, 4, 8:
+    """Microseconds per launch of qmv at each layer shape and M = 1, 4, 8, 16:
     back-to-back launches over enough weight copies (at least 1.1 GB) that
     nothing is served from the 256 MB last-level cache; then a least-squares
     line through the N sweep, whose slope is the incremental bandwidth and
@@ -137,7 +137,7 @@ def shapes(dev, steps):
         return res
 
     for name, (bits, N, K) in SHAPES.items():
-        for M, (us, nb, nc) in timed(bits, N, K, (1, 4, 8)).items():
+        for M, (us, nb, nc) in timed(bits, N, K, (1, 4, 8, 16)).items():
             print(json.dumps({"shape": name, "bits": bits, "N": N, "K": K, "M": M,
                               "us_per_launch": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
                               "frac": round(nb / us / 1e3 / 8000.0, 4), "weight_copies": nc}),

@@ -48,7 +48,7 @@ extern "C" {
 typedef enum spec_status {
     SPEC_OK = 0,
     SPEC_ERR_INVALID = 1,     /* NULL pointer where one is required, size out of range */
-    SPEC_ERR_UNSUPPORTED = 2, /* well formed but not implemented (group size, M > 8, alignment) */
+    SPEC_ERR_UNSUPPORTED = 2, /* well formed but not implemented (group size, M > 16, alignment) */
     SPEC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than its size query */
     SPEC_ERR_DEVICE = 4       /* a HIP runtime call failed */
 } spec_status;
@@ -90,10 +90,15 @@ int spec_version(void);
  * spec_qmv_*:
  *  x       bf16 bit patterns [M][K], 16-byte aligned
  *  y       fp32 [M][N], written (never read)
- *  M       1..8 rows (0 is a no-op); N, K, G as given to spec_pack_*.
+ *  M       1..16 rows (0 is a no-op); N, K, G as given to spec_pack_*.
+ *          Up to 8 rows fill the verify blocks of MTP depths D <= 7; 9..16
+ *          rows cover the 16-wide blocks of DFlash drafters (mlxcel manual,
+ *          "MTP and DFlash": the comparison table's typical width, and
+ *          split-mtp's block size of at most 16).
  *
  * Results are deterministic, and row m of an M-row call is bitwise equal to
- * the one-row call on x[m] (the reduction order does not depend on M).
+ * the one-row call on x[m] (the reduction order does not depend on M, also
+ * across the 8-row boundary).
  */
 size_t spec_qmv_packed_weight_bytes(int bits, int N, int K, int G);
 size_t spec_qmv_packed_sb_bytes(int N, int K, int G);

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kMaxM = 8;
+constexpr int kMaxM = 16;
 constexpr int kMaxD = 15;
 constexpr int kMaxCand = 256;
 constexpr int kMaxV = (1 << 24) - 1;

@@ -33,7 +33,9 @@
 //    (each zero on the other group's k slots), so M <= 8 rows use the whole
 //    16-row tile and every MFMA output belongs to one group.  A second MFMA
 //    against a ones operand yields the group sums of x in the same lane
-//    layout.  The per-group affine terms are applied in fp32:
+//    layout.  Blocks of 9..16 rows (the 16-wide drafter blocks of the mlxcel
+//    manual's DFlash section) fill all 16 A rows and run one MFMA per group
+//    instead (the wide form, below).  The per-group affine terms are applied in fp32:
 //        acc += s * C + (b - 128 s) * sum_x            (W4)
 //        acc += s * C + b * sum_x                      (W8)
 //  * The two group halves and the waves meet in LDS in a fixed order, so
@@ -178,19 +180,32 @@ __global__ __launch_bounds__(256) void pack_kernel(
 }
 
 // XH: 16-byte x loads per lane and pair -- 1 when M <= 4 (rows 0..3),
-// 2 when M <= 8.  Rows a launch does not stage are never read (their MFMA
-// operand lanes read zeros), so both variants compute bitwise the same.
+// 2 when M <= 8, 4 when M <= 16.  Rows a launch does not stage are never
+// read (their MFMA operand lanes read zeros), so the M <= 4 and M <= 8
+// variants compute bitwise the same.
+//
+// XH = 4 is the wide form for 9..16 rows: every A row is an x row, so the
+// two groups of a pair can no longer share an MFMA through the row split.
+// Each 32-k step then runs two MFMAs per tile on the same B operand, with A
+// masked to group 0's k slots (lanes j = 0, 1) and to group 1's (j = 2, 3),
+// into separate accumulators that get their own group's scale and bias.
+// The per-group FMA chains and the final sum are those of the pair form, so
+// rows 0..7 of a wide call equal an M <= 8 call bitwise.
 template <int BITS, int WAVES, int T, int U, int S, int XH>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
     const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
     static_assert(U == 1 || U == 2, "a stage is one or two pairs");
+    static_assert(XH == 1 || XH == 2 || XH == 4, "x loads per lane and pair");
+    constexpr bool WIDE = XH == 4;  // 9..16 rows: one MFMA per group
+    constexpr int XR = WIDE ? 16 : 8;   // staged x rows
+    constexpr int NG = WIDE ? 2 : 1;    // groups (accumulators) per lane
     constexpr int L = BITS / 4;     // 1 KB loads per pair, tile and wave
     constexpr int kPitch = 136;     // bf16 per staged x row: 256 B + 16 B against bank conflicts
     // Each wave stages its x rows in its own slot; the cross-wave reduction
     // reuses the same memory after the main loop.
     union Shared {
-        uint16_t xs[WAVES][U][8][kPitch];
+        uint16_t xs[WAVES][U][XR][kPitch];
         f32x4 red[WAVES][T][64];
     };
     __shared__ __attribute__((aligned(16))) Shared sh;
@@ -233,23 +248,35 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const __amdgpu_buffer_rsrc_t xres =
         __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, M * K * 2, kBufferFlags);
     const unsigned woff = (unsigned)lane * 16u;
-    const unsigned sboff = (unsigned)(h * 16 + r) * 8u;
+    // pair form: this lane's group h; wide form: both groups of row r
+    unsigned sboff[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        sboff[g] = (unsigned)((WIDE ? g : h) * 16 + r) * 8u;
     // x is loaded compactly: lane -> row (lane >> 4) + 4 i, 16-byte chunk
     // (lane & 15) of the pair's 128 k; rows >= M read zeros.
     const int xrow0 = lane >> 4, xch = lane & 15;
-    // MFMA A operand: row r carries x row (r & 7) for group half (r >> 3)
-    // and is zero on the other half's k slots (and for rows >= M).
-    const bool a_act = (h == (r >> 3)) && ((r & 7) < M);
+    // MFMA A operand.  Pair form: row r carries x row (r & 7) for group
+    // half (r >> 3) and is zero on the other half's k slots (and for rows
+    // >= M).  Wide form: row r is x row r, masked to group g's k slots for
+    // the group-g MFMA.
+    const int a_row = WIDE ? r : (r & 7);
+    bool a_act[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        a_act[g] = (h == (WIDE ? g : (r >> 3))) && (a_row < M);
     if (threadIdx.x < 8)
         xzero[threadIdx.x] = 0;
     __syncthreads();
 
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     const unsigned w4base = w4_base_vgpr();
-    f32x4 acc[T];
+    f32x4 acc[T][NG];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
-        acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            acc[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // A stage is U pairs: the T tiles' codes and scale/bias words, and the
     // compact x rows, all issued together.  Pairs outside this wave's range
@@ -258,7 +285,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     // exactly.
     struct Stage {
         u32x4 raw[U][T][L];
-        uint32_t sb[U][T];
+        uint32_t sb[U][T][NG];
         u32x4 xc[U][XH];
     };
     auto issue = [&](Stage &st, int p0) {
@@ -278,15 +305,18 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         }
         // one load gives this lane's scale/bias words of both pairs of a block
         const int pc0 = in0 ? p0 : 0;
-        const unsigned sv = in0 ? sboff : kOutOfRange;
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
-            if (U == 2) {
-                const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sbres[tt], sv, (pc0 >> 1) * 256, 0);
-                st.sb[0][tt] = v2[0];
-                st.sb[U - 1][tt] = v2[1];
-            } else {
-                st.sb[0][tt] = __builtin_amdgcn_raw_buffer_load_b32(sbres[tt], sv, (pc0 >> 1) * 256 + (pc0 & 1) * 4, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const unsigned sv = in0 ? sboff[g] : kOutOfRange;
+                if (U == 2) {
+                    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sbres[tt], sv, (pc0 >> 1) * 256, 0);
+                    st.sb[0][tt][g] = v2[0];
+                    st.sb[U - 1][tt][g] = v2[1];
+                } else {
+                    st.sb[0][tt][g] = __builtin_amdgcn_raw_buffer_load_b32(sbres[tt], sv, (pc0 >> 1) * 256 + (pc0 & 1) * 4, 0);
+                }
             }
         }
 #pragma unroll
@@ -318,16 +348,24 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         for (int u = 0; u < U; ++u) {
             if (p0 + u >= p_hi)
                 break;
-            f32x4 c[T];
-            f32x4 cx = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 c[T][NG];
+            f32x4 cx[NG];
 #pragma unroll
-            for (int tt = 0; tt < T; ++tt)
-                c[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int g = 0; g < NG; ++g) {
+                cx[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int tt = 0; tt < T; ++tt)
+                    c[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const uint16_t *src = a_act ? &sh.xs[wave][u][r & 7][64 * h + 32 * sub + 8 * s4] : xzero;
-                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(src);
-                cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, cx, 0, 0, 0);
+                bf16x8 av[NG];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const uint16_t *src = a_act[g] ? &sh.xs[wave][u][a_row][64 * h + 32 * sub + 8 * s4] : xzero;
+                    av[g] = *reinterpret_cast<const bf16x8 *>(src);
+                    cx[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], ones, cx[g], 0, 0, 0);
+                }
 #pragma unroll
                 for (int tt = 0; tt < T; ++tt) {
                     bf16x8 bv;
@@ -337,20 +375,26 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
                         const u32x4 &lo = st.raw[u][tt][s4 >> 1];
                         bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
                     }
-                    c[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c[tt], 0, 0, 0);
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], bv, c[tt][g], 0, 0, 0);
                 }
             }
-            // C row 4*j + i is x row m = 4*sub + i of half h; cx holds the
-            // same rows' sums of x over the group.
+            // Pair form: C row 4*j + i is x row m = 4*sub + i of half h.
+            // Wide form: C row 4*j + i is x row 4*j + i, one accumulator per
+            // group.  cx holds the same rows' sums of x over the group.
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
-                const float s = half_bits_to_float((uint16_t)(st.sb[u][tt] & 0xFFFFu));
-                const float bias = half_bits_to_float((uint16_t)(st.sb[u][tt] >> 16));
-                const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[tt][i] = fmaf(s, c[tt][i], acc[tt][i]);
-                    acc[tt][i] = fmaf(bb, cx[i], acc[tt][i]);
+                for (int g = 0; g < NG; ++g) {
+                    const float s = half_bits_to_float((uint16_t)(st.sb[u][tt][g] & 0xFFFFu));
+                    const float bias = half_bits_to_float((uint16_t)(st.sb[u][tt][g] >> 16));
+                    const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[tt][g][i] = fmaf(s, c[tt][g][i], acc[tt][g][i]);
+                        acc[tt][g][i] = fmaf(bb, cx[g][i], acc[tt][g][i]);
+                    }
                 }
             }
         }
@@ -372,25 +416,26 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         }
     }
 
-    // Fixed-order reduction: the two groups of a pair (lanes l, l ^ 32), then
-    // the waves in index order.  Neither depends on M.
+    // Fixed-order reduction: the two groups of a pair (pair form: lanes l,
+    // l ^ 32; wide form: the two accumulators of a lane), then the waves in
+    // index order.  Neither depends on M.
     __syncthreads();   // every wave is done with its x slot
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
-        sh.red[wave][tt][lane] = acc[tt];
+        sh.red[wave][tt][lane] = WIDE ? acc[tt][0] + acc[tt][NG - 1] : acc[tt][0];
     __syncthreads();
-    if (wave == 0 && lane < 32) {
+    if (WIDE ? wave == 0 : (wave == 0 && lane < 32)) {
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
             const int n = (blockIdx.x * T + tt) * 16 + r;
             if (n >= N)
                 continue;
-            f32x4 tot = sh.red[0][tt][lane] + sh.red[0][tt][lane + 32];
+            f32x4 tot = WIDE ? sh.red[0][tt][lane] : sh.red[0][tt][lane] + sh.red[0][tt][lane + 32];
             for (int ww = 1; ww < WAVES; ++ww)
-                tot += sh.red[ww][tt][lane] + sh.red[ww][tt][lane + 32];
+                tot += WIDE ? sh.red[ww][tt][lane] : sh.red[ww][tt][lane] + sh.red[ww][tt][lane + 32];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = 4 * sub + i;
+                const int m = (WIDE ? 4 * j : 4 * sub) + i;
                 if (m < M)
                     y[(size_t)m * N + n] = tot[i];
             }
@@ -479,8 +524,10 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
     if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.pairs_per_stage == UU) { \
         if (M <= 4)                                                                         \
             qmv_kernel<B, W, TT, UU, 2, 1><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
-        else                                                                                \
+        else if (M <= 8)                                                                    \
             qmv_kernel<B, W, TT, UU, 2, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+        else                                                                                \
+            qmv_kernel<B, W, TT, UU, 2, 4><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
         return hipGetLastError();                                                           \
     }
 #define SPEC_QMV_SHAPES(B) \

@@ -60,7 +60,8 @@ def test_qmv_validation(L, fn):
     assert qmv(L, fn, M=-1) == INVALID
     assert qmv(L, fn, K=100) == INVALID            # K % G != 0
     assert qmv(L, fn, G=32, K=128) == UNSUPPORTED
-    assert qmv(L, fn, M=9) == UNSUPPORTED
+    assert qmv(L, fn, M=17) == UNSUPPORTED
+    assert qmv(L, fn, M=0) == OK
     assert qmv(L, fn, w=None) == INVALID
     assert qmv(L, fn, sb=None) == INVALID
     assert qmv(L, fn, x=None) == INVALID

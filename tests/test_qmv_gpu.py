@@ -1,7 +1,8 @@
 """GPU parity of the verify qmv against the fp64 oracle, through the C ABI.
 
 Shapes: the 4096 x 1024 M=4 case; the verify-MLP projections (gate/up
-5120 -> 17408, down 17408 -> 5120) at M = 1..8; the attention projections
+5120 -> 17408, down 17408 -> 5120) at M = 1..8 and, in the wide form for
+16-wide drafter blocks, M = 9, 12, 16; the attention projections
 of the 64-layer 5120-hidden decoder (q 5120 -> 6144, k/v 5120 -> 1024, o
 6144 -> 5120) at M = 3..6; the 151936-row LM head (W4 at M = 6, W8 at M = 8)
 on sampled outputs; ragged and degenerate shapes.  Plus row independence
@@ -48,7 +49,7 @@ def test_pr1_reference_shape(dev):
     full_check(4, 4, 4096, 1024, dev, cfg=0)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("shape", [(17408, 5120), (5120, 17408)], ids=["gate_up", "down"])
 def test_verify_mlp_shapes(dev, M, shape):
     N, K = shape
@@ -80,7 +81,8 @@ def test_lm_head_sampled(dev, bits, M):
 
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (3, 100, 192), (8, 77, 320), (5, 1000, 64 * 13),
-                                   (2, 4095, 1024), (7, 129, 17408)])
+                                   (2, 4095, 1024), (7, 129, 17408), (9, 77, 320),
+                                   (13, 1000, 64 * 13), (16, 4095, 1024), (11, 129, 17408)])
 def test_ragged_shapes(dev, bits, M, N, K):
     full_check(bits, M, N, K, dev, cfg=5, salt=M * 100000 + N + K)
 
@@ -111,17 +113,19 @@ def test_degenerate_shapes(dev):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("N,K", [(5120, 17408), (4096, 1024)])
 def test_row_independence_and_determinism(dev, bits, N, K):
+    """Row m of any call equals the one-row call bitwise, across the 8-row
+    boundary between the pair form and the wide form as well."""
     w, s, b = synth.qweights(6, bits, N, K, 64)
-    x = synth.activations(6, 8, K)
+    x = synth.activations(6, 16, K)
     full = run(bits, w, s, b, x, dev)
     again = run(bits, w, s, b, x, dev)
     assert np.array_equal(full.view(np.uint32), again.view(np.uint32))
-    for m in range(8):
+    for m in range(16):
         one = run(bits, w, s, b, np.ascontiguousarray(x[m:m + 1]), dev)
         assert np.array_equal(one[0].view(np.uint32), full[m].view(np.uint32)), m
-    for M in (3, 5):
+    for M in (3, 5, 8, 9, 12):
         part = run(bits, w, s, b, np.ascontiguousarray(x[:M]), dev)
-        assert np.array_equal(part.view(np.uint32), full[:M].view(np.uint32))
+        assert np.array_equal(part.view(np.uint32), full[:M].view(np.uint32)), M
 
 
 def test_bound_call_matches_plain_call(dev):
