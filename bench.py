@@ -122,8 +122,8 @@ def shapes(dev, steps):
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             calls = [spec.bind_qmv(w, x, y) for w in copies]
             reps = max(steps * 3, 2 * nc)
-            for i in range(min(nc, 8)):
-                calls[i]()
+            for c in calls:      # touch every copy once before timing
+                c()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
