@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_accept.argtypes = [vp, vp, vp, vp, lg, lg, lg, f, i, f, vp, vp, vp,
                                     vp, vp]
         L.oracle_accept.restype = i
+        L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_double_to_bf16.restype = ctypes.c_uint16
+        L.oracle_gate_up_silu.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, lg, lg, lg, lg,
+                                          lg, lg, vp, vp]
+        L.oracle_gate_up_silu.restype = i
         L.oracle_verify_greedy.argtypes = [vp, vp, lg, lg, lg, vp, vp]
         L.oracle_verify_greedy.restype = i
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
@@ -101,6 +106,32 @@ def qmv(bits: int, w: np.ndarray, scales: np.ndarray, biases: np.ndarray,
     if rc != 0:
         raise ValueError(f"oracle_qmv rejected its arguments (rc={rc})")
     return (y, a) if with_abs else y
+
+
+def double_to_bf16(v: float) -> int:
+    """Nearest-even bfloat16 bit pattern of a double."""
+    return int(lib().oracle_double_to_bf16(float(v)))
+
+
+def gate_up_silu(bits: int, gate: tuple, up: tuple, x: np.ndarray, group: int = 64,
+                 rows: tuple[int, int] | None = None):
+    """(h fp64 [M][n1-n0], h as bf16 bit patterns uint16 [M][n1-n0]) with
+    h = silu(x G^T) * (x U^T); ``gate`` and ``up`` are (w, scales, biases)
+    in the layout of :func:`qmv`."""
+    gw, gs, gb = [np.ascontiguousarray(a) for a in gate]
+    uw, us, ub = [np.ascontiguousarray(a) for a in up]
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    F = gw.shape[0]
+    n0, n1 = rows if rows is not None else (0, F)
+    h = np.empty((M, n1 - n0), np.float64)
+    hb = np.empty((M, n1 - n0), np.uint16)
+    rc = lib().oracle_gate_up_silu(bits, _ptr(gw), _ptr(gs), _ptr(gb), _ptr(uw), _ptr(us),
+                                   _ptr(ub), _ptr(x), M, F, K, group, n0, n1, _ptr(h),
+                                   _ptr(hb))
+    if rc != 0:
+        raise ValueError(f"oracle_gate_up_silu rejected its arguments (rc={rc})")
+    return h, hb
 
 
 def qmv_points(bits: int, w: np.ndarray, scales: np.ndarray, biases: np.ndarray,

@@ -16,6 +16,12 @@
  *             Plain definition: dequantize every weight, then an fp64 dot
  *             product summed sequentially in k order.
  *
+ *   gate_up_silu
+ *             h = silu(x W_gate^T) * (x W_up^T), rounded to bf16: the MLP
+ *             block's activation between its projections (MTPLX re-post,
+ *             "3) MLX verify bottleneck": MLP operations dominate verify;
+ *             the SiLU-gated form of the Qwen target is a reading).
+ *
  *   probs     The sampling distribution at temperature T with top-k and
  *             top-p: MTPLX announcement, "QWEN 3.6 27B @ 63 TPS" (T 0.6,
  *             top_p 0.95, top_k 20; exact temperature sampling, not greedy).
@@ -177,6 +183,66 @@ int oracle_qmv_points(int bits, const void *w, const uint16_t *scales,
         if (abs_sum)
             abs_sum[i] = mag;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* SiLU-gated MLP activation                                            */
+/* ------------------------------------------------------------------ */
+
+/* Round-to-nearest-even of a double to bfloat16 (8 significant bits, the
+ * exponent range of binary32, subnormals included), as its bit pattern.
+ * Direct from the double, so there is no double rounding. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0x0000;
+    int e;
+    frexp(fabs(v), &e);                 /* |v| = f * 2^e, f in [0.5, 1) */
+    int ulp_exp = e - 8;                /* 8 significant bits */
+    if (ulp_exp < -133)                 /* below the normal range: fixed ulp */
+        ulp_exp = -133;
+    double q = ldexp(v, -ulp_exp);      /* exact: a power-of-two scaling */
+    double r = nearbyint(q);            /* ties to even (default rounding) */
+    double rv = ldexp(r, ulp_exp);
+    if (fabs(rv) >= ldexp(1.0, 128))
+        return v > 0 ? 0x7F80 : 0xFF80;
+    float f = (float)rv;                /* exact: rv has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* The gated activation of the MLP block: h[m][n] = silu(g) * u with
+ * g = (x W_gate^T)[m][n], u = (x W_up^T)[m][n] (each the plain qmv of this
+ * file, in fp64) and silu(g) = g / (1 + exp(-g)).  The pages put the MLP at
+ * about half of verify time (MTPLX re-post, "3) MLX verify bottleneck")
+ * without spelling out its form; the target is a Qwen model, whose MLP is
+ * this SiLU-gated product followed by the down projection (a reading).  h
+ * feeds the down projection as bf16, like every qmv input, so h_bf16 is h
+ * rounded to nearest-even bf16.  Rows n0..n1-1, laid out [M][n1 - n0];
+ * either output may be NULL. */
+int oracle_gate_up_silu(int bits, const void *gw, const uint16_t *gs,
+                        const uint16_t *gb, const void *uw, const uint16_t *us,
+                        const uint16_t *ub, const uint16_t *x, long M, long F,
+                        long K, long G, long n0, long n1, double *h,
+                        uint16_t *h_bf16)
+{
+    if (!qmv_args_ok(bits, M, F, K, G) || n0 < 0 || n1 > F || n0 > n1)
+        return -1;
+    long w_out = n1 - n0;
+    for (long m = 0; m < M; ++m)
+        for (long n = n0; n < n1; ++n) {
+            double g = qmv_one(bits, gw, gs, gb, x, K, G, m, n, NULL);
+            double u = qmv_one(bits, uw, us, ub, x, K, G, m, n, NULL);
+            double v = g / (1.0 + exp(-g)) * u;
+            if (h)
+                h[m * w_out + (n - n0)] = v;
+            if (h_bf16)
+                h_bf16[m * w_out + (n - n0)] = oracle_double_to_bf16(v);
+        }
     return 0;
 }
 

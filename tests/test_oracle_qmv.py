@@ -159,3 +159,76 @@ def test_rejects_bad_arguments():
         oracle.qmv(4, w, s, b, x, 48)     # K % G != 0
     with pytest.raises(ValueError):
         oracle.qmv(5, w, s, b, x, 64)     # unsupported width
+
+
+# ------------------------------------------- SiLU-gated MLP activation ----
+
+def test_double_to_bf16_known_patterns_and_ties():
+    r = oracle.double_to_bf16
+    assert r(1.0) == 0x3F80 and r(-2.0) == 0xC000 and r(0.0) == 0x0000
+    assert r(-0.0) == 0x8000
+    assert r(1 + 2**-8) == 0x3F80            # halfway: to the even neighbour 1.0
+    assert r(1 + 3 * 2**-8) == 0x3F82        # halfway: to the even neighbour above
+    assert r(1 + 2**-8 + 2**-40) == 0x3F81   # just above halfway (a double-only case)
+    assert r(-123.5) == 0xC2F7
+    assert r(2.0**-133) == 0x0001            # smallest subnormal
+    assert r(2.0**-134) == 0x0000            # halfway to zero: even
+    assert r(3 * 2.0**-134) == 0x0002        # halfway between 1 and 2 subnormal ulps
+    assert r(2.0**128) == 0x7F80             # overflow
+    assert r(float.fromhex("0x1.fffp127")) == 0x7F80   # rounds up past the largest finite
+
+
+def test_double_to_bf16_matches_torch_on_float32_values():
+    # Every float32 is a double, and torch's float32 -> bfloat16 conversion is
+    # nearest-even: the two must agree on all of them (subnormals included).
+    import torch
+    rng = np.random.default_rng(6)
+    a = np.concatenate([rng.normal(0, 3, 3000), rng.normal(0, 1e-39, 500),
+                        rng.normal(0, 1e30, 500)]).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.double_to_bf16(float(v)) for v in a], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_double_to_bf16_is_the_nearest():
+    rng = np.random.default_rng(7)
+    for v in rng.normal(0, 10, 2000):
+        b = oracle.double_to_bf16(v)
+        d = abs(oracle.bf16_to_double(b) - v)
+        assert d <= abs(oracle.bf16_to_double(b + 1) - v)
+        assert d <= abs(oracle.bf16_to_double(b - 1) - v)
+
+
+def test_gate_up_silu_matches_numpy():
+    import scipy.special
+    M, F, K, G = 3, 40, 256, 64
+    gate = synth.qweights(12, 4, F, K, G, salt=1)
+    up = synth.qweights(12, 4, F, K, G, salt=2)
+    x = synth.activations(12, M, K)
+    h, hb = oracle.gate_up_silu(4, gate, up, x, G)
+    g = _np_x(x) @ _np_dequant(4, *gate, K, G).T
+    u = _np_x(x) @ _np_dequant(4, *up, K, G).T
+    ref = g * scipy.special.expit(g) * u
+    np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(hb, np.vectorize(oracle.double_to_bf16)(h).astype(np.uint16))
+    h2, hb2 = oracle.gate_up_silu(4, gate, up, x, G, rows=(7, 19))
+    assert np.array_equal(h2, h[:, 7:19]) and np.array_equal(hb2, hb[:, 7:19])
+
+
+def test_gate_up_silu_closed_forms():
+    # Zero gate codes and biases: g = 0, silu(0) = 0, h = 0 for any up.
+    M, F, K, G = 2, 16, 128, 64
+    up = synth.qweights(13, 8, F, K, G)
+    x = synth.activations(13, M, K)
+    z = (np.zeros((F, K), np.uint8), up[1], np.zeros_like(up[2]))
+    h, hb = oracle.gate_up_silu(8, z, up, x, G)
+    assert np.all(h == 0.0) and np.all((hb & 0x7FFF) == 0)
+    # Opposite gates: silu(g) - silu(-g) = g, so h(g) - h(-g) = g * u.
+    b = np.full((F, K // G), 0x3C00, np.uint16)          # bias +1.0
+    gp = (np.zeros((F, K), np.uint8), up[1], b)
+    gm = (np.zeros((F, K), np.uint8), up[1], b | 0x8000)  # bias -1.0
+    hp, _ = oracle.gate_up_silu(8, gp, up, x, G)
+    hm, _ = oracle.gate_up_silu(8, gm, up, x, G)
+    g = oracle.qmv(8, *gp, x, G)
+    u = oracle.qmv(8, *up, x, G)
+    np.testing.assert_allclose(hp - hm, g * u, rtol=1e-12, atol=1e-12)
