@@ -3,20 +3,22 @@
 One step = one pass of the whole hot path over resident synthetic inputs:
   * verify qmv: the MLP block of a 5120-hidden decoder (gate and up
     5120 -> 17408, down 17408 -> 5120, W4 group 64) at every verify width
-    M = 1..8.  Gate and up share their input, so they are packed as one
-    5120 -> 34816 matrix and computed by one launch (its outputs are bitwise
-    those of two separate launches); down is a second launch.  Each M uses
-    its own copy of the weights, so one step streams 1.2 GB of distinct
-    weights -- far beyond the 256 MB last-level cache -- and nothing is
-    served from cache across steps either.
+    M = 1..8, chained as the model runs it: gate and up share their input,
+    so they stream as one launch that also applies the SiLU-gated
+    activation and writes h = bf16(silu(g) * u); the down projection reads
+    that h.  Two launches per M, 16 per step.  Each M uses its own copy of
+    the weights, so one step streams 1.2 GB of distinct weights -- far
+    beyond the 256 MB last-level cache -- and nothing is served from cache
+    across steps either.
   * verification: probability-ratio acceptance with residual / bonus draws
     for B = 256 sequences of depth D = 5 over a 151936-token vocabulary
     (fp32 logits, T = 0.6), i.e. 1536 verify positions.
 
-Launches go through pre-marshalled calls (`bind_qmv`, `bind_verify_accept`),
-so the host queues them far faster than the GPU runs them.  The same qmv
-work with gate and up as separate launches is timed as well and reported
-under `variants`.  (Replaying the step from a HIP graph measured slower than
+Launches go through pre-marshalled calls (`bind_qmv_gate_up_silu`,
+`bind_qmv`, `bind_verify_accept`), so the host queues them far faster than
+the GPU runs them.  Under `variants`: the same weights streamed with gate/up
+as one launch writing fp32 outputs (no activation), and gate, up and down as
+24 separate launches.  (Replaying the step from a HIP graph measured slower than
 these eager launches on this system -- 359 vs 322 us for the qmv part -- so
 graphs are not used here; the library's calls are capture-safe all the same.)
 
@@ -38,6 +40,8 @@ launch from the committed counter summary under profiles/ (FETCH_SIZE +
 WRITE_SIZE scaled by a plain-copy calibration), and null when qmv.hip or the
 step's launches have changed since those counters were taken.
 
+`--step-only` times the steps alone (no variants, no greedy verification, no
+CPU baseline): the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
 `--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
@@ -76,6 +80,8 @@ def parse():
                     help="target CPU time of each oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the steps only (no variants, greedy pass or CPU baseline)")
     ap.add_argument("--shapes", action="store_true",
                     help="only time qmv per layer shape and M (one JSON line each) and exit")
     return ap.parse_args()
@@ -189,10 +195,11 @@ def measured_traffic(bytes_per_launch):
         return None, "no counter summary"
 
 
-def build_inputs(dev):
+def build_inputs(dev, variants=True):
     """Packed W4 weights (packing is a load-time step, outside the timing):
-    per M, the fused gate/up matrix, the down matrix, and gate and up packed
-    separately (for the unfused comparison)."""
+    per M, gate/up packed for the gated launch, the down matrix, and (for
+    the variants) gate/up packed as one plain matrix and gate and up packed
+    separately."""
     import torch
     import speculative_decoding_spec_amd as spec
     from speculative_decoding_spec_amd import synth
@@ -202,18 +209,20 @@ def build_inputs(dev):
         g = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1000 + 10 * i, dev)
         u = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1001 + 10 * i, dev)
         d = synth.torch_qweights(4, HIDDEN, FFN, GROUP, 1002 + 10 * i, dev)
-        gate_up = spec.spec_pack_w4(*[torch.cat([a, b]) for a, b in zip(g, u)], G=GROUP)
-        gate, up = spec.spec_pack_w4(*g, G=GROUP), spec.spec_pack_w4(*u, G=GROUP)
+        glu = spec.spec_pack_gate_up(4, g, u, G=GROUP)
         down = spec.spec_pack_w4(*d, G=GROUP)
+        blk = dict(M=M, glu=glu, down=down)
+        if variants:
+            blk["gate_up"] = spec.spec_pack_w4(*[torch.cat([a, b]) for a, b in zip(g, u)], G=GROUP)
+            blk["gate"], blk["up"] = spec.spec_pack_w4(*g, G=GROUP), spec.spec_pack_w4(*u, G=GROUP)
         del g, u, d
-        x = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
-        h = synth.torch_activations(M, FFN, 1004 + 10 * i, dev)
-        ygu = torch.empty((M, 2 * FFN), dtype=torch.float32, device=dev)
-        yg = torch.empty((M, FFN), dtype=torch.float32, device=dev)
-        yu = torch.empty((M, FFN), dtype=torch.float32, device=dev)
-        yd = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
-        blocks.append(dict(M=M, gate_up=gate_up, gate=gate, up=up, down=down, x=x, h=h,
-                           ygu=ygu, yg=yg, yu=yu, yd=yd))
+        blk["x"] = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
+        blk["h"] = torch.empty((M, FFN), dtype=torch.bfloat16, device=dev)
+        blk["ygu"] = torch.empty((M, 2 * FFN), dtype=torch.float32, device=dev)
+        blk["yg"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
+        blk["yu"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
+        blk["yd"] = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
+        blocks.append(blk)
     torch.cuda.synchronize()
     return blocks
 
@@ -243,35 +252,38 @@ def run_accept(a):
 def cpu_baseline(seconds):
     """The fp64 oracle, as it stands, on a bounded sample of the step.
 
-    qmv: the step's 24 products (gate, up and down at M = 1..8) with one
-    seeded weight set per shape, rows split over the host threads, stopping
-    once `seconds` have passed; acceptance: the 256-sequence batch, drafts
-    drawn from the draft rows as on the GPU, likewise bounded.  Rates use the
-    GPU figure's algorithmic bytes (GB/s) and verify positions per second."""
+    qmv: the step's MLP chain at M = 1..8 (the gated gate/up activation,
+    then down on the oracle's own bf16 h) with one seeded weight set per
+    shape, rows split over the host threads, stopping once `seconds` have
+    passed; acceptance: the 256-sequence batch, drafts drawn from the draft
+    rows as on the GPU, likewise bounded.  Rates use the GPU figure's
+    algorithmic bytes (GB/s) and verify positions per second."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     from speculative_decoding_spec_amd import roofline, synth
     threads = min(16, os.cpu_count() or 1)
-    shapes = {"gate_up": (FFN, HIDDEN), "down": (HIDDEN, FFN)}
-    weights = {k: synth.qweights(1, 4, N, K, GROUP, salt=N) for k, (N, K) in shapes.items()}
-    work = []
-    for M in MS:
-        for name in ("gate_up", "gate_up", "down"):
-            work.append((name, M))
+    gate = synth.qweights(1, 4, FFN, HIDDEN, GROUP, salt=1)
+    up = synth.qweights(1, 4, FFN, HIDDEN, GROUP, salt=2)
+    down = synth.qweights(1, 4, HIDDEN, FFN, GROUP, salt=3)
     chunk = 256
-    done_bytes, products, t0 = 0, 0, time.perf_counter()
+    done_bytes, launches, t0 = 0, 0, time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        for name, M in work:
+        for M in MS:
             if time.perf_counter() - t0 >= seconds:
                 break
-            N, K = shapes[name]
-            w, s, b = weights[name]
-            x = synth.activations(1, M, K, salt=M)
-            spans = [(r, min(N, r + chunk)) for r in range(0, N, chunk)]
-            list(ex.map(lambda sp: oracle.qmv(4, w, s, b, x, GROUP, rows=sp), spans))
-            done_bytes += roofline.qmv_bytes(4, M, N, K, GROUP)
-            products += 1
+            x = synth.activations(1, M, HIDDEN, salt=M)
+            spans = [(r, min(FFN, r + chunk)) for r in range(0, FFN, chunk)]
+            parts = list(ex.map(lambda sp: oracle.gate_up_silu(4, gate, up, x, GROUP, rows=sp), spans))
+            hb = np.ascontiguousarray(np.concatenate([p[1] for p in parts], axis=1))
+            done_bytes += roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN, GROUP)
+            launches += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+            spans = [(r, min(HIDDEN, r + chunk)) for r in range(0, HIDDEN, chunk)]
+            list(ex.map(lambda sp: oracle.qmv(4, *down, hb, GROUP, rows=sp), spans))
+            done_bytes += roofline.qmv_bytes(4, M, HIDDEN, FFN, GROUP)
+            launches += 1
     dt = time.perf_counter() - t0
     tl, dl = synth.logits_pair(4, ACC_B, ACC_D, ACC_V)
     ud = synth.uniforms(4, synth.U_DRAFT, ACC_B * ACC_D)
@@ -287,9 +299,10 @@ def cpu_baseline(seconds):
     at = time.perf_counter() - t1
     return {
         "value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": (f"W4 g64 qmv: {products} of the step's 24 products (gate/up 5120->17408, "
-                   f"down 17408->5120, M=1..8), {done_bytes / 1e6:.0f} MB algorithmic in {dt:.1f} s; "
-                   f"acceptance: {nseq} of 256 sequences (D=5, V=151936, T=0.6) in {at:.2f} s"),
+        "sample": (f"W4 g64 MLP chain: {launches} of the step's 16 launches (gated gate/up "
+                   f"5120->2x17408, down 17408->5120, M=1..8), {done_bytes / 1e6:.0f} MB "
+                   f"algorithmic in {dt:.1f} s; acceptance: {nseq} of 256 sequences (D=5, "
+                   f"V=151936, T=0.6) in {at:.2f} s"),
         "accept_positions_per_s": round(nseq * (ACC_D + 1) / at, 1),
         "cpu": platform.processor() or platform.machine(),
     }
@@ -315,7 +328,8 @@ def main():
     if args.shapes:
         shapes(dev, args.steps)
         return
-    blocks = build_inputs(dev)
+    full = not args.step_only
+    blocks = build_inputs(dev, variants=full)
     acc = build_accept(dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -324,8 +338,18 @@ def main():
     def pair():
         return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
-    def fused_launches():
-        """(bound call, shape name, algorithmic bytes) of the 16 launches."""
+    def chain_launches():
+        """(bound call, shape name, algorithmic bytes) of the step's 16
+        launches: the gated gate/up launch, then down reading its h."""
+        out = []
+        for b in blocks:
+            out.append((spec.bind_qmv_gate_up_silu(b["glu"], b["x"], b["h"]), "gate_up_silu",
+                        roofline.gate_up_silu_bytes(4, b["M"], FFN, HIDDEN)))
+            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
+                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
+        return out
+
+    def plain_fused_launches():
         out = []
         for b in blocks:
             out.append((spec.bind_qmv(b["gate_up"], b["x"], b["ygu"]), "gate_up",
@@ -345,8 +369,7 @@ def main():
                         roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
         return out
 
-    launches = fused_launches()
-    unfused = unfused_launches()
+    launches = chain_launches()
     accept_call = spec.bind_verify_accept(acc["t"], acc["d"], acc["toks"], acc["u"], ACC_T,
                                           out=(acc["acc"], acc["nxt"], None, None))
     qmv_bytes_step = sum(l[2] for l in launches)
@@ -379,6 +402,64 @@ def main():
     qspan_ms = sum(e["q"][0].elapsed_time(e["q"][1]) for e in ev) / args.steps
     acc_ms = sum(e["a"][0].elapsed_time(e["a"][1]) for e in ev) / args.steps
     qmv_gbs = qmv_bytes_step / (qspan_ms * 1e-3) / 1e9
+    positions = ACC_B * (ACC_D + 1)
+    acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
+    accept = {"positions_per_s": round(positions / (acc_ms * 1e-3), 1), "us": round(acc_ms * 1e3, 2),
+              "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4),
+              "algorithmic_bytes": acc_bytes,
+              "mean_accepted": float(acc["acc"].float().mean().item())}
+
+    # Roofline of qmv_kernel: algorithmic bytes per launch over the average
+    # launch duration, i.e. the qmv part of a step (16 launches back to back,
+    # no events between them) divided by 16.  The per-launch events of the
+    # variants add about 2 us of marker time to each launch, so they only
+    # split the time by shape.
+    bytes_per_launch = qmv_bytes_step / len(launches)
+    launch_us = qspan_ms / len(launches) * 1e3
+    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
+    traffic, tinfo = measured_traffic(bytes_per_launch)
+    roof = {"kernel": ("qmv_kernel (W4; 16 launches per step: gate/up with the gated activation, "
+                       "and down, at M=1..8)"),
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+            "frac": round(achieved / 8000.0, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "algorithmic_bytes_per_launch": round(bytes_per_launch),
+            "avg_launch_us": round(launch_us, 2),
+            "traffic_source": (os.path.relpath(TRAFFIC_FILE, ROOT) if traffic is not None else tinfo)}
+    out = {
+        "metric": METRIC, "value": round(qmv_gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "w4-bf16xfp32 qmv; fp32 accept",
+        "data": "synthetic (seeded, on-device generators)",
+        "config": {"workload": ("verify MLP block W4 g64 (gate/up 5120->2x17408 as one launch "
+                                "applying silu(gate)*up, down 17408->5120 on that activation) at "
+                                "M=1..8 on distinct weight copies + batched acceptance B=256 D=5 "
+                                "V=151936 T=0.6"),
+                   "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
+        "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
+        "qmv_us_per_step": round(qspan_ms * 1e3, 2), "accept": accept, "roofline": roof,
+    }
+    if not full:
+        print(json.dumps(out), flush=True)
+        return
+
+    # Greedy verification of the same block (target logits only), drafts
+    # from the greedy draft (argmax of each draft row).
+    g_toks = torch.argmax(acc["d"], dim=2).to(torch.int32).contiguous()
+    g_out = (torch.empty(ACC_B, dtype=torch.int32, device=dev),
+             torch.empty(ACC_B, dtype=torch.int32, device=dev))
+    greedy_call = spec.bind_verify_greedy(acc["t"], g_toks, out=g_out)
+    for _ in range(args.warmup):
+        greedy_call()
+    g_ev = [pair() for _ in range(args.steps)]
+    for e in g_ev:
+        e[0].record(stream)
+        greedy_call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    g_ms = sum(e[0].elapsed_time(e[1]) for e in g_ev) / args.steps
+    g_bytes = roofline.greedy_bytes(ACC_B, ACC_D, ACC_V)
 
     def eager(calls, per_launch):
         """K eager steps of `calls`: the span of each step and, if asked, the
@@ -401,24 +482,10 @@ def main():
                     for i in range(len(calls))] if per_launch else None)
         return span_ms, each_ms
 
-    # Greedy verification of the same block (target logits only), drafts
-    # from the greedy draft (argmax of each draft row).
-    g_toks = torch.argmax(acc["d"], dim=2).to(torch.int32).contiguous()
-    g_out = (torch.empty(ACC_B, dtype=torch.int32, device=dev),
-             torch.empty(ACC_B, dtype=torch.int32, device=dev))
-    greedy_call = spec.bind_verify_greedy(acc["t"], g_toks, out=g_out)
-    for _ in range(args.warmup):
-        greedy_call()
-    g_ev = [pair() for _ in range(args.steps)]
-    for e in g_ev:
-        e[0].record(stream)
-        greedy_call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    g_ms = sum(e[0].elapsed_time(e[1]) for e in g_ev) / args.steps
-    g_bytes = roofline.greedy_bytes(ACC_B, ACC_D, ACC_V)
-
-    eager_unfused_ms, _ = eager(unfused, False)
+    plain = plain_fused_launches()
+    unfused = unfused_launches()
+    plain_ms, _ = eager(plain, False)
+    unfused_ms, _ = eager(unfused, False)
     _, q_ms = eager(launches, True)
     per_m = {}
     for j, b in enumerate(blocks):
@@ -427,71 +494,37 @@ def main():
         per_m[str(b["M"])] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                               "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
     per_shape = {}
-    for name in ("gate_up", "down"):
+    for name in ("gate_up_silu", "down"):
         idx = [i for i, l in enumerate(launches) if l[1] == name]
         ms = sum(q_ms[i] for i in idx) / len(idx)
         nb = sum(launches[i][2] for i in idx) / len(idx)
         per_shape[name] = {"us_per_launch": round(ms * 1e3, 2),
                            "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                            "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
+    plain_bytes = sum(l[2] for l in plain)
     unfused_bytes = sum(l[2] for l in unfused)
-    variants = {
-        "fused gate/up, 16 launches (value)": {"qmv_us_per_step": round(qspan_ms * 1e3, 2),
-                                               "GB/s": round(qmv_gbs, 1)},
-        "separate gate and up, 24 launches": {"qmv_us_per_step": round(eager_unfused_ms * 1e3, 2),
-                                              "GB/s": round(unfused_bytes / (eager_unfused_ms * 1e-3) / 1e9, 1)},
+    out["variants"] = {
+        "chained MLP: gate/up with the gated activation, then down on its h (value)": {
+            "qmv_us_per_step": round(qspan_ms * 1e3, 2), "GB/s": round(qmv_gbs, 1)},
+        "gate/up as one launch with fp32 outputs, no activation; down on a separate h": {
+            "qmv_us_per_step": round(plain_ms * 1e3, 2),
+            "GB/s": round(plain_bytes / (plain_ms * 1e-3) / 1e9, 1)},
+        "separate gate, up and down launches (24)": {
+            "qmv_us_per_step": round(unfused_ms * 1e3, 2),
+            "GB/s": round(unfused_bytes / (unfused_ms * 1e-3) / 1e9, 1)},
     }
-    positions = ACC_B * (ACC_D + 1)
-    acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
-    accept = {"positions_per_s": round(positions / (acc_ms * 1e-3), 1), "us": round(acc_ms * 1e3, 2),
-              "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4),
-              "algorithmic_bytes": acc_bytes,
-              "mean_accepted": float(acc["acc"].float().mean().item())}
-
-    greedy = {"positions_per_s": round(positions / (g_ms * 1e-3), 1), "us": round(g_ms * 1e3, 2),
-              "GB/s": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
-              "frac": round(g_bytes / (g_ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4),
-              "algorithmic_bytes": g_bytes,
-              "mean_accepted": float(g_out[0].float().mean().item())}
-
-    # Roofline of qmv_kernel: algorithmic bytes per launch over the average
-    # launch duration, i.e. the qmv part of a step (16 launches back to back,
-    # no events between them) divided by 16.  The per-launch events of the
-    # second set of steps add about 2 us of marker time to each launch, so
-    # they only split the time by shape.
-    bytes_per_launch = qmv_bytes_step / len(launches)
-    launch_us = qspan_ms / len(launches) * 1e3
-    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
-    traffic, tinfo = measured_traffic(bytes_per_launch)
-    roof = {"kernel": "qmv_kernel (W4; 16 launches per step: fused gate/up and down at M=1..8)",
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-            "frac": round(achieved / 8000.0, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "algorithmic_bytes_per_launch": round(bytes_per_launch),
-            "avg_launch_us": round(launch_us, 2),
-            "traffic_source": (os.path.relpath(TRAFFIC_FILE, ROOT) if traffic is not None else tinfo)}
-    other = {"qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
-                            "per_shape (per-launch events)": per_shape},
-             "accept (row_chunk + draw_sums + draw_final)": {
-                 "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
-                 "us_per_call": round(acc_ms * 1e3, 2)}}
-
-    out = {
-        "metric": METRIC, "value": round(qmv_gbs, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "w4-bf16xfp32 qmv; fp32 accept",
-        "data": "synthetic (seeded, on-device generators)",
-        "config": {"workload": ("verify MLP block W4 g64 (gate/up 5120->17408 packed as one "
-                                "5120->34816 launch, down 17408->5120) at M=1..8 on distinct "
-                                "weight copies + batched acceptance B=256 D=5 V=151936 T=0.6"),
-                   "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
-        "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
-        "qmv_us_per_step": round(qspan_ms * 1e3, 2), "variants": variants,
-        "per_M (per-launch events)": per_m, "accept": accept,
-        "accept_greedy (same block, target logits only; not part of the step)": greedy,
-        "roofline": roof, "roofline_parts": other,
-    }
+    out["per_M (per-launch events)"] = per_m
+    out["accept_greedy (same block, target logits only; not part of the step)"] = {
+        "positions_per_s": round(positions / (g_ms * 1e-3), 1), "us": round(g_ms * 1e3, 2),
+        "GB/s": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+        "frac": round(g_bytes / (g_ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        "algorithmic_bytes": g_bytes, "mean_accepted": float(g_out[0].float().mean().item())}
+    out["roofline_parts"] = {
+        "qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
+                       "per_shape (per-launch events)": per_shape},
+        "accept (row_chunk + draw_sums + draw_final)": {
+            "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
+            "us_per_call": round(acc_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

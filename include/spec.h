@@ -120,6 +120,45 @@ spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
                         int G, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Gated MLP activation: h = silu(x G^T) * (x U^T), one launch           */
+/* ------------------------------------------------------------------ */
+/*
+ * The MLP block dominates verify time (MTPLX re-post, "3) MLX verify
+ * bottleneck"); in the Qwen target it is down(silu(gate(x)) * up(x)) (the
+ * SiLU-gated form is a reading: the pages do not spell it out).  Gate and up
+ * share x, so they stream as one launch, and the activation between the two
+ * halves of the block is applied to their fp32 results in the same launch:
+ *   h[m][f] = bf16( silu(g) * u ),  g = (x G^T)[m][f], u = (x U^T)[m][f],
+ *   silu(g) = g / (1 + exp(-g)), rounded to nearest-even bf16,
+ * which is the x of the down projection.  g and u are computed exactly as
+ * spec_qmv_* computes each (bitwise the same fp32 values).
+ *
+ * spec_pack_gate_up packs G and U (each in the interchange layout of
+ * spec_pack_w4 / spec_pack_w8 with N = F rows) into one buffer with
+ * alternating 16-row tiles.  Its packed buffers have the sizes of an
+ * R-row matrix, R = spec_gate_up_packed_rows(F) = 32 * ceil(F / 16):
+ *   w_packed   spec_qmv_packed_weight_bytes(bits, R, K, G) bytes, 16-byte aligned
+ *   sb_packed  spec_qmv_packed_sb_bytes(R, K, G) bytes, 4-byte aligned
+ * spec_qmv_gate_up_silu reads them:
+ *  bits    4 or 8, as packed
+ *  x       bf16 [M][K], 16-byte aligned; M 0..16
+ *  h       bf16 [M][F] out, 2-byte aligned
+ *  F, K, G as packed (K % G == 0, G == 64)
+ * Errors as for spec_qmv_*.
+ */
+int spec_gate_up_packed_rows(int F);
+
+spec_status spec_pack_gate_up(int bits, const void *gate_w, const uint16_t *gate_scales,
+                              const uint16_t *gate_biases, const void *up_w,
+                              const uint16_t *up_scales, const uint16_t *up_biases,
+                              int F, int K, int G, void *w_packed, void *sb_packed,
+                              hipStream_t stream);
+
+spec_status spec_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,
+                                  const uint16_t *x, uint16_t *h, int M, int F, int K,
+                                  int G, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Sampling distribution                                                */
 /* ------------------------------------------------------------------ */
 /*

@@ -10,6 +10,8 @@ Names follow the C ABI:
 
     spec_pack_w4 / spec_pack_w8      one-time repack of quantized weights
     spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv
+    spec_pack_gate_up /              gate and up projections as one launch with
+    spec_qmv_gate_up_silu            the SiLU-gated activation applied (bf16 out)
     spec_verify_accept               ratio acceptance + residual / bonus draw
     spec_sample_probs                filtered sampling distribution
     spec_sample_tokens               inverse-CDF draw from that distribution
@@ -82,6 +84,12 @@ def lib() -> ctypes.CDLL:
         L.spec_sample_probs.argtypes = [vp, i, i, f, i, f, vp, vp, sz, vp]
         L.spec_sample_probs.restype = i
         L.spec_sample_tokens.argtypes = [vp, i, i, f, i, f, vp, vp, vp, sz, vp]
+        L.spec_gate_up_packed_rows.argtypes = [i]
+        L.spec_gate_up_packed_rows.restype = i
+        L.spec_pack_gate_up.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
+        L.spec_pack_gate_up.restype = i
+        L.spec_qmv_gate_up_silu.argtypes = [i, vp, vp, vp, vp, i, i, i, i, vp]
+        L.spec_qmv_gate_up_silu.restype = i
         L.spec_verify_greedy_workspace.argtypes = [i, i, i]
         L.spec_verify_greedy_workspace.restype = sz
         L.spec_verify_greedy.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
@@ -189,6 +197,72 @@ def spec_pack_w4(w, scales, biases, G: int = 64) -> PackedWeights:
 def spec_pack_w8(w, scales, biases, G: int = 64) -> PackedWeights:
     """Pack W8 weights: w uint8 [N][K], scales / biases fp16 [N][K/G]."""
     return _pack("spec_pack_w8", 8, w, scales, biases, G)
+
+
+class PackedGateUp:
+    """A gate/up pair packed with alternating tiles by spec_pack_gate_up."""
+
+    def __init__(self, bits, F, K, G, w, sb):
+        self.bits, self.F, self.K, self.G, self.w, self.sb = bits, F, K, G, w, sb
+
+
+def spec_pack_gate_up(bits: int, gate, up, G: int = 64) -> PackedGateUp:
+    """Pack the gate and up projections (each (w, scales, biases) as for
+    spec_pack_w4 / spec_pack_w8, F rows) for spec_qmv_gate_up_silu."""
+    import torch
+    dev = gate[0].device
+    wdt = torch.int32 if bits == 4 else torch.uint8
+    for name, t in (("gate", gate), ("up", up)):
+        _require(t[0], wdt, f"{name} w", dev)
+        _require(t[1], torch.float16, f"{name} scales", dev)
+        _require(t[2], torch.float16, f"{name} biases", dev)
+    F = gate[0].shape[0]
+    K = gate[0].shape[1] * 8 if bits == 4 else gate[0].shape[1]
+    if tuple(up[0].shape) != tuple(gate[0].shape):
+        raise ValueError("gate and up must have the same shape")
+    if G <= 0 or K % G:
+        raise ValueError("K must be a multiple of G")
+    for t in (gate, up):
+        if tuple(t[1].shape) != (F, K // G) or tuple(t[2].shape) != (F, K // G):
+            raise ValueError(f"scales / biases must be [{F}][{K // G}]")
+    R = int(lib().spec_gate_up_packed_rows(F))
+    wp = torch.empty(max(spec_qmv_packed_weight_bytes(bits, R, K, G), 16), dtype=torch.uint8,
+                     device=dev)
+    sbp = torch.empty(max(spec_qmv_packed_sb_bytes(R, K, G), 16), dtype=torch.uint8, device=dev)
+    st = lib().spec_pack_gate_up(bits, _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]),
+                                 _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), F, K, G,
+                                 _ptr(wp), _ptr(sbp), _stream(dev))
+    _check("spec_pack_gate_up", st)
+    return PackedGateUp(bits, F, K, G, wp, sbp)
+
+
+def spec_qmv_gate_up_silu(packed: PackedGateUp, x, h=None):
+    """h[M][F] bf16 = silu(x G^T) * (x U^T) for a pair packed by spec_pack_gate_up."""
+    import torch
+    dev = x.device
+    _require(x, torch.bfloat16, "x", dev)
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has K={K}, weights have K={packed.K}")
+    if h is None:
+        h = torch.empty((M, packed.F), dtype=torch.bfloat16, device=dev)
+    _require(h, torch.bfloat16, "h", dev)
+    if tuple(h.shape) != (M, packed.F):
+        raise ValueError(f"h must be [{M}][{packed.F}]")
+    st = lib().spec_qmv_gate_up_silu(packed.bits, _ptr(packed.w), _ptr(packed.sb), _ptr(x),
+                                     _ptr(h), M, packed.F, K, packed.G, _stream(dev))
+    _check("spec_qmv_gate_up_silu", st)
+    return h
+
+
+def bind_qmv_gate_up_silu(packed: PackedGateUp, x, h) -> "_Bound":
+    """spec_qmv_gate_up_silu on fixed tensors, marshalled once (first call
+    checked)."""
+    spec_qmv_gate_up_silu(packed, x, h)
+    M, K = x.shape
+    args = (packed.bits, _ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(h), M, packed.F, K,
+            packed.G, _stream(x.device))
+    return _Bound("spec_qmv_gate_up_silu", lib().spec_qmv_gate_up_silu, args, (packed, x, h))
 
 
 def _qmv(name, bits, packed, x, y):

@@ -40,7 +40,8 @@ spec_status pack_common(int bits, const void *w, const uint16_t *scales,
         return SPEC_ERR_INVALID;
     if (!aligned16(w) || !aligned16(w_packed) || !aligned4(sb_packed))
         return SPEC_ERR_UNSUPPORTED;
-    if (spec::launch_pack(bits, w, scales, biases, N, K, w_packed, sb_packed, stream) != hipSuccess)
+    if (spec::launch_pack(bits, w, scales, biases, nullptr, nullptr, nullptr, N, K, w_packed,
+                          sb_packed, stream) != hipSuccess)
         return SPEC_ERR_DEVICE;
     return SPEC_OK;
 }
@@ -137,6 +138,67 @@ spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
                         const uint16_t *x, float *y, int M, int N, int K, int G,
                         hipStream_t stream) {
     return qmv_common(8, w_packed, sb_packed, x, y, M, N, K, G, stream);
+}
+
+int spec_gate_up_packed_rows(int F) {
+    if (F < 0 || F > (1 << 27))
+        return 0;
+    return spec::gate_up_rows(F);
+}
+
+spec_status spec_pack_gate_up(int bits, const void *gate_w, const uint16_t *gate_scales,
+                              const uint16_t *gate_biases, const void *up_w,
+                              const uint16_t *up_scales, const uint16_t *up_biases,
+                              int F, int K, int G, void *w_packed, void *sb_packed,
+                              hipStream_t stream) {
+    if (bits != 4 && bits != 8)
+        return SPEC_ERR_INVALID;
+    if (bits == 4 && K % 8 != 0)
+        return SPEC_ERR_INVALID;
+    if (F < 0 || F > (1 << 27))
+        return F < 0 ? SPEC_ERR_INVALID : SPEC_ERR_UNSUPPORTED;
+    const spec_status s = qmv_shape_ok(spec::gate_up_rows(F), K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (F == 0 || K == 0)
+        return SPEC_OK;
+    if (!gate_w || !gate_scales || !gate_biases || !up_w || !up_scales || !up_biases ||
+        !w_packed || !sb_packed)
+        return SPEC_ERR_INVALID;
+    if (!aligned16(gate_w) || !aligned16(up_w) || !aligned16(w_packed) || !aligned4(sb_packed))
+        return SPEC_ERR_UNSUPPORTED;
+    if (spec::launch_pack(bits, gate_w, gate_scales, gate_biases, up_w, up_scales, up_biases,
+                          F, K, w_packed, sb_packed, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,
+                                  const uint16_t *x, uint16_t *h, int M, int F, int K,
+                                  int G, hipStream_t stream) {
+    if (bits != 4 && bits != 8)
+        return SPEC_ERR_INVALID;
+    if (M < 0 || F < 0)
+        return SPEC_ERR_INVALID;
+    if (F > (1 << 27))
+        return SPEC_ERR_UNSUPPORTED;
+    const spec_status s = qmv_shape_ok(spec::gate_up_rows(F), K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (M > kMaxM)
+        return SPEC_ERR_UNSUPPORTED;
+    if (M == 0 || F == 0)
+        return SPEC_OK;
+    if (!h || (K > 0 && (!w_packed || !sb_packed || !x)))
+        return SPEC_ERR_INVALID;
+    if (K > 0 && (!aligned16(w_packed) || !aligned16(x) || !aligned4(sb_packed)))
+        return SPEC_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(h) & 1u)
+        return SPEC_ERR_INVALID;
+    if (spec::launch_qmv_gate_up_silu(bits, w_packed, sb_packed, x, h, M, F, K, stream) !=
+        hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
 }
 
 size_t spec_verify_accept_workspace(int B, int D, int V, int top_k) {

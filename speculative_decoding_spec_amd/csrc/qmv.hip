@@ -120,14 +120,21 @@ __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
 // groups past K/64 are zero, so they contribute exactly nothing.
 // ---------------------------------------------------------------------------
 
+// With a second matrix (w2, scales2, biases2 non-null: the up projection
+// next to the gate projection w) the tiles alternate: tile 2i holds rows
+// 16i..16i+15 of the first matrix and tile 2i + 1 the same rows of the
+// second, so one workgroup owning two tiles sees both halves of a gated
+// product.  N is then the row count of each matrix.
 template <int BITS>
 __global__ __launch_bounds__(256) void pack_kernel(
     const void *__restrict__ w, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, u32x4 *__restrict__ wp,
-    uint32_t *__restrict__ sbp, int N, int K) {
+    const uint16_t *__restrict__ biases, const void *__restrict__ w2,
+    const uint16_t *__restrict__ scales2, const uint16_t *__restrict__ biases2,
+    u32x4 *__restrict__ wp, uint32_t *__restrict__ sbp, int N, int K) {
+    const bool two = w2 != nullptr;
     const int ng = K >> 6;
     const int n_pairs = (ng + 1) >> 1;
-    const int n_tiles = (N + 15) >> 4;
+    const int n_tiles = two ? 2 * ((N + 15) >> 4) : (N + 15) >> 4;
     constexpr int L = BITS / 4;   // 16-byte slots per lane and tile
     const size_t slots = (size_t)n_tiles * n_pairs * 64 * L;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < slots;
@@ -139,12 +146,13 @@ __global__ __launch_bounds__(256) void pack_kernel(
         const int p = (int)(tp % n_pairs);
         const int t = (int)(tp / n_pairs);
         const int r = lane & 15, j = lane >> 4;
-        const int n = 16 * t + r;
+        const int n = two ? 16 * (t >> 1) + r : 16 * t + r;
+        const void *src = (two && (t & 1)) ? w2 : w;
         const int k = 128 * p + 64 * (j >> 1) + 32 * (j & 1) + 16 * v;  // first k of the 16 bytes
         u32x4 val = {0u, 0u, 0u, 0u};
         if (n < N && k < K) {
             if (BITS == 4) {
-                val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 5];
+                val = reinterpret_cast<const u32x4 *>(src)[((size_t)n * K + k) >> 5];
                 // k-slot e of each word moves to nibble (e & 1) * 4 + (e >> 1)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
                     val[c] = out;
                 }
             } else {
-                val = reinterpret_cast<const u32x4 *>(w)[((size_t)n * K + k) >> 4];
+                val = reinterpret_cast<const u32x4 *>(src)[((size_t)n * K + k) >> 4];
             }
         }
         wp[i] = val;
@@ -170,11 +178,14 @@ __global__ __launch_bounds__(256) void pack_kernel(
         const size_t rest = i >> 6;
         const int pp = (int)(rest % npp);
         const int t = (int)(rest / npp);
-        const int n = 16 * t + (hr & 15);
+        const int n = two ? 16 * (t >> 1) + (hr & 15) : 16 * t + (hr & 15);
+        const bool second = two && (t & 1);
+        const uint16_t *sc = second ? scales2 : scales;
+        const uint16_t *bi = second ? biases2 : biases;
         const int g = 2 * (2 * pp + e) + (hr >> 4);
         uint32_t val = 0;
         if (n < N && g < ng)
-            val = (uint32_t)scales[(size_t)n * ng + g] | ((uint32_t)biases[(size_t)n * ng + g] << 16);
+            val = (uint32_t)sc[(size_t)n * ng + g] | ((uint32_t)bi[(size_t)n * ng + g] << 16);
         sbp[i] = val;
     }
 }
@@ -191,12 +202,20 @@ __global__ __launch_bounds__(256) void pack_kernel(
 // into separate accumulators that get their own group's scale and bias.
 // The per-group FMA chains and the final sum are those of the pair form, so
 // rows 0..7 of a wide call equal an M <= 8 call bitwise.
-template <int BITS, int WAVES, int T, int U, int S, int XH>
+//
+// GLU: the weights are a gate/up pair packed with alternating tiles (see
+// pack_kernel), T is even, and instead of y the kernel writes the gated
+// activation h[m][f] = silu(g) * u as bf16 [M][n_out], g and u being the
+// outputs of tiles 2i and 2i + 1 for f = 16i + r.  g and u are reduced
+// exactly as a plain launch reduces them.
+template <int BITS, int WAVES, int T, int U, int S, int XH, bool GLU = false>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
-    const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K) {
+    const uint16_t *__restrict__ x, void *__restrict__ out, int M, int N, int K,
+    int n_out) {
     static_assert(U == 1 || U == 2, "a stage is one or two pairs");
     static_assert(XH == 1 || XH == 2 || XH == 4, "x loads per lane and pair");
+    static_assert(!GLU || T % 2 == 0, "a gated launch pairs gate and up tiles");
     constexpr bool WIDE = XH == 4;  // 9..16 rows: one MFMA per group
     constexpr int XR = WIDE ? 16 : 8;   // staged x rows
     constexpr int NG = WIDE ? 2 : 1;    // groups (accumulators) per lane
@@ -425,28 +444,56 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         sh.red[wave][tt][lane] = WIDE ? acc[tt][0] + acc[tt][NG - 1] : acc[tt][0];
     __syncthreads();
     if (WIDE ? wave == 0 : (wave == 0 && lane < 32)) {
+        f32x4 tot[T];
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
-            const int n = (blockIdx.x * T + tt) * 16 + r;
-            if (n >= N)
-                continue;
-            f32x4 tot = WIDE ? sh.red[0][tt][lane] : sh.red[0][tt][lane] + sh.red[0][tt][lane + 32];
+            tot[tt] = WIDE ? sh.red[0][tt][lane] : sh.red[0][tt][lane] + sh.red[0][tt][lane + 32];
             for (int ww = 1; ww < WAVES; ++ww)
-                tot += WIDE ? sh.red[ww][tt][lane] : sh.red[ww][tt][lane] + sh.red[ww][tt][lane + 32];
+                tot[tt] += WIDE ? sh.red[ww][tt][lane] : sh.red[ww][tt][lane] + sh.red[ww][tt][lane + 32];
+        }
+        const int m0 = WIDE ? 4 * j : 4 * sub;
+        if (!GLU) {
+            float *y = static_cast<float *>(out);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = (WIDE ? 4 * j : 4 * sub) + i;
-                if (m < M)
-                    y[(size_t)m * N + n] = tot[i];
+            for (int tt = 0; tt < T; ++tt) {
+                const int n = (blockIdx.x * T + tt) * 16 + r;
+                if (n >= N)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (m0 + i < M)
+                        y[(size_t)(m0 + i) * N + n] = tot[tt][i];
+            }
+        } else {
+            uint16_t *h = static_cast<uint16_t *>(out);
+#pragma unroll
+            for (int tt = 0; tt < T; tt += 2) {
+                const int f = ((blockIdx.x * T + tt) >> 1) * 16 + r;
+                if (f >= n_out)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (m0 + i >= M)
+                        continue;
+                    const float g = tot[tt][i], u = tot[tt + 1][i];
+                    const float v = g / (1.0f + expf(-g)) * u;
+                    // nearest-even bf16 (finite values and infinities; the
+                    // quiet-NaN pattern for NaN)
+                    const unsigned bits = __float_as_uint(v);
+                    const unsigned rnd = (v != v) ? 0x7FC00000u
+                                                  : bits + 0x7FFFu + ((bits >> 16) & 1u);
+                    h[(size_t)(m0 + i) * n_out + f] = (uint16_t)(rnd >> 16);
+                }
             }
         }
     }
 }
 
-__global__ void fill_zero_kernel(float *__restrict__ y, size_t count) {
+template <typename V>
+__global__ void fill_zero_kernel(V *__restrict__ y, size_t count) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (size_t)gridDim.x * blockDim.x)
-        y[i] = 0.0f;
+        y[i] = V(0);
 }
 
 } // namespace
@@ -490,20 +537,24 @@ size_t qmv_packed_sb_bytes(int N, int K) {
 }
 
 hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
-                       const uint16_t *biases, int N, int K, void *w_packed,
-                       void *sb_packed, hipStream_t stream) {
+                       const uint16_t *biases, const void *w2,
+                       const uint16_t *scales2, const uint16_t *biases2, int N,
+                       int K, void *w_packed, void *sb_packed, hipStream_t stream) {
     if (N == 0 || K == 0)
         return hipSuccess;
-    const size_t slots = qmv_packed_bytes(bits, N, K) / 16;
+    const int n_rows = w2 ? gate_up_rows(N) : N;
+    const size_t slots = qmv_packed_bytes(bits, n_rows, K) / 16;
     const int blocks = (int)std::min<size_t>((slots + 255) / 256, 65536);
     if (bits == 4)
-        pack_kernel<4><<<blocks, 256, 0, stream>>>(w, scales, biases, (u32x4 *)w_packed,
-                                                   (uint32_t *)sb_packed, N, K);
+        pack_kernel<4><<<blocks, 256, 0, stream>>>(w, scales, biases, w2, scales2, biases2,
+                                                   (u32x4 *)w_packed, (uint32_t *)sb_packed, N, K);
     else
-        pack_kernel<8><<<blocks, 256, 0, stream>>>(w, scales, biases, (u32x4 *)w_packed,
-                                                   (uint32_t *)sb_packed, N, K);
+        pack_kernel<8><<<blocks, 256, 0, stream>>>(w, scales, biases, w2, scales2, biases2,
+                                                   (u32x4 *)w_packed, (uint32_t *)sb_packed, N, K);
     return hipGetLastError();
 }
+
+int gate_up_rows(int F) { return 32 * ((F + 15) / 16); }
 
 hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
                       const uint16_t *x, float *y, int M, int N, int K,
@@ -523,11 +574,11 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
 #define SPEC_QMV_LAUNCH(B, W, TT, UU)                                                       \
     if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.pairs_per_stage == UU) { \
         if (M <= 4)                                                                         \
-            qmv_kernel<B, W, TT, UU, 2, 1><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+            qmv_kernel<B, W, TT, UU, 2, 1><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
         else if (M <= 8)                                                                    \
-            qmv_kernel<B, W, TT, UU, 2, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+            qmv_kernel<B, W, TT, UU, 2, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
         else                                                                                \
-            qmv_kernel<B, W, TT, UU, 2, 4><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K); \
+            qmv_kernel<B, W, TT, UU, 2, 4><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
         return hipGetLastError();                                                           \
     }
 #define SPEC_QMV_SHAPES(B) \
@@ -537,6 +588,44 @@ hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
     SPEC_QMV_SHAPES(8)
 #undef SPEC_QMV_SHAPES
 #undef SPEC_QMV_LAUNCH
+    return hipErrorInvalidConfiguration;   // no kernel for this plan (unreachable)
+}
+
+hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,
+                                   const uint16_t *x, uint16_t *h, int M, int F, int K,
+                                   hipStream_t stream) {
+    if (M == 0 || F == 0)
+        return hipSuccess;
+    if (K == 0) {   // g = u = 0, so h = silu(0) * 0 = +0
+        const size_t count = (size_t)M * F;
+        const int blocks = (int)std::min<size_t>((count + 255) / 256, 4096);
+        fill_zero_kernel<<<blocks, 256, 0, stream>>>(h, count);
+        return hipGetLastError();
+    }
+    const int N = gate_up_rows(F);
+    const QmvPlan plan = qmv_plan(bits, N, K);
+    // The plain launch shape with at least one gate/up tile pair per
+    // workgroup: the waves (hence every output's reduction order) are the
+    // plain launch's, only the tiles per workgroup may double.
+    const int T = std::max(plan.tiles_per_wave, 2);
+    const u32x4 *wp = (const u32x4 *)w_packed;
+    const uint32_t *sbp = (const uint32_t *)sb_packed;
+    // n_tiles is even, so no workgroup splits a gate/up pair; tiles past the
+    // end (T = 4) read zeros and write nothing.
+    const dim3 grid((plan.n_tiles + T - 1) / T);
+#define SPEC_QMV_GLU_LAUNCH(B, W, TT)                                                      \
+    if (bits == B && plan.waves == W && T == TT && plan.pairs_per_stage == 1) {            \
+        if (M <= 4)                                                                         \
+            qmv_kernel<B, W, TT, 1, 2, 1, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
+        else if (M <= 8)                                                                    \
+            qmv_kernel<B, W, TT, 1, 2, 2, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
+        else                                                                                \
+            qmv_kernel<B, W, TT, 1, 2, 4, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
+        return hipGetLastError();                                                           \
+    }
+    SPEC_QMV_GLU_LAUNCH(4, 4, 4) SPEC_QMV_GLU_LAUNCH(4, 4, 2) SPEC_QMV_GLU_LAUNCH(4, 8, 2)
+    SPEC_QMV_GLU_LAUNCH(8, 8, 2)
+#undef SPEC_QMV_GLU_LAUNCH
     return hipErrorInvalidConfiguration;   // no kernel for this plan (unreachable)
 }
 

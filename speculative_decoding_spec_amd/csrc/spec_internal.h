@@ -23,12 +23,21 @@ struct QmvPlan {
 QmvPlan qmv_plan(int bits, int N, int K);
 size_t qmv_packed_bytes(int bits, int N, int K);
 size_t qmv_packed_sb_bytes(int N, int K);
+// Packs one matrix (w2 == nullptr) or a gate/up pair with alternating
+// 16-row tiles (N = rows of each, packed as gate_up_rows(N) rows).
 hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
-                       const uint16_t *biases, int N, int K, void *w_packed,
-                       void *sb_packed, hipStream_t stream);
+                       const uint16_t *biases, const void *w2,
+                       const uint16_t *scales2, const uint16_t *biases2, int N,
+                       int K, void *w_packed, void *sb_packed, hipStream_t stream);
+int gate_up_rows(int F);
 hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
                       const uint16_t *x, float *y, int M, int N, int K,
                       hipStream_t stream);
+// h (bf16 [M][F]) = silu(x G^T) * (x U^T) from a gate/up pair packed with
+// alternating tiles.
+hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,
+                                   const uint16_t *x, uint16_t *h, int M, int F, int K,
+                                   hipStream_t stream);
 
 // ------------------------------------------------------------ sampling ----
 struct SamplingParams {

@@ -24,6 +24,12 @@ def qmv_bytes(bits: int, M: int, N: int, K: int, group: int = 64) -> int:
     return N * K * bits // 8 + N * (K // group) * 4 + M * K * 2 + M * N * 4
 
 
+def gate_up_silu_bytes(bits: int, M: int, F: int, K: int, group: int = 64) -> int:
+    """Bytes of the gated gate/up launch: both packed matrices with their
+    scale/bias words, bf16 x in, bf16 h [M][F] out."""
+    return 2 * F * K * bits // 8 + 2 * F * (K // group) * 4 + M * K * 2 + M * F * 2
+
+
 def qmv_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 
