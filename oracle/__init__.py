@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_gate_up_silu.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, lg, lg, lg, lg,
                                           lg, lg, vp, vp]
         L.oracle_gate_up_silu.restype = i
+        L.oracle_gdn_record.argtypes = [vp, vp, vp, vp, vp, vp, lg, lg, lg, lg, lg, vp, vp, vp]
+        L.oracle_gdn_record.restype = i
+        L.oracle_gdn_commit.argtypes = [vp, vp, vp, vp, vp, lg, lg, lg, lg, lg, vp]
+        L.oracle_gdn_commit.restype = i
         L.oracle_verify_greedy.argtypes = [vp, vp, lg, lg, lg, vp, vp]
         L.oracle_verify_greedy.restype = i
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
@@ -234,3 +238,37 @@ def verify_greedy(target_logits: np.ndarray, draft_tokens: np.ndarray | None) ->
     if rc != 0:
         raise ValueError(f"oracle_verify_greedy failed (rc={rc})")
     return {"accepted_len": acc, "next_token": nxt}
+
+
+def gdn_record(S0, q, k, v, alpha, beta) -> dict:
+    """Gated-delta-rule steps over T positions with the innovation tape:
+    S0 [B][H][dv][dk], q/k [B][T][H][dk], v [B][T][H][dv], alpha/beta
+    [B][T][H] (fp32).  Returns o and delta [B][T][H][dv] and S_final, fp64."""
+    S0, q, k, v, alpha, beta = [np.ascontiguousarray(a, dtype=np.float32)
+                                for a in (S0, q, k, v, alpha, beta)]
+    B, H, dv, dk = S0.shape
+    T = q.shape[1]
+    assert q.shape == (B, T, H, dk) and k.shape == (B, T, H, dk) and v.shape == (B, T, H, dv)
+    assert alpha.shape == (B, T, H) and beta.shape == (B, T, H)
+    o = np.empty((B, T, H, dv))
+    d = np.empty((B, T, H, dv))
+    Sf = np.empty((B, H, dv, dk))
+    rc = lib().oracle_gdn_record(_ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 B, T, H, dk, dv, _ptr(o), _ptr(d), _ptr(Sf))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_record failed (rc={rc})")
+    return {"o": o, "delta": d, "S_final": Sf}
+
+
+def gdn_commit(S0, alpha, k, delta, n) -> np.ndarray:
+    """The state after the first n[b] steps, from S0 and the tape alone."""
+    S0, alpha, k, delta = [np.ascontiguousarray(a, dtype=np.float32) for a in (S0, alpha, k, delta)]
+    n = np.ascontiguousarray(n, dtype=np.int32)
+    B, H, dv, dk = S0.shape
+    T = alpha.shape[1]
+    out = np.empty((B, H, dv, dk))
+    rc = lib().oracle_gdn_commit(_ptr(S0), _ptr(alpha), _ptr(k), _ptr(delta), _ptr(n), B, T, H,
+                                 dk, dv, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_commit failed (rc={rc})")
+    return out

@@ -38,6 +38,11 @@
  *             savepearlharbor.com llama.cpp MTP article, section on how
  *             speculative decoding works.
  *
+ *   gdn       Innovation-tape capture and commit of the recurrent (GDN)
+ *             state: MTPLX announcement, "Layer 0" custom kernels and
+ *             "Layer 2" (the tape commits accepted state deltas); the gated
+ *             delta rule is a reading.
+ *
  *   greedy    Verification with greedy sampling: keep each draft while it
  *             equals the target's argmax at its position, emit the target's
  *             argmax at the first mismatch (or at the bonus position):
@@ -567,5 +572,110 @@ int oracle_verify_greedy(const float *target_logits, const int32_t *draft_tokens
         accepted_len[b] = (int32_t)i;
         next_token[b] = (int32_t)t;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Recurrent (GDN) state: innovation tape capture and commit            */
+/* ------------------------------------------------------------------ */
+
+/* The recurrent layers of the target keep a per-head state S (dv x dk).
+ * During a speculative cycle the state is not snapshotted per position;
+ * each step records a small tuple instead, and after verification only the
+ * accepted steps are committed (MTPLX announcement, "Layer 0" custom kernels:
+ * innovation-tape GDN capture of (token, gate, state-delta) tuples, replayed
+ * on rejection instead of restoring the whole recurrent state; "Layer 2":
+ * the tape commits accepted GDN state deltas and rolls back rejected ones).
+ *
+ * The pages do not write out the GDN update; the reading is the gated delta
+ * rule of Gated DeltaNet, one head at a time:
+ *   innovation  delta_t = beta_t * (v_t - alpha_t * S_{t-1} k_t)      (dv)
+ *   state       S_t     = alpha_t * S_{t-1} + delta_t k_t^T
+ *   output      o_t     = S_t q_t                                    (dv)
+ * so the tape tuple of a step is (alpha_t, delta_t) with k_t: the state
+ * delta is the rank-1 delta_t k_t^T, the gate alpha_t.
+ *
+ * Layouts (row-major): S0, S_final [B][H][dv][dk]; q, k [B][T][H][dk];
+ * v [B][T][H][dv]; alpha, beta [B][T][H]; o, delta [B][T][H][dv].  Inputs
+ * are fp32 as a kernel sees them, everything else fp64.  S_final (nullable)
+ * gets S_T. */
+int oracle_gdn_record(const float *S0, const float *q, const float *k,
+                      const float *v, const float *alpha, const float *beta,
+                      long B, long T, long H, long dk, long dv, double *o,
+                      double *delta, double *S_final)
+{
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1)
+        return -1;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(dv * dk));
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !u) {
+        free(S); free(u);
+        return -2;
+    }
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < H; ++h) {
+            const float *s0 = S0 + (b * H + h) * dv * dk;
+            for (long e = 0; e < dv * dk; ++e)
+                S[e] = (double)s0[e];
+            for (long t = 0; t < T; ++t) {
+                const long bth = (b * T + t) * H + h;
+                const float *kt = k + bth * dk, *qt = q + bth * dk, *vt = v + bth * dv;
+                const double a = (double)alpha[bth], be = (double)beta[bth];
+                double *dt = delta + bth * dv, *ot = o + bth * dv;
+                for (long i = 0; i < dv; ++i) {          /* u = S_{t-1} k_t */
+                    double acc = 0.0;
+                    for (long c = 0; c < dk; ++c)
+                        acc += S[i * dk + c] * (double)kt[c];
+                    u[i] = acc;
+                }
+                for (long i = 0; i < dv; ++i)            /* the innovation */
+                    dt[i] = be * ((double)vt[i] - a * u[i]);
+                for (long i = 0; i < dv; ++i)            /* gated rank-1 update */
+                    for (long c = 0; c < dk; ++c)
+                        S[i * dk + c] = a * S[i * dk + c] + dt[i] * (double)kt[c];
+                for (long i = 0; i < dv; ++i) {          /* readout */
+                    double acc = 0.0;
+                    for (long c = 0; c < dk; ++c)
+                        acc += S[i * dk + c] * (double)qt[c];
+                    ot[i] = acc;
+                }
+            }
+            if (S_final)
+                for (long e = 0; e < dv * dk; ++e)
+                    S_final[(b * H + h) * dv * dk + e] = S[e];
+        }
+    free(S); free(u);
+    return 0;
+}
+
+/* Commit after verification: S_out = the state after the first n[b] steps
+ * of sequence b, rebuilt from S0 and the tape alone:
+ *   S_t = alpha_t * S_{t-1} + delta_t k_t^T,   t = 0 .. n[b] - 1,
+ * with 0 <= n[b] <= T (n[b] = 0 keeps S0: nothing committed).  delta is the
+ * tape as fp32 (what a kernel stored).  n[b] < 0 or > T is an error. */
+int oracle_gdn_commit(const float *S0, const float *alpha, const float *k,
+                      const float *delta, const int32_t *n, long B, long T,
+                      long H, long dk, long dv, double *S_out)
+{
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1)
+        return -1;
+    for (long b = 0; b < B; ++b)
+        if (n[b] < 0 || n[b] > T)
+            return -1;
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < H; ++h) {
+            double *S = S_out + (b * H + h) * dv * dk;
+            const float *s0 = S0 + (b * H + h) * dv * dk;
+            for (long e = 0; e < dv * dk; ++e)
+                S[e] = (double)s0[e];
+            for (long t = 0; t < n[b]; ++t) {
+                const long bth = (b * T + t) * H + h;
+                const double a = (double)alpha[bth];
+                for (long i = 0; i < dv; ++i)
+                    for (long c = 0; c < dk; ++c)
+                        S[i * dk + c] = a * S[i * dk + c] +
+                                        (double)delta[bth * dv + i] * (double)k[bth * dk + c];
+            }
+        }
     return 0;
 }

@@ -97,6 +97,27 @@ def logits_pair(cfg: int, B: int, D: int, V: int, draft_sd: float = 2.0,
     return target, draft
 
 
+GDN = 8   # tensor id of the recurrent-layer inputs
+
+
+def gdn_inputs(cfg: int, B: int, T: int, H: int, dk: int = 128, dv: int = 128):
+    """Inputs of T recurrent (gated delta rule) steps for B sequences x H heads,
+    fp32: S0 [B][H][dv][dk] ~ N(0, 0.1); q, k [B][T][H][dk] unit vectors
+    (normal draws scaled to length 1, as the layer normalizes them); v
+    [B][T][H][dv] ~ N(0, 1); alpha [B][T][H] ~ U(0.8, 1) (decay gates near
+    one); beta [B][T][H] ~ U(0, 1)."""
+    r = rng(cfg, GDN)
+    S0 = r.normal(0.0, 0.1, size=(B, H, dv, dk)).astype(np.float32)
+    q = r.normal(size=(B, T, H, dk))
+    k = r.normal(size=(B, T, H, dk))
+    q = (q / np.linalg.norm(q, axis=-1, keepdims=True)).astype(np.float32)
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = r.normal(size=(B, T, H, dv)).astype(np.float32)
+    alpha = r.uniform(0.8, 1.0, size=(B, T, H)).astype(np.float32)
+    beta = r.uniform(0.0, 1.0, size=(B, T, H)).astype(np.float32)
+    return S0, q, k, v, alpha, beta
+
+
 # ---- device-side generators for benchmark working sets -------------------
 # Large working sets (hundreds of MB to GB) are drawn on the GPU with torch's
 # seeded generator instead: the values differ from the numpy streams above,
@@ -143,3 +164,19 @@ def torch_uniforms(shape, seed: int, device):
     g.manual_seed(seed)
     k = torch.randint(0, 2**24, shape, generator=g, device=device, dtype=torch.int64)
     return (k.to(torch.float64) * 2.0**-24).to(torch.float32)
+
+
+def torch_gdn_inputs(B: int, T: int, H: int, seed: int, device, dk: int = 128, dv: int = 128):
+    """gdn_inputs' distributions drawn on the device (timing only)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    S0 = torch.randn((B, H, dv, dk), generator=g, device=device) * 0.1
+    q = torch.randn((B, T, H, dk), generator=g, device=device)
+    k = torch.randn((B, T, H, dk), generator=g, device=device)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((B, T, H, dv), generator=g, device=device)
+    alpha = torch.rand((B, T, H), generator=g, device=device) * 0.2 + 0.8
+    beta = torch.rand((B, T, H), generator=g, device=device)
+    return S0, q.contiguous(), k.contiguous(), v, alpha, beta
