@@ -44,6 +44,8 @@ step's launches have changed since those counters were taken.
 CPU baseline): the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
+`--gdn` times the recurrent-state capture and commit of one verify cycle
+over 36 layers (one JSON line) and exits.
 `--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
 weight copies) plus an N sweep that splits a launch's time into a fixed
 cost and an incremental bandwidth, prints one JSON line each, and exits.
@@ -82,6 +84,8 @@ def parse():
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no variants, greedy pass or CPU baseline)")
+    ap.add_argument("--gdn", action="store_true",
+                    help="only time the recurrent-state capture and commit and exit")
     ap.add_argument("--shapes", action="store_true",
                     help="only time qmv per layer shape and M (one JSON line each) and exit")
     return ap.parse_args()
@@ -104,6 +108,79 @@ SHAPES = {
 }
 # N sweep at K = 5120, M = 1: time per launch against bytes per launch.
 SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
+
+
+# Recurrent layers of the target: 36 gated-delta-rule layers of 32 heads
+# (dk = dv = 128), 8 sequences, one verify block of T = 6 positions (D = 5).
+GDN_LAYERS, GDN_B, GDN_H, GDN_T = 36, 8, 32, 6
+
+
+def gdn(dev, steps):
+    """The recurrent-state kernels of one verify cycle: per layer, the capture
+    over the T verify positions (spec_gdn_record) and, after acceptance, the
+    commit of the accepted steps (spec_gdn_commit, n = accepted + 1 drawn
+    uniformly from 1..T).  Each layer has its own state (36 x 8 x 32 heads x
+    64 KB = 604 MB, beyond the 256 MB last-level cache); one timed pass runs
+    all 36 layers back to back."""
+    import numpy as np
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    layers = []
+    for li in range(GDN_LAYERS):
+        S0, q, k, v, a, b = synth.torch_gdn_inputs(GDN_B, GDN_T, GDN_H, 7000 + li, dev)
+        layers.append(dict(S=S0, q=q, k=k, v=v, a=a, b=b,
+                           o=torch.empty_like(v), d=torch.empty_like(v)))
+    n_host = np.random.default_rng(7).integers(1, GDN_T + 1, size=GDN_B).astype(np.int32)
+    n = torch.from_numpy(n_host).to(dev)
+
+    # pre-marshalled launches, so the host stays ahead of the GPU
+    rec_calls = [spec.bind_gdn_record(L["S"], L["q"], L["k"], L["v"], L["a"], L["b"], L["o"], L["d"])
+                 for L in layers]
+    com_calls = [spec.bind_gdn_commit(L["S"], L["a"], L["k"], L["d"], n) for L in layers]
+
+    def timed(calls):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for c in calls:
+                c()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (steps * len(calls))
+
+    rec_us = timed(rec_calls)
+    com_us = timed(com_calls)
+    # After verification the commits of all layers are independent: with the
+    # layers' states and tapes laid out [layer][sequence], one launch commits
+    # the whole model (sequence index layer * B + b, step counts repeated).
+    allS = torch.empty((GDN_LAYERS * GDN_B, GDN_H, 128, 128), dtype=torch.float32, device=dev)
+    allA = torch.empty((GDN_LAYERS * GDN_B, GDN_T, GDN_H), dtype=torch.float32, device=dev)
+    allK = torch.empty((GDN_LAYERS * GDN_B, GDN_T, GDN_H, 128), dtype=torch.float32, device=dev)
+    allD = torch.empty((GDN_LAYERS * GDN_B, GDN_T, GDN_H, 128), dtype=torch.float32, device=dev)
+    for li, L in enumerate(layers):
+        sl = slice(li * GDN_B, (li + 1) * GDN_B)
+        allS[sl].copy_(L["S"]); allA[sl].copy_(L["a"]); allK[sl].copy_(L["k"]); allD[sl].copy_(L["d"])
+    del layers, rec_calls, com_calls
+    n_all = n.repeat(GDN_LAYERS)
+    all_us = timed([spec.bind_gdn_commit(allS, allA, allK, allD, n_all)]) 
+    rb = roofline.gdn_record_bytes(GDN_B, GDN_T, GDN_H)
+    cb = roofline.gdn_commit_bytes(n_host.tolist(), GDN_H)
+    out = {"gdn": (f"{GDN_LAYERS} layers x {GDN_B} sequences x {GDN_H} heads, dk=dv=128, "
+                   f"T={GDN_T} verify positions; commit steps {n_host.tolist()}"),
+           "record": {"us_per_layer": round(rec_us, 2), "bytes_per_layer": rb,
+                      "GB/s": round(rb / rec_us / 1e3, 1), "frac": round(rb / rec_us / 1e3 / 8000.0, 4)},
+           "commit": {"us_per_layer": round(com_us, 2), "bytes_per_layer": cb,
+                      "GB/s": round(cb / com_us / 1e3, 1), "frac": round(cb / com_us / 1e3 / 8000.0, 4)},
+           "commit_all_layers_one_launch": {
+               "us": round(all_us, 2), "bytes": cb * GDN_LAYERS,
+               "GB/s": round(cb * GDN_LAYERS / all_us / 1e3, 1),
+               "frac": round(cb * GDN_LAYERS / all_us / 1e3 / 8000.0, 4)},
+           "snapshot_alternative_bytes_per_layer": GDN_B * GDN_H * 128 * 128 * 4 * (GDN_T + 1)}
+    print(json.dumps(out), flush=True)
 
 
 def shapes(dev, steps):
@@ -327,6 +404,9 @@ def main():
         return
     if args.shapes:
         shapes(dev, args.steps)
+        return
+    if args.gdn:
+        gdn(dev, args.steps)
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)

@@ -263,6 +263,46 @@ spec_status spec_verify_greedy(const float *target_logits,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ------------------------------------------------------------------ */
+/* Recurrent (GDN) layer state: innovation tape capture and commit      */
+/* ------------------------------------------------------------------ */
+/*
+ * The MTPLX announcement ("Layer 0" custom kernels: innovation-tape GDN
+ * capture; "Layer 2": the tape commits accepted GDN state deltas and rolls
+ * back rejected ones) keeps the recurrent state of the target out of
+ * per-position snapshots during a speculative cycle.  Each verify position
+ * records a small tuple; after acceptance only the accepted steps are
+ * applied to the committed state.  The update is the gated delta rule, per
+ * head (the pages name GDN without writing it out; this form is a reading):
+ *     delta_t = beta_t * (v_t - alpha_t * S_{t-1} k_t)
+ *     S_t     = alpha_t * S_{t-1} + delta_t k_t^T
+ *     o_t     = S_t q_t
+ * Layouts, all fp32, row-major:
+ *  S0, S, S_final  [B][H][dv][dk], 16-byte aligned
+ *  q, k            [B][T][H][dk] (the caller normalizes them), 16-byte aligned
+ *  v, o, delta     [B][T][H][dv]
+ *  alpha, beta     [B][T][H]
+ *  dk = dv = 128, 0 <= T <= 16 (D + 1 verify positions), B * H < 2^28
+ *
+ * spec_gdn_record runs the T steps from S0 (left untouched), writes o and
+ * the tape delta, and S_T to S_final when it is not NULL.
+ * spec_gdn_commit rebuilds, in place in S (holding S0), the state after the
+ * first n_steps[b] steps of sequence b from the tape (alpha, k, delta) alone;
+ * after verification n_steps[b] = accepted_len[b] + 1 (the position of the
+ * last committed token and the accepted drafts).  n_steps[b] <= 0 leaves S
+ * unchanged (so accepted_len = -1 commits nothing), values above T count as
+ * T.  Committing n steps reproduces bitwise the S_final that spec_gdn_record
+ * returns when run for n steps.
+ */
+spec_status spec_gdn_record(const float *S0, const float *q, const float *k, const float *v,
+                            const float *alpha, const float *beta, int B, int T, int H,
+                            int dk, int dv, float *o, float *delta, float *S_final,
+                            hipStream_t stream);
+
+spec_status spec_gdn_commit(float *S, const float *alpha, const float *k, const float *delta,
+                            const int32_t *n_steps, int B, int T, int H, int dk, int dv,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,9 +16,12 @@ Names follow the C ABI:
     spec_sample_probs                filtered sampling distribution
     spec_sample_tokens               inverse-CDF draw from that distribution
     spec_verify_greedy               greedy verification (match the target argmax)
+    spec_gdn_record / spec_gdn_commit  recurrent-layer state over the verify
+                                     positions with an innovation tape, and
+                                     the commit of the accepted steps
     spec_*_workspace_size            workspace queries
     bind_qmv / bind_verify_accept /  the same calls with arguments marshalled
-    bind_verify_greedy               once, for launch loops
+    bind_verify_greedy / bind_gdn_*  once, for launch loops
 """
 from __future__ import annotations
 
@@ -90,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.spec_pack_gate_up.restype = i
         L.spec_qmv_gate_up_silu.argtypes = [i, vp, vp, vp, vp, i, i, i, i, vp]
         L.spec_qmv_gate_up_silu.restype = i
+        L.spec_gdn_record.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
+        L.spec_gdn_record.restype = i
+        L.spec_gdn_commit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.spec_gdn_commit.restype = i
         L.spec_verify_greedy_workspace.argtypes = [i, i, i]
         L.spec_verify_greedy_workspace.restype = sz
         L.spec_verify_greedy.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
@@ -489,3 +496,71 @@ def bind_verify_greedy(target_logits, draft_tokens, out=None) -> _Bound:
             _ptr(acc), _ptr(nxt), _ptr(ws), ws.numel(), _stream(dev))
     keep = (target_logits, draft_tokens, out, ws)
     return _Bound("spec_verify_greedy", lib().spec_verify_greedy, args, keep)
+
+
+def spec_gdn_record(S0, q, k, v, alpha, beta, o=None, delta=None, S_final=None,
+                    want_final: bool = False):
+    """Gated-delta-rule steps over T positions from S0 [B][H][dv][dk] (left
+    untouched) with q, k [B][T][H][dk], v [B][T][H][dv], alpha, beta
+    [B][T][H]; returns (o, delta, S_final or None)."""
+    import torch
+    dev = S0.device
+    for name, t in (("S0", S0), ("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        _require(t, torch.float32, name, dev)
+    B, H, dv, dk = S0.shape
+    T = q.shape[1]
+    if (tuple(q.shape) != (B, T, H, dk) or tuple(k.shape) != (B, T, H, dk)
+            or tuple(v.shape) != (B, T, H, dv) or tuple(alpha.shape) != (B, T, H)
+            or tuple(beta.shape) != (B, T, H)):
+        raise ValueError("shapes must be S0 [B][H][dv][dk], q/k [B][T][H][dk], v [B][T][H][dv], "
+                         "alpha/beta [B][T][H]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if delta is None:
+        delta = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if S_final is None and want_final:
+        S_final = torch.empty_like(S0)
+    st = lib().spec_gdn_record(_ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               B, T, H, dk, dv, _ptr(o), _ptr(delta), _ptr(S_final), _stream(dev))
+    _check("spec_gdn_record", st)
+    return o, delta, S_final
+
+
+def spec_gdn_commit(S, alpha, k, delta, n_steps):
+    """In place: S (holding S0, [B][H][dv][dk]) becomes the state after the
+    first n_steps[b] steps of the tape (alpha [B][T][H], k [B][T][H][dk],
+    delta [B][T][H][dv]); n_steps int32 [B]."""
+    import torch
+    dev = S.device
+    for name, t in (("S", S), ("alpha", alpha), ("k", k), ("delta", delta)):
+        _require(t, torch.float32, name, dev)
+    _require(n_steps, torch.int32, "n_steps", dev)
+    B, H, dv, dk = S.shape
+    T = alpha.shape[1]
+    st = lib().spec_gdn_commit(_ptr(S), _ptr(alpha), _ptr(k), _ptr(delta), _ptr(n_steps),
+                               B, T, H, dk, dv, _stream(dev))
+    _check("spec_gdn_commit", st)
+    return S
+
+
+def bind_gdn_record(S0, q, k, v, alpha, beta, o, delta, S_final=None) -> _Bound:
+    """spec_gdn_record on fixed tensors, marshalled once (first call checked)."""
+    spec_gdn_record(S0, q, k, v, alpha, beta, o=o, delta=delta, S_final=S_final)
+    B, H, dv, dk = S0.shape
+    T = q.shape[1]
+    args = (_ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B, T, H, dk, dv,
+            _ptr(o), _ptr(delta), _ptr(S_final), _stream(S0.device))
+    return _Bound("spec_gdn_record", lib().spec_gdn_record, args,
+                  (S0, q, k, v, alpha, beta, o, delta, S_final))
+
+
+def bind_gdn_commit(S, alpha, k, delta, n_steps, check: bool = True) -> _Bound:
+    """spec_gdn_commit on fixed tensors, marshalled once.  The commit works in
+    place, so the checked first call (check=True) already applies it once."""
+    if check:
+        spec_gdn_commit(S, alpha, k, delta, n_steps)
+    B, H, dv, dk = S.shape
+    T = alpha.shape[1]
+    args = (_ptr(S), _ptr(alpha), _ptr(k), _ptr(delta), _ptr(n_steps), B, T, H, dk, dv,
+            _stream(S.device))
+    return _Bound("spec_gdn_commit", lib().spec_gdn_commit, args, (S, alpha, k, delta, n_steps))

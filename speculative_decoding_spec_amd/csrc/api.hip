@@ -4,6 +4,7 @@
 #include "../../include/spec.h"
 #include "spec_internal.h"
 
+#include <climits>
 #include <cmath>
 
 namespace {
@@ -342,6 +343,50 @@ spec_status spec_verify_greedy(const float *target_logits,
         return SPEC_ERR_WORKSPACE;
     if (spec::launch_greedy(target_logits, draft_tokens, plan, accepted_len,
                             next_token, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_gdn_record(const float *S0, const float *q, const float *k, const float *v,
+                            const float *alpha, const float *beta, int B, int T, int H,
+                            int dk, int dv, float *o, float *delta, float *S_final,
+                            hipStream_t stream) {
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1)
+        return SPEC_ERR_INVALID;
+    if (dk != 128 || dv != 128 || T > kMaxD + 1 || (int64_t)B * H >= (1 << 28))
+        return SPEC_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0)
+        return SPEC_OK;
+    if (!S0 || (T > 0 && (!q || !k || !v || !alpha || !beta || !o || !delta)))
+        return SPEC_ERR_INVALID;
+    if (!aligned16(S0) || (S_final && !aligned16(S_final)) ||
+        (T > 0 && (!aligned16(q) || !aligned16(k))))
+        return SPEC_ERR_UNSUPPORTED;
+    if (T > 0 && (!aligned4(v) || !aligned4(alpha) || !aligned4(beta) || !aligned4(o) ||
+                  !aligned4(delta)))
+        return SPEC_ERR_INVALID;
+    if (spec::launch_gdn_record(S0, q, k, v, alpha, beta, B, T, H, o, delta, S_final, stream) !=
+        hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_gdn_commit(float *S, const float *alpha, const float *k, const float *delta,
+                            const int32_t *n_steps, int B, int T, int H, int dk, int dv,
+                            hipStream_t stream) {
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1)
+        return SPEC_ERR_INVALID;
+    if (dk != 128 || dv != 128 || T > kMaxD + 1 || (int64_t)B * H >= (1 << 28))
+        return SPEC_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0)
+        return SPEC_OK;
+    if (!S || !alpha || !k || !delta || !n_steps)
+        return SPEC_ERR_INVALID;
+    if (!aligned16(S) || !aligned16(k))
+        return SPEC_ERR_UNSUPPORTED;
+    if (!aligned4(alpha) || !aligned4(delta) || !aligned4(n_steps))
+        return SPEC_ERR_INVALID;
+    if (spec::launch_gdn_commit(S, alpha, k, delta, n_steps, B, T, H, stream) != hipSuccess)
         return SPEC_ERR_DEVICE;
     return SPEC_OK;
 }

@@ -95,4 +95,13 @@ hipError_t launch_greedy(const float *target, const int32_t *draft_tokens,
                          const GreedyPlan &plan, int32_t *accepted_len,
                          int32_t *next_token, void *ws, hipStream_t stream);
 
+// ----------------------------------------------------------- recurrent ----
+// Gated-delta-rule state (dk = dv = 128) over T steps with the innovation
+// tape, and the commit of the first n[b] steps from the tape.
+hipError_t launch_gdn_record(const float *S0, const float *q, const float *k, const float *v,
+                             const float *alpha, const float *beta, int B, int T, int H,
+                             float *o, float *delta, float *S_final, hipStream_t stream);
+hipError_t launch_gdn_commit(float *S, const float *alpha, const float *k, const float *delta,
+                             const int32_t *n_steps, int B, int T, int H, hipStream_t stream);
+
 } // namespace spec

@@ -30,6 +30,23 @@ def gate_up_silu_bytes(bits: int, M: int, F: int, K: int, group: int = 64) -> in
     return 2 * F * K * bits // 8 + 2 * F * (K // group) * 4 + M * K * 2 + M * F * 2
 
 
+def gdn_record_bytes(B: int, T: int, H: int, d: int = 128) -> int:
+    """Bytes of the recurrent capture over T steps: each head's state read
+    once, q, k, v, alpha, beta read, o and the tape delta written."""
+    return B * H * d * d * 4 + B * T * H * (3 * d + 2) * 4 + 2 * B * T * H * d * 4
+
+
+def gdn_commit_bytes(n_steps, H: int, d: int = 128) -> int:
+    """Bytes of the commit: for every sequence with n >= 1 steps, its heads'
+    states read and written once and n steps of (alpha, k, delta) read; the
+    step counts themselves."""
+    total = 4 * len(n_steps)
+    for n in n_steps:
+        if n > 0:
+            total += 2 * H * d * d * 4 + n * H * (2 * d + 1) * 4
+    return total
+
+
 def qmv_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 

@@ -174,3 +174,23 @@ def test_greedy_validation(L):
     # a single row splits into chunks of whole 1024-logit multiples
     assert L.spec_verify_greedy_workspace(1, 0, 151936) == 75 * 16
     assert L.spec_verify_greedy_workspace(0, 0, 1000) == 0
+
+
+def test_gdn_validation(L):
+    def rec(S0=P, q=P, k=P, v=P, a=P, b=P, B=2, T=6, H=4, dk=128, dv=128, o=P, d=P, sf=None):
+        return L.spec_gdn_record(S0, q, k, v, a, b, B, T, H, dk, dv, o, d, sf, None)
+
+    def com(S=P, a=P, k=P, d=P, n=P, B=2, T=6, H=4, dk=128, dv=128):
+        return L.spec_gdn_commit(S, a, k, d, n, B, T, H, dk, dv, None)
+
+    assert rec(B=-1) == INVALID and rec(T=-1) == INVALID and rec(dk=0) == INVALID
+    assert rec(dk=64) == UNSUPPORTED and rec(dv=256) == UNSUPPORTED
+    assert rec(T=17) == UNSUPPORTED
+    assert rec(B=1 << 15, H=1 << 15) == UNSUPPORTED
+    assert rec(S0=None) == INVALID and rec(q=None) == INVALID and rec(d=None) == INVALID
+    assert rec(S0=MIS) == UNSUPPORTED and rec(k=MIS) == UNSUPPORTED
+    assert rec(B=0) == OK and rec(H=0) == OK
+    assert com(B=-1) == INVALID and com(dk=64) == UNSUPPORTED and com(T=17) == UNSUPPORTED
+    assert com(S=None) == INVALID and com(n=None) == INVALID
+    assert com(S=MIS) == UNSUPPORTED
+    assert com(T=0) == OK and com(B=0) == OK

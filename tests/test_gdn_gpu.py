@@ -1,0 +1,167 @@
+"""GPU parity of the recurrent-state kernels (spec_gdn_record: T gated-delta-
+rule steps with the innovation tape; spec_gdn_commit: the first n steps
+rebuilt from the tape) against the fp64 oracle, and the bitwise rollback
+property the pages claim for the tape.
+
+Tolerance: a first-order rounding-error bound carried along the recurrence
+(unit roundoff u = 2^-24).  The kernel's dot products pass every product
+through at most 9 roundings (a 4-term fused chain, two pair sums, a 3-step
+butterfly across lanes); the bound below uses 21, which also covers other
+summation trees.  The innovation adds three roundings, and the update
+S' = fma(a, S, fl(d k)) two.  With magnitudes taken from an fp64 transcription,
+    e_u     = E_S |k| + 21 u sum_c |S_ic k_c|
+    e_delta = |beta| |alpha| e_u + 3 u |beta| (|v| + |alpha u|)
+    E_S'    = |alpha| E_S + e_delta |k|^T + 2 u (|alpha S| + |delta k^T|)
+    e_o     = E_S' |q| + 21 u sum_c |S'_ic q_c|
+and outputs must lie within twice these bounds (second-order terms are far
+below the factor two at these sizes).  The commit of n steps must equal the
+recording of n steps bit for bit: both apply the same update to the same
+fp32 values."""
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_spec_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0**-24
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def T_(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def error_bounds(S0, q, k, v, a, b):
+    """First-order bounds (E_S after the last step, e_delta, e_o) for the fp32
+    recurrence; magnitudes from an fp64 transcription."""
+    S = S0.astype(np.float64)
+    E = np.zeros_like(S)
+    B, T, H, dk = q.shape
+    ed_all = np.zeros(v.shape)
+    eo_all = np.zeros(v.shape)
+    for t in range(T):
+        kt, qt, vt = (x[:, t].astype(np.float64) for x in (k, q, v))      # [B][H][d]
+        at = a[:, t].astype(np.float64)[..., None]
+        bt = b[:, t].astype(np.float64)[..., None]
+        u = np.einsum("bhic,bhc->bhi", S, kt)
+        e_u = np.einsum("bhic,bhc->bhi", E, np.abs(kt)) + 21 * U * np.einsum(
+            "bhic,bhc->bhi", np.abs(S), np.abs(kt))
+        d = bt * (vt - at * u)
+        e_d = np.abs(bt) * np.abs(at) * e_u + 3 * U * np.abs(bt) * (np.abs(vt) + np.abs(at * u))
+        outer = d[..., :, None] * kt[..., None, :]
+        E = (np.abs(at)[..., None] * E + e_d[..., :, None] * np.abs(kt)[..., None, :]
+             + 2 * U * (np.abs(at[..., None] * S) + np.abs(outer)))
+        S = at[..., None] * S + outer
+        e_o = np.einsum("bhic,bhc->bhi", E, np.abs(qt)) + 21 * U * np.einsum(
+            "bhic,bhc->bhi", np.abs(S), np.abs(qt))
+        ed_all[:, t] = e_d
+        eo_all[:, t] = e_o
+    return E, ed_all, eo_all
+
+
+def gpu_record(inp, dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    t = [T_(x, dev) for x in inp]
+    o, d, sf = spec.spec_gdn_record(*t, want_final=True)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), d.cpu().numpy(), sf.cpu().numpy()
+
+
+def check_record(inp, dev):
+    o, d, sf = gpu_record(inp, dev)
+    ref = oracle.gdn_record(*inp)
+    E, ed, eo = error_bounds(*inp)
+    bad = [(name, int((np.abs(g - r) > 2 * e + 1e-30).sum()))
+           for name, g, r, e in (("o", o, ref["o"], eo), ("delta", d, ref["delta"], ed),
+                                 ("S_final", sf, ref["S_final"], E))]
+    worst = max(float(np.max(np.abs(g - r) / (2 * e + 1e-30)))
+                for g, r, e in ((o, ref["o"], eo), (d, ref["delta"], ed), (sf, ref["S_final"], E)))
+    print(f"record B,T,H={inp[1].shape[:3]}: outside bound {bad}, worst err/bound={worst:.3f}",
+          flush=True)
+    assert all(n == 0 for _, n in bad)
+    return o, d, sf
+
+
+@pytest.mark.parametrize("B,T,H", [(3, 6, 5), (2, 16, 3), (4, 1, 2), (1, 4, 1)])
+def test_record_parity(dev, B, T, H):
+    check_record(synth.gdn_inputs(900 + T, B, T, H), dev)
+
+
+def test_record_zero_steps_copies_the_state(dev):
+    S0, q, k, v, a, b = synth.gdn_inputs(910, 2, 0, 3)
+    _, _, sf = gpu_record((S0, q, k, v, a, b), dev)
+    assert np.array_equal(sf.view(np.uint32), S0.view(np.uint32))
+
+
+def test_commit_reproduces_the_recording_bitwise(dev):
+    """The tape rollback of the pages: committing the first n steps gives
+    exactly the state the recurrence reached after n steps, for every n."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    B, T, H = 7, 6, 4
+    S0, q, k, v, a, b = synth.gdn_inputs(911, B, T, H)
+    _, d_full, _ = gpu_record((S0, q, k, v, a, b), dev)
+    n = np.array([0, 1, 2, 3, 4, 5, 6], np.int32)
+    S = T_(S0, dev)
+    spec.spec_gdn_commit(S, T_(a, dev), T_(k, dev), T_(d_full, dev), T_(n, dev))
+    torch.cuda.synchronize()
+    got = S.cpu().numpy()
+    for i in range(B):
+        m = int(n[i])
+        sl = lambda x: x[i:i + 1, :m]
+        _, _, sf = gpu_record((S0[i:i + 1], sl(q), sl(k), sl(v), sl(a), sl(b)), dev)
+        assert np.array_equal(got[i].view(np.uint32), sf[0].view(np.uint32)), m
+
+
+def test_commit_parity_and_step_counts(dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    B, T, H = 6, 5, 3
+    S0, q, k, v, a, b = synth.gdn_inputs(912, B, T, H)
+    _, d_gpu, _ = gpu_record((S0, q, k, v, a, b), dev)
+    n = np.array([-1, 0, 2, 5, 9, 3], np.int32)     # below 0 and above T included
+    S = T_(S0, dev)
+    spec.spec_gdn_commit(S, T_(a, dev), T_(k, dev), T_(d_gpu, dev), T_(n, dev))
+    torch.cuda.synchronize()
+    got = S.cpu().numpy()
+    n_eff = np.clip(n, 0, T)
+    ref = oracle.gdn_commit(S0, a, k, d_gpu, n_eff)
+    # bound: n steps of fma(a, S, fl(d k)), two roundings each
+    mag = np.abs(S0.astype(np.float64))
+    bound = np.zeros_like(mag)
+    for t in range(T):
+        live = (t < n_eff)[:, None, None, None]
+        at = np.abs(a[:, t].astype(np.float64))[..., None, None]
+        dk = np.abs(d_gpu[:, t].astype(np.float64))[..., :, None] * np.abs(k[:, t].astype(np.float64))[..., None, :]
+        bound = np.where(live, at * bound + 2 * U * (at * mag + dk), bound)
+        mag = np.where(live, at * mag + dk, mag)
+    assert np.all(np.abs(got - ref) <= 2 * bound + 1e-30)
+    for i in (0, 1):                                  # nothing committed: untouched
+        assert np.array_equal(got[i].view(np.uint32), S0[i].view(np.uint32))
+
+
+def test_bench_shape_sampled_heads(dev):
+    """The benchmark's shape (B = 8 sequences, H = 32 heads, T = 6), every head
+    recorded on the GPU, 24 heads checked against the oracle."""
+    B, T, H = 8, 6, 32
+    inp = synth.gdn_inputs(913, B, T, H)
+    o, d, sf = gpu_record(inp, dev)
+    rng = np.random.default_rng(913)
+    for bi, hi in zip(rng.integers(0, B, 24), rng.integers(0, H, 24)):
+        sub = tuple(x[bi:bi + 1, hi:hi + 1] if x.ndim == 4 and x is inp[0] else
+                    x[bi:bi + 1, :, hi:hi + 1] for x in inp)
+        ref = oracle.gdn_record(*sub)
+        E, ed, eo = error_bounds(*sub)
+        assert np.all(np.abs(o[bi:bi + 1, :, hi:hi + 1] - ref["o"]) <= 2 * eo + 1e-30)
+        assert np.all(np.abs(d[bi:bi + 1, :, hi:hi + 1] - ref["delta"]) <= 2 * ed + 1e-30)
+        assert np.all(np.abs(sf[bi:bi + 1, hi:hi + 1] - ref["S_final"]) <= 2 * E + 1e-30)
