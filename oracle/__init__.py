@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_gdn_record.restype = i
         L.oracle_gdn_commit.argtypes = [vp, vp, vp, vp, vp, lg, lg, lg, lg, lg, vp]
         L.oracle_gdn_commit.restype = i
+        L.oracle_float_to_half.argtypes = [ctypes.c_float]
+        L.oracle_float_to_half.restype = ctypes.c_uint16
+        L.oracle_requantize_w4.argtypes = [vp, lg, lg, lg, vp, vp, vp]
+        L.oracle_requantize_w4.restype = i
         L.oracle_verify_greedy.argtypes = [vp, vp, lg, lg, lg, vp, vp]
         L.oracle_verify_greedy.restype = i
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
@@ -272,3 +276,22 @@ def gdn_commit(S0, alpha, k, delta, n) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle_gdn_commit failed (rc={rc})")
     return out
+
+
+def requantize_w4(w_bf16: np.ndarray, group: int = 64):
+    """(w4 uint32 [N][K/8], scales fp16 bits [N][K/G], biases fp16 bits) from
+    bf16 bit patterns [N][K]: the draft-only 4-bit copy of a weight matrix."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    N, K = w.shape
+    w4 = np.empty((N, K // 8), np.uint32)
+    s = np.empty((N, K // group), np.uint16)
+    b = np.empty((N, K // group), np.uint16)
+    rc = lib().oracle_requantize_w4(_ptr(w), N, K, group, _ptr(w4), _ptr(s), _ptr(b))
+    if rc != 0:
+        raise ValueError(f"oracle_requantize_w4 rejected its arguments (rc={rc})")
+    return w4, s, b
+
+
+def float_to_half(f: float) -> int:
+    """Nearest-even binary16 bit pattern of a float32 value."""
+    return int(lib().oracle_float_to_half(float(f)))

@@ -43,6 +43,10 @@
  *             "Layer 2" (the tape commits accepted state deltas); the gated
  *             delta rule is a reading.
  *
+ *   requantize_w4
+ *             The draft-only 4-bit LM head: MTPLX announcement, "Layer 0"
+ *             custom kernels; the min/max affine fit is a reading.
+ *
  *   greedy    Verification with greedy sampling: keep each draft while it
  *             equals the target's argmax at its position, emit the target's
  *             argmax at the first mismatch (or at the bonus position):
@@ -677,5 +681,87 @@ int oracle_gdn_commit(const float *S0, const float *alpha, const float *k,
                                         (double)delta[bth * dv + i] * (double)k[bth * dk + c];
             }
         }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Draft-only 4-bit LM head: requantization                             */
+/* ------------------------------------------------------------------ */
+
+/* The target keeps its LM head at model precision; a separate 4-bit copy is
+ * built in memory for drafting only (MTPLX announcement, "Layer 0" custom
+ * kernels: draft-only requantised LM head, draft time down 29%).  The pages
+ * do not give the quantizer; the reading is the affine group quantization
+ * the qmv path reads (ŵ = s q + b, groups of G along K, codes 0..15), with
+ * the usual min/max fit per group:
+ *   b = min_g w,  s = (max_g w - min_g w) / 15   (fp32, then to fp16, nearest even)
+ *   q = round_half_even((w - b16) / s16) clamped to 0..15   (fp32)
+ *   q = 0 where s16 is 0 or not finite.
+ * The code is an integer decided by floating point, so it is decided in the
+ * kernel's precision (fp32 subtraction and division, correctly rounded), not
+ * in fp64.  Source: bf16 bit patterns [N][K]; outputs in the interchange
+ * layout of the qmv path: W4 words [N][K/8] (element k at bits 4*(k%8) of
+ * word k/8), fp16 scales and biases [N][K/G]. */
+/* Nearest-even binary16 bit pattern of a float (11 significant bits,
+ * normal exponents -14..15, subnormal ulp 2^-24, overflow to infinity). */
+static uint16_t float_to_half_bits(float f)
+{
+    double v = (double)f;
+    if (isnan(v))
+        return 0x7E00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    v = fabs(v);
+    if (v == 0.0)
+        return sign;
+    int e;
+    frexp(v, &e);                       /* v = m * 2^e, m in [0.5, 1) */
+    int ulp_exp = e - 11;
+    if (ulp_exp < -24)
+        ulp_exp = -24;
+    double r = ldexp(nearbyint(ldexp(v, -ulp_exp)), ulp_exp);
+    if (r >= 65536.0)
+        return sign | 0x7C00;
+    if (r < ldexp(1.0, -14))            /* subnormal (or rounded up to 2^-14) */
+        return sign | (uint16_t)ldexp(r, 24);
+    frexp(r, &e);
+    int E = e - 1;                      /* r = 1.f * 2^E */
+    uint16_t mant = (uint16_t)(ldexp(r, -E) * 1024.0 - 1024.0);
+    return sign | (uint16_t)((E + 15) << 10) | mant;
+}
+
+uint16_t oracle_float_to_half(float f) { return float_to_half_bits(f); }
+
+int oracle_requantize_w4(const uint16_t *w_bf16, long N, long K, long G,
+                         uint32_t *w4, uint16_t *scales, uint16_t *biases)
+{
+    if (N < 0 || K < 0 || G <= 0 || K % G != 0 || K % 8 != 0)
+        return -1;
+    long ng = K / G;
+    for (long n = 0; n < N; ++n) {
+        for (long k8 = 0; k8 < K / 8; ++k8)
+            w4[n * (K / 8) + k8] = 0;
+        for (long g = 0; g < ng; ++g) {
+            float lo = INFINITY, hi = -INFINITY;
+            for (long k = g * G; k < (g + 1) * G; ++k) {
+                float v = (float)bf16_to_double(w_bf16[n * K + k]);
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            float sf = (hi - lo) / 15.0f;
+            uint16_t s16 = float_to_half_bits(sf), b16 = float_to_half_bits(lo);
+            scales[n * ng + g] = s16;
+            biases[n * ng + g] = b16;
+            float s = (float)half_to_double(s16), b = (float)half_to_double(b16);
+            for (long k = g * G; k < (g + 1) * G; ++k) {
+                unsigned q = 0;
+                if (s != 0.0f && isfinite(s)) {
+                    float v = (float)bf16_to_double(w_bf16[n * K + k]);
+                    float r = nearbyintf((v - b) / s);
+                    q = r < 0.0f ? 0u : (r > 15.0f ? 15u : (unsigned)r);
+                }
+                w4[n * (K / 8) + k / 8] |= (uint32_t)q << (4 * (k % 8));
+            }
+        }
+    }
     return 0;
 }

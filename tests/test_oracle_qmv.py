@@ -232,3 +232,85 @@ def test_gate_up_silu_closed_forms():
     g = oracle.qmv(8, *gp, x, G)
     u = oracle.qmv(8, *up, x, G)
     np.testing.assert_allclose(hp - hm, g * u, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------ draft-only 4-bit requantization ----
+
+def test_float_to_half_matches_numpy():
+    # numpy's float32 -> float16 conversion is nearest-even: agree on normal,
+    # subnormal, overflowing and halfway values
+    rng = np.random.default_rng(8)
+    a = np.concatenate([rng.normal(0, 3, 4000), rng.normal(0, 1e-5, 2000),
+                        rng.normal(0, 3e4, 1000),
+                        [65504, 65519.99, 65520, 2.0**-25, 3 * 2.0**-26, 1 + 2.0**-11]]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = a.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(float(v)) for v in a], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def _bf16(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_requantize_recovers_grid_values_exactly():
+    # weights on the affine grid b + s q with s, b exact in fp16 and the
+    # group's min and max present: codes, scales and biases come back exactly
+    rng = np.random.default_rng(9)
+    N, K, G = 6, 128, 64
+    q = rng.integers(0, 16, size=(N, K))
+    q[:, ::G] = 0
+    q[:, 1::G] = 15
+    # power-of-two steps and biases on a 1/32 grid: every b + s q is an
+    # integer over 32 below 2^7, exact in bf16 (8 significant bits) and fp16
+    s = (2.0 ** -rng.integers(3, 6, size=(N, K // G))).astype(np.float32)
+    b = (rng.integers(-32, 33, size=(N, K // G)) / 32.0).astype(np.float32)
+    w = q * np.repeat(s, G, axis=1) + np.repeat(b, G, axis=1)
+    wb = _bf16(w)
+    assert np.array_equal(synth.bf16_bits_to_f32(wb), w.astype(np.float32))  # exact in bf16
+    w4, s16, b16 = oracle.requantize_w4(wb, G)
+    assert np.array_equal(s16.view(np.float16).astype(np.float32), s)
+    assert np.array_equal(b16.view(np.float16).astype(np.float32), b)
+    shifts = 4 * np.arange(8, dtype=np.uint32)
+    codes = ((w4[:, :, None] >> shifts) & 0xF).reshape(N, K)
+    assert np.array_equal(codes, q)
+
+
+def test_requantize_error_is_at_most_half_a_step():
+    rng = np.random.default_rng(10)
+    N, K, G = 8, 256, 64
+    wb = _bf16(rng.normal(0, 0.05, size=(N, K)))
+    w = synth.bf16_bits_to_f32(wb).astype(np.float64)
+    w4, s16, b16 = oracle.requantize_w4(wb, G)
+    s = np.repeat(s16.view(np.float16).astype(np.float64), G, axis=1)
+    b = np.repeat(b16.view(np.float16).astype(np.float64), G, axis=1)
+    shifts = 4 * np.arange(8, dtype=np.uint32)
+    q = ((w4[:, :, None] >> shifts) & 0xF).reshape(N, K)
+    err = np.abs(q * s + b - w)
+    # half a step, plus what the fp16 rounding of s and b can add at the ends
+    slack = 15 * np.abs(s) * 2.0**-11 + np.abs(b) * 2.0**-11 + 1e-12
+    assert np.all(err <= s / 2 + slack)
+    # and the codes use the whole range in every group
+    assert np.all(q.reshape(N, K // G, G).min(axis=2) == 0)
+    assert np.all(q.reshape(N, K // G, G).max(axis=2) == 15)
+
+
+def test_requantize_ties_and_constant_groups():
+    G = 64
+    # a constant group: scale 0, codes 0, the bias carries the value
+    w = np.full((1, G), 0.375, np.float32)
+    w4, s16, b16 = oracle.requantize_w4(_bf16(w), G)
+    assert s16[0, 0] == 0 and b16.view(np.float16)[0, 0] == 0.375 and np.all(w4 == 0)
+    # min 0, max 15 (step 1): a value 2.5 lies halfway, nearest even is 2;
+    # 3.5 rounds to 4
+    w = np.zeros((1, G), np.float32)
+    w[0, 1] = 15.0
+    w[0, 2] = 2.5
+    w[0, 3] = 3.5
+    w4, s16, b16 = oracle.requantize_w4(_bf16(w), G)
+    q = [(int(w4[0, 0]) >> (4 * i)) & 0xF for i in range(4)]
+    assert q == [0, 15, 2, 4]
+    # requantized codes feed the qmv oracle like any other W4 matrix
+    x = synth.activations(11, 2, G)
+    y = oracle.qmv(4, w4, s16, b16, x, G)
+    assert y.shape == (2, 1) and np.all(np.isfinite(y))
