@@ -44,6 +44,8 @@ step's launches have changed since those counters were taken.
 CPU baseline): the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
+`--draft` times the draft step: the LM head at M = 1 (a 4-bit copy built by
+`spec_requantize_w4`, and an 8-bit head for comparison) and one draw.
 `--gdn` times the recurrent-state capture and commit of one verify cycle
 over 36 layers (one JSON line) and exits.
 `--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
@@ -84,6 +86,8 @@ def parse():
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no variants, greedy pass or CPU baseline)")
+    ap.add_argument("--draft", action="store_true",
+                    help="only time the draft step (4-bit LM head copy + sampling) and exit")
     ap.add_argument("--gdn", action="store_true",
                     help="only time the recurrent-state capture and commit and exit")
     ap.add_argument("--shapes", action="store_true",
@@ -108,6 +112,76 @@ SHAPES = {
 }
 # N sweep at K = 5120, M = 1: time per launch against bytes per launch.
 SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
+
+
+def draft(dev, steps):
+    """The draft side of a cycle (one drafted token): the LM head at M = 1,
+    then one draw from its distribution (T = 0.6).  The draft-only 4-bit head
+    is built from a bf16 head by spec_requantize_w4 (a load-time step, timed
+    once); the comparison keeps the head at 8 bits, standing in for the
+    target's model-precision head.  Weight copies rotate so that nothing is
+    served from the 256 MB last-level cache."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    V, K = 151936, HIDDEN
+    g = torch.Generator(device=dev)
+    g.manual_seed(8100)
+    heads4 = []
+    req_us = None
+    for c in range(3):
+        w = (torch.randn((V, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q4 = spec.spec_requantize_w4(w)
+        e1.record()
+        torch.cuda.synchronize()
+        if req_us is None:
+            req_us = e0.elapsed_time(e1) * 1e3
+        del w
+        heads4.append(spec.spec_pack_w4(*q4, G=GROUP))
+        del q4
+    heads8 = [spec.spec_pack_w8(*synth.torch_qweights(8, V, K, GROUP, 8200 + c, dev), G=GROUP)
+              for c in range(2)]
+    x = synth.torch_activations(1, K, 8300, dev)
+    logits = torch.empty((1, V), dtype=torch.float32, device=dev)
+    u = synth.torch_uniforms((1,), 8301, dev)
+    sample = spec.bind_sample_tokens(logits, u, ACC_T)
+
+    def timed(heads):
+        calls = [spec.bind_qmv(h, x, logits) for h in heads]
+        for c in calls:
+            c()
+            sample()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b_, c_) in enumerate(ev):
+            a.record()
+            calls[i % len(calls)]()
+            b_.record()
+            sample()
+            c_.record()
+        torch.cuda.synchronize()
+        head = sum(a.elapsed_time(b_) for a, b_, _ in ev) / steps * 1e3
+        samp = sum(b_.elapsed_time(c_) for _, b_, c_ in ev) / steps * 1e3
+        return head, samp
+
+    h4, s4 = timed(heads4)
+    h8, s8 = timed(heads8)
+    b4 = roofline.qmv_bytes(4, 1, V, K)
+    b8 = roofline.qmv_bytes(8, 1, V, K)
+    out = {"draft": f"LM head {K}->{V} at M=1, then one draw (T={ACC_T}) from its logits",
+           "w4_draft_head": {"head_us": round(h4, 2), "sample_us": round(s4, 2),
+                             "step_us": round(h4 + s4, 2), "head_GB/s": round(b4 / h4 / 1e3, 1),
+                             "head_frac": round(b4 / h4 / 1e3 / 8000.0, 4)},
+           "w8_head": {"head_us": round(h8, 2), "sample_us": round(s8, 2),
+                       "step_us": round(h8 + s8, 2), "head_GB/s": round(b8 / h8 / 1e3, 1),
+                       "head_frac": round(b8 / h8 / 1e3 / 8000.0, 4)},
+           "draft_step_reduction": round(1.0 - (h4 + s4) / (h8 + s8), 4),
+           "requantize_us_once": round(req_us, 1)}
+    print(json.dumps(out), flush=True)
 
 
 # Recurrent layers of the target: 36 gated-delta-rule layers of 32 heads
@@ -407,6 +481,9 @@ def main():
         return
     if args.gdn:
         gdn(dev, args.steps)
+        return
+    if args.draft:
+        draft(dev, args.steps)
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)

@@ -120,6 +120,28 @@ spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
                         int G, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Draft-only 4-bit copy of a weight matrix                             */
+/* ------------------------------------------------------------------ */
+/*
+ * The target keeps its LM head at model precision; a separate 4-bit copy is
+ * built in memory and used only for drafting (MTPLX announcement, "Layer 0"
+ * custom kernels: draft-only requantised LM head, 29% less draft time).  The
+ * quantizer is the min/max affine fit of the qmv path's format (a reading):
+ * per row and group of G = 64 along K,
+ *   b = min w,  s = (max w - min w) / 15  (fp32, rounded to nearest-even fp16),
+ *   q = round_half_even((w - b) / s) with the fp16 s and b, in fp32,
+ *       clamped to 0..15 (0 where s is 0 or not finite).
+ *  w_bf16  bf16 bit patterns [N][K], 16-byte aligned; K % 64 == 0
+ *  w4      uint32 [N][K/8] out (element k at bits 4*(k%8) of word k/8),
+ *          16-byte aligned: the interchange layout of spec_pack_w4
+ *  scales, biases  fp16 bit patterns [N][K/64] out
+ * Results are bitwise deterministic (the codes are integer decisions taken
+ * in fp32 with correctly rounded operations).
+ */
+spec_status spec_requantize_w4(const uint16_t *w_bf16, int N, int K, int G, uint32_t *w4,
+                               uint16_t *scales, uint16_t *biases, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Gated MLP activation: h = silu(x G^T) * (x U^T), one launch           */
 /* ------------------------------------------------------------------ */
 /*

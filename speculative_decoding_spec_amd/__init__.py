@@ -10,6 +10,7 @@ Names follow the C ABI:
 
     spec_pack_w4 / spec_pack_w8      one-time repack of quantized weights
     spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv
+    spec_requantize_w4               draft-only 4-bit copy of a bf16 matrix
     spec_pack_gate_up /              gate and up projections as one launch with
     spec_qmv_gate_up_silu            the SiLU-gated activation applied (bf16 out)
     spec_verify_accept               ratio acceptance + residual / bonus draw
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.spec_sample_probs.argtypes = [vp, i, i, f, i, f, vp, vp, sz, vp]
         L.spec_sample_probs.restype = i
         L.spec_sample_tokens.argtypes = [vp, i, i, f, i, f, vp, vp, vp, sz, vp]
+        L.spec_requantize_w4.argtypes = [vp, i, i, i, vp, vp, vp, vp]
+        L.spec_requantize_w4.restype = i
         L.spec_gate_up_packed_rows.argtypes = [i]
         L.spec_gate_up_packed_rows.restype = i
         L.spec_pack_gate_up.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
@@ -564,3 +567,39 @@ def bind_gdn_commit(S, alpha, k, delta, n_steps, check: bool = True) -> _Bound:
     args = (_ptr(S), _ptr(alpha), _ptr(k), _ptr(delta), _ptr(n_steps), B, T, H, dk, dv,
             _stream(S.device))
     return _Bound("spec_gdn_commit", lib().spec_gdn_commit, args, (S, alpha, k, delta, n_steps))
+
+
+def spec_requantize_w4(w_bf16, G: int = 64):
+    """(w int32 [N][K/8], scales fp16 [N][K/G], biases fp16 [N][K/G]): the
+    draft-only 4-bit copy of a bf16 [N][K] matrix, in spec_pack_w4's input
+    layout."""
+    import torch
+    dev = w_bf16.device
+    _require(w_bf16, torch.bfloat16, "w_bf16", dev)
+    N, K = w_bf16.shape
+    if G <= 0 or K % G or K % 8:
+        raise ValueError("K must be a multiple of G and of 8")
+    w4 = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    s = torch.empty((N, K // G), dtype=torch.float16, device=dev)
+    b = torch.empty((N, K // G), dtype=torch.float16, device=dev)
+    st = lib().spec_requantize_w4(_ptr(w_bf16), N, K, G, _ptr(w4), _ptr(s), _ptr(b), _stream(dev))
+    _check("spec_requantize_w4", st)
+    return w4, s, b
+
+
+def bind_sample_tokens(logits, uniforms, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                       tokens=None) -> _Bound:
+    """spec_sample_tokens on fixed tensors, marshalled once (first call
+    checked), with a workspace of its own."""
+    import torch
+    dev = logits.device
+    R, V = logits.shape
+    if tokens is None:
+        tokens = torch.empty(R, dtype=torch.int32, device=dev)
+    need = spec_sample_workspace_size(R, V, top_k)
+    ws = torch.empty(max(need, 4096), dtype=torch.uint8, device=dev)
+    spec_sample_tokens(logits, uniforms, temperature, top_k, top_p, tokens=tokens, workspace=ws)
+    args = (_ptr(logits), R, V, ctypes.c_float(temperature), int(top_k), ctypes.c_float(top_p),
+            _ptr(uniforms), _ptr(tokens), _ptr(ws), ws.numel(), _stream(dev))
+    return _Bound("spec_sample_tokens", lib().spec_sample_tokens, args,
+                  (logits, uniforms, tokens, ws))

@@ -141,6 +141,25 @@ spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
     return qmv_common(8, w_packed, sb_packed, x, y, M, N, K, G, stream);
 }
 
+spec_status spec_requantize_w4(const uint16_t *w_bf16, int N, int K, int G, uint32_t *w4,
+                               uint16_t *scales, uint16_t *biases, hipStream_t stream) {
+    if (N < 0 || K < 0 || G <= 0 || K % G != 0)
+        return SPEC_ERR_INVALID;
+    if (G != 64)
+        return SPEC_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0)
+        return SPEC_OK;
+    if (!w_bf16 || !w4 || !scales || !biases)
+        return SPEC_ERR_INVALID;
+    if (!aligned16(w_bf16) || !aligned16(w4))
+        return SPEC_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) & 1u)
+        return SPEC_ERR_INVALID;
+    if (spec::launch_requantize_w4(w_bf16, N, K, w4, scales, biases, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
 int spec_gate_up_packed_rows(int F) {
     if (F < 0 || F > (1 << 27))
         return 0;

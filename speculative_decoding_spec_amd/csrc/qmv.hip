@@ -489,6 +489,60 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     }
 }
 
+// Draft-only 4-bit copy of a weight matrix (MTPLX announcement, "Layer 0"
+// custom kernels: the target's LM head stays at model precision, a 4-bit
+// copy serves drafting).  One thread per (row, 64-group): min/max fit,
+// b = min, s = (max - min) / 15 (fp32, then nearest-even fp16), codes
+// round_half_even((w - b16) / s16) clamped to 0..15 (0 where s16 is 0 or
+// not finite), in the interchange layout spec_pack_w4 reads.
+__global__ __launch_bounds__(256) void requantize_w4_kernel(
+    const uint16_t *__restrict__ w, int N, int K, uint32_t *__restrict__ w4,
+    uint16_t *__restrict__ scales, uint16_t *__restrict__ biases) {
+    const int ng = K >> 6;
+    const size_t count = (size_t)N * ng;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const size_t n = i / ng;
+        const int g = (int)(i - n * ng);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(w + n * K + 64 * g);
+        u32x4 raw[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            raw[c] = src[c];
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(raw[c][e] << 16);
+                const float b = __uint_as_float(raw[c][e] & 0xFFFF0000u);
+                lo = fminf(lo, fminf(a, b));
+                hi = fmaxf(hi, fmaxf(a, b));
+            }
+        const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
+        const _Float16 b16 = (_Float16)lo;
+        scales[i] = __builtin_bit_cast(uint16_t, s16);
+        biases[i] = __builtin_bit_cast(uint16_t, b16);
+        const float sf = (float)s16, bf = (float)b16;
+        const bool use = sf != 0.0f && __builtin_isfinite(sf);
+        uint32_t *dst = w4 + n * (K >> 3) + 8 * g;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {          // 8 codes per output word
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(raw[c][e] << 16);
+                const float b = __uint_as_float(raw[c][e] & 0xFFFF0000u);
+                const float ra = rintf((a - bf) / sf), rb = rintf((b - bf) / sf);
+                const uint32_t qa = use ? (uint32_t)fminf(fmaxf(ra, 0.0f), 15.0f) : 0u;
+                const uint32_t qb = use ? (uint32_t)fminf(fmaxf(rb, 0.0f), 15.0f) : 0u;
+                word |= qa << (8 * e) | qb << (8 * e + 4);
+            }
+            dst[c] = word;
+        }
+    }
+}
+
 template <typename V>
 __global__ void fill_zero_kernel(V *__restrict__ y, size_t count) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
@@ -555,6 +609,16 @@ hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
 }
 
 int gate_up_rows(int F) { return 32 * ((F + 15) / 16); }
+
+hipError_t launch_requantize_w4(const uint16_t *w, int N, int K, uint32_t *w4,
+                                uint16_t *scales, uint16_t *biases, hipStream_t stream) {
+    if (N == 0 || K == 0)
+        return hipSuccess;
+    const size_t count = (size_t)N * (K / 64);
+    const int blocks = (int)std::min<size_t>((count + 255) / 256, 65536);
+    requantize_w4_kernel<<<blocks, 256, 0, stream>>>(w, N, K, w4, scales, biases);
+    return hipGetLastError();
+}
 
 hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
                       const uint16_t *x, float *y, int M, int N, int K,

@@ -30,6 +30,9 @@ hipError_t launch_pack(int bits, const void *w, const uint16_t *scales,
                        const uint16_t *scales2, const uint16_t *biases2, int N,
                        int K, void *w_packed, void *sb_packed, hipStream_t stream);
 int gate_up_rows(int F);
+// Draft-only 4-bit copy (G = 64) of a bf16 [N][K] matrix, interchange layout.
+hipError_t launch_requantize_w4(const uint16_t *w, int N, int K, uint32_t *w4,
+                                uint16_t *scales, uint16_t *biases, hipStream_t stream);
 hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
                       const uint16_t *x, float *y, int M, int N, int K,
                       hipStream_t stream);

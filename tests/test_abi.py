@@ -194,3 +194,14 @@ def test_gdn_validation(L):
     assert com(S=None) == INVALID and com(n=None) == INVALID
     assert com(S=MIS) == UNSUPPORTED
     assert com(T=0) == OK and com(B=0) == OK
+
+
+def test_requantize_validation(L):
+    f = L.spec_requantize_w4
+    assert f(P, -1, 128, 64, P, P, P, None) == INVALID
+    assert f(P, 4, 100, 64, P, P, P, None) == INVALID      # K % G
+    assert f(P, 4, 128, 32, P, P, P, None) == UNSUPPORTED
+    assert f(None, 4, 128, 64, P, P, P, None) == INVALID
+    assert f(MIS, 4, 128, 64, P, P, P, None) == UNSUPPORTED
+    assert f(P, 4, 128, 64, P, ctypes.c_void_p(0x10001), P, None) == INVALID
+    assert f(P, 0, 128, 64, P, P, P, None) == OK

@@ -1,0 +1,99 @@
+"""GPU parity of the draft-only 4-bit LM head: spec_requantize_w4 against the
+oracle (codes, scales and biases are integer or rounding decisions taken in
+fp32 and fp16 on both sides, so bit-exact), and the M = 1 product on the
+requantized head against the oracle's product on its own (identical) codes.
+Workloads: N(0, 0.02) weights (a trained head's scale), groups with equal
+values and exact halfway codes, and rows sampled from the full 151936 x 5120
+head generated on the device."""
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_spec_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def gpu_requant(wb, dev):
+    import torch
+    import speculative_decoding_spec_amd as spec
+    w = torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, s, b = spec.spec_requantize_w4(w)
+    torch.cuda.synchronize()
+    return (q.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint16),
+            b.cpu().numpy().view(np.uint16))
+
+
+def weights(seed, N, K):
+    rng = np.random.default_rng(seed)
+    return synth.f32_to_bf16_bits(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+
+
+@pytest.mark.parametrize("N,K", [(300, 5120), (16, 64), (7, 17408)])
+def test_requantize_bit_exact(dev, N, K):
+    wb = weights(N + K, N, K)
+    got = gpu_requant(wb, dev)
+    ref = oracle.requantize_w4(wb, 64)
+    for g, r, name in zip(got, ref, ("codes", "scales", "biases")):
+        assert np.array_equal(g, r), name
+
+
+def test_requantize_constant_groups_and_ties(dev):
+    G = 64
+    w = np.zeros((4, 2 * G), np.float32)
+    w[0, :G] = 0.375                        # constant group: scale 0, codes 0
+    w[1, 1], w[1, 2], w[1, 3] = 15.0, 2.5, 3.5          # halfway codes, step 1
+    w[2, :G] = np.arange(G) % 16 * 0.25 - 1.0           # an exact grid
+    w[3] = np.linspace(-3, 3, 2 * G)
+    wb = synth.f32_to_bf16_bits(w)
+    got = gpu_requant(wb, dev)
+    ref = oracle.requantize_w4(wb, G)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
+def test_draft_head_product(dev):
+    """The M = 1 product on the requantized head (the draft step's LM head)
+    against the oracle's product on its own requantized codes."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    N, K = 4096, 5120
+    wb = weights(5, N, K)
+    x = synth.activations(5, 1, K)
+    w = torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    packed = spec.spec_pack_w4(*spec.spec_requantize_w4(w))
+    y = spec.spec_qmv_w4(packed, parity.dev_x(x, dev)).cpu().numpy()
+    q, s, b = oracle.requantize_w4(wb, 64)
+    ref, mag = parity.oracle_qmv_threaded(4, q, s, b, x, 64)
+    nf, nabs, worst = parity.check_qmv(y, ref, mag)
+    print(f"draft head N={N}: fail={nf} abs-only={nabs} worst_rel={worst:.2e}", flush=True)
+    assert nf == 0
+
+
+def test_full_head_sampled_rows(dev):
+    """The full 151936 x 5120 head requantized on the device; 512 rows spread
+    over it (first, last and random) checked bit for bit."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    V, K = 151936, 5120
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    w = (torch.randn((V, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    q, s, b = spec.spec_requantize_w4(w)
+    rows = np.concatenate([np.arange(8), np.arange(V - 8, V),
+                           np.random.default_rng(6).integers(0, V, 496)])
+    idx = torch.from_numpy(rows).to(dev)
+    wb = w[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.requantize_w4(wb, 64)
+    got = (q[idx].cpu().numpy().view(np.uint32), s[idx].view(torch.int16).cpu().numpy().view(np.uint16),
+           b[idx].view(torch.int16).cpu().numpy().view(np.uint16))
+    for gg, r in zip(got, ref):
+        assert np.array_equal(gg, r)
