@@ -363,7 +363,59 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
     if (!sp.candidates) {
         // ---- running max and normalizer over the chunk ----
         float m = -INFINITY, S = 0.0f;
-        if ((V & 3) == 0) {
+        if (sp.block_stats) {
+            // Plain sampling: the same pass also leaves, per 256-token block
+            // (one wave's 64 lanes x 4 logits for each u), the block's max
+            // and its sum of exp2((z - max) * scale).  The loop bound is the
+            // same for every thread, so each wave reduces whole blocks.
+            const float4 *z4 = reinterpret_cast<const float4 *>(z);
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+            const int nblocks = (V + kBlock - 1) / kBlock;
+            float2 *bsum = ws.block_sums + (size_t)r * nblocks;
+            for (int base_w = lo; base_w < hi; base_w += kThreads * 16) {
+                float v[16];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = base_w + 4 * threadIdx.x + u * kThreads * 4;
+                    const float4 t = load_once(&z4[min(e, hi - 4) >> 2]);
+                    const bool in = e < hi;
+                    v[4 * u + 0] = in ? t.x : -INFINITY;
+                    v[4 * u + 1] = in ? t.y : -INFINITY;
+                    v[4 * u + 2] = in ? t.z : -INFINITY;
+                    v[4 * u + 3] = in ? t.w : -INFINITY;
+                }
+                float bm = m;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    bad |= (v[q] != v[q]) | (v[q] == INFINITY);
+                    finite |= (v[q] > -INFINITY) & (v[q] < INFINITY);
+                    bm = fmaxf(bm, v[q]);
+                }
+                if (bm > -INFINITY) {
+                    float s = (m == bm) ? S : S * weight(m, bm, scale);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        s += weight(v[q], bm, scale);
+                    S = s;
+                    m = bm;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int blk = (base_w + u * kThreads * 4) / kBlock + wave;
+                    float lm = fmaxf(fmaxf(v[4 * u], v[4 * u + 1]), fmaxf(v[4 * u + 2], v[4 * u + 3]));
+                    const float mb = wave_max(lm);
+                    float sb = 0.0f;
+                    if (mb > -INFINITY && mb < INFINITY) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            sb += weight(v[4 * u + q], mb, scale);
+                    }
+                    sb = wave_sum(sb);
+                    if (lane == 0 && blk * kBlock < hi)
+                        bsum[blk] = make_float2(mb, sb);
+                }
+            }
+        } else if ((V & 3) == 0) {
             const float4 *z4 = reinterpret_cast<const float4 *>(z);
             for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 16) {
                 // Branch-free: clamp each load into the chunk and mask the
@@ -737,15 +789,22 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     // ---- full vocabulary: find the block holding u * total ----
     const int nblocks = (V + kBlock - 1) / kBlock;
     const float2 *bs = ws.block_sums + (size_t)b * nblocks;
+    // Block masses: from the draw pass (residual mass, target mass), or, for
+    // plain sampling, from the statistics pass's (block max, block sum).
+    auto mass = [&](int k, bool target_mass) -> float {
+        const float2 v = bs[k];
+        if (sp.block_stats)
+            return v.y * weight(v.x, d.ft.m, scale) * d.ft.inv;
+        return target_mass ? v.y : v.x;
+    };
     // thread t owns a contiguous run of blocks
     const int per = (nblocks + kThreads - 1) / kThreads;
     const int b_lo = min(nblocks, (int)threadIdx.x * per);
     const int b_hi = min(nblocks, b_lo + per);
     float my_r = 0.0f, my_p = 0.0f;
     for (int k = b_lo; k < b_hi; ++k) {
-        const float2 v = bs[k];
-        my_r += v.x;
-        my_p += v.y;
+        my_r += mass(k, false);
+        my_p += mass(k, true);
     }
     float incl_r = block_incl_scan_f(my_r, sh.fsh);
     __syncthreads();
@@ -773,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         int pick = -1, last_pos = -1;
         float before = excl, last_before = excl;
         for (int k = b_lo; k < b_hi; ++k) {
-            const float w = use_p ? bs[k].y : bs[k].x;
+            const float w = mass(k, use_p);
             before = cum;
             cum += w;
             if (w > 0.0f) {
@@ -796,12 +855,12 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         // rounding left the target at or past the end: the last block with
         // positive mass
         int k = nblocks - 1;
-        while (k > 0 && !((use_p ? bs[k].y : bs[k].x) > 0.0f))
+        while (k > 0 && !(mass(k, use_p) > 0.0f))
             --k;
         sh.blk = k;
         float before = 0.0f;
         for (int kk = 0; kk < k; ++kk)
-            before += use_p ? bs[kk].y : bs[kk].x;
+            before += mass(kk, use_p);
         sh.before = before;
     }
     __syncthreads();
@@ -968,10 +1027,12 @@ hipError_t launch_accept(const float *target, const float *draft,
         return hipSuccess;
     Rows rows{target, draft, plan.D, plan.V};
     Ws w = carve(plan, ws);
-    hipError_t e = launch_row_stats(rows, plan, sp, w, stream);
+    SamplingParams spl = sp;
+    spl.block_stats = plan.D == 0 && !sp.candidates && (plan.V & 3) == 0;
+    hipError_t e = launch_row_stats(rows, plan, spl, w, stream);
     if (e != hipSuccess)
         return e;
-    if (!sp.candidates) {
+    if (!sp.candidates && !spl.block_stats) {
         draw_sums_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
             rows, sp, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
         e = hipGetLastError();
@@ -979,7 +1040,7 @@ hipError_t launch_accept(const float *target, const float *draft,
             return e;
     }
     draw_final_kernel<<<plan.B, kThreads, 0, stream>>>(
-        rows, sp, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
+        rows, spl, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
     return hipGetLastError();
 }
 

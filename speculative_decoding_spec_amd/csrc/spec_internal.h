@@ -49,6 +49,9 @@ struct SamplingParams {
     float top_p;     // applied when use_p
     bool use_p;
     bool candidates; // true: distributions live on <= 256 sorted candidates
+    bool block_stats; // plain sampling (D = 0, full vocabulary, V % 4 == 0): the
+                      // statistics pass also leaves each 256-token block's
+                      // (max, sum of exponentials), so no re-read is needed
 };
 
 struct AcceptPlan {
