@@ -44,6 +44,9 @@ step's launches have changed since those counters were taken.
 CPU baseline): the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
+`--depth` times the projections of a whole 64-layer verify pass (12.3 GB
+of weights) at M = 3..6, fused as the model runs them and as separate
+launches.
 `--draft` times the draft step: the LM head at M = 1 (a 4-bit copy built by
 `spec_requantize_w4`, and an 8-bit head for comparison) and one draw.
 `--gdn` times the recurrent-state capture and commit of one verify cycle
@@ -86,6 +89,8 @@ def parse():
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no variants, greedy pass or CPU baseline)")
+    ap.add_argument("--depth", action="store_true",
+                    help="only time the verify pass of a 64-layer decoder at M=3..6 and exit")
     ap.add_argument("--draft", action="store_true",
                     help="only time the draft step (4-bit LM head copy + sampling) and exit")
     ap.add_argument("--gdn", action="store_true",
@@ -112,6 +117,88 @@ SHAPES = {
 }
 # N sweep at K = 5120, M = 1: time per launch against bytes per launch.
 SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
+
+
+DEPTH_LAYERS, Q_N, KV_N, O_K = 64, 6144, 1024, 6144
+
+
+def depth(dev, steps):
+    """The linear projections of a whole verify pass: 64 decoder layers of
+    q 5120->6144, k and v 5120->1024, o 6144->5120, gate and up
+    5120->17408, down 17408->5120, all W4 g64 with each layer's own weights
+    (12.3 GB), at M = 3..6 (depths D2..D5).  Streamed as the model runs it:
+    q, k and v as one launch (they share x), o, gate/up with the gated
+    activation, and down on that activation, 4 launches per layer; and, for
+    comparison, the same weights as 7 separate launches per layer."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    fused, separate = [], []
+    for li in range(DEPTH_LAYERS):
+        sd = 9000 + 10 * li
+        q = synth.torch_qweights(4, Q_N, HIDDEN, GROUP, sd, dev)
+        k = synth.torch_qweights(4, KV_N, HIDDEN, GROUP, sd + 1, dev)
+        v = synth.torch_qweights(4, KV_N, HIDDEN, GROUP, sd + 2, dev)
+        o = synth.torch_qweights(4, HIDDEN, O_K, GROUP, sd + 3, dev)
+        g = synth.torch_qweights(4, FFN, HIDDEN, GROUP, sd + 4, dev)
+        u = synth.torch_qweights(4, FFN, HIDDEN, GROUP, sd + 5, dev)
+        d = synth.torch_qweights(4, HIDDEN, FFN, GROUP, sd + 6, dev)
+        qkv = spec.spec_pack_w4(*[torch.cat(t) for t in zip(q, k, v)], G=GROUP)
+        po, pd = spec.spec_pack_w4(*o, G=GROUP), spec.spec_pack_w4(*d, G=GROUP)
+        fused.append((qkv, po, spec.spec_pack_gate_up(4, g, u, G=GROUP), pd))
+        separate.append(tuple(spec.spec_pack_w4(*t, G=GROUP) for t in (q, k, v, o, g, u, d)))
+        del q, k, v, o, g, u, d
+    torch.cuda.synchronize()
+    res = {}
+    for M in (3, 4, 5, 6):
+        x = synth.torch_activations(M, HIDDEN, 9500 + M, dev)
+        a = synth.torch_activations(M, O_K, 9510 + M, dev)          # attention output
+        yqkv = torch.empty((M, Q_N + 2 * KV_N), device=dev)
+        yo = torch.empty((M, HIDDEN), device=dev)
+        h = torch.empty((M, FFN), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((M, HIDDEN), device=dev)
+        yq = torch.empty((M, Q_N), device=dev)
+        ykv = torch.empty((M, KV_N), device=dev)
+        yg = torch.empty((M, FFN), device=dev)
+        f_calls, s_calls = [], []
+        f_bytes = s_bytes = 0
+        for (qkv, po, glu, pd), (q, k, v, o, g, u, d) in zip(fused, separate):
+            f_calls += [spec.bind_qmv(qkv, x, yqkv), spec.bind_qmv(po, a, yo),
+                        spec.bind_qmv_gate_up_silu(glu, x, h), spec.bind_qmv(pd, h, yd)]
+            f_bytes += (roofline.qmv_bytes(4, M, Q_N + 2 * KV_N, HIDDEN)
+                        + roofline.qmv_bytes(4, M, HIDDEN, O_K)
+                        + roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN)
+                        + roofline.qmv_bytes(4, M, HIDDEN, FFN))
+            s_calls += [spec.bind_qmv(q, x, yq), spec.bind_qmv(k, x, ykv), spec.bind_qmv(v, x, ykv),
+                        spec.bind_qmv(o, a, yo), spec.bind_qmv(g, x, yg), spec.bind_qmv(u, x, yg),
+                        spec.bind_qmv(d, h, yd)]
+            s_bytes += (roofline.qmv_bytes(4, M, Q_N, HIDDEN) + 2 * roofline.qmv_bytes(4, M, KV_N, HIDDEN)
+                        + roofline.qmv_bytes(4, M, HIDDEN, O_K) + 2 * roofline.qmv_bytes(4, M, FFN, HIDDEN)
+                        + roofline.qmv_bytes(4, M, HIDDEN, FFN))
+
+        def cycle_us(calls):
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                for c in calls:
+                    c()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / steps
+
+        fu, su = cycle_us(f_calls), cycle_us(s_calls)
+        res[str(M)] = {"fused_4_launches_per_layer": {"us": round(fu, 1), "bytes": f_bytes,
+                                                      "GB/s": round(f_bytes / fu / 1e3, 1),
+                                                      "frac": round(f_bytes / fu / 1e3 / 8000.0, 4)},
+                       "separate_7_launches_per_layer": {"us": round(su, 1), "bytes": s_bytes,
+                                                         "GB/s": round(s_bytes / su / 1e3, 1),
+                                                         "frac": round(s_bytes / su / 1e3 / 8000.0, 4)}}
+    print(json.dumps({"depth": (f"verify-pass projections of a {DEPTH_LAYERS}-layer 5120-hidden "
+                                "decoder, W4 g64, each layer its own weights, per M"),
+                      "per_M": res}), flush=True)
 
 
 def draft(dev, steps):
@@ -484,6 +571,9 @@ def main():
         return
     if args.draft:
         draft(dev, args.steps)
+        return
+    if args.depth:
+        depth(dev, args.steps)
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)
