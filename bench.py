@@ -44,6 +44,8 @@ step's launches have changed since those counters were taken.
 CPU baseline): the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
+`--lmhead` times the end of one sequence's verify pass: the W4 LM head at
+M = 6 and the acceptance with top-k 20 / top-p 0.95 on its logits.
 `--depth` times the projections of a whole 64-layer verify pass (12.3 GB
 of weights) at M = 3..6, fused as the model runs them and as separate
 launches.
@@ -89,6 +91,8 @@ def parse():
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no variants, greedy pass or CPU baseline)")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="only time the LM head at M=6 plus acceptance with top-k/top-p (B=1) and exit")
     ap.add_argument("--depth", action="store_true",
                     help="only time the verify pass of a 64-layer decoder at M=3..6 and exit")
     ap.add_argument("--draft", action="store_true",
@@ -117,6 +121,56 @@ SHAPES = {
 }
 # N sweep at K = 5120, M = 1: time per launch against bytes per launch.
 SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
+
+
+def lmhead(dev, steps):
+    """The end of a verify pass for one sequence at depth D = 5: the W4 LM
+    head at M = 6 writes the target logits, and the acceptance (T = 0.6,
+    top-k 20, top-p 0.95) runs on them; the draft logits are the target's
+    minus N(0, 0.5) noise and the drafts are drawn from them.  Head copies
+    rotate beyond the last-level cache."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    V, K, D = 151936, HIDDEN, 5
+    heads = [spec.spec_pack_w4(*synth.torch_qweights(4, V, K, GROUP, 8400 + c, dev), G=GROUP)
+             for c in range(3)]
+    x = synth.torch_activations(D + 1, K, 8410, dev)
+    logits = torch.empty((D + 1, V), dtype=torch.float32, device=dev)
+    spec.spec_qmv_w4(heads[0], x, logits)
+    g = torch.Generator(device=dev)
+    g.manual_seed(8411)
+    draft = (logits[:D] - torch.randn((D, V), generator=g, device=dev) * 0.5).contiguous()
+    ud = synth.torch_uniforms((D,), 8412, dev)
+    toks = spec.spec_sample_tokens(draft, ud, ACC_T, 20, 0.95).view(1, D).contiguous()
+    u = synth.torch_uniforms((1, D + 1), 8413, dev)
+    t3 = logits.view(1, D + 1, V)
+    d3 = draft.view(1, D, V)
+    out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+           None, None)
+    accept = spec.bind_verify_accept(t3, d3, toks, u, ACC_T, 20, 0.95, out=out)
+    calls = [spec.bind_qmv(h, x, logits) for h in heads]
+    for c in calls:
+        c()
+        accept()
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i, (a, b_, c_) in enumerate(ev):
+        a.record()
+        calls[i % len(calls)]()
+        b_.record()
+        accept()
+        c_.record()
+    torch.cuda.synchronize()
+    head = sum(a.elapsed_time(b_) for a, b_, _ in ev) / steps * 1e3
+    acc = sum(b_.elapsed_time(c_) for _, b_, c_ in ev) / steps * 1e3
+    nb = roofline.qmv_bytes(4, D + 1, V, K)
+    print(json.dumps({"lmhead": ("W4 g64 LM head 5120->151936 at M=6, then acceptance of D=5 drafts "
+                                 "(T=0.6, top-k 20, top-p 0.95) for one sequence"),
+                      "head_us": round(head, 2), "head_GB/s": round(nb / head / 1e3, 1),
+                      "head_frac": round(nb / head / 1e3 / 8000.0, 4), "accept_us": round(acc, 2),
+                      "accepted_len": int(out[0].item()), "next_token": int(out[1].item())}),
+          flush=True)
 
 
 DEPTH_LAYERS, Q_N, KV_N, O_K = 64, 6144, 1024, 6144
@@ -574,6 +628,9 @@ def main():
         return
     if args.depth:
         depth(dev, args.steps)
+        return
+    if args.lmhead:
+        lmhead(dev, args.steps)
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)
