@@ -603,7 +603,7 @@ def cpu_baseline(seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
                           f"--gpus {args.gpus} is not supported (use --gpus 1)"}))
         sys.exit(2)
     import torch
