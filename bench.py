@@ -826,7 +826,7 @@ def main():
     out["roofline_parts"] = {
         "qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
                        "per_shape (per-launch events)": per_shape},
-        "accept (row_chunk + draw_sums + draw_final)": {
+        "accept (row statistics pass + fused decide/sum/draw)": {
             "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
             "us_per_call": round(acc_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:

@@ -16,9 +16,10 @@
 // fences, counters or spin waits):
 //  1. row_chunk  -- grid (row, chunk).  One streaming pass over every fp32
 //     logit.  Full-vocabulary mode: per-chunk running max and sum of
-//     exp2((z - max) * log2(e)/T).  Candidate mode (top-k active, top-p, or
-//     greedy): the chunk's top-k (logit, index) keys by radix select.  A row
-//     that is a single chunk is finalized right here.
+//     exp2((z - max) * log2(e)/T) (row_stats_kernel when the rows are
+//     16-byte aligned and no per-block output is wanted).  Candidate mode
+//     (top-k active, top-p, or greedy): the chunk's top-k (logit, index) keys
+//     by radix select.  A row that is a single chunk is finalized right here.
 //  2. row_merge  -- grid (row), only when rows span several chunks: merges
 //     the chunks in chunk order into the row's final statistics.
 //  3. draw_sums  -- grid (sequence, chunk), full-vocabulary mode: recomputes
@@ -29,6 +30,8 @@
 //     scan the block sums for the block holding u * total, re-read that one
 //     block and scan it in vocabulary order.  In candidate mode the draw runs
 //     over the <= 256 kept candidates instead.
+//     draw_fused    -- 3 and 4 in one 1024-thread workgroup per sequence, for
+//     batches of 128 sequences or more (same sums, same draw).
 //  5. probs      -- dense write of the distributions (spec_sample_probs).
 //
 // Every reduction runs in a fixed order, so results are deterministic.
@@ -46,6 +49,12 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxCand = 256;       // top-k cap in candidate mode
 constexpr int kCandChunk = 4096;    // logits per workgroup in candidate mode
 constexpr int kTargetBlocks = 1024;
+constexpr int kFusedMinB = 128;     // batches drawn by the fused kernel (half the CUs)
+// Statistics pass over 16-byte aligned rows: workgroup size and 16-byte
+// loads per thread in flight (measured: 256 x 8 slightly ahead of 256 x 4
+// and 512 x 4; 128-thread workgroups 4-5% slower).
+constexpr int kStatsThreads = 256;
+constexpr int kStatsLoads = 8;
 constexpr int kBlock = 256;         // tokens per draw block (64 lanes x 4)
 
 constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
@@ -124,17 +133,34 @@ __device__ __forceinline__ float weight(float z, float m, float scale) {
 }
 
 // ------------------------------------------------------ block reductions ----
+// Wave reductions by DPP lane moves (no LDS round trip per step): neighbour
+// pairs, quads, half rows and rows of 16 lanes, then the row broadcasts fold
+// row 0 into row 1, row 2 into row 3, and rows 0-1 into rows 2-3, leaving the
+// total in lane 63, which every lane reads back.  A fixed tree, so the sum is
+// deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op, float identity) {
+    v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+    v = op(v, dpp_f<0x140>(v));   // row_mirror
+    // row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3; the
+    // other rows take the identity
+    v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                  __float_as_int(identity), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                  __float_as_int(identity), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; }, 0.0f);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, -INFINITY);
 }
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
@@ -348,6 +374,10 @@ __device__ void finalize_candidates(const uint64_t *keys, int got, int flags,
         rk[i] = (i < got) ? keys[i] : 0;
 }
 
+// CAND: candidate mode (top-k / top-p / greedy).  The two modes are separate
+// instantiations so the full-vocabulary pass is not held to the register
+// budget of the radix selection (fewer registers, more waves per CU).
+template <bool CAND>
 __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
     Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
     __shared__ StatsShared sh;
@@ -360,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
     const float scale = sp.scale;
     int bad = 0, finite = 0;
 
-    if (!sp.candidates) {
+    if (!CAND) {
         // ---- running max and normalizer over the chunk ----
         float m = -INFINITY, S = 0.0f;
         if (sp.block_stats) {
@@ -387,8 +417,7 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
                 float bm = m;
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
-                    bad |= (v[q] != v[q]) | (v[q] == INFINITY);
-                    finite |= (v[q] > -INFINITY) & (v[q] < INFINITY);
+                    bad |= !(v[q] < INFINITY);   // NaN or +inf
                     bm = fmaxf(bm, v[q]);
                 }
                 if (bm > -INFINITY) {
@@ -415,43 +444,11 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
                         bsum[blk] = make_float2(mb, sb);
                 }
             }
-        } else if ((V & 3) == 0) {
-            const float4 *z4 = reinterpret_cast<const float4 *>(z);
-            for (int base = lo + threadIdx.x * 4; base < hi; base += kThreads * 16) {
-                // Branch-free: clamp each load into the chunk and mask the
-                // lanes past its end to -inf (which adds nothing below).
-                float v[16];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = base + u * kThreads * 4;
-                    const float4 t = load_once(&z4[min(e, hi - 4) >> 2]);
-                    const bool in = e < hi;
-                    v[4 * u + 0] = in ? t.x : -INFINITY;
-                    v[4 * u + 1] = in ? t.y : -INFINITY;
-                    v[4 * u + 2] = in ? t.z : -INFINITY;
-                    v[4 * u + 3] = in ? t.w : -INFINITY;
-                }
-                float bm = m;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    bad |= (v[q] != v[q]) | (v[q] == INFINITY);
-                    finite |= (v[q] > -INFINITY) & (v[q] < INFINITY);
-                    bm = fmaxf(bm, v[q]);
-                }
-                if (bm > -INFINITY) {
-                    float s = (m == bm) ? S : S * weight(m, bm, scale);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        s += weight(v[q], bm, scale);
-                    S = s;
-                    m = bm;
-                }
-            }
         } else {
+            // rows not 16-byte aligned (aligned rows go to row_stats_kernel)
             for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
                 const float v = load_once(&z[e]);
-                bad |= (v != v) | (v == INFINITY);
-                finite |= (v > -INFINITY) & (v < INFINITY);
+                bad |= !(v < INFINITY);   // NaN or +inf
                 const float bm = fmaxf(m, v);
                 if (bm > -INFINITY) {
                     S = ((m == bm) ? S : S * weight(m, bm, scale)) + weight(v, bm, scale);
@@ -459,6 +456,9 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
                 }
             }
         }
+        // A finite logit was seen iff the running max left -inf (a +inf
+        // sets bad as well, and NaN never enters the max).
+        finite = m > -INFINITY;
         wave_merge_ms(m, S, scale);
         __syncthreads();
         if ((threadIdx.x & 63) == 0) {
@@ -514,6 +514,79 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
         dst[i] = (i < got) ? sh.keys[i] : 0;
     if (threadIdx.x == 0)
         ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{0.0f, 0.0f, bad, finite};
+}
+
+// The full-vocabulary statistics pass on its own (rows of 16-byte aligned
+// logits, no per-block output): NT threads, NV 16-byte loads per thread in
+// flight per step, the same per-thread online update as row_chunk_kernel,
+// then the waves merged in index order.
+template <int NT, int NV>
+__global__ __launch_bounds__(NT) void row_stats_kernel(
+    Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
+    constexpr int NW = NT / 64;
+    __shared__ float s_m[NW], s_S[NW];
+    __shared__ int s_flags[NW];
+    const int r = blockIdx.x;
+    const int c = blockIdx.y;
+    const int V = rows.V;
+    const float4 *z4 = reinterpret_cast<const float4 *>(rows.row(r));
+    const int lo = c * chunk_len;
+    const int hi = min(V, lo + chunk_len);
+    const float scale = sp.scale;
+    float m = -INFINITY, S = 0.0f;
+    int bad = 0;
+    for (int base = lo + threadIdx.x * 4; base < hi; base += NT * 4 * NV) {
+        // Branch-free: clamp each load into the chunk and mask the lanes
+        // past its end to -inf (which adds nothing below).
+        float v[4 * NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int e = base + u * NT * 4;
+            const float4 t = load_once(&z4[min(e, hi - 4) >> 2]);
+            const bool in = e < hi;
+            v[4 * u + 0] = in ? t.x : -INFINITY;
+            v[4 * u + 1] = in ? t.y : -INFINITY;
+            v[4 * u + 2] = in ? t.z : -INFINITY;
+            v[4 * u + 3] = in ? t.w : -INFINITY;
+        }
+        float bm = m;
+#pragma unroll
+        for (int q = 0; q < 4 * NV; ++q) {
+            bad |= !(v[q] < INFINITY);   // NaN or +inf
+            bm = fmaxf(bm, v[q]);
+        }
+        if (bm > -INFINITY) {
+            float s = (m == bm) ? S : S * weight(m, bm, scale);
+#pragma unroll
+            for (int q = 0; q < 4 * NV; ++q)
+                s += weight(v[q], bm, scale);
+            S = s;
+            m = bm;
+        }
+    }
+    // a finite logit was seen iff the running max left -inf
+    int flags = bad | ((m > -INFINITY) ? 2 : 0);
+    wave_merge_ms(m, S, scale);
+    flags = wave_or(flags);
+    if ((threadIdx.x & 63) == 0) {
+        s_m[threadIdx.x >> 6] = m;
+        s_S[threadIdx.x >> 6] = S;
+        s_flags[threadIdx.x >> 6] = flags;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float mm = s_m[0], SS = s_S[0];
+        int f = s_flags[0];
+        for (int w = 1; w < NW; ++w) {
+            merge_ms(mm, SS, s_m[w], s_S[w], scale);
+            f |= s_flags[w];
+        }
+        const int rbad = f & 1, rfin = (f >> 1) & 1;
+        if (chunks == 1)
+            ws.row_final[r] = RowFinal{mm, 1.0f / SS, 0, (rbad || !rfin) ? kInvalid : 0};
+        else
+            ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{mm, SS, rbad, rfin};
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void row_merge_kernel(
@@ -647,37 +720,63 @@ __device__ __forceinline__ float2 draw_weight(const DrawRows &d, float scale, fl
     return make_float2(fmaxf(p - q, 0.0f), p);
 }
 
-// Kernel 3: per 256-token block, the sums of the draw weights.
-__global__ __launch_bounds__(kThreads) void draw_sums_kernel(
-    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
-    const float *__restrict__ uniforms, int blocks_per_chunk, Ws ws) {
-    __shared__ int s_L;
-    const int b = blockIdx.x;
-    const int c = blockIdx.y;
-    const int V = rows.V;
-    const int nblocks = (V + kBlock - 1) / kBlock;
-    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
-    if (L < 0)
-        return;
-    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+// Sums of the draw weights over 256-token blocks [blk_lo, blk_hi) of
+// sequence b's draw rows, into out[blk]: wave w takes blocks w, w + NW, ...
+// and each block is summed by one wave (four tokens per lane, then a fixed
+// wave reduction), so the sums do not depend on the workgroup size.
+template <int NW>
+__device__ void block_draw_sums(const DrawRows &d, const SamplingParams &sp, int V, int blk_lo,
+                                int blk_hi, float2 *out) {
+    constexpr int kW = NW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int blk_lo = c * blocks_per_chunk;
-    const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
-    float2 *out = ws.block_sums + (size_t)b * nblocks;
-    for (int blk = blk_lo + wave; blk < blk_hi; blk += kWaves) {
+    if ((V & 3) == 0) {
+        // kAhead blocks per wave in flight: their loads are all issued
+        // before the first is reduced.  (A bonus draw has no draft row: both
+        // pointers name the target row, and the second load hits the cache.)
+        constexpr int kAhead = 4;
+        const float4 *zt4 = reinterpret_cast<const float4 *>(d.zt);
+        const float4 *zd4 = reinterpret_cast<const float4 *>(d.zd);
+        for (int blk0 = blk_lo + wave; blk0 < blk_hi; blk0 += kW * kAhead) {
+            float4 t[kAhead], q[kAhead];
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k) {
+                const int blk = min(blk0 + k * kW, blk_hi - 1);
+                const int e4 = min(blk * kBlock + 4 * lane, V - 4) >> 2;
+                t[k] = load_once(&zt4[e4]);
+                q[k] = load_once(&zd4[e4]);
+            }
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k) {
+                const int blk = blk0 + k * kW;
+                if (blk >= blk_hi)
+                    break;
+                const int e = blk * kBlock + 4 * lane;
+                const float zt[4] = {t[k].x, t[k].y, t[k].z, t[k].w};
+                const float zd[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+                float wr = 0.0f, wp = 0.0f;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float2 wv = draw_weight(d, sp.scale, zt[qq], zd[qq]);
+                    const bool in = e + qq < V;
+                    wr += in ? wv.x : 0.0f;
+                    wp += in ? wv.y : 0.0f;
+                }
+                wr = wave_sum(wr);
+                wp = wave_sum(wp);
+                if (lane == 0)
+                    out[blk] = make_float2(wr, wp);
+            }
+        }
+        return;
+    }
+    // rows not 16-byte aligned: scalar loads
+    for (int blk = blk_lo + wave; blk < blk_hi; blk += kW) {
         const int e = blk * kBlock + 4 * lane;   // this lane's 4 tokens
         float zt4[4], zd4[4];
-        if ((V & 3) == 0) {
-            const float4 t = reinterpret_cast<const float4 *>(d.zt)[min(e, V - 4) >> 2];
-            const float4 q = reinterpret_cast<const float4 *>(d.zd)[min(e, V - 4) >> 2];
-            zt4[0] = t.x; zt4[1] = t.y; zt4[2] = t.z; zt4[3] = t.w;
-            zd4[0] = q.x; zd4[1] = q.y; zd4[2] = q.z; zd4[3] = q.w;
-        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                zt4[q] = d.zt[min(e + q, V - 1)];
-                zd4[q] = d.zd[min(e + q, V - 1)];
-            }
+        for (int q = 0; q < 4; ++q) {
+            zt4[q] = d.zt[min(e + q, V - 1)];
+            zd4[q] = d.zd[min(e + q, V - 1)];
         }
         float wr = 0.0f, wp = 0.0f;
 #pragma unroll
@@ -694,9 +793,29 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     }
 }
 
-struct FinalShared {
-    float fsh[kWaves];
-    int ish[kWaves];
+// Kernel 3: per 256-token block, the sums of the draw weights, for small
+// batches (several workgroups per sequence).
+__global__ __launch_bounds__(kThreads) void draw_sums_kernel(
+    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
+    const float *__restrict__ uniforms, int blocks_per_chunk, Ws ws) {
+    __shared__ int s_L;
+    const int b = blockIdx.x;
+    const int c = blockIdx.y;
+    const int V = rows.V;
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
+    if (L < 0)
+        return;
+    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const int blk_lo = c * blocks_per_chunk;
+    const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
+    block_draw_sums<kWaves>(d, sp, V, blk_lo, blk_hi, ws.block_sums + (size_t)b * nblocks);
+}
+
+template <int NW>
+struct FinalSharedT {
+    float fsh[NW];
+    int ish[NW];
     int found;
     int L;
     float before, target;
@@ -706,86 +825,19 @@ struct FinalShared {
     float cw[kMaxCand];
     float cp[kMaxCand];
 };
+using FinalShared = FinalSharedT<kWaves>;
 
-// Kernel 4: decisions, then the inverse-CDF draw.
-__global__ __launch_bounds__(kThreads) void draw_final_kernel(
-    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
-    const float *__restrict__ uniforms, int32_t *__restrict__ accepted_len,
-    int32_t *__restrict__ next_token, float *__restrict__ p_draft,
-    float *__restrict__ q_draft, Ws ws) {
-    __shared__ FinalShared sh;
-    const int b = blockIdx.x;
-    const int D = rows.D, V = rows.V;
+// The full-vocabulary inverse-CDF draw of sequence b from its block sums:
+// find the 256-token block holding u * total, then scan that block in
+// vocabulary order.  The block runs belong to kThreads logical threads; in a
+// larger workgroup the other threads own none and only join the barriers.
+template <int NW>
+__device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, const Ws &ws,
+                                const DrawRows &d, int b, int L, float u, FinalSharedT<NW> &sh,
+                                int32_t *__restrict__ accepted_len,
+                                int32_t *__restrict__ next_token) {
+    const int V = rows.V;
     const float scale = sp.scale;
-
-    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
-    if (L < 0) {
-        if (threadIdx.x == 0) {
-            if (accepted_len) accepted_len[b] = -1;
-            next_token[b] = -1;
-        }
-        return;
-    }
-    const float u = uniforms[(size_t)b * (D + 1) + D];
-    const DrawRows d = draw_rows(rows, ws, sp, b, L);
-
-    if (sp.candidates) {
-        // ---- draw over the kept candidates of the target row ----
-        const int n = d.ft.n_kept;
-        for (int i = threadIdx.x; i < kMaxCand; i += kThreads) {
-            if (i < n) {
-                const uint64_t key = d.kt[i];
-                const int x = key_index(key);
-                const float p = weight(key_logit(key), d.ft.m, scale) * d.ft.inv;
-                float w = p;
-                if (d.residual) {
-                    const float q = row_prob(d.fd, d.kd, true, scale, d.zd[x], x);
-                    w = fmaxf(p - q, 0.0f);
-                }
-                // index-major sort key, complemented so a descending sort
-                // yields ascending vocabulary order
-                sh.ckey[i] = ~(((uint64_t)(uint32_t)x << 32) | (uint32_t)i);
-                sh.cw[i] = w;
-                sh.cp[i] = p;
-            } else {
-                sh.ckey[i] = 0;  // sorts last
-            }
-        }
-        __syncthreads();
-        block_sort_desc(sh.ckey, kMaxCand);
-        if (threadIdx.x == 0) {
-            float tot = 0.0f;
-            for (int i = 0; i < n; ++i)
-                tot += sh.cw[(uint32_t)~sh.ckey[i]];
-            const bool use_p = !(tot > 0.0f);
-            if (use_p) {
-                tot = 0.0f;
-                for (int i = 0; i < n; ++i)
-                    tot += sh.cp[(uint32_t)~sh.ckey[i]];
-            }
-            const float target = u * tot;
-            float cum = 0.0f;
-            int pick = -1, last_pos = -1;
-            for (int i = 0; i < n; ++i) {
-                const int slot = (int)(uint32_t)~sh.ckey[i];
-                const float w = use_p ? sh.cp[slot] : sh.cw[slot];
-                const int x = (int)((~sh.ckey[i]) >> 32);
-                cum += w;
-                if (w > 0.0f)
-                    last_pos = x;
-                if (cum > target) {
-                    pick = x;
-                    break;
-                }
-            }
-            if (pick < 0)
-                pick = last_pos;
-            if (accepted_len) accepted_len[b] = L;
-            next_token[b] = pick;
-        }
-        return;
-    }
-
     // ---- full vocabulary: find the block holding u * total ----
     const int nblocks = (V + kBlock - 1) / kBlock;
     const float2 *bs = ws.block_sums + (size_t)b * nblocks;
@@ -925,6 +977,117 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     }
 }
 
+// Kernel 4: decisions, then the inverse-CDF draw.
+__global__ __launch_bounds__(kThreads) void draw_final_kernel(
+    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
+    const float *__restrict__ uniforms, int32_t *__restrict__ accepted_len,
+    int32_t *__restrict__ next_token, float *__restrict__ p_draft,
+    float *__restrict__ q_draft, Ws ws) {
+    __shared__ FinalShared sh;
+    const int b = blockIdx.x;
+    const int D = rows.D;
+    const float scale = sp.scale;
+
+    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    if (L < 0) {
+        if (threadIdx.x == 0) {
+            if (accepted_len) accepted_len[b] = -1;
+            next_token[b] = -1;
+        }
+        return;
+    }
+    const float u = uniforms[(size_t)b * (D + 1) + D];
+    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+
+    if (sp.candidates) {
+        // ---- draw over the kept candidates of the target row ----
+        const int n = d.ft.n_kept;
+        for (int i = threadIdx.x; i < kMaxCand; i += kThreads) {
+            if (i < n) {
+                const uint64_t key = d.kt[i];
+                const int x = key_index(key);
+                const float p = weight(key_logit(key), d.ft.m, scale) * d.ft.inv;
+                float w = p;
+                if (d.residual) {
+                    const float q = row_prob(d.fd, d.kd, true, scale, d.zd[x], x);
+                    w = fmaxf(p - q, 0.0f);
+                }
+                // index-major sort key, complemented so a descending sort
+                // yields ascending vocabulary order
+                sh.ckey[i] = ~(((uint64_t)(uint32_t)x << 32) | (uint32_t)i);
+                sh.cw[i] = w;
+                sh.cp[i] = p;
+            } else {
+                sh.ckey[i] = 0;  // sorts last
+            }
+        }
+        __syncthreads();
+        block_sort_desc(sh.ckey, kMaxCand);
+        if (threadIdx.x == 0) {
+            float tot = 0.0f;
+            for (int i = 0; i < n; ++i)
+                tot += sh.cw[(uint32_t)~sh.ckey[i]];
+            const bool use_p = !(tot > 0.0f);
+            if (use_p) {
+                tot = 0.0f;
+                for (int i = 0; i < n; ++i)
+                    tot += sh.cp[(uint32_t)~sh.ckey[i]];
+            }
+            const float target = u * tot;
+            float cum = 0.0f;
+            int pick = -1, last_pos = -1;
+            for (int i = 0; i < n; ++i) {
+                const int slot = (int)(uint32_t)~sh.ckey[i];
+                const float w = use_p ? sh.cp[slot] : sh.cw[slot];
+                const int x = (int)((~sh.ckey[i]) >> 32);
+                cum += w;
+                if (w > 0.0f)
+                    last_pos = x;
+                if (cum > target) {
+                    pick = x;
+                    break;
+                }
+            }
+            if (pick < 0)
+                pick = last_pos;
+            if (accepted_len) accepted_len[b] = L;
+            next_token[b] = pick;
+        }
+        return;
+    }
+    draw_full_vocab(rows, sp, ws, d, b, L, u, sh, accepted_len, next_token);
+}
+
+// Kernels 3 and 4 as one, for large batches (full vocabulary, verification):
+// one 1024-thread workgroup per sequence decides, sums the draw blocks with
+// 16 waves, then draws.  Same block sums and draw as the two-kernel path, one
+// launch and one decision pass fewer.
+constexpr int kFusedThreads = 1024;
+__global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
+    Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
+    const float *__restrict__ uniforms, int32_t *__restrict__ accepted_len,
+    int32_t *__restrict__ next_token, float *__restrict__ p_draft,
+    float *__restrict__ q_draft, Ws ws) {
+    constexpr int NW = kFusedThreads / 64;
+    __shared__ FinalSharedT<NW> sh;
+    const int b = blockIdx.x;
+    const int D = rows.D, V = rows.V;
+    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    if (L < 0) {
+        if (threadIdx.x == 0) {
+            if (accepted_len) accepted_len[b] = -1;
+            next_token[b] = -1;
+        }
+        return;
+    }
+    const float u = uniforms[(size_t)b * (D + 1) + D];
+    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    block_draw_sums<NW>(d, sp, V, 0, nblocks, ws.block_sums + (size_t)b * nblocks);
+    __syncthreads();   // the block sums, written above, are read by other waves below
+    draw_full_vocab(rows, sp, ws, d, b, L, u, sh, accepted_len, next_token);
+}
+
 // ----------------------------------------------------------------- probs ----
 __global__ __launch_bounds__(kThreads) void probs_kernel(
     Rows rows, SamplingParams sp, int chunk_len, float *__restrict__ probs, Ws ws) {
@@ -955,8 +1118,15 @@ Ws carve(const AcceptPlan &p, void *base) {
 
 hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
                             const SamplingParams &sp, const Ws &w, hipStream_t stream) {
-    row_chunk_kernel<<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
-        rows, plan.chunks, plan.chunk_len, sp, w);
+    if (sp.candidates)
+        row_chunk_kernel<true><<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
+            rows, plan.chunks, plan.chunk_len, sp, w);
+    else if (!sp.block_stats && (rows.V & 3) == 0)
+        row_stats_kernel<kStatsThreads, kStatsLoads><<<dim3(plan.rows, plan.chunks), kStatsThreads, 0, stream>>>(
+            rows, plan.chunks, plan.chunk_len, sp, w);
+    else
+        row_chunk_kernel<false><<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
+            rows, plan.chunks, plan.chunk_len, sp, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.chunks == 1)
         return e;
@@ -1001,7 +1171,11 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
     }
     p.chunks = std::max(1, (V + p.chunk_len - 1) / p.chunk_len);
     p.nblocks = (V + kBlock - 1) / kBlock;
-    // draw-sum workgroups: about kTargetBlocks in total, whole 256-token blocks
+    // The draw: from kFusedMinB sequences on, one fused 1024-thread
+    // workgroup per sequence (half the CUs or more busy); below, draw-sum
+    // workgroups of whole 256-token blocks, about kTargetBlocks in total,
+    // then one draw workgroup per sequence.
+    p.fused_draw = B >= kFusedMinB;
     int C3 = (kTargetBlocks + std::max(B, 1) - 1) / std::max(B, 1);
     C3 = std::max(1, std::min(C3, (p.nblocks + 31) / 32));
     p.blocks_per_chunk3 = (p.nblocks + C3 - 1) / C3;
@@ -1033,6 +1207,11 @@ hipError_t launch_accept(const float *target, const float *draft,
     if (e != hipSuccess)
         return e;
     if (!sp.candidates && !spl.block_stats) {
+        if (plan.fused_draw) {
+            draw_fused_kernel<<<plan.B, kFusedThreads, 0, stream>>>(
+                rows, spl, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
+            return hipGetLastError();
+        }
         draw_sums_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
             rows, sp, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
         e = hipGetLastError();

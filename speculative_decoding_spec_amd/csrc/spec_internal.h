@@ -61,6 +61,7 @@ struct AcceptPlan {
     int chunk_len;   // elements per chunk
     int nblocks;     // 256-token draw blocks per row
     int chunks3;     // draw-sum workgroups per sequence
+    bool fused_draw;    // one fused decide/sum/draw workgroup per sequence
     int blocks_per_chunk3;
     size_t ws_bytes;
     // workspace offsets

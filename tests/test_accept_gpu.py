@@ -338,3 +338,29 @@ def test_two_token_vocabulary(dev):
     toks = draft_tokens(d, 0.8, 0, 1.0, 703)
     u = synth.uniforms(703, synth.U_ACCEPT, (B, D + 1))
     check(t, d, toks, u, 0.8, 0, 1.0, dev)
+
+
+@pytest.mark.parametrize("B,D,V", [(200, 5, 151936), (130, 3, 1001)])
+def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
+    """From 128 sequences on, each sequence is decided, summed and drawn by
+    one fused workgroup; below, by separate block-sum and draw launches.
+    Sequences are independent, and both halves here keep one statistics chunk
+    per row (as the whole batch does), so the whole batch must give, bit for
+    bit, what its two halves give: residual and bonus draws, invalid
+    sequences, and an odd vocabulary on the scalar-load path."""
+    t, d = synth.logits_pair(720 + D, B, D, V)
+    d[: B // 4] = t[: B // 4, :D]            # some sequences accept every draft
+    toks = draft_tokens(d, 0.6, 0, 1.0, 720 + D)
+    u = synth.uniforms(720 + D, synth.U_ACCEPT, (B, D + 1))
+    t[5, 1, 7] = np.nan                       # two invalid sequences
+    toks[B // 2 + 9, 0] = V
+    big = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    L = big["accepted_len"]
+    assert (L == D).sum() > 0 and ((L >= 0) & (L < D)).sum() > 0 and (L < 0).sum() == 2
+    h = B // 2
+    for lo, hi in ((0, h), (h, B)):
+        part = gpu_accept(t[lo:hi], d[lo:hi], toks[lo:hi], u[lo:hi], 0.6, 0, 1.0, dev)
+        for key in ("accepted_len", "next_token"):
+            assert np.array_equal(part[key], big[key][lo:hi]), key
+        for key in ("p_draft", "q_draft"):
+            assert np.array_equal(part[key].view(np.uint64), big[key][lo:hi].view(np.uint64)), key
