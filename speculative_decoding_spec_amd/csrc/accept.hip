@@ -162,6 +162,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) {
     return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, -INFINITY);
 }
+// The same tree for unsigned 64-bit keys (max; 0 is the identity).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t t;
+    t = dpp_u64<0xB1, 0xF>(v);  v = t > v ? t : v;
+    t = dpp_u64<0x4E, 0xF>(v);  v = t > v ? t : v;
+    t = dpp_u64<0x141, 0xF>(v); v = t > v ? t : v;
+    t = dpp_u64<0x140, 0xF>(v); v = t > v ? t : v;
+    t = dpp_u64<0x142, 0xA>(v); v = t > v ? t : v;
+    t = dpp_u64<0x143, 0xC>(v); v = t > v ? t : v;
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
@@ -210,15 +229,21 @@ __device__ void wave_merge_ms(float &m, float &S, float scale) {
     }
 }
 
-// Inclusive scan of one int per thread, in thread order.
+// Inclusive scan of one int per thread, in thread order.  Inside the wave
+// by DPP: shifts by 1, 2, 4, 8 within each row of 16 lanes, then the row
+// broadcasts carry row totals into the rows above (no LDS round trips).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_shift_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
 __device__ int block_incl_scan(int v, int *sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o);
-        if (lane >= o)
-            v += t;
-    }
+    v += dpp_shift_i<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_shift_i<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_shift_i<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_shift_i<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_shift_i<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    v += dpp_shift_i<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
     __syncthreads();
     if (lane == 63)
         sh[wave] = v;
@@ -309,30 +334,24 @@ __device__ int block_select_topk(Each each, int n, int k, uint64_t *out, int cap
     return min(want, min(sh.out_n, cap));
 }
 
-// Bitonic sort of n <= 256 keys in LDS, descending (padding with 0 keys).
+// Sorts keys[0..n) in LDS (n <= kThreads, keys unique) into descending
+// order, in place, by rank: thread t's key moves to the number of keys
+// greater than it.  n broadcast reads per thread and two barriers -- far
+// fewer steps than a sorting network for the short lists sorted here.
 __device__ void block_sort_desc(uint64_t *keys, int n) {
-    int P = 1;
-    while (P < n)
-        P <<= 1;
-    for (int i = n + (int)threadIdx.x; i < P; i += kThreads)
-        keys[i] = 0;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < P; i += kThreads) {
-                const int partner = i ^ stride;
-                if (partner > i) {
-                    const bool desc = ((i & size) == 0);
-                    const uint64_t a = keys[i], b = keys[partner];
-                    if (desc ? (a < b) : (a > b)) {
-                        keys[i] = b;
-                        keys[partner] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    __syncthreads();   // the caller's writes to keys
+    const int t = threadIdx.x;
+    uint64_t mine = 0;
+    int rank = 0;
+    if (t < n) {
+        mine = keys[t];
+        for (int j = 0; j < n; ++j)
+            rank += keys[j] > mine;
     }
+    __syncthreads();
+    if (t < n)
+        keys[rank] = mine;
+    __syncthreads();
 }
 
 // ------------------------------------------------------- row statistics ----
@@ -502,10 +521,12 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
                 f(mine[q]);
     };
     const int got = block_select_topk(each, n, sp.k_eff, sh.keys, kMaxCand, sh.sel);
+    // the chunk's keys leave sorted (descending), so a small-k merge can walk
+    // the chunks' lists from their heads
+    block_sort_desc(sh.keys, got);
     bad = block_or(bad, sh.ish);
     finite = block_or(finite, sh.ish);
     if (chunks == 1) {
-        block_sort_desc(sh.keys, got);
         finalize_candidates(sh.keys, got, (bad || !finite) ? kInvalid : 0, sp, r, ws);
         return;
     }
@@ -589,18 +610,45 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     }
 }
 
+// Chunk keys per thread held in registers by the merge (totals up to
+// kThreads x this; larger totals are re-read from memory each round).
+constexpr int kMergeRegKeys = 4;
+// The k-way merge of sorted chunk lists: for k up to kMergeWalkK, at most
+// 64 chunks (one per lane), and at most kMergeWalkMax keys in all (in LDS).
+constexpr int kMergeWalkK = 64;
+constexpr int kMergeWalkMax = 4096;
+
+struct MergeShared : StatsShared {
+    uint64_t walk[kMergeWalkMax];
+};
+
 __global__ __launch_bounds__(kThreads) void row_merge_kernel(
     Rows rows, int chunks, int chunk_len, SamplingParams sp, Ws ws) {
-    __shared__ StatsShared sh;
+    __shared__ MergeShared sh;
     const int r = blockIdx.x;
     const int V = rows.V;
-    int rbad = 0, rfin = 0;
-    for (int cc = 0; cc < chunks; ++cc) {
-        const ChunkStat st = ws.chunk_stats[(size_t)r * chunks + cc];
-        rbad |= st.bad;
-        rfin |= st.finite;
+    const int k = sp.k_eff;
+    const uint64_t *ck = ws.chunk_keys + (size_t)r * chunks * k;
+    const int total = chunks * k;
+    // Small k: the chunks' sorted lists are merged by a walk over their
+    // heads (below).  Their loads go out first, beside the chunk flags'.
+    const bool walk = sp.candidates && k <= kMergeWalkK && chunks <= 64 && total <= kMergeWalkMax;
+    uint64_t staged[kMergeWalkMax / kThreads];
+    if (walk) {
+#pragma unroll
+        for (int q = 0; q < kMergeWalkMax / kThreads; ++q) {
+            const int i = q * kThreads + (int)threadIdx.x;
+            staged[q] = i < total ? ck[i] : 0;
+        }
     }
-    const int flags = (rbad || !rfin) ? kInvalid : 0;
+    // row flags: thread t folds chunks t, t + kThreads, ...
+    int fl = 0;
+    for (int cc = threadIdx.x; cc < chunks; cc += kThreads) {
+        const ChunkStat st = ws.chunk_stats[(size_t)r * chunks + cc];
+        fl |= (st.bad ? 1 : 0) | (st.finite ? 2 : 0);
+    }
+    fl = block_or(fl, sh.ish);
+    const int flags = ((fl & 1) || !(fl & 2)) ? kInvalid : 0;
     if (!sp.candidates) {
         if (threadIdx.x == 0) {
             float m = -INFINITY, S = 0.0f;
@@ -612,24 +660,73 @@ __global__ __launch_bounds__(kThreads) void row_merge_kernel(
         }
         return;
     }
-    const int k = sp.k_eff;
-    const uint64_t *ck = ws.chunk_keys + (size_t)r * chunks * k;
-    const int total = chunks * k;
-    auto each_g = [&](auto f) {
-        for (int i = threadIdx.x; i < total; i += kThreads) {
-            const uint64_t key = ck[i];
-            if (key != 0)
-                f(key);
-        }
-    };
     // number of real keys: min(k, chunk length) per chunk
     int n_real = 0;
     for (int cc = 0; cc < chunks; ++cc)
         n_real += min(k, min(V, (cc + 1) * chunk_len) - cc * chunk_len);
-    const int got = block_select_topk(each_g, n_real, k, sh.keys, kMaxCand, sh.sel);
+    int got;
+    if (walk) {
+        // The chunks' lists arrive sorted, so the row's top-k is a k-way
+        // merge.  The lists are staged in LDS; wave 0 keeps list c's head in
+        // lane c and k times takes the largest head (keys are unique) and
+        // advances that list.
+        uint64_t *lists = sh.walk;
+#pragma unroll
+        for (int q = 0; q < kMergeWalkMax / kThreads; ++q) {
+            const int i = q * kThreads + (int)threadIdx.x;
+            if (i < total)
+                lists[i] = staged[q];
+        }
+        __syncthreads();
+        got = min(k, n_real);
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            int pos = 0;
+            uint64_t head = lane < chunks ? lists[lane * k] : 0;
+            for (int i = 0; i < got; ++i) {
+                const uint64_t top = wave_max_u64(head);
+                if (lane == 0)
+                    sh.keys[i] = top;
+                if (head == top) {   // the one list holding it
+                    ++pos;
+                    head = pos < k ? lists[lane * k + pos] : 0;
+                }
+            }
+        }
+        __syncthreads();
+        finalize_candidates(sh.keys, got, flags, sp, r, ws);
+        return;
+    }
+    if (total <= kThreads * kMergeRegKeys) {
+        // Few keys (small k): each thread holds its share in registers for
+        // all the selection rounds instead of re-reading them.
+        uint64_t mine[kMergeRegKeys];
+#pragma unroll
+        for (int q = 0; q < kMergeRegKeys; ++q) {
+            const int i = q * kThreads + (int)threadIdx.x;
+            mine[q] = i < total ? ck[i] : 0;
+        }
+        auto each_r = [&](auto f) {
+#pragma unroll
+            for (int q = 0; q < kMergeRegKeys; ++q)
+                if (mine[q] != 0)
+                    f(mine[q]);
+        };
+        got = block_select_topk(each_r, n_real, k, sh.keys, kMaxCand, sh.sel);
+    } else {
+        auto each_g = [&](auto f) {
+            for (int i = threadIdx.x; i < total; i += kThreads) {
+                const uint64_t key = ck[i];
+                if (key != 0)
+                    f(key);
+            }
+        };
+        got = block_select_topk(each_g, n_real, k, sh.keys, kMaxCand, sh.sel);
+    }
     block_sort_desc(sh.keys, got);
     finalize_candidates(sh.keys, got, flags, sp, r, ws);
 }
+
 
 // ---------------------------------------------------------- verification ----
 // Probability of token x under row r's final distribution, given its logit.
@@ -1022,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
             }
         }
         __syncthreads();
-        block_sort_desc(sh.ckey, kMaxCand);
+        block_sort_desc(sh.ckey, n);   // entries n.. are zero and stay last
         if (threadIdx.x == 0) {
             float tot = 0.0f;
             for (int i = 0; i < n; ++i)
