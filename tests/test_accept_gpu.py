@@ -364,3 +364,20 @@ def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
             assert np.array_equal(part[key], big[key][lo:hi]), key
         for key in ("p_draft", "q_draft"):
             assert np.array_equal(part[key].view(np.uint64), big[key][lo:hi].view(np.uint64)), key
+
+
+@pytest.mark.parametrize("V,k,p", [
+    (151936, 64, 1.0),      # largest k of the head-walk merge (38 chunk lists)
+    (151936, 1, 1.0),       # greedy through the walk
+    (32768, 100, 0.9),      # radix merge over register-held keys (800 keys)
+    (32768, 200, 1.0),      # radix merge re-reading keys (1600 keys)
+    (300000, 20, 0.95),     # 74 chunks: more lists than lanes, radix merge
+])
+def test_candidate_merge_paths(dev, V, k, p):
+    """Rows spanning several 4096-logit chunks, for each way the chunks'
+    top-k lists are merged; every path must keep exactly the oracle's set."""
+    B, D = 2, 2
+    t, d = synth.logits_pair(730 + k, B, D, V)
+    toks = draft_tokens(d, 0.7, k, p, 730 + k)
+    u = synth.uniforms(730 + k, synth.U_ACCEPT, (B, D + 1))
+    check(t, d, toks, u, 0.7, k, p, dev)
