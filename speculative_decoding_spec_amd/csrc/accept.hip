@@ -732,9 +732,10 @@ __global__ __launch_bounds__(kThreads) void row_merge_kernel(
 // Probability of token x under row r's final distribution, given its logit.
 __device__ __forceinline__ float row_prob(const RowFinal &f, const uint64_t *keys,
                                           bool candidates, float scale, float zx, int x) {
+#pragma clang fp contract(off)
     if (candidates && make_key(zx, x) < keys[f.n_kept - 1])
         return 0.0f;
-    return weight(zx, f.m, scale) * f.inv;
+    return weight(zx, f.m, scale) * f.inv;   // rounded here, never fused
 }
 
 // Decisions of sequence b from the row statistics, one position per lane
@@ -809,7 +810,12 @@ __device__ DrawRows draw_rows(const Rows &rows, const Ws &ws, const SamplingPara
 }
 
 // Weights of token x: (residual max(0, p - q) or p, and p), full vocabulary.
+// p and q are each rounded before the subtraction (contraction into a fused
+// multiply-add is off here): where the two distributions agree, p - q is then
+// exactly zero, as the rule has it, and an all-zero residual is recognized
+// (draw from p instead).
 __device__ __forceinline__ float2 draw_weight(const DrawRows &d, float scale, float zt, float zd) {
+#pragma clang fp contract(off)
     const float p = weight(zt, d.ft.m, scale) * d.ft.inv;
     if (!d.residual)
         return make_float2(p, p);
@@ -1103,7 +1109,7 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
             if (i < n) {
                 const uint64_t key = d.kt[i];
                 const int x = key_index(key);
-                const float p = weight(key_logit(key), d.ft.m, scale) * d.ft.inv;
+                const float p = row_prob(d.ft, d.kt, false, scale, key_logit(key), x);
                 float w = p;
                 if (d.residual) {
                     const float q = row_prob(d.fd, d.kd, true, scale, d.zd[x], x);

@@ -381,3 +381,25 @@ def test_candidate_merge_paths(dev, V, k, p):
     toks = draft_tokens(d, 0.7, k, p, 730 + k)
     u = synth.uniforms(730 + k, synth.U_ACCEPT, (B, D + 1))
     check(t, d, toks, u, 0.7, k, p, dev)
+
+
+@pytest.mark.parametrize("B", [3, 130])
+def test_zero_residual_draws_from_target(dev, B):
+    """The R11 reading: target and draft rows identical, and every position-0
+    draft token has probability zero under both (its logit far below the
+    rest, so its weight underflows).  The ratio p/q is then taken as 0, the
+    draft is rejected, and the residual max(0, p - q) is zero everywhere, so
+    the token is drawn from the target row itself.  Small batches and the
+    fused large-batch draw both."""
+    D, V = 2, 40000
+    t, _ = synth.logits_pair(740 + B, B, D, V)
+    d = np.ascontiguousarray(t[:, :D]).copy()
+    toks = np.zeros((B, D), np.int32)
+    for b in range(B):
+        x = (17 * b + 5) % V
+        t[b, 0, x] = -1000.0
+        d[b, 0, x] = -1000.0
+        toks[b, 0] = x
+    u = synth.uniforms(740 + B, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert np.all(ref["accepted_len"] == 0) and np.all(got["accepted_len"] == 0)
