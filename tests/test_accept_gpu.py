@@ -403,3 +403,22 @@ def test_zero_residual_draws_from_target(dev, B):
     u = synth.uniforms(740 + B, synth.U_ACCEPT, (B, D + 1))
     got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
     assert np.all(ref["accepted_len"] == 0) and np.all(got["accepted_len"] == 0)
+
+
+@pytest.mark.parametrize("B", [3, 130])
+def test_zero_draft_probability_is_accepted(dev, B):
+    """The R12 reading: a draft token the draft gives probability zero (its
+    draft logit far below the rest, weight underflowing) but the target does
+    not has ratio +inf, so it is accepted whatever the uniform."""
+    D, V = 3, 40000
+    t, d = synth.logits_pair(750 + B, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 750 + B)
+    for b in range(B):
+        x = (29 * b + 11) % V
+        d[b, 0, x] = -1000.0
+        toks[b, 0] = x
+    u = synth.uniforms(750 + B, synth.U_ACCEPT, (B, D + 1))
+    u[:, 0] = np.float32(0.99999994)           # the largest uniform below 1
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert np.all(ref["accepted_len"] >= 1) and np.all(got["accepted_len"] >= 1)
+    assert np.all(got["q_draft"][:, 0] == 0.0) and np.all(got["p_draft"][:, 0] > 0.0)

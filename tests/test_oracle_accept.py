@@ -397,3 +397,20 @@ def test_verify_greedy_invalid_and_depth_zero():
     zi = np.full((1, 1, 4), -np.inf, np.float32)
     zi[0, 0, 2] = -1e30
     assert int(oracle.verify_greedy(zi, None)["next_token"][0]) == 2   # -inf is never the max
+
+
+def test_zero_draft_probability_is_accepted_and_zero_target_rejected():
+    """Limits of the ratio (the R12 reading): Q(d) = 0 < P(d) accepts the
+    draft whatever the uniform; P(d) = 0 rejects it whatever the uniform."""
+    V = 50
+    r = np.random.default_rng(5)
+    t = r.normal(0, 1, size=(2, 2, V)).astype(np.float32)
+    d = t[:, :1].copy()
+    toks = np.array([[7], [9]], np.int32)
+    d[0, 0, 7] = -1000.0            # q(7) = 0, p(7) > 0
+    t[1, 0, 9] = -1000.0            # p(9) = 0, q(9) > 0
+    u = np.array([[0.99999994, 0.5], [1e-30, 0.5]], np.float32)
+    out = oracle.accept(t, d, toks, u, 1.0, 0, 1.0)
+    assert out["accepted_len"].tolist() == [1, 0]
+    assert out["q_draft"][0, 0] == 0.0 and out["p_draft"][0, 0] > 0.0
+    assert out["p_draft"][1, 0] == 0.0 and out["q_draft"][1, 0] > 0.0
