@@ -422,3 +422,26 @@ def test_zero_draft_probability_is_accepted(dev, B):
     got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
     assert np.all(ref["accepted_len"] >= 1) and np.all(got["accepted_len"] >= 1)
     assert np.all(got["q_draft"][:, 0] == 0.0) and np.all(got["p_draft"][:, 0] > 0.0)
+
+
+@pytest.mark.parametrize("V,k,p", [(4096, 0, 1.0), (151936, 0, 1.0), (4096, 40, 0.9)])
+def test_zero_weight_tokens_are_never_drawn(dev, V, k, p):
+    """The R10 reading (strict crossing): tokens of weight zero -- here every
+    odd token, at -inf -- are never drawn, also for uniforms at 0 and just
+    below 1, with and without filters; draws match the oracle."""
+    import speculative_decoding_spec_amd as spec
+    R = 256
+    z = synth.rng(760 + V + k, synth.DRAFT).normal(0, 2, size=(R, V)).astype(np.float32)
+    z[:, 1::2] = -np.inf
+    u = synth.uniforms(760 + V + k, synth.U_ACCEPT, R)
+    u[:8] = 0.0
+    u[8:16] = np.float32(0.99999994)
+    got = spec.spec_sample_tokens(T_(z, dev), T_(u, dev), 0.7, k, p).cpu().numpy()
+    assert np.all(got % 2 == 0)
+    ref = oracle.sample_rows(z, 0.7, k, p, u)
+    ties = 0
+    for r in np.nonzero(got != ref)[0]:
+        w = oracle.probs(z[r], 0.7, k, p)
+        assert parity.top_p_tie(z[r], 0.7, k, p) or parity.draw_tie(w, u[r], int(got[r]), int(ref[r])), r
+        ties += 1
+    assert ties <= 3
