@@ -58,6 +58,7 @@ constexpr int kStatsLoads = 8;
 constexpr int kBlock = 256;         // tokens per draw block (64 lanes x 4)
 
 constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
+constexpr int kMaxDepth = 15;       // drafts per sequence at most (the ABI's limit)
 
 // Logit loads of the statistics pass are non-temporal: every logit is read
 // once there, and keeping it out of the caches measured 12% faster for the
@@ -610,6 +611,23 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     }
 }
 
+// Final statistics of row r from its C chunk statistics, by one wave: lane
+// l folds chunks l, l + 64, ... in order, then the lanes merge in a fixed
+// butterfly.  Called by all 64 lanes; every lane returns the result.
+__device__ RowFinal wave_row_final(const Ws &ws, int r, int C, float scale) {
+    const int lane = threadIdx.x & 63;
+    float m = -INFINITY, S = 0.0f;
+    int f = 0;
+    for (int cc = lane; cc < C; cc += 64) {
+        const ChunkStat st = ws.chunk_stats[(size_t)r * C + cc];
+        merge_ms(m, S, st.m, st.S, scale);
+        f |= (st.bad ? 1 : 0) | (st.finite ? 2 : 0);
+    }
+    wave_merge_ms(m, S, scale);
+    f = wave_or(f);
+    return RowFinal{m, 1.0f / S, 0, ((f & 1) || !(f & 2)) ? kInvalid : 0};
+}
+
 // Chunk keys per thread held in registers by the merge (totals up to
 // kThreads x this; larger totals are re-read from memory each round).
 constexpr int kMergeRegKeys = 4;
@@ -650,13 +668,11 @@ __global__ __launch_bounds__(kThreads) void row_merge_kernel(
     fl = block_or(fl, sh.ish);
     const int flags = ((fl & 1) || !(fl & 2)) ? kInvalid : 0;
     if (!sp.candidates) {
-        if (threadIdx.x == 0) {
-            float m = -INFINITY, S = 0.0f;
-            for (int cc = 0; cc < chunks; ++cc) {
-                const ChunkStat st = ws.chunk_stats[(size_t)r * chunks + cc];
-                merge_ms(m, S, st.m, st.S, sp.scale);
-            }
-            ws.row_final[r] = RowFinal{m, 1.0f / S, 0, flags};
+        // the same merge the draw kernels do for themselves (wave_row_final)
+        if (threadIdx.x < 64) {
+            const RowFinal f = wave_row_final(ws, r, chunks, sp.scale);
+            if (threadIdx.x == 0)
+                ws.row_final[r] = f;
         }
         return;
     }
@@ -738,24 +754,43 @@ __device__ __forceinline__ float row_prob(const RowFinal &f, const uint64_t *key
     return weight(zx, f.m, scale) * f.inv;   // rounded here, never fused
 }
 
+// The final statistics of sequence b's 2D + 1 rows, staged in LDS: rf[i] for
+// target position i, rf[D + 1 + i] for draft position i.  Full-vocabulary
+// rows that span several chunks are merged here (sp.merge_chunks > 0), so
+// no separate merge launch runs before the draw.  Called by all threads.
+template <int NW>
+__device__ void stage_row_finals(const Rows &rows, const Ws &ws, const SamplingParams &sp, int b,
+                                 RowFinal *rf) {
+    const int D = rows.D, n = 2 * D + 1;
+    for (int i = (int)(threadIdx.x >> 6); i < n; i += NW) {
+        const int r = i <= D ? rows.target_row(b, i) : rows.draft_row(b, i - D - 1);
+        const RowFinal f = sp.merge_chunks > 0 ? wave_row_final(ws, r, sp.merge_chunks, sp.scale)
+                                               : ws.row_final[r];
+        if ((threadIdx.x & 63) == 0)
+            rf[i] = f;
+    }
+    __syncthreads();
+}
+
 // Decisions of sequence b from the row statistics, one position per lane
 // of wave 0: returns L (0..D) or -1 for an invalid sequence to every thread
 // of the block (through *sh_L).  When p_out / q_out are given, wave 0 also
 // writes P_i(d_i), Q_i(d_i) for the sequence (NaN if it is invalid).  Called
 // by all threads of the block.
 __device__ int decide_block(const Rows &rows, const Ws &ws, const SamplingParams &sp,
-                            const int32_t *draft_tokens, const float *uniforms, int b,
-                            float *p_out, float *q_out, int *sh_L) {
+                            const RowFinal *rf, const int32_t *draft_tokens,
+                            const float *uniforms, int b, float *p_out, float *q_out,
+                            int *sh_L) {
     const int D = rows.D, V = rows.V;
     if (threadIdx.x < 64) {
         const int i = threadIdx.x;
         bool bad = false, rej = false;
         float p = 0.0f, q = 0.0f;
         if (i <= D)
-            bad = ws.row_final[rows.target_row(b, i)].flags != 0;
+            bad = rf[i].flags != 0;
         if (i < D) {
             const int tr = rows.target_row(b, i), dr = rows.draft_row(b, i);
-            const RowFinal ft = ws.row_final[tr], fd = ws.row_final[dr];
+            const RowFinal ft = rf[i], fd = rf[D + 1 + i];
             const int d = draft_tokens[(size_t)b * D + i];
             bad = bad || fd.flags != 0 || d < 0 || d >= V;
             if (!bad) {
@@ -789,16 +824,17 @@ struct DrawRows {
     const uint64_t *kt, *kd;
 };
 
-__device__ DrawRows draw_rows(const Rows &rows, const Ws &ws, const SamplingParams &sp, int b, int L) {
+__device__ DrawRows draw_rows(const Rows &rows, const Ws &ws, const SamplingParams &sp,
+                              const RowFinal *rf, int b, int L) {
     DrawRows d;
     d.residual = L < rows.D;
     const int tr = rows.target_row(b, L);
-    d.ft = ws.row_final[tr];
+    d.ft = rf[L];
     d.zt = rows.row(tr);
     d.kt = ws.row_keys + (size_t)tr * sp.k_eff;
     if (d.residual) {
         const int dr = rows.draft_row(b, L);
-        d.fd = ws.row_final[dr];
+        d.fd = rf[rows.D + 1 + L];
         d.zd = rows.row(dr);
         d.kd = ws.row_keys + (size_t)dr * sp.k_eff;
     } else {
@@ -906,10 +942,12 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const int c = blockIdx.y;
     const int V = rows.V;
     const int nblocks = (V + kBlock - 1) / kBlock;
-    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
+    __shared__ RowFinal s_rf[2 * kMaxDepth + 1];
+    stage_row_finals<kWaves>(rows, ws, sp, b, s_rf);
+    const int L = decide_block(rows, ws, sp, s_rf, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
     if (L < 0)
         return;
-    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const DrawRows d = draw_rows(rows, ws, sp, s_rf, b, L);
     const int blk_lo = c * blocks_per_chunk;
     const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
     block_draw_sums<kWaves>(d, sp, V, blk_lo, blk_hi, ws.block_sums + (size_t)b * nblocks);
@@ -917,6 +955,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
 
 template <int NW>
 struct FinalSharedT {
+    RowFinal rf[2 * kMaxDepth + 1];   // the sequence's row statistics
     float fsh[NW];
     int ish[NW];
     int found;
@@ -1091,7 +1130,8 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     const int D = rows.D;
     const float scale = sp.scale;
 
-    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    stage_row_finals<kWaves>(rows, ws, sp, b, sh.rf);
+    const int L = decide_block(rows, ws, sp, sh.rf, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
     if (L < 0) {
         if (threadIdx.x == 0) {
             if (accepted_len) accepted_len[b] = -1;
@@ -1100,7 +1140,7 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         return;
     }
     const float u = uniforms[(size_t)b * (D + 1) + D];
-    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const DrawRows d = draw_rows(rows, ws, sp, sh.rf, b, L);
 
     if (sp.candidates) {
         // ---- draw over the kept candidates of the target row ----
@@ -1175,7 +1215,8 @@ __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
     __shared__ FinalSharedT<NW> sh;
     const int b = blockIdx.x;
     const int D = rows.D, V = rows.V;
-    const int L = decide_block(rows, ws, sp, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    stage_row_finals<NW>(rows, ws, sp, b, sh.rf);
+    const int L = decide_block(rows, ws, sp, sh.rf, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
     if (L < 0) {
         if (threadIdx.x == 0) {
             if (accepted_len) accepted_len[b] = -1;
@@ -1184,7 +1225,7 @@ __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
         return;
     }
     const float u = uniforms[(size_t)b * (D + 1) + D];
-    const DrawRows d = draw_rows(rows, ws, sp, b, L);
+    const DrawRows d = draw_rows(rows, ws, sp, sh.rf, b, L);
     const int nblocks = (V + kBlock - 1) / kBlock;
     block_draw_sums<NW>(d, sp, V, 0, nblocks, ws.block_sums + (size_t)b * nblocks);
     __syncthreads();   // the block sums, written above, are read by other waves below
@@ -1219,8 +1260,12 @@ Ws carve(const AcceptPlan &p, void *base) {
     return w;
 }
 
+// merge_full: also merge full-vocabulary rows that span chunks into
+// row_final (the draw kernels merge those themselves; the dense probs pass
+// reads row_final).  Candidate rows are always merged here.
 hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
-                            const SamplingParams &sp, const Ws &w, hipStream_t stream) {
+                            const SamplingParams &sp, const Ws &w, bool merge_full,
+                            hipStream_t stream) {
     if (sp.candidates)
         row_chunk_kernel<true><<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
             rows, plan.chunks, plan.chunk_len, sp, w);
@@ -1231,7 +1276,7 @@ hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
         row_chunk_kernel<false><<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
             rows, plan.chunks, plan.chunk_len, sp, w);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.chunks == 1)
+    if (e != hipSuccess || plan.chunks == 1 || !(sp.candidates || merge_full))
         return e;
     row_merge_kernel<<<plan.rows, kThreads, 0, stream>>>(rows, plan.chunks, plan.chunk_len, sp, w);
     return hipGetLastError();
@@ -1306,7 +1351,8 @@ hipError_t launch_accept(const float *target, const float *draft,
     Ws w = carve(plan, ws);
     SamplingParams spl = sp;
     spl.block_stats = plan.D == 0 && !sp.candidates && (plan.V & 3) == 0;
-    hipError_t e = launch_row_stats(rows, plan, spl, w, stream);
+    spl.merge_chunks = (!sp.candidates && plan.chunks > 1) ? plan.chunks : 0;
+    hipError_t e = launch_row_stats(rows, plan, spl, w, false, stream);
     if (e != hipSuccess)
         return e;
     if (!sp.candidates && !spl.block_stats) {
@@ -1316,7 +1362,7 @@ hipError_t launch_accept(const float *target, const float *draft,
             return hipGetLastError();
         }
         draw_sums_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
-            rows, sp, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
+            rows, spl, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1333,7 +1379,7 @@ hipError_t launch_probs(const float *logits, const AcceptPlan &plan,
         return hipSuccess;
     Rows rows{logits, nullptr, 0, plan.V};
     Ws w = carve(plan, ws);
-    hipError_t e = launch_row_stats(rows, plan, sp, w, stream);
+    hipError_t e = launch_row_stats(rows, plan, sp, w, true, stream);
     if (e != hipSuccess)
         return e;
     const int pc = (plan.V + 4095) / 4096;

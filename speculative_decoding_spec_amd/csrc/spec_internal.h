@@ -52,6 +52,8 @@ struct SamplingParams {
     bool block_stats; // plain sampling (D = 0, full vocabulary, V % 4 == 0): the
                       // statistics pass also leaves each 256-token block's
                       // (max, sum of exponentials), so no re-read is needed
+    int merge_chunks; // > 0: full-vocabulary rows span this many chunks and the
+                      // draw kernels merge their statistics themselves
 };
 
 struct AcceptPlan {
