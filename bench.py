@@ -52,7 +52,8 @@ launches.
 `--draft` times the draft step: the LM head at M = 1 (a 4-bit copy built by
 `spec_requantize_w4`, and an 8-bit head for comparison) and one draw.
 `--gdn` times the recurrent-state capture and commit of one verify cycle
-over 36 layers (one JSON line) and exits.
+over 36 layers, as two calls and as the one-pass cycle boundary (one JSON
+line), and exits.
 `--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
 weight copies) plus an N sweep that splits a launch's time into a fixed
 cost and an incremental bandwidth, prints one JSON line each, and exits.
@@ -369,6 +370,15 @@ def gdn(dev, steps):
 
     rec_us = timed(rec_calls)
     com_us = timed(com_calls)
+    # The same boundary in one pass per layer: the commit of the tape just
+    # recorded and the capture of the next block (here the same step inputs)
+    # from the committed state, the new tape in buffers of its own.
+    for L in layers:
+        L["o2"], L["d2"] = torch.empty_like(L["v"]), torch.empty_like(L["v"])
+    cr_calls = [spec.bind_gdn_commit_record(L["S"], L["a"], L["k"], L["d"], n, L["q"], L["k"],
+                                            L["v"], L["a"], L["b"], L["o2"], L["d2"])
+                for L in layers]
+    cr_us = timed(cr_calls)
     # After verification the commits of all layers are independent: with the
     # layers' states and tapes laid out [layer][sequence], one launch commits
     # the whole model (sequence index layer * B + b, step counts repeated).
@@ -379,17 +389,22 @@ def gdn(dev, steps):
     for li, L in enumerate(layers):
         sl = slice(li * GDN_B, (li + 1) * GDN_B)
         allS[sl].copy_(L["S"]); allA[sl].copy_(L["a"]); allK[sl].copy_(L["k"]); allD[sl].copy_(L["d"])
-    del layers, rec_calls, com_calls
+    del layers, rec_calls, com_calls, cr_calls
     n_all = n.repeat(GDN_LAYERS)
     all_us = timed([spec.bind_gdn_commit(allS, allA, allK, allD, n_all)]) 
     rb = roofline.gdn_record_bytes(GDN_B, GDN_T, GDN_H)
     cb = roofline.gdn_commit_bytes(n_host.tolist(), GDN_H)
+    crb = roofline.gdn_commit_record_bytes(n_host.tolist(), GDN_T, GDN_H)
     out = {"gdn": (f"{GDN_LAYERS} layers x {GDN_B} sequences x {GDN_H} heads, dk=dv=128, "
                    f"T={GDN_T} verify positions; commit steps {n_host.tolist()}"),
            "record": {"us_per_layer": round(rec_us, 2), "bytes_per_layer": rb,
                       "GB/s": round(rb / rec_us / 1e3, 1), "frac": round(rb / rec_us / 1e3 / 8000.0, 4)},
            "commit": {"us_per_layer": round(com_us, 2), "bytes_per_layer": cb,
                       "GB/s": round(cb / com_us / 1e3, 1), "frac": round(cb / com_us / 1e3 / 8000.0, 4)},
+           "commit_record": {"us_per_layer": round(cr_us, 2), "bytes_per_layer": crb,
+                             "GB/s": round(crb / cr_us / 1e3, 1),
+                             "frac": round(crb / cr_us / 1e3 / 8000.0, 4),
+                             "vs_two_calls_us": round(rec_us + com_us, 2)},
            "commit_all_layers_one_launch": {
                "us": round(all_us, 2), "bytes": cb * GDN_LAYERS,
                "GB/s": round(cb * GDN_LAYERS / all_us / 1e3, 1),

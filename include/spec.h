@@ -325,6 +325,32 @@ spec_status spec_gdn_commit(float *S, const float *alpha, const float *k, const 
                             const int32_t *n_steps, int B, int T, int H, int dk, int dv,
                             hipStream_t stream);
 
+/*
+ * spec_gdn_commit_record joins the two calls of a cycle boundary (the same
+ * "Layer 2" cycle: commit the accepted steps, then capture the next verify
+ * block) in one pass over the state.  In place in S it commits the first
+ * n_steps[b] steps of the previous cycle's tape (prev_alpha [B][T_prev][H],
+ * prev_k [B][T_prev][H][dk], prev_delta [B][T_prev][H][dv]) exactly as
+ * spec_gdn_commit does, then records the T steps of the next verify block
+ * from the committed state (q, k, v, alpha, beta -> o, delta, and S_T to
+ * S_final when it is not NULL) exactly as spec_gdn_record does.  S is read
+ * and written once, where the two calls read it twice and write it once.
+ * Every output is bitwise the one of spec_gdn_commit followed by
+ * spec_gdn_record on the same arguments.
+ * T_prev = 0 commits nothing (then prev_* and n_steps may be NULL); T = 0
+ * records nothing (then q, k, v, alpha, beta, o, delta may be NULL);
+ * 0 <= T_prev, T <= 16.  Other workgroups read what one writes, so no
+ * output (S, o, delta, S_final) may share memory with any other argument:
+ * the previous and the next tape live in separate buffers
+ * (SPEC_ERR_INVALID otherwise).  Layouts and alignment as above.
+ */
+spec_status spec_gdn_commit_record(float *S, const float *prev_alpha, const float *prev_k,
+                                   const float *prev_delta, const int32_t *n_steps, int T_prev,
+                                   const float *q, const float *k, const float *v,
+                                   const float *alpha, const float *beta, int B, int T, int H,
+                                   int dk, int dv, float *o, float *delta, float *S_final,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

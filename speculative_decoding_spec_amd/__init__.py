@@ -20,6 +20,8 @@ Names follow the C ABI:
     spec_gdn_record / spec_gdn_commit  recurrent-layer state over the verify
                                      positions with an innovation tape, and
                                      the commit of the accepted steps
+    spec_gdn_commit_record           both at a cycle boundary, one pass
+                                     over the state
     spec_*_workspace_size            workspace queries
     bind_qmv / bind_verify_accept /  the same calls with arguments marshalled
     bind_verify_greedy / bind_gdn_*  once, for launch loops
@@ -100,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.spec_gdn_record.restype = i
         L.spec_gdn_commit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.spec_gdn_commit.restype = i
+        L.spec_gdn_commit_record.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp,
+                                             i, i, i, i, i, vp, vp, vp, vp]
+        L.spec_gdn_commit_record.restype = i
         L.spec_verify_greedy_workspace.argtypes = [i, i, i]
         L.spec_verify_greedy_workspace.restype = sz
         L.spec_verify_greedy.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
@@ -544,6 +549,74 @@ def spec_gdn_commit(S, alpha, k, delta, n_steps):
                                B, T, H, dk, dv, _stream(dev))
     _check("spec_gdn_commit", st)
     return S
+
+
+def _gdn_commit_record_args(S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha, beta,
+                            o, delta, S_final):
+    import torch
+    dev = S.device
+    _require(S, torch.float32, "S", dev)
+    B, H, dv, dk = S.shape
+    Tp = 0 if prev_alpha is None else prev_alpha.shape[1]
+    T = q.shape[1]
+    if Tp > 0:
+        for name, t in (("prev_alpha", prev_alpha), ("prev_k", prev_k), ("prev_delta", prev_delta)):
+            _require(t, torch.float32, name, dev)
+        _require(n_steps, torch.int32, "n_steps", dev)
+        if (tuple(prev_alpha.shape) != (B, Tp, H) or tuple(prev_k.shape) != (B, Tp, H, dk)
+                or tuple(prev_delta.shape) != (B, Tp, H, dv) or tuple(n_steps.shape) != (B,)):
+            raise ValueError("previous tape must be alpha [B][Tp][H], k [B][Tp][H][dk], "
+                             "delta [B][Tp][H][dv], n_steps [B]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("o", o), ("delta", delta)):
+        _require(t, torch.float32, name, dev)
+    if (tuple(q.shape) != (B, T, H, dk) or tuple(k.shape) != (B, T, H, dk)
+            or tuple(v.shape) != (B, T, H, dv) or tuple(alpha.shape) != (B, T, H)
+            or tuple(beta.shape) != (B, T, H) or tuple(o.shape) != (B, T, H, dv)
+            or tuple(delta.shape) != (B, T, H, dv)):
+        raise ValueError("shapes must be S [B][H][dv][dk], q/k [B][T][H][dk], "
+                         "v/o/delta [B][T][H][dv], alpha/beta [B][T][H]")
+    if S_final is not None:
+        _require(S_final, torch.float32, "S_final", dev)
+    if Tp == 0:
+        prev_alpha = prev_k = prev_delta = n_steps = None
+    return (_ptr(S), _ptr(prev_alpha), _ptr(prev_k), _ptr(prev_delta), _ptr(n_steps), Tp,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B, T, H, dk, dv,
+            _ptr(o), _ptr(delta), _ptr(S_final), _stream(dev))
+
+
+def spec_gdn_commit_record(S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha, beta,
+                           o=None, delta=None, S_final=None, want_final: bool = False):
+    """At a cycle boundary, in place in S [B][H][dv][dk]: commit the first
+    n_steps[b] steps of the previous tape (prev_alpha [B][Tp][H], prev_k
+    [B][Tp][H][dk], prev_delta [B][Tp][H][dv]; prev_alpha None commits
+    nothing), then record the next T steps from the committed state; returns
+    (o, delta, S_final or None), bitwise those of spec_gdn_commit followed by
+    spec_gdn_record.  The new tape must not share memory with the old one."""
+    import torch
+    B, H, dv, dk = S.shape
+    T = q.shape[1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=S.device)
+    if delta is None:
+        delta = torch.empty((B, T, H, dv), dtype=torch.float32, device=S.device)
+    if S_final is None and want_final:
+        S_final = torch.empty_like(S)
+    args = _gdn_commit_record_args(S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha,
+                                   beta, o, delta, S_final)
+    _check("spec_gdn_commit_record", lib().spec_gdn_commit_record(*args))
+    return o, delta, S_final
+
+
+def bind_gdn_commit_record(S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha, beta,
+                           o, delta, S_final=None) -> _Bound:
+    """spec_gdn_commit_record on fixed tensors, marshalled once (no checked
+    first call: the call works in place on S)."""
+    args = _gdn_commit_record_args(S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha,
+                                   beta, o, delta, S_final)
+    return _Bound("spec_gdn_commit_record", lib().spec_gdn_commit_record, args,
+                  (S, prev_alpha, prev_k, prev_delta, n_steps, q, k, v, alpha, beta, o, delta,
+                   S_final))
 
 
 def bind_gdn_record(S0, q, k, v, alpha, beta, o, delta, S_final=None) -> _Bound:

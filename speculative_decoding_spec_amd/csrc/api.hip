@@ -18,6 +18,18 @@ constexpr size_t kMaxRows = (size_t)1 << 23;  // grid x of 256-thread workgroups
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// A byte range of an argument; empty when the pointer is null or the size 0.
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+bool disjoint(const Span &a, const Span &b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0)
+        return true;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 + a.bytes <= b0 || b0 + b.bytes <= a0;
+}
+
 spec_status qmv_shape_ok(int N, int K, int G) {
     if (N < 0 || K < 0 || G <= 0 || K % G != 0)
         return SPEC_ERR_INVALID;
@@ -406,6 +418,54 @@ spec_status spec_gdn_commit(float *S, const float *alpha, const float *k, const 
     if (!aligned4(alpha) || !aligned4(delta) || !aligned4(n_steps))
         return SPEC_ERR_INVALID;
     if (spec::launch_gdn_commit(S, alpha, k, delta, n_steps, B, T, H, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_gdn_commit_record(float *S, const float *prev_alpha, const float *prev_k,
+                                   const float *prev_delta, const int32_t *n_steps, int T_prev,
+                                   const float *q, const float *k, const float *v,
+                                   const float *alpha, const float *beta, int B, int T, int H,
+                                   int dk, int dv, float *o, float *delta, float *S_final,
+                                   hipStream_t stream) {
+    if (B < 0 || T_prev < 0 || T < 0 || H < 0 || dk < 1 || dv < 1)
+        return SPEC_ERR_INVALID;
+    if (dk != 128 || dv != 128 || T_prev > kMaxD + 1 || T > kMaxD + 1 ||
+        (int64_t)B * H >= (1 << 28))
+        return SPEC_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0)
+        return SPEC_OK;
+    if (!S || (T_prev > 0 && (!prev_alpha || !prev_k || !prev_delta || !n_steps)) ||
+        (T > 0 && (!q || !k || !v || !alpha || !beta || !o || !delta)))
+        return SPEC_ERR_INVALID;
+    if (!aligned16(S) || (S_final && !aligned16(S_final)) ||
+        (T_prev > 0 && !aligned16(prev_k)) || (T > 0 && (!aligned16(q) || !aligned16(k))))
+        return SPEC_ERR_UNSUPPORTED;
+    if ((T_prev > 0 && (!aligned4(prev_alpha) || !aligned4(prev_delta) || !aligned4(n_steps))) ||
+        (T > 0 && (!aligned4(v) || !aligned4(alpha) || !aligned4(beta) || !aligned4(o) ||
+                   !aligned4(delta))))
+        return SPEC_ERR_INVALID;
+    // Workgroups of one head write what those of another read: no output may
+    // share memory with any other argument (the two tapes are separate).
+    const size_t heads = (size_t)B * H, f = sizeof(float);
+    const size_t state = heads * 128 * 128 * f;
+    const size_t tp = T_prev > 0 ? heads * T_prev : 0, tn = T > 0 ? heads * T : 0;
+    const Span outs[] = {{S, state}, {o, tn * 128 * f}, {delta, tn * 128 * f}, {S_final, state}};
+    const Span ins[] = {{prev_alpha, tp * f}, {prev_k, tp * 128 * f}, {prev_delta, tp * 128 * f},
+                        {T_prev > 0 ? n_steps : nullptr, (size_t)B * sizeof(int32_t)},
+                        {q, tn * 128 * f}, {k, tn * 128 * f}, {v, tn * 128 * f},
+                        {alpha, tn * f}, {beta, tn * f}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (!disjoint(outs[i], outs[j]))
+                return SPEC_ERR_INVALID;
+        for (const Span &in : ins)
+            if (!disjoint(outs[i], in))
+                return SPEC_ERR_INVALID;
+    }
+    if (spec::launch_gdn_commit_record(S, prev_alpha, prev_k, prev_delta, n_steps, T_prev, q, k,
+                                       v, alpha, beta, B, T, H, o, delta, S_final,
+                                       stream) != hipSuccess)
         return SPEC_ERR_DEVICE;
     return SPEC_OK;
 }

@@ -27,7 +27,11 @@
 //     delta, and optionally S_T; S_0 itself is left untouched.
 //  2. gdn_commit -- reads S_0 once, applies the first n[b] rank-1 updates
 //     from the tape, writes the committed state in place.
-// Both apply the update through the same function, so committing n steps
+//  3. gdn_commit_record -- both at a cycle boundary: commits the previous
+//     cycle's tape in place and records the next verify block from the
+//     committed rows, so the state crosses HBM once each way instead of
+//     three times (commit read and write, then the capture's read).
+// All apply the update through the same function, so committing n steps
 // reproduces bitwise the state the recording reached after n steps.
 #include "spec_internal.h"
 
@@ -88,27 +92,30 @@ struct RecordShared {
     float beta[kMaxT];
 };
 
-__global__ __launch_bounds__(kThreads) void gdn_record_kernel(
-    const float *__restrict__ S0, const float *__restrict__ q, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ alpha, const float *__restrict__ beta,
-    int T, int H, int n_heads, float *__restrict__ o, float *__restrict__ delta,
-    float *__restrict__ S_final) {
-    __shared__ RecordShared sh;
-    const HeadBlock hb = head_block(blockIdx.x);
-    if (hb.bh >= n_heads)
-        return;
-    const int bh = hb.bh, row0 = hb.row0;
-    const int b = bh / H, h = bh - b * H;
-    const int t = threadIdx.x;
-    const int lr = t >> 3, l8 = t & 7;       // row within the block, lane within the row
-    const int row = row0 + lr;
+struct CommitShared {
+    float4 k[kMaxT][kD / 4];
+    float d[kMaxT][kRowsPerBlock];
+    float alpha[kMaxT];
+};
 
-    // the state rows first (the long HBM reads), then the step inputs
-    float4 S[4];
-    const float *srow = S0 + ((size_t)bh * kD + row) * kD + 4 * l8;
+// The block's 32 state rows: lane l8 of row lr holds columns 4 l8 + 32 j.
+__device__ __forceinline__ void load_rows(float4 S[4], const float *srow) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         S[j] = load_once4(srow + 32 * j);
+}
+
+__device__ __forceinline__ void store_rows(float *srow, const float4 S[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(srow + 32 * j) = S[j];
+}
+
+// Step inputs of the T positions of (b, h) for the block's rows, into LDS.
+__device__ __forceinline__ void stage_record(RecordShared &sh, const float *q, const float *k,
+                                             const float *v, const float *alpha,
+                                             const float *beta, int b, int h, int T, int H,
+                                             int row0, int t) {
     for (int i = t; i < T * (kD / 4); i += kThreads) {
         const int s = i / (kD / 4), c4 = i - s * (kD / 4);
         const size_t bth = ((size_t)b * T + s) * H + h;
@@ -124,8 +131,30 @@ __global__ __launch_bounds__(kThreads) void gdn_record_kernel(
         sh.alpha[t] = alpha[bth];
         sh.beta[t] = beta[bth];
     }
-    __syncthreads();
+}
 
+// The first n tape entries of (b, h) (a tape of T positions) for the block's
+// rows, into LDS.
+__device__ __forceinline__ void stage_commit(CommitShared &sh, const float *alpha,
+                                             const float *k, const float *delta, int b, int h,
+                                             int n, int T, int H, int row0, int t) {
+    for (int i = t; i < n * (kD / 4); i += kThreads) {
+        const int s = i / (kD / 4), c4 = i - s * (kD / 4);
+        sh.k[s][c4] = reinterpret_cast<const float4 *>(k + (((size_t)b * T + s) * H + h) * kD)[c4];
+    }
+    for (int i = t; i < n * kRowsPerBlock; i += kThreads) {
+        const int s = i / kRowsPerBlock, r = i - s * kRowsPerBlock;
+        sh.d[s][r] = delta[(((size_t)b * T + s) * H + h) * kD + row0 + r];
+    }
+    if (t < n)
+        sh.alpha[t] = alpha[((size_t)b * T + t) * H + h];
+}
+
+// T steps of the rule on the registers S (row lr, lane l8), writing o_t and
+// the innovation delta_t of the row (lane 0 of the row).
+__device__ __forceinline__ void record_steps(float4 S[4], const RecordShared &sh, int T, int H,
+                                             int b, int h, int row, int lr, int l8,
+                                             float *__restrict__ o, float *__restrict__ delta) {
     for (int s = 0; s < T; ++s) {
         const float a = sh.alpha[s], be = sh.beta[s];
         float4 k4[4];
@@ -154,19 +183,48 @@ __global__ __launch_bounds__(kThreads) void gdn_record_kernel(
         if (l8 == 0)
             o[off] = ov;
     }
-    if (S_final) {
-        float *frow = S_final + ((size_t)bh * kD + row) * kD + 4 * l8;
+}
+
+// The n staged tape steps applied to the registers S.
+__device__ __forceinline__ void commit_steps(float4 S[4], const CommitShared &sh, int n, int lr,
+                                             int l8) {
+    for (int s = 0; s < n; ++s) {
+        const float a = sh.alpha[s], d = sh.d[s][lr];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4 *>(frow + 32 * j) = S[j];
+        for (int j = 0; j < 4; ++j) {
+            const float4 k4 = sh.k[s][l8 + 8 * j];
+            S[j].x = gdn_update(S[j].x, a, d, k4.x);
+            S[j].y = gdn_update(S[j].y, a, d, k4.y);
+            S[j].z = gdn_update(S[j].z, a, d, k4.z);
+            S[j].w = gdn_update(S[j].w, a, d, k4.w);
+        }
     }
 }
 
-struct CommitShared {
-    float4 k[kMaxT][kD / 4];
-    float d[kMaxT][kRowsPerBlock];
-    float alpha[kMaxT];
-};
+__global__ __launch_bounds__(kThreads) void gdn_record_kernel(
+    const float *__restrict__ S0, const float *__restrict__ q, const float *__restrict__ k,
+    const float *__restrict__ v, const float *__restrict__ alpha, const float *__restrict__ beta,
+    int T, int H, int n_heads, float *__restrict__ o, float *__restrict__ delta,
+    float *__restrict__ S_final) {
+    __shared__ RecordShared sh;
+    const HeadBlock hb = head_block(blockIdx.x);
+    if (hb.bh >= n_heads)
+        return;
+    const int bh = hb.bh, row0 = hb.row0;
+    const int b = bh / H, h = bh - b * H;
+    const int t = threadIdx.x;
+    const int lr = t >> 3, l8 = t & 7;       // row within the block, lane within the row
+    const int row = row0 + lr;
+
+    // the state rows first (the long HBM reads), then the step inputs
+    float4 S[4];
+    load_rows(S, S0 + ((size_t)bh * kD + row) * kD + 4 * l8);
+    stage_record(sh, q, k, v, alpha, beta, b, h, T, H, row0, t);
+    __syncthreads();
+    record_steps(S, sh, T, H, b, h, row, lr, l8, o, delta);
+    if (S_final)
+        store_rows(S_final + ((size_t)bh * kD + row) * kD + 4 * l8, S);
+}
 
 __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(
     float *__restrict__ S, const float *__restrict__ alpha, const float *__restrict__ k,
@@ -186,34 +244,54 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(
     const int row = row0 + lr;
     float *srow = S + ((size_t)bh * kD + row) * kD + 4 * l8;
     float4 st[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        st[j] = load_once4(srow + 32 * j);
-    for (int i = t; i < n * (kD / 4); i += kThreads) {
-        const int s = i / (kD / 4), c4 = i - s * (kD / 4);
-        sh.k[s][c4] = reinterpret_cast<const float4 *>(k + (((size_t)b * T + s) * H + h) * kD)[c4];
-    }
-    for (int i = t; i < n * kRowsPerBlock; i += kThreads) {
-        const int s = i / kRowsPerBlock, r = i - s * kRowsPerBlock;
-        sh.d[s][r] = delta[(((size_t)b * T + s) * H + h) * kD + row0 + r];
-    }
-    if (t < n)
-        sh.alpha[t] = alpha[((size_t)b * T + t) * H + h];
+    load_rows(st, srow);
+    stage_commit(sh, alpha, k, delta, b, h, n, T, H, row0, t);
     __syncthreads();
-    for (int s = 0; s < n; ++s) {
-        const float a = sh.alpha[s], d = sh.d[s][lr];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 k4 = sh.k[s][l8 + 8 * j];
-            st[j].x = gdn_update(st[j].x, a, d, k4.x);
-            st[j].y = gdn_update(st[j].y, a, d, k4.y);
-            st[j].z = gdn_update(st[j].z, a, d, k4.z);
-            st[j].w = gdn_update(st[j].w, a, d, k4.w);
-        }
+    commit_steps(st, sh, n, lr, l8);
+    store_rows(srow, st);
+}
+
+// One cycle boundary in one pass over the state: the commit of the previous
+// cycle's accepted steps (tape of Tp positions), written back in place, then
+// the capture of the next T verify positions from the committed rows still
+// in registers.  The same staging and step functions as the two kernels
+// above, in the same order, so the results are theirs bit for bit.
+struct CycleShared {
+    CommitShared c;
+    RecordShared r;
+};
+
+__global__ __launch_bounds__(kThreads) void gdn_commit_record_kernel(
+    float *__restrict__ S, const float *__restrict__ prev_alpha,
+    const float *__restrict__ prev_k, const float *__restrict__ prev_delta,
+    const int32_t *__restrict__ n_steps, int Tp, const float *__restrict__ q,
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ alpha,
+    const float *__restrict__ beta, int T, int H, int n_heads, float *__restrict__ o,
+    float *__restrict__ delta, float *__restrict__ S_final) {
+    __shared__ CycleShared sh;
+    const HeadBlock hb = head_block(blockIdx.x);
+    if (hb.bh >= n_heads)
+        return;
+    const int bh = hb.bh, row0 = hb.row0;
+    const int b = bh / H, h = bh - b * H;
+    const int n = Tp > 0 ? min(n_steps[b], Tp) : 0;
+    const int t = threadIdx.x;
+    const int lr = t >> 3, l8 = t & 7;
+    const int row = row0 + lr;
+    float *srow = S + ((size_t)bh * kD + row) * kD + 4 * l8;
+    float4 st[4];
+    load_rows(st, srow);
+    if (n > 0)
+        stage_commit(sh.c, prev_alpha, prev_k, prev_delta, b, h, n, Tp, H, row0, t);
+    stage_record(sh.r, q, k, v, alpha, beta, b, h, T, H, row0, t);
+    __syncthreads();
+    if (n > 0) {
+        commit_steps(st, sh.c, n, lr, l8);
+        store_rows(srow, st);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4 *>(srow + 32 * j) = st[j];
+    record_steps(st, sh.r, T, H, b, h, row, lr, l8, o, delta);
+    if (S_final)
+        store_rows(S_final + ((size_t)bh * kD + row) * kD + 4 * l8, st);
 }
 
 } // namespace
@@ -236,6 +314,20 @@ hipError_t launch_gdn_commit(float *S, const float *alpha, const float *k, const
     const int groups = (B * H + 7) / 8;
     gdn_commit_kernel<<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
         S, alpha, k, delta, n_steps, T, H, B * H);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_commit_record(float *S, const float *prev_alpha, const float *prev_k,
+                                    const float *prev_delta, const int32_t *n_steps, int Tp,
+                                    const float *q, const float *k, const float *v,
+                                    const float *alpha, const float *beta, int B, int T, int H,
+                                    float *o, float *delta, float *S_final, hipStream_t stream) {
+    if (B == 0 || H == 0 || (Tp == 0 && T == 0 && !S_final))
+        return hipSuccess;
+    const int groups = (B * H + 7) / 8;
+    gdn_commit_record_kernel<<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
+        S, prev_alpha, prev_k, prev_delta, n_steps, Tp, q, k, v, alpha, beta, T, H, B * H, o,
+        delta, S_final);
     return hipGetLastError();
 }
 

@@ -112,5 +112,10 @@ hipError_t launch_gdn_record(const float *S0, const float *q, const float *k, co
                              float *o, float *delta, float *S_final, hipStream_t stream);
 hipError_t launch_gdn_commit(float *S, const float *alpha, const float *k, const float *delta,
                              const int32_t *n_steps, int B, int T, int H, hipStream_t stream);
+hipError_t launch_gdn_commit_record(float *S, const float *prev_alpha, const float *prev_k,
+                                    const float *prev_delta, const int32_t *n_steps, int Tp,
+                                    const float *q, const float *k, const float *v,
+                                    const float *alpha, const float *beta, int B, int T, int H,
+                                    float *o, float *delta, float *S_final, hipStream_t stream);
 
 } // namespace spec

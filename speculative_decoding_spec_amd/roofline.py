@@ -47,6 +47,20 @@ def gdn_commit_bytes(n_steps, H: int, d: int = 128) -> int:
     return total
 
 
+def gdn_commit_record_bytes(n_steps, T: int, H: int, d: int = 128) -> int:
+    """Bytes of the cycle boundary in one pass: every head's state read once
+    and, for sequences with n >= 1 steps, written back committed; n steps of
+    (alpha, k, delta) of the previous tape read; the step counts; then the
+    capture's step inputs read and its o and delta written (the state is
+    already in registers)."""
+    B = len(n_steps)
+    total = B * H * d * d * 4 + 4 * B
+    for n in n_steps:
+        if n > 0:
+            total += H * d * d * 4 + n * H * (2 * d + 1) * 4
+    return total + B * T * H * (3 * d + 2) * 4 + 2 * B * T * H * d * 4
+
+
 def qmv_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 

@@ -196,6 +196,40 @@ def test_gdn_validation(L):
     assert com(T=0) == OK and com(B=0) == OK
 
 
+def test_gdn_commit_record_validation(L):
+    # separate fake buffers 16 MB apart, so only the cases named overlap
+    buf = {n: ctypes.c_void_p((i + 1) << 24) for i, n in enumerate(
+        ["S", "pa", "pk", "pd", "n", "q", "k", "v", "a", "b", "o", "d", "sf"])}
+
+    def cr(B=2, Tp=6, T=6, H=4, dk=128, dv=128, **kw):
+        a = dict(buf, **kw)
+        return L.spec_gdn_commit_record(a["S"], a["pa"], a["pk"], a["pd"], a["n"], Tp, a["q"],
+                                        a["k"], a["v"], a["a"], a["b"], B, T, H, dk, dv,
+                                        a["o"], a["d"], a["sf"], None)
+
+    assert cr(B=-1) == INVALID and cr(Tp=-1) == INVALID and cr(T=-1) == INVALID
+    assert cr(dk=64) == UNSUPPORTED and cr(Tp=17) == UNSUPPORTED and cr(T=17) == UNSUPPORTED
+    assert cr(B=1 << 15, H=1 << 15) == UNSUPPORTED
+    assert cr(S=None) == INVALID and cr(n=None) == INVALID and cr(pd=None) == INVALID
+    assert cr(q=None) == INVALID and cr(o=None) == INVALID
+    assert cr(S=MIS) == UNSUPPORTED and cr(pk=MIS) == UNSUPPORTED and cr(k=MIS) == UNSUPPORTED
+    assert cr(pa=ctypes.c_void_p(0x10002)) == INVALID
+    assert cr(B=0) == OK and cr(H=0) == OK
+    # outputs sharing memory with any other argument are refused
+    assert cr(d=buf["pd"]) == INVALID                   # one tape buffer for both cycles
+    assert cr(o=buf["d"]) == INVALID
+    assert cr(sf=buf["S"]) == INVALID
+    assert cr(S=buf["k"]) == INVALID
+    assert cr(o=ctypes.c_void_p(buf["q"].value + 4096)) == INVALID   # partial overlap
+    # with nothing to commit (or record) those arguments may be NULL: the
+    # first error met is then the misaligned state
+    none_prev = dict(pa=None, pk=None, pd=None, n=None)
+    none_next = dict(q=None, k=None, v=None, a=None, b=None, o=None, d=None)
+    assert cr(Tp=0, S=MIS, **none_prev) == UNSUPPORTED
+    assert cr(T=0, S=MIS, **none_next) == UNSUPPORTED
+    assert cr(Tp=0, T=0, S=MIS, sf=None, **none_prev, **none_next) == UNSUPPORTED
+
+
 def test_requantize_validation(L):
     f = L.spec_requantize_w4
     assert f(P, -1, 128, 64, P, P, P, None) == INVALID

@@ -68,6 +68,19 @@ def error_bounds(S0, q, k, v, a, b):
     return E, ed_all, eo_all
 
 
+def commit_bound(S0, a, k, d, n_eff):
+    """First-order bound of n steps of fma(a, S, fl(d k)), two roundings each."""
+    mag = np.abs(S0.astype(np.float64))
+    bound = np.zeros_like(mag)
+    for t in range(a.shape[1]):
+        live = (t < n_eff)[:, None, None, None]
+        at = np.abs(a[:, t].astype(np.float64))[..., None, None]
+        dk = np.abs(d[:, t].astype(np.float64))[..., :, None] * np.abs(k[:, t].astype(np.float64))[..., None, :]
+        bound = np.where(live, at * bound + 2 * U * (at * mag + dk), bound)
+        mag = np.where(live, at * mag + dk, mag)
+    return bound
+
+
 def gpu_record(inp, dev):
     import torch
     import speculative_decoding_spec_amd as spec
@@ -136,16 +149,7 @@ def test_commit_parity_and_step_counts(dev):
     got = S.cpu().numpy()
     n_eff = np.clip(n, 0, T)
     ref = oracle.gdn_commit(S0, a, k, d_gpu, n_eff)
-    # bound: n steps of fma(a, S, fl(d k)), two roundings each
-    mag = np.abs(S0.astype(np.float64))
-    bound = np.zeros_like(mag)
-    for t in range(T):
-        live = (t < n_eff)[:, None, None, None]
-        at = np.abs(a[:, t].astype(np.float64))[..., None, None]
-        dk = np.abs(d_gpu[:, t].astype(np.float64))[..., :, None] * np.abs(k[:, t].astype(np.float64))[..., None, :]
-        bound = np.where(live, at * bound + 2 * U * (at * mag + dk), bound)
-        mag = np.where(live, at * mag + dk, mag)
-    assert np.all(np.abs(got - ref) <= 2 * bound + 1e-30)
+    assert np.all(np.abs(got - ref) <= 2 * commit_bound(S0, a, k, d_gpu, n_eff) + 1e-30)
     for i in (0, 1):                                  # nothing committed: untouched
         assert np.array_equal(got[i].view(np.uint32), S0[i].view(np.uint32))
 
@@ -165,3 +169,66 @@ def test_bench_shape_sampled_heads(dev):
         assert np.all(np.abs(o[bi:bi + 1, :, hi:hi + 1] - ref["o"]) <= 2 * eo + 1e-30)
         assert np.all(np.abs(d[bi:bi + 1, :, hi:hi + 1] - ref["delta"]) <= 2 * ed + 1e-30)
         assert np.all(np.abs(sf[bi:bi + 1, hi:hi + 1] - ref["S_final"]) <= 2 * E + 1e-30)
+
+
+@pytest.mark.parametrize("B,Tp,T,H", [(7, 6, 6, 4), (5, 3, 16, 3), (9, 16, 2, 1), (4, 6, 0, 2),
+                                      (3, 0, 5, 5), (8, 6, 6, 32)])
+def test_commit_record_equals_commit_then_record(dev, B, Tp, T, H):
+    """One pass at the cycle boundary (commit the previous tape, record the next
+    block) against spec_gdn_commit followed by spec_gdn_record: every output
+    bit for bit, with step counts below 0, 0, inside and above Tp."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    S0, _, pk, _, pa, _ = synth.gdn_inputs(920 + Tp, B, Tp, H)
+    _, q, k, v, a, b = synth.gdn_inputs(940 + T, B, T, H)
+    # a previous tape recorded from S0, and step counts of every kind
+    _, pd, _ = gpu_record(synth.gdn_inputs(920 + Tp, B, Tp, H), dev) if Tp else (None, None, None)
+    n = np.random.default_rng(B * 100 + Tp).integers(-1, Tp + 3, size=B).astype(np.int32)
+    n[:min(B, 4)] = np.array([-1, 0, Tp, 1], np.int32)[:min(B, 4)]
+    prev = (T_(pa, dev), T_(pk, dev), T_(pd, dev), T_(n, dev)) if Tp else (None,) * 4
+    nxt = [T_(x, dev) for x in (q, k, v, a, b)]
+
+    S_two = T_(S0, dev)
+    if Tp:
+        spec.spec_gdn_commit(S_two, *prev)
+    o2, d2, f2 = spec.spec_gdn_record(S_two, *nxt, want_final=True)
+    S_one = T_(S0, dev)
+    o1, d1, f1 = spec.spec_gdn_commit_record(S_one, *prev, *nxt, want_final=True)
+    torch.cuda.synchronize()
+    for name, x, y in (("S", S_one, S_two), ("o", o1, o2), ("delta", d1, d2),
+                       ("S_final", f1, f2)):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), name
+    print(f"commit_record B,Tp,T,H={B, Tp, T, H} n={n.tolist()}: bitwise equal", flush=True)
+
+
+def test_commit_record_cycles_match_the_oracle(dev):
+    """Three cycle boundaries chained through the fused call, each new tape in
+    its own buffer: per call, the committed state against the oracle's commit
+    of the previous tape (from the state the call started with) and o, delta
+    against the oracle's recording from that committed state, within the
+    bounds of the two tests above."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    B, T, H = 4, 5, 3
+    S = T_(synth.gdn_inputs(960, B, T, H)[0], dev)
+    prev, prev_host = (None,) * 4, None
+    for c in range(3):
+        _, q, k, v, a, b = synth.gdn_inputs(961 + c, B, T, H)
+        S_before = S.cpu().numpy()
+        o, d, _ = spec.spec_gdn_commit_record(S, *prev, *(T_(x, dev) for x in (q, k, v, a, b)))
+        torch.cuda.synchronize()
+        S_start = S.cpu().numpy()
+        if prev_host is None:
+            assert np.array_equal(S_start.view(np.uint32), S_before.view(np.uint32))
+        else:
+            pa, pk, pd, n_eff = prev_host
+            ref_S = oracle.gdn_commit(S_before, pa, pk, pd, n_eff)
+            assert np.all(np.abs(S_start - ref_S) <=
+                          2 * commit_bound(S_before, pa, pk, pd, n_eff) + 1e-30), c
+        ref = oracle.gdn_record(S_start, q, k, v, a, b)
+        _, ed, eo = error_bounds(S_start, q, k, v, a, b)
+        assert np.all(np.abs(o.cpu().numpy() - ref["o"]) <= 2 * eo + 1e-30), c
+        assert np.all(np.abs(d.cpu().numpy() - ref["delta"]) <= 2 * ed + 1e-30), c
+        n = np.array([(c + i) % (T + 2) - 1 for i in range(B)], np.int32)
+        prev = (T_(a, dev), T_(k, dev), d, T_(n, dev))
+        prev_host = (a, k, d.cpu().numpy(), np.clip(n, 0, T))
