@@ -182,6 +182,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
     return ((uint64_t)hi << 32) | lo;
 }
+// The k-th largest (1 <= k <= 64) of the wave's 64 distinct keys, to every
+// lane: k rounds of the wave max, each retiring the lane that holds it.
+__device__ __forceinline__ uint64_t wave_kth_largest(uint64_t v, int k) {
+    uint64_t top = 0;
+    for (int i = 0; i < k; ++i) {
+        top = wave_max_u64(v);
+        if (v == top)
+            v = 0;
+    }
+    return top;
+}
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
@@ -359,6 +370,7 @@ __device__ void block_sort_desc(uint64_t *keys, int n) {
 struct StatsShared {
     SelectShared sel;
     uint64_t keys[kMaxCand * 2];
+    uint64_t kth[kWaves];
     float fsh[kWaves];
     float fsh2[kWaves];
     int ish[kWaves];
@@ -521,10 +533,53 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
             if (lo + q * kThreads + (int)threadIdx.x < hi)
                 f(mine[q]);
     };
-    const int got = block_select_topk(each, n, sp.k_eff, sh.keys, kMaxCand, sh.sel);
+    const int want = min(sp.k_eff, n);
+    int got = -1;
+    if (n >= kThreads && want < kThreads) {
+        // Every thread holds a key.  Each wave finds the ceil(want / 4)-th
+        // largest of its 64 per-thread maxima; the smallest of those four is
+        // at most the want-th largest key (at least want distinct keys lie
+        // at or above it), so the keys at or above it hold the whole top-k.
+        // Those few are sorted by rank: no radix passes.
+        uint64_t tmax = 0;
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            tmax = max(tmax, mine[q]);
+        const uint64_t kth = wave_kth_largest(tmax, (want + kWaves - 1) / kWaves);
+        if ((threadIdx.x & 63) == 0)
+            sh.kth[threadIdx.x >> 6] = kth;
+        if (threadIdx.x == 0)
+            sh.sel.out_n = 0;
+        __syncthreads();
+        uint64_t theta = sh.kth[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            theta = min(theta, sh.kth[w]);
+        uint64_t *cand = sh.keys + kMaxCand;   // second half; the result goes to the first
+        each([&](uint64_t key) {
+            if (key >= theta) {
+                const int slot = atomicAdd(&sh.sel.out_n, 1);
+                if (slot < kMaxCand)
+                    cand[slot] = key;
+            }
+        });
+        __syncthreads();
+        const int C = sh.sel.out_n;
+        if (C <= kMaxCand) {   // else (many equal-valued... or spread keys): the general select
+            block_sort_desc(cand, C);
+            for (int i = threadIdx.x; i < want; i += kThreads)
+                sh.keys[i] = cand[i];
+            got = want;
+        }
+        __syncthreads();
+    }
+    const bool sorted = got >= 0;
+    if (!sorted)   // few keys, or too many above the bound: select among all
+        got = block_select_topk(each, n, sp.k_eff, sh.keys, kMaxCand, sh.sel);
     // the chunk's keys leave sorted (descending), so a small-k merge can walk
     // the chunks' lists from their heads
-    block_sort_desc(sh.keys, got);
+    if (!sorted)
+        block_sort_desc(sh.keys, got);
     bad = block_or(bad, sh.ish);
     finite = block_or(finite, sh.ish);
     if (chunks == 1) {
