@@ -29,7 +29,10 @@ block is timed on its own after the steps and reported under
 
 Printed: one JSON line.  `value` is the verify qmv throughput in HBM GB/s
 (algorithmic bytes / time of the qmv part of the steps); the acceptance
-throughput (verify positions per second) and per-M figures ride along.
+throughput (verify positions per second) and per-M figures ride along, and
+`stream_read` gives the rate of a plain streaming read of 2 GiB
+(`spec_stream_read`), of which `qmv_frac_of_stream` and
+`accept.frac_of_stream` are the two parts' shares.
 
 `roofline` covers qmv_kernel, the kernel with the most time per step (16
 launches): algorithmic bytes per launch over the average launch duration,
@@ -483,6 +486,33 @@ def copy_probe(dev):
     print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
+STREAM_BYTES = 2 << 30
+
+
+def stream_read_rate(dev, reps=10):
+    """GB/s of a plain streaming read of STREAM_BYTES (spec_stream_read: every
+    byte once, 16-byte non-temporal loads), 8x the last-level cache."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    src = torch.zeros(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(spec.STREAM_READ_GROUPS, dtype=torch.int32, device=dev)
+    call = spec.bind_stream_read(src, sink)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = STREAM_BYTES / (us * 1e-6) / 1e9
+    del src
+    return {"bytes": STREAM_BYTES, "us": round(us, 2), "GB/s": round(gbs, 1),
+            "frac": round(gbs / 8000.0, 4)}
+
+
 def measured_traffic(bytes_per_launch):
     """HBM bytes per qmv launch from the committed counter summary, or None
     when the summary is missing, belongs to another qmv.hip, or was taken on
@@ -844,6 +874,12 @@ def main():
         "accept (row statistics pass + fused decide/sum/draw)": {
             "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
             "us_per_call": round(acc_ms * 1e3, 2)}}
+    # The attainable read rate beside the published peak: a plain streaming
+    # read of 2 GiB (spec_stream_read), and each part's share of it.
+    sr = stream_read_rate(dev)
+    out["stream_read"] = sr
+    out["qmv_frac_of_stream"] = round(qmv_gbs / sr["GB/s"], 4)
+    out["accept"]["frac_of_stream"] = round(acc_gbs / sr["GB/s"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -351,6 +351,28 @@ spec_status spec_gdn_commit_record(float *S, const float *prev_alpha, const floa
                                    int dk, int dv, float *o, float *delta, float *S_final,
                                    hipStream_t stream);
 
+/* ------------------------------------------------------------------ */
+/* Measurement: attainable HBM read rate                                */
+/* ------------------------------------------------------------------ */
+/*
+ * The llama.cpp MTP article (section on the theoretical maximum of
+ * generation speed) bounds token generation by memory bandwidth -- memory
+ * speed over the bytes of the active weights -- and sets measured rates
+ * beside that bound.  spec_stream_read is the measured side on this GPU: a
+ * plain read of `bytes` bytes at `src` (16-byte aligned, bytes a multiple
+ * of 16; every byte read once, with the 16-byte non-temporal loads the hot
+ * kernels stream with), so a kernel's rate can be given as a share of the
+ * published peak and of what a plain read attains.  SPEC_STREAM_READ_GROUPS
+ * workgroups each fold the 32-bit words they read by XOR into sink[g]
+ * (SPEC_STREAM_READ_GROUPS uint32 words, 4-byte aligned, overwritten), so
+ * the XOR of all sink words is the XOR of all 32-bit words of src: no load
+ * is dead, and a caller can check that all were read.  bytes = 0 writes
+ * zeros.
+ */
+#define SPEC_STREAM_READ_GROUPS 2048
+
+spec_status spec_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

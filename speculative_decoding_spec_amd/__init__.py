@@ -22,6 +22,8 @@ Names follow the C ABI:
                                      the commit of the accepted steps
     spec_gdn_commit_record           both at a cycle boundary, one pass
                                      over the state
+    spec_stream_read                 a plain streaming read (attainable
+                                     HBM read rate, for measurement)
     spec_*_workspace_size            workspace queries
     bind_qmv / bind_verify_accept /  the same calls with arguments marshalled
     bind_verify_greedy / bind_gdn_*  once, for launch loops
@@ -105,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.spec_gdn_commit_record.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp,
                                              i, i, i, i, i, vp, vp, vp, vp]
         L.spec_gdn_commit_record.restype = i
+        L.spec_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.spec_stream_read.restype = i
         L.spec_verify_greedy_workspace.argtypes = [i, i, i]
         L.spec_verify_greedy_workspace.restype = sz
         L.spec_verify_greedy.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
@@ -640,6 +644,33 @@ def bind_gdn_commit(S, alpha, k, delta, n_steps, check: bool = True) -> _Bound:
     args = (_ptr(S), _ptr(alpha), _ptr(k), _ptr(delta), _ptr(n_steps), B, T, H, dk, dv,
             _stream(S.device))
     return _Bound("spec_gdn_commit", lib().spec_gdn_commit, args, (S, alpha, k, delta, n_steps))
+
+
+STREAM_READ_GROUPS = 2048   # SPEC_STREAM_READ_GROUPS
+
+
+def spec_stream_read(src, sink=None):
+    """A plain streaming read of a device tensor's bytes (16-byte aligned, a
+    multiple of 16 bytes); returns the int32 sink [2048] whose XOR is the XOR
+    of src's 32-bit words."""
+    import torch
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(STREAM_READ_GROUPS, dtype=torch.int32, device=src.device)
+    _require(sink, torch.int32, "sink", src.device)
+    if sink.numel() < STREAM_READ_GROUPS:
+        raise ValueError(f"sink must hold {STREAM_READ_GROUPS} words")
+    nbytes = src.numel() * src.element_size()
+    _check("spec_stream_read", lib().spec_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(src.device)))
+    return sink
+
+
+def bind_stream_read(src, sink) -> _Bound:
+    """spec_stream_read on fixed tensors, marshalled once (first call checked)."""
+    spec_stream_read(src, sink)
+    args = (_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src.device))
+    return _Bound("spec_stream_read", lib().spec_stream_read, args, (src, sink))
 
 
 def spec_requantize_w4(w_bf16, G: int = 64):

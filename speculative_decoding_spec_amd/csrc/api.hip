@@ -470,4 +470,14 @@ spec_status spec_gdn_commit_record(float *S, const float *prev_alpha, const floa
     return SPEC_OK;
 }
 
+spec_status spec_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    if (bytes % 16 != 0 || !sink || !aligned4(sink) || (bytes > 0 && !src))
+        return SPEC_ERR_INVALID;
+    if (bytes > 0 && !aligned16(src))
+        return SPEC_ERR_UNSUPPORTED;
+    if (spec::launch_stream_read(src, bytes, sink, SPEC_STREAM_READ_GROUPS, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
 } // extern "C"

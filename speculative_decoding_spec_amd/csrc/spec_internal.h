@@ -118,4 +118,10 @@ hipError_t launch_gdn_commit_record(float *S, const float *prev_alpha, const flo
                                     const float *alpha, const float *beta, int B, int T, int H,
                                     float *o, float *delta, float *S_final, hipStream_t stream);
 
+// ----------------------------------------------------------- measurement ----
+// A plain streaming read of `bytes` (a multiple of 16) with `groups`
+// workgroups; sink[g] receives the XOR of the 32-bit words workgroup g read.
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int groups,
+                              hipStream_t stream);
+
 } // namespace spec

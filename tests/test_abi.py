@@ -230,6 +230,16 @@ def test_gdn_commit_record_validation(L):
     assert cr(Tp=0, T=0, S=MIS, sf=None, **none_prev, **none_next) == UNSUPPORTED
 
 
+def test_stream_read_validation(L):
+    L.spec_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    f = L.spec_stream_read
+    assert f(P, 100, P2, None) == INVALID                      # not a multiple of 16
+    assert f(None, 64, P2, None) == INVALID
+    assert f(P, 64, None, None) == INVALID
+    assert f(P, 64, ctypes.c_void_p(0x20002), None) == INVALID  # sink not 4-byte aligned
+    assert f(MIS, 64, P2, None) == UNSUPPORTED                 # src not 16-byte aligned
+
+
 def test_requantize_validation(L):
     f = L.spec_requantize_w4
     assert f(P, -1, 128, 64, P, P, P, None) == INVALID
