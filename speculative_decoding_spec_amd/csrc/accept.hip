@@ -827,15 +827,37 @@ __device__ void stage_row_finals(const Rows &rows, const Ws &ws, const SamplingP
     __syncthreads();
 }
 
+// The inputs of sequence b's D ratio tests that do not depend on the row
+// statistics, loaded before those are staged so the two waits overlap:
+// lane i < D of wave 0 holds draft token i, its target and draft logits
+// (when the token is in range) and its uniform.  Called by all threads.
+struct DecideInputs {
+    int d;
+    float zt, zd, u;
+};
+__device__ DecideInputs load_decide_inputs(const Rows &rows, const int32_t *draft_tokens,
+                                           const float *uniforms, int b) {
+    DecideInputs in{-1, 0.0f, 0.0f, 0.0f};
+    const int i = threadIdx.x;
+    if (i < rows.D) {
+        in.d = draft_tokens[(size_t)b * rows.D + i];
+        in.u = uniforms[(size_t)b * (rows.D + 1) + i];
+        if (in.d >= 0 && in.d < rows.V) {
+            in.zt = rows.row(rows.target_row(b, i))[in.d];
+            in.zd = rows.row(rows.draft_row(b, i))[in.d];
+        }
+    }
+    return in;
+}
+
 // Decisions of sequence b from the row statistics, one position per lane
 // of wave 0: returns L (0..D) or -1 for an invalid sequence to every thread
 // of the block (through *sh_L).  When p_out / q_out are given, wave 0 also
 // writes P_i(d_i), Q_i(d_i) for the sequence (NaN if it is invalid).  Called
 // by all threads of the block.
 __device__ int decide_block(const Rows &rows, const Ws &ws, const SamplingParams &sp,
-                            const RowFinal *rf, const int32_t *draft_tokens,
-                            const float *uniforms, int b, float *p_out, float *q_out,
-                            int *sh_L) {
+                            const RowFinal *rf, const DecideInputs &in, int b, float *p_out,
+                            float *q_out, int *sh_L) {
     const int D = rows.D, V = rows.V;
     if (threadIdx.x < 64) {
         const int i = threadIdx.x;
@@ -846,14 +868,13 @@ __device__ int decide_block(const Rows &rows, const Ws &ws, const SamplingParams
         if (i < D) {
             const int tr = rows.target_row(b, i), dr = rows.draft_row(b, i);
             const RowFinal ft = rf[i], fd = rf[D + 1 + i];
-            const int d = draft_tokens[(size_t)b * D + i];
+            const int d = in.d;
             bad = bad || fd.flags != 0 || d < 0 || d >= V;
             if (!bad) {
-                const float zt = rows.row(tr)[d], zd = rows.row(dr)[d];
-                p = row_prob(ft, ws.row_keys + (size_t)tr * sp.k_eff, sp.candidates, sp.scale, zt, d);
-                q = row_prob(fd, ws.row_keys + (size_t)dr * sp.k_eff, sp.candidates, sp.scale, zd, d);
+                p = row_prob(ft, ws.row_keys + (size_t)tr * sp.k_eff, sp.candidates, sp.scale, in.zt, d);
+                q = row_prob(fd, ws.row_keys + (size_t)dr * sp.k_eff, sp.candidates, sp.scale, in.zd, d);
                 const float a = (p == 0.0f) ? 0.0f : p / q;
-                rej = !(uniforms[(size_t)b * (D + 1) + i] < a);
+                rej = !(in.u < a);
             }
         }
         const unsigned long long any_bad = __ballot(bad);
@@ -998,8 +1019,9 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const int V = rows.V;
     const int nblocks = (V + kBlock - 1) / kBlock;
     __shared__ RowFinal s_rf[2 * kMaxDepth + 1];
+    const DecideInputs din = load_decide_inputs(rows, draft_tokens, uniforms, b);
     stage_row_finals<kWaves>(rows, ws, sp, b, s_rf);
-    const int L = decide_block(rows, ws, sp, s_rf, draft_tokens, uniforms, b, nullptr, nullptr, &s_L);
+    const int L = decide_block(rows, ws, sp, s_rf, din, b, nullptr, nullptr, &s_L);
     if (L < 0)
         return;
     const DrawRows d = draw_rows(rows, ws, sp, s_rf, b, L);
@@ -1029,7 +1051,7 @@ using FinalShared = FinalSharedT<kWaves>;
 // vocabulary order.  The block runs belong to kThreads logical threads; in a
 // larger workgroup the other threads own none and only join the barriers.
 template <int NW>
-__device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, const Ws &ws,
+__device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, const float2 *bs,
                                 const DrawRows &d, int b, int L, float u, FinalSharedT<NW> &sh,
                                 int32_t *__restrict__ accepted_len,
                                 int32_t *__restrict__ next_token) {
@@ -1037,7 +1059,6 @@ __device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, cons
     const float scale = sp.scale;
     // ---- full vocabulary: find the block holding u * total ----
     const int nblocks = (V + kBlock - 1) / kBlock;
-    const float2 *bs = ws.block_sums + (size_t)b * nblocks;
     // Block masses: from the draw pass (residual mass, target mass), or, for
     // plain sampling, from the statistics pass's (block max, block sum).
     auto mass = [&](int k, bool target_mass) -> float {
@@ -1185,8 +1206,9 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     const int D = rows.D;
     const float scale = sp.scale;
 
+    const DecideInputs din = load_decide_inputs(rows, draft_tokens, uniforms, b);
     stage_row_finals<kWaves>(rows, ws, sp, b, sh.rf);
-    const int L = decide_block(rows, ws, sp, sh.rf, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    const int L = decide_block(rows, ws, sp, sh.rf, din, b, p_draft, q_draft, &sh.L);
     if (L < 0) {
         if (threadIdx.x == 0) {
             if (accepted_len) accepted_len[b] = -1;
@@ -1253,7 +1275,8 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         }
         return;
     }
-    draw_full_vocab(rows, sp, ws, d, b, L, u, sh, accepted_len, next_token);
+    draw_full_vocab(rows, sp, ws.block_sums + (size_t)b * ((rows.V + kBlock - 1) / kBlock), d, b, L, u,
+                    sh, accepted_len, next_token);
 }
 
 // Kernels 3 and 4 as one, for large batches (full vocabulary, verification):
@@ -1261,17 +1284,25 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
 // 16 waves, then draws.  Same block sums and draw as the two-kernel path, one
 // launch and one decision pass fewer.
 constexpr int kFusedThreads = 1024;
+// Block sums of rows up to this many 256-token blocks (262144 tokens) stay
+// in LDS; longer rows use the workspace.
+constexpr int kFusedLdsBlocks = 1024;
+template <int NW>
+struct FusedShared : FinalSharedT<NW> {
+    float2 bsum[kFusedLdsBlocks];
+};
 __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
     Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
     const float *__restrict__ uniforms, int32_t *__restrict__ accepted_len,
     int32_t *__restrict__ next_token, float *__restrict__ p_draft,
     float *__restrict__ q_draft, Ws ws) {
     constexpr int NW = kFusedThreads / 64;
-    __shared__ FinalSharedT<NW> sh;
+    __shared__ FusedShared<NW> sh;
     const int b = blockIdx.x;
     const int D = rows.D, V = rows.V;
+    const DecideInputs din = load_decide_inputs(rows, draft_tokens, uniforms, b);
     stage_row_finals<NW>(rows, ws, sp, b, sh.rf);
-    const int L = decide_block(rows, ws, sp, sh.rf, draft_tokens, uniforms, b, p_draft, q_draft, &sh.L);
+    const int L = decide_block(rows, ws, sp, sh.rf, din, b, p_draft, q_draft, &sh.L);
     if (L < 0) {
         if (threadIdx.x == 0) {
             if (accepted_len) accepted_len[b] = -1;
@@ -1282,9 +1313,10 @@ __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
     const float u = uniforms[(size_t)b * (D + 1) + D];
     const DrawRows d = draw_rows(rows, ws, sp, sh.rf, b, L);
     const int nblocks = (V + kBlock - 1) / kBlock;
-    block_draw_sums<NW>(d, sp, V, 0, nblocks, ws.block_sums + (size_t)b * nblocks);
+    float2 *bs = nblocks <= kFusedLdsBlocks ? sh.bsum : ws.block_sums + (size_t)b * nblocks;
+    block_draw_sums<NW>(d, sp, V, 0, nblocks, bs);
     __syncthreads();   // the block sums, written above, are read by other waves below
-    draw_full_vocab(rows, sp, ws, d, b, L, u, sh, accepted_len, next_token);
+    draw_full_vocab(rows, sp, bs, d, b, L, u, sh, accepted_len, next_token);
 }
 
 // ----------------------------------------------------------------- probs ----

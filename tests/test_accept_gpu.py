@@ -366,6 +366,25 @@ def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
             assert np.array_equal(part[key].view(np.uint64), big[key][lo:hi].view(np.uint64)), key
 
 
+def test_fused_draw_long_rows_parity(dev):
+    """Rows of more than 1024 draw blocks (300000 tokens): the fused kernel
+    keeps their block sums in the workspace instead of LDS.  Against the
+    oracle (the halves of this batch would be chunked differently, so the
+    bitwise comparison above does not apply).  Each differing pick must
+    still be a tie (within 1e-5 of the total mass of a boundary); at 300000
+    tokens the mean token mass, 3.3e-6 of the total, is below that window,
+    so near-boundary picks are likelier than on shorter rows and up to 5%
+    of the sequences may be ties."""
+    B, D, V = 130, 1, 300000
+    t, d = synth.logits_pair(770, B, D, V)
+    d[: B // 4] = t[: B // 4, :D]
+    toks = draft_tokens(d, 0.6, 0, 1.0, 770)
+    u = synth.uniforms(770, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev, max_tie_frac=0.05)
+    L = got["accepted_len"]
+    assert (L == D).sum() > 0 and (L == 0).sum() > 0
+
+
 @pytest.mark.parametrize("V,k,p", [
     (151936, 64, 1.0),      # largest k of the head-walk merge (38 chunk lists)
     (151936, 1, 1.0),       # greedy through the walk
