@@ -35,6 +35,8 @@
 // reproduces bitwise the state the recording reached after n steps.
 #include "spec_internal.h"
 
+#include <type_traits>
+
 namespace spec {
 namespace {
 
@@ -77,19 +79,29 @@ __device__ __forceinline__ float dot4(const float4 &s, const float4 &x) {
 // Sum over the 8 lanes of a row: swap neighbours, then pairs, then the two
 // quads (half-row mirror).  Every lane adds the same two values at each
 // step, so all 8 end with the same bits.
+// (Every lane is a valid source for these patterns, so the moves are free to
+// fold into the adds as DPP operands.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row8_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
     return x;
 }
 
+// Step inputs of a capture of TT steps (TT is a template argument so the
+// step loop unrolls fully: no loop-carried register copies of the state).
+template <int TT>
 struct RecordShared {
-    float4 k[kMaxT][kD / 4];
-    float4 q[kMaxT][kD / 4];
-    float v[kMaxT][kRowsPerBlock];
-    float alpha[kMaxT];
-    float beta[kMaxT];
+    static constexpr int N = TT > 0 ? TT : 1;
+    float4 k[N][kD / 4];
+    float4 q[N][kD / 4];
+    float v[N][kRowsPerBlock];
+    float alpha[N];
+    float beta[N];
 };
 
 struct CommitShared {
@@ -112,7 +124,8 @@ __device__ __forceinline__ void store_rows(float *srow, const float4 S[4]) {
 }
 
 // Step inputs of the T positions of (b, h) for the block's rows, into LDS.
-__device__ __forceinline__ void stage_record(RecordShared &sh, const float *q, const float *k,
+template <int TT>
+__device__ __forceinline__ void stage_record(RecordShared<TT> &sh, const float *q, const float *k,
                                              const float *v, const float *alpha,
                                              const float *beta, int b, int h, int T, int H,
                                              int row0, int t) {
@@ -152,9 +165,12 @@ __device__ __forceinline__ void stage_commit(CommitShared &sh, const float *alph
 
 // T steps of the rule on the registers S (row lr, lane l8), writing o_t and
 // the innovation delta_t of the row (lane 0 of the row).
-__device__ __forceinline__ void record_steps(float4 S[4], const RecordShared &sh, int T, int H,
+template <int TT>
+__device__ __forceinline__ void record_steps(float4 S[4], const RecordShared<TT> &sh, int H,
                                              int b, int h, int row, int lr, int l8,
                                              float *__restrict__ o, float *__restrict__ delta) {
+    constexpr int T = TT;
+#pragma unroll
     for (int s = 0; s < T; ++s) {
         const float a = sh.alpha[s], be = sh.beta[s];
         float4 k4[4];
@@ -201,12 +217,14 @@ __device__ __forceinline__ void commit_steps(float4 S[4], const CommitShared &sh
     }
 }
 
+template <int TT>
 __global__ __launch_bounds__(kThreads) void gdn_record_kernel(
     const float *__restrict__ S0, const float *__restrict__ q, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ alpha, const float *__restrict__ beta,
-    int T, int H, int n_heads, float *__restrict__ o, float *__restrict__ delta,
+    int H, int n_heads, float *__restrict__ o, float *__restrict__ delta,
     float *__restrict__ S_final) {
-    __shared__ RecordShared sh;
+    constexpr int T = TT;
+    __shared__ RecordShared<TT> sh;
     const HeadBlock hb = head_block(blockIdx.x);
     if (hb.bh >= n_heads)
         return;
@@ -221,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void gdn_record_kernel(
     load_rows(S, S0 + ((size_t)bh * kD + row) * kD + 4 * l8);
     stage_record(sh, q, k, v, alpha, beta, b, h, T, H, row0, t);
     __syncthreads();
-    record_steps(S, sh, T, H, b, h, row, lr, l8, o, delta);
+    record_steps<TT>(S, sh, H, b, h, row, lr, l8, o, delta);
     if (S_final)
         store_rows(S_final + ((size_t)bh * kD + row) * kD + 4 * l8, S);
 }
@@ -256,19 +274,22 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(
 // the capture of the next T verify positions from the committed rows still
 // in registers.  The same staging and step functions as the two kernels
 // above, in the same order, so the results are theirs bit for bit.
+template <int TT>
 struct CycleShared {
     CommitShared c;
-    RecordShared r;
+    RecordShared<TT> r;
 };
 
+template <int TT>
 __global__ __launch_bounds__(kThreads) void gdn_commit_record_kernel(
     float *__restrict__ S, const float *__restrict__ prev_alpha,
     const float *__restrict__ prev_k, const float *__restrict__ prev_delta,
     const int32_t *__restrict__ n_steps, int Tp, const float *__restrict__ q,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ alpha,
-    const float *__restrict__ beta, int T, int H, int n_heads, float *__restrict__ o,
+    const float *__restrict__ beta, int H, int n_heads, float *__restrict__ o,
     float *__restrict__ delta, float *__restrict__ S_final) {
-    __shared__ CycleShared sh;
+    constexpr int T = TT;
+    __shared__ CycleShared<TT> sh;
     const HeadBlock hb = head_block(blockIdx.x);
     if (hb.bh >= n_heads)
         return;
@@ -289,9 +310,24 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_record_kernel(
         commit_steps(st, sh.c, n, lr, l8);
         store_rows(srow, st);
     }
-    record_steps(st, sh.r, T, H, b, h, row, lr, l8, o, delta);
+    record_steps<TT>(st, sh.r, H, b, h, row, lr, l8, o, delta);
     if (S_final)
         store_rows(S_final + ((size_t)bh * kD + row) * kD + 4 * l8, st);
+}
+
+// Calls f(std::integral_constant<int, T>) for 0 <= T <= kMaxT (the kernels'
+// step count is a template argument), then reports the launch status.
+template <int TT = 0, class F>
+hipError_t with_steps(int T, F &&f) {
+    if constexpr (TT > kMaxT) {
+        return hipErrorInvalidValue;
+    } else {
+        if (T == TT) {
+            f(std::integral_constant<int, TT>{});
+            return hipGetLastError();
+        }
+        return with_steps<TT + 1>(T, f);
+    }
 }
 
 } // namespace
@@ -302,9 +338,10 @@ hipError_t launch_gdn_record(const float *S0, const float *q, const float *k, co
     if (B == 0 || H == 0 || (T == 0 && !S_final))
         return hipSuccess;
     const int groups = (B * H + 7) / 8;   // 8 heads per group of 32 workgroups
-    gdn_record_kernel<<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
-        S0, q, k, v, alpha, beta, T, H, B * H, o, delta, S_final);
-    return hipGetLastError();
+    return with_steps(T, [&](auto tt) {
+        gdn_record_kernel<decltype(tt)::value><<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
+            S0, q, k, v, alpha, beta, H, B * H, o, delta, S_final);
+    });
 }
 
 hipError_t launch_gdn_commit(float *S, const float *alpha, const float *k, const float *delta,
@@ -325,10 +362,12 @@ hipError_t launch_gdn_commit_record(float *S, const float *prev_alpha, const flo
     if (B == 0 || H == 0 || (Tp == 0 && T == 0 && !S_final))
         return hipSuccess;
     const int groups = (B * H + 7) / 8;
-    gdn_commit_record_kernel<<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
-        S, prev_alpha, prev_k, prev_delta, n_steps, Tp, q, k, v, alpha, beta, T, H, B * H, o,
-        delta, S_final);
-    return hipGetLastError();
+    return with_steps(T, [&](auto tt) {
+        gdn_commit_record_kernel<decltype(tt)::value>
+            <<<groups * 8 * kBlocksPerHead, kThreads, 0, stream>>>(
+                S, prev_alpha, prev_k, prev_delta, n_steps, Tp, q, k, v, alpha, beta, H, B * H, o,
+                delta, S_final);
+    });
 }
 
 } // namespace spec
