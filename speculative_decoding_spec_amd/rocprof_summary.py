@@ -4,6 +4,10 @@
         per kernel: calls, average / min / max duration (us), grid, workgroup
     python -m speculative_decoding_spec_amd.rocprof_summary counters DB [--match S ...]
         per kernel and counter: dispatches and average value per dispatch
+    python -m speculative_decoding_spec_amd.rocprof_summary derived DB [--match S ...]
+        per kernel, from SQ_WAVES, SQ_INSTS_VALU, SQ_INSTS_SALU, TCC_HIT_sum and
+        TCC_MISS_sum: waves per dispatch, VALU and SALU instructions per wave,
+        and the L2 hit rate of its requests
     python -m speculative_decoding_spec_amd.rocprof_summary traffic \
             --fetch DB --write DB --copy-fetch DB --copy-write DB \
             --copy-bytes N --match S --source FILE [--mix GRID_X:N ...]
@@ -160,9 +164,25 @@ def traffic(a) -> None:
     print(f"traffic_bytes_per_launch: {fk * 1024 * fetch_factor + wk * 1024 * write_factor:.0f}")
 
 
+def derived(db: str, match=None):
+    """Per kernel and grid: instructions per wave and L2 hit rate."""
+    per: dict = {}
+    for r in counter_rows(db, match):
+        per.setdefault((r["kernel"], r["grid"]), {})[r["counter"]] = r["avg"]
+    print(f"{'kernel':<44} {'grid':>14} {'waves':>8} {'VALU/wave':>10} {'SALU/wave':>10} "
+          f"{'L2 hit %':>9}")
+    for (k, g), c in sorted(per.items()):
+        waves = c.get("SQ_WAVES", 0.0)
+        hit, miss = c.get("TCC_HIT_sum"), c.get("TCC_MISS_sum")
+        v = c.get("SQ_INSTS_VALU", 0.0) / waves if waves else float("nan")
+        sa = c.get("SQ_INSTS_SALU", 0.0) / waves if waves else float("nan")
+        h = 100.0 * hit / (hit + miss) if hit is not None and miss is not None and hit + miss else float("nan")
+        print(f"{k:<44} {g:>14} {waves:>8.0f} {v:>10.1f} {sa:>10.1f} {h:>9.1f}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["trace", "counters", "traffic"])
+    ap.add_argument("mode", choices=["trace", "counters", "traffic", "derived"])
     ap.add_argument("db", nargs="?")
     ap.add_argument("--match", nargs="*")
     ap.add_argument("--fetch")
@@ -175,6 +195,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.mode == "traffic":
         traffic(a)
+    elif a.mode == "derived":
+        derived(a.db, a.match)
     elif a.mode == "trace":
         print(f"{'kernel':<44} {'grid':>14} {'wg':>5} {'calls':>6} {'avg_us':>9} "
               f"{'min_us':>9} {'max_us':>9} {'total_us':>10}")
