@@ -163,24 +163,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) {
     return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, -INFINITY);
 }
-// The same tree for unsigned 64-bit keys (max; 0 is the identity).
+// The same tree on unsigned 32-bit words (max; 0 is the identity), to every
+// lane.
 template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1, 0xF>(v));
+    v = max(v, dpp_u32<0x4E, 0xF>(v));
+    v = max(v, dpp_u32<0x141, 0xF>(v));
+    v = max(v, dpp_u32<0x140, 0xF>(v));
+    v = max(v, dpp_u32<0x142, 0xA>(v));
+    v = max(v, dpp_u32<0x143, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Largest key of the wave, to every lane: the largest high word first (the
+// logit's code), then, only if several lanes hold it, the largest low word
+// among them; otherwise the one lane's low word is read directly.  The same
+// result as a 64-bit tree, in about a third of the instructions.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    uint64_t t;
-    t = dpp_u64<0xB1, 0xF>(v);  v = t > v ? t : v;
-    t = dpp_u64<0x4E, 0xF>(v);  v = t > v ? t : v;
-    t = dpp_u64<0x141, 0xF>(v); v = t > v ? t : v;
-    t = dpp_u64<0x140, 0xF>(v); v = t > v ? t : v;
-    t = dpp_u64<0x142, 0xA>(v); v = t > v ? t : v;
-    t = dpp_u64<0x143, 0xC>(v); v = t > v ? t : v;
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const unsigned long long at = __ballot(hi == mh);
+    uint32_t lo;
+    if (__popcll(at) == 1)
+        lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __ffsll((long long)at) - 1);
+    else
+        lo = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+    return ((uint64_t)mh << 32) | lo;
 }
 // The k-th largest (1 <= k <= 64) of the wave's 64 distinct keys, to every
 // lane: k rounds of the wave max, each retiring the lane that holds it.
