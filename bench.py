@@ -141,7 +141,7 @@ def lmhead(dev, steps):
              for c in range(3)]
     x = synth.torch_activations(D + 1, K, 8410, dev)
     logits = torch.empty((D + 1, V), dtype=torch.float32, device=dev)
-    spec.spec_qmv_w4(heads[0], x, logits)
+    spec.spec_qmv_w4_packed(heads[0], x, logits)
     g = torch.Generator(device=dev)
     g.manual_seed(8411)
     draft = (logits[:D] - torch.randn((D, V), generator=g, device=dev) * 0.5).contiguous()

@@ -67,39 +67,50 @@ int spec_version(void);
  * m < M, n < N: every weight of the target's linear layer is streamed once
  * and serves all M = D + 1 verify rows (affine group quantization as in the
  * mlxcel manual's "MTP and DFlash" page, draft block width section; MTPLX
- * "Layer 0: MLX Runtime").
+ * "Layer 0: MLX Runtime", the small-M quantized matrix-vector product on the
+ * model's own quantized weights).
  *
- * Weights are given once in the interchange layout below and packed by
- * spec_pack_w4 / spec_pack_w8 into the layout the kernel streams (tiles of
- * 16 rows x 128 k, each read by one wave as 1 KB contiguous; scale and bias
- * interleaved).  Packing is a one-time, load-time step; spec_qmv_* read only
- * the packed buffers.
- *
- * Interchange layout (inputs of spec_pack_*):
+ * spec_qmv_w4 / spec_qmv_w8 read the weights as stored (interchange layout):
  *  w       W4: uint32 [N][K/8]; element k of row n is bits 4*(k%8)..4*(k%8)+3
  *          of word k/8 (unsigned code 0..15).  16-byte aligned.
  *          W8: uint8 [N][K]; one unsigned code 0..255 per byte.  16-byte aligned.
- *  scales  fp16 bit patterns [N][K/G]  (s)
- *  biases  fp16 bit patterns [N][K/G]  (b)
- *  N >= 0, K >= 0 with K % G == 0, G == 64 (SPEC_ERR_UNSUPPORTED otherwise).
+ *  scales  fp16 bit patterns [N][K/G]  (s), 2-byte aligned
+ *  biases  fp16 bit patterns [N][K/G]  (b), 2-byte aligned
+ *  x       bf16 bit patterns [M][K], 16-byte aligned
+ *  y       fp32 [M][N], written (never read), 4-byte aligned
+ *  M       1..16 rows (0 is a no-op).  Up to 8 rows fill the verify blocks of
+ *          MTP depths D <= 7; 9..16 rows cover the 16-wide blocks of DFlash
+ *          drafters (mlxcel manual, "MTP and DFlash": the comparison table's
+ *          typical width, and split-mtp's block size of at most 16).
+ *  N >= 0, 0 <= K < 2^24 with K % G == 0, G == 64, N <= 2^28
+ *          (SPEC_ERR_UNSUPPORTED otherwise; a misaligned w or x is
+ *          SPEC_ERR_UNSUPPORTED, a misaligned scales, biases or y
+ *          SPEC_ERR_INVALID).
  *
- * Packed buffers (outputs of spec_pack_*, device memory owned by the caller):
+ * spec_qmv_w4_packed / spec_qmv_w8_packed compute the same products from a
+ * copy of the weights that spec_pack_w4 / spec_pack_w8 rearranged once, at
+ * load time, into the order the kernel streams (tiles of 16 rows x 128 k,
+ * each read by one wave as contiguous 1 KB runs; scale and bias interleaved
+ * in one 32-bit word).  Both forms give bitwise the same y; the packed form
+ * is the faster one on the verify shapes (a load instruction reads 1 KB of
+ * contiguous memory instead of 64 or 128 bytes from each of 16 rows), at the
+ * cost of a second copy of the weights.
  *  w_packed   spec_qmv_packed_weight_bytes(bits, N, K, G) bytes, 16-byte aligned
  *  sb_packed  spec_qmv_packed_sb_bytes(N, K, G) bytes, 4-byte aligned
- *
- * spec_qmv_*:
- *  x       bf16 bit patterns [M][K], 16-byte aligned
- *  y       fp32 [M][N], written (never read)
- *  M       1..16 rows (0 is a no-op); N, K, G as given to spec_pack_*.
- *          Up to 8 rows fill the verify blocks of MTP depths D <= 7; 9..16
- *          rows cover the 16-wide blocks of DFlash drafters (mlxcel manual,
- *          "MTP and DFlash": the comparison table's typical width, and
- *          split-mtp's block size of at most 16).
+ *  spec_pack_* take w, scales and biases in the interchange layout above.
  *
  * Results are deterministic, and row m of an M-row call is bitwise equal to
  * the one-row call on x[m] (the reduction order does not depend on M, also
  * across the 8-row boundary).
  */
+spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                        const uint16_t *x, float *y, int M, int N, int K, int G,
+                        hipStream_t stream);
+
+spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales, const uint16_t *biases,
+                        const uint16_t *x, float *y, int M, int N, int K, int G,
+                        hipStream_t stream);
+
 size_t spec_qmv_packed_weight_bytes(int bits, int N, int K, int G);
 size_t spec_qmv_packed_sb_bytes(int N, int K, int G);
 
@@ -111,13 +122,13 @@ spec_status spec_pack_w8(const uint8_t *w, const uint16_t *scales,
                          const uint16_t *biases, int N, int K, int G,
                          void *w_packed, void *sb_packed, hipStream_t stream);
 
-spec_status spec_qmv_w4(const void *w_packed, const void *sb_packed,
-                        const uint16_t *x, float *y, int M, int N, int K,
-                        int G, hipStream_t stream);
+spec_status spec_qmv_w4_packed(const void *w_packed, const void *sb_packed,
+                               const uint16_t *x, float *y, int M, int N, int K,
+                               int G, hipStream_t stream);
 
-spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
-                        const uint16_t *x, float *y, int M, int N, int K,
-                        int G, hipStream_t stream);
+spec_status spec_qmv_w8_packed(const void *w_packed, const void *sb_packed,
+                               const uint16_t *x, float *y, int M, int N, int K,
+                               int G, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* Draft-only 4-bit copy of a weight matrix                             */

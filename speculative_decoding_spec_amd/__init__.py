@@ -8,8 +8,12 @@ built library (``libspec.so`` next to this file) raises immediately.
 
 Names follow the C ABI:
 
-    spec_pack_w4 / spec_pack_w8      one-time repack of quantized weights
-    spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv
+    spec_qmv_w4 / spec_qmv_w8        small-M group-quantized verify qmv on the
+                                     weights as stored (w, scales, biases)
+    spec_pack_w4 / spec_pack_w8      one-time repack of quantized weights into
+                                     the order the kernel streams
+    spec_qmv_w4_packed /             the same product from the repacked copy
+    spec_qmv_w8_packed               (the faster form)
     spec_requantize_w4               draft-only 4-bit copy of a bf16 matrix
     spec_pack_gate_up /              gate and up projections as one launch with
     spec_qmv_gate_up_silu            the SiLU-gated activation applied (bf16 out)
@@ -79,6 +83,10 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
             fn.restype = i
         for name in ("spec_qmv_w4", "spec_qmv_w8"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
+            fn.restype = i
+        for name in ("spec_qmv_w4_packed", "spec_qmv_w8_packed"):
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
             fn.restype = i
@@ -284,35 +292,84 @@ def bind_qmv_gate_up_silu(packed: PackedGateUp, x, h) -> "_Bound":
     return _Bound("spec_qmv_gate_up_silu", lib().spec_qmv_gate_up_silu, args, (packed, x, h))
 
 
-def _qmv(name, bits, packed, x, y):
+class QWeights:
+    """Quantized weights in the interchange layout, as stored: w int32
+    [N][K/8] (W4, element k at bits 4*(k%8) of word k/8) or uint8 [N][K]
+    (W8), scales / biases fp16 [N][K/G].  Read directly by spec_qmv_w4 /
+    spec_qmv_w8."""
+
+    def __init__(self, bits, w, scales, biases, G=64):
+        import torch
+        dev = w.device
+        _require(w, torch.int32 if bits == 4 else torch.uint8, "w", dev)
+        _require(scales, torch.float16, "scales", dev)
+        _require(biases, torch.float16, "biases", dev)
+        N = w.shape[0]
+        K = w.shape[1] * 8 if bits == 4 else w.shape[1]
+        if G <= 0 or K % G:
+            raise ValueError("K must be a multiple of G")
+        if tuple(scales.shape) != (N, K // G) or tuple(biases.shape) != (N, K // G):
+            raise ValueError(f"scales / biases must be [{N}][{K // G}]")
+        self.bits, self.N, self.K, self.G = bits, N, K, G
+        self.w, self.scales, self.biases = w, scales, biases
+
+
+def _qmv_args(weights, x, y):
+    """(C function name, argument tuple) of one qmv call, checked."""
     import torch
     dev = x.device
-    if packed.bits != bits:
-        raise ValueError(f"{name} needs W{bits} packed weights, got W{packed.bits}")
     _require(x, torch.bfloat16, "x", dev)
     M, K = x.shape
-    if K != packed.K:
-        raise ValueError(f"x has K={K}, weights have K={packed.K}")
-    N = packed.N
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if K != weights.K:
+        raise ValueError(f"x has K={K}, weights have K={weights.K}")
     _require(y, torch.float32, "y", dev)
-    if tuple(y.shape) != (M, N):
-        raise ValueError(f"y must be [{M}][{N}]")
-    st = getattr(lib(), name)(_ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(y),
-                              M, N, K, packed.G, _stream(dev))
-    _check(name, st)
+    if tuple(y.shape) != (M, weights.N):
+        raise ValueError(f"y must be [{M}][{weights.N}]")
+    if isinstance(weights, PackedWeights):
+        name = f"spec_qmv_w{weights.bits}_packed"
+        args = (_ptr(weights.w), _ptr(weights.sb), _ptr(x), _ptr(y), M, weights.N, K, weights.G,
+                _stream(dev))
+    elif isinstance(weights, QWeights):
+        name = f"spec_qmv_w{weights.bits}"
+        args = (_ptr(weights.w), _ptr(weights.scales), _ptr(weights.biases), _ptr(x), _ptr(y), M,
+                weights.N, K, weights.G, _stream(dev))
+    else:
+        raise TypeError("weights must be QWeights or PackedWeights")
+    return name, args
+
+
+def _qmv(weights, x, y):
+    import torch
+    if y is None:
+        y = torch.empty((x.shape[0], weights.N), dtype=torch.float32, device=x.device)
+    name, args = _qmv_args(weights, x, y)
+    _check(name, getattr(lib(), name)(*args))
     return y
 
 
-def spec_qmv_w4(packed: PackedWeights, x, y=None):
-    """y[M][N] fp32 = x[M][K] (bf16) times the dequantized W4 matrix."""
-    return _qmv("spec_qmv_w4", 4, packed, x, y)
+def spec_qmv_w4(w, scales, biases, x, y=None, G: int = 64):
+    """y[M][N] fp32 = x[M][K] (bf16) times the dequantized W4 matrix given as
+    stored: w int32 [N][K/8], scales / biases fp16 [N][K/G]."""
+    return _qmv(QWeights(4, w, scales, biases, G), x, y)
 
 
-def spec_qmv_w8(packed: PackedWeights, x, y=None):
-    """As spec_qmv_w4 for W8 packed weights."""
-    return _qmv("spec_qmv_w8", 8, packed, x, y)
+def spec_qmv_w8(w, scales, biases, x, y=None, G: int = 64):
+    """As spec_qmv_w4 for W8 weights: w uint8 [N][K]."""
+    return _qmv(QWeights(8, w, scales, biases, G), x, y)
+
+
+def spec_qmv_w4_packed(packed: PackedWeights, x, y=None):
+    """spec_qmv_w4 from weights repacked by spec_pack_w4."""
+    if packed.bits != 4:
+        raise ValueError(f"spec_qmv_w4_packed needs W4 packed weights, got W{packed.bits}")
+    return _qmv(packed, x, y)
+
+
+def spec_qmv_w8_packed(packed: PackedWeights, x, y=None):
+    """spec_qmv_w8 from weights repacked by spec_pack_w8."""
+    if packed.bits != 8:
+        raise ValueError(f"spec_qmv_w8_packed needs W8 packed weights, got W{packed.bits}")
+    return _qmv(packed, x, y)
 
 
 class _Bound:
@@ -330,15 +387,13 @@ class _Bound:
             raise SpecError(self.name, st)
 
 
-def bind_qmv(packed: PackedWeights, x, y) -> _Bound:
-    """spec_qmv_w4 / spec_qmv_w8 on fixed tensors, marshalled once.  The
-    first call is checked like spec_qmv_* (it runs through them)."""
-    name = "spec_qmv_w4" if packed.bits == 4 else "spec_qmv_w8"
-    _qmv(name, packed.bits, packed, x, y)
-    M, K = x.shape
-    args = (_ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(y), M, packed.N, K, packed.G,
-            _stream(x.device))
-    return _Bound(name, getattr(lib(), name), args, (packed, x, y))
+def bind_qmv(weights, x, y) -> _Bound:
+    """A qmv on fixed tensors, marshalled once: weights are PackedWeights
+    (spec_qmv_w*_packed) or QWeights (spec_qmv_w*, interchange layout).  The
+    first call is checked like the unbound functions."""
+    name, args = _qmv_args(weights, x, y)
+    _check(name, getattr(lib(), name)(*args))
+    return _Bound(name, getattr(lib(), name), args, (weights, x, y))
 
 
 def spec_verify_accept_workspace(B: int, D: int, V: int, top_k: int) -> int:

@@ -35,8 +35,10 @@ spec_status qmv_shape_ok(int N, int K, int G) {
         return SPEC_ERR_INVALID;
     if (G != 64)
         return SPEC_ERR_UNSUPPORTED;
-    // 32-bit byte offsets inside one 16-row tile and inside x
-    if ((size_t)K * 2 > ((size_t)1 << 30) || N > (1 << 28))
+    // Buffer ranges and offsets inside the kernels are 32-bit: with K below
+    // 2^24 a packed tile (K/128 pairs of up to 2 KB), sixteen interchange rows
+    // (16 K bytes at W8) and x (16 rows of 2 K bytes) all stay below 2^29.
+    if (K >= (1 << 24) || N > (1 << 28))
         return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
 }
@@ -59,9 +61,9 @@ spec_status pack_common(int bits, const void *w, const uint16_t *scales,
     return SPEC_OK;
 }
 
-spec_status qmv_common(int bits, const void *w_packed, const void *sb_packed,
-                       const uint16_t *x, float *y, int M, int N, int K, int G,
-                       hipStream_t stream) {
+spec_status qmv_common(int bits, bool interchange, const void *w, const void *sb,
+                       const uint16_t *biases, const uint16_t *x, float *y, int M, int N,
+                       int K, int G, hipStream_t stream) {
     if (M < 0)
         return SPEC_ERR_INVALID;
     const spec_status s = qmv_shape_ok(N, K, G);
@@ -71,13 +73,18 @@ spec_status qmv_common(int bits, const void *w_packed, const void *sb_packed,
         return SPEC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0)
         return SPEC_OK;
-    if (!y || (K > 0 && (!w_packed || !sb_packed || !x)))
+    if (!y || (K > 0 && (!w || !sb || !x || (interchange && !biases))))
         return SPEC_ERR_INVALID;
-    if (K > 0 && (!aligned16(w_packed) || !aligned16(x) || !aligned4(sb_packed)))
+    if (K > 0 && (!aligned16(w) || !aligned16(x)))
         return SPEC_ERR_UNSUPPORTED;
+    if (K > 0 && !interchange && !aligned4(sb))
+        return SPEC_ERR_UNSUPPORTED;
+    if (K > 0 && interchange &&
+        ((reinterpret_cast<uintptr_t>(sb) | reinterpret_cast<uintptr_t>(biases)) & 1u))
+        return SPEC_ERR_INVALID;
     if (!aligned4(y))
         return SPEC_ERR_INVALID;
-    if (spec::launch_qmv(bits, w_packed, sb_packed, x, y, M, N, K, stream) != hipSuccess)
+    if (spec::launch_qmv(bits, interchange, w, sb, biases, x, y, M, N, K, stream) != hipSuccess)
         return SPEC_ERR_DEVICE;
     return SPEC_OK;
 }
@@ -141,16 +148,28 @@ spec_status spec_pack_w8(const uint8_t *w, const uint16_t *scales,
     return pack_common(8, w, scales, biases, N, K, G, w_packed, sb_packed, stream);
 }
 
-spec_status spec_qmv_w4(const void *w_packed, const void *sb_packed,
+spec_status spec_qmv_w4(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
                         const uint16_t *x, float *y, int M, int N, int K, int G,
                         hipStream_t stream) {
-    return qmv_common(4, w_packed, sb_packed, x, y, M, N, K, G, stream);
+    return qmv_common(4, true, w, scales, biases, x, y, M, N, K, G, stream);
 }
 
-spec_status spec_qmv_w8(const void *w_packed, const void *sb_packed,
+spec_status spec_qmv_w8(const uint8_t *w, const uint16_t *scales, const uint16_t *biases,
                         const uint16_t *x, float *y, int M, int N, int K, int G,
                         hipStream_t stream) {
-    return qmv_common(8, w_packed, sb_packed, x, y, M, N, K, G, stream);
+    return qmv_common(8, true, w, scales, biases, x, y, M, N, K, G, stream);
+}
+
+spec_status spec_qmv_w4_packed(const void *w_packed, const void *sb_packed,
+                               const uint16_t *x, float *y, int M, int N, int K, int G,
+                               hipStream_t stream) {
+    return qmv_common(4, false, w_packed, sb_packed, nullptr, x, y, M, N, K, G, stream);
+}
+
+spec_status spec_qmv_w8_packed(const void *w_packed, const void *sb_packed,
+                               const uint16_t *x, float *y, int M, int N, int K, int G,
+                               hipStream_t stream) {
+    return qmv_common(8, false, w_packed, sb_packed, nullptr, x, y, M, N, K, G, stream);
 }
 
 spec_status spec_requantize_w4(const uint16_t *w_bf16, int N, int K, int G, uint32_t *w4,

@@ -12,21 +12,32 @@
 //    and its 4 or 8 waves split K, each wave taking a contiguous run of
 //    128-wide steps ("pairs" of two 64-groups) for all of the workgroup's
 //    tiles.  Nothing crosses workgroups: no fences, no workspace.
-//  * Each lane streams 16 bytes of packed codes per pair and tile (W4: 32
-//    nibbles; W8: two 16-byte loads), so one load instruction moves 1 KB of
-//    contiguous weights.  A wave keeps two stages of loads in flight: the
-//    codes, scale/bias words and x rows of one pair are issued together while
-//    the previous pair is computed.  Edges use out-of-range buffer offsets
-//    (zeros, no memory traffic) instead of branches.
+//  * Two weight layouts are streamed by the same kernel:
+//      - packed: tiles of 16 rows x 128 k stored as 1 KB (W4) runs in MFMA
+//        operand order, so each load instruction of a wave reads 1 KB of
+//        contiguous memory (written once by pack_kernel);
+//      - interchange: the caller's row-major codes [N][K*bits/8] with fp16
+//        scales and biases [N][K/64]; a load instruction then reads 64 bytes
+//        (W4) or 128 bytes (W8) from each of 16 rows.
+//    In both, lane 16j + r of a wave holds row r of the tile and the 32
+//    consecutive k starting at 32j of the pair.
+//  * A wave keeps S stages of loads in flight: the codes, scale/bias words
+//    and x rows of one pair are issued together while earlier pairs are
+//    computed.  Edges use out-of-range buffer offsets (zeros, no memory
+//    traffic) instead of branches.
 //  * x is read compactly (the M rows of the pair, 16 bytes per lane) and
-//    staged through a per-wave LDS slot, from which each lane reads its MFMA
-//    operand.  Reading the operand straight from memory would cost four
-//    mostly-empty 16-byte loads per lane and pair, which measured as the
-//    largest single cost of the kernel.
+//    staged through a per-wave 16 x 128 bf16 matrix in LDS in exactly the
+//    shape of the MFMA A operand (zero where a row carries no x), from which
+//    each lane reads its operand with one 16-byte read per 32-k step.  The
+//    16-byte chunks of row r are XOR-swizzled by swz(r), so that neither the
+//    writes (one x row, 16 chunks) nor the reads (16 rows, one chunk) meet
+//    bank conflicts.
 //  * Codes become bf16 in registers with no conversion instruction for W4:
-//    OR-ing a nibble q into the mantissa of 128.0 (0x4300) gives 128 + q
-//    exactly; the 128 offset is removed with the group sum of x.  W8 codes
-//    convert with the byte-to-float instructions (exact below 256).
+//    a nibble q placed in the top four mantissa bits of bf16 16.0 gives
+//    16 + q exactly; the offset is removed per group with the group sum of
+//    x.  (It is 16 code steps, so the fold loses little to cancellation; a
+//    nibble in the low mantissa bits of 128.0 would put 128 there.)  W8
+//    codes convert with the byte-to-float instructions (exact below 256).
 //  * v_mfma_f32_16x16x32_bf16 does the multiply-accumulate: B = 16 weight
 //    rows x 32 k, A = the x rows.  The two groups of a pair are kept apart by
 //    feeding group 0 through A rows 0..7 and group 1 through A rows 8..15
@@ -36,7 +47,7 @@
 //    layout.  Blocks of 9..16 rows (the 16-wide drafter blocks of the mlxcel
 //    manual's DFlash section) fill all 16 A rows and run one MFMA per group
 //    instead (the wide form, below).  The per-group affine terms are applied in fp32:
-//        acc += s * C + (b - 128 s) * sum_x            (W4)
+//        acc += s * C + (b - 16 s) * sum_x             (W4, C over 16 + q)
 //        acc += s * C + b * sum_x                      (W8)
 //  * The two group halves and the waves meet in LDS in a fixed order, so
 //    results are deterministic and row m never depends on M.
@@ -50,45 +61,84 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw (unformatted, stride 0) buffer resource flags for gfx9-family parts,
-// and a byte offset beyond any x buffer: loads there return zeros.
+// and a byte offset beyond any buffer: loads there return zeros.
 constexpr int kBufferFlags = 0x00020000;
 // Cache policy of the weight loads: non-temporal (each code is read once
 // per launch, so it need not displace x and the scale/bias words in L2);
 // measured 3-8% faster than the default policy on the verify shapes.
 constexpr int kStreamOnce = 2;
+// Interchange weights: a load reads 64 bytes (W4) of each of 16 rows, half a
+// 128-byte cache line; the next pair's load reads the other half, so these
+// loads keep the default policy and the line stays in L2 between the two.
+constexpr int kRowHalfLine = 0;
 constexpr unsigned kOutOfRange = 0x40000000u;
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// One packed 32-bit word of 8 codes -> 8 bf16 values 128 + q in k order.
-// The packing step stores the codes of k-slots 0..7 as
-//     q0 | q2 << 4 | q4 << 8 | q6 << 12 | q1 << 16 | q3 << 20 | q5 << 24 | q7 << 28
-// so each output register (two bf16: k-slot 2i low, 2i + 1 high) is one
-// mask-and-or of the word shifted by 4i: OR-ing a nibble into the mantissa of
-// bf16 128.0 (0x4300) gives 128 + q exactly (128 has 7 mantissa bits of ulp
-// 1).  Seven VALU operations per 8 codes.
-__device__ __forceinline__ bf16x8 unpack_w4(unsigned d, unsigned base) {
-    constexpr unsigned kMask = 0x000F000Fu;
-    u32x4 o;
-    o.x = (d & kMask) | base;
-    o.y = ((d >> 4) & kMask) | base;
-    o.z = ((d >> 8) & kMask) | base;
-    o.w = ((d >> 12) & kMask) | base;
-    return __builtin_bit_cast(bf16x8, o);
+// Codes to bf16 for W4.  A code q placed in bits 3..6 (the top four of the
+// seven mantissa bits) of bf16 16.0 gives 16 + q exactly, so each output
+// register is ((word >> s) & 0x00780078) | 0x41804180: k-slot i of a 32-bit
+// word (bits 4i..4i+3) in its low half and k-slot i + 4 in its high half, in
+// the k order (k0, k4, k1, k5, k2, k6, k3, k7); the x operand is staged in
+// the same order (stage_w4_order).  The shifts are 64-bit, each serving two
+// words at once: the bits a 64-bit shift carries across the word boundary
+// land outside the mask.  Six VALU operations per 8 codes.
+__device__ __forceinline__ uint64_t shr64(uint64_t v, int s) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(s), "v"(v));
+    return r;
+}
+__device__ __forceinline__ uint64_t shl64(uint64_t v, int s) {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(s), "v"(v));
+    return r;
 }
 
-// 0x43004300 (two bf16 128.0) in a vector register: with the mask as the one
-// scalar operand, each (d & mask) | base is a single v_and_or_b32.
-__device__ __forceinline__ unsigned w4_base_vgpr() {
+// Two 32-bit words of codes (words 2 half and 2 half + 1 of the 16 bytes a
+// lane holds per tile and pair) -> the MFMA B operands of 32-k steps
+// 2 half and 2 half + 1.
+__device__ __forceinline__ void unpack_w4(u32x4 raw, int half, unsigned base, bf16x8 b[2]) {
+    constexpr unsigned kMask = 0x00780078u;
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    const uint64_t w = __builtin_bit_cast(u64x2, raw)[half];
+    const uint64_t l3 = shl64(w, 3), r1 = shr64(w, 1), r5 = shr64(w, 5), r9 = shr64(w, 9);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int sh = 32 * e;
+        u32x4 o;
+        o.x = ((unsigned)(l3 >> sh) & kMask) | base;
+        o.y = ((unsigned)(r1 >> sh) & kMask) | base;
+        o.z = ((unsigned)(r5 >> sh) & kMask) | base;
+        o.w = ((unsigned)(r9 >> sh) & kMask) | base;
+        b[e] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+
+// A value in a vector register the compiler cannot rematerialize: constants
+// the loop reads every iteration stay put instead of being rebuilt there
+// (with the mask as the one scalar operand, each (v & mask) | base above is
+// a single v_and_or_b32).
+__device__ __forceinline__ unsigned vgpr_const(unsigned c) {
     unsigned v;
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(v));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
     return v;
 }
 
-// Two words of 4 bytes each -> 8 bf16 values q (exact: q < 256 needs 8
-// significant bits, the upper half of the fp32 holds them all).
+// Eight consecutive bf16 x values (k0..k7, two per 32-bit word) reordered
+// to (k0, k4, k1, k5, k2, k6, k3, k7), the k order of unpack_w4.
+__device__ __forceinline__ u32x4 stage_w4_order(u32x4 v) {
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+    return o;
+}
+
+// Two words of 4 bytes each -> 8 bf16 values q in k order (exact: q < 256
+// needs 8 significant bits, the upper half of the fp32 holds them all).
 __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
     u32x4 o;
     o.x = (__float_as_uint((float)(d0 & 0xFFu)) >> 16) |
@@ -102,6 +152,18 @@ __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
+// Swizzle of the staged A matrix: 16-byte chunk c of row r is stored at
+// chunk c ^ swz(r), swz(r) = 2 (r mod 8) + r / 8, a permutation of 0..15.
+// The operand read of one 32-k step (row r = lane mod 16, chunk 4 (lane / 16)
+// + s) and the staging write of one x row (chunks 0..7 into row m, 8..15
+// into row m + 8) both measure zero bank-conflict cycles with it on gfx950
+// (SQ_LDS_BANK_CONFLICT over every lane pattern of the kernel, in a probe);
+// unswizzled rows, a 272-byte row pitch and an XOR with r itself each cost
+// four conflict cycles per 16-byte read there.
+__device__ __forceinline__ int swz(int r) {
+    return 2 * (r & 7) + (r >> 3);
+}
+
 // ---------------------------------------------------------------------------
 // Packed layout (written once by pack_kernel, read by qmv_kernel).
 //
@@ -109,15 +171,14 @@ __device__ __forceinline__ bf16x8 unpack_w8(unsigned d0, unsigned d1) {
 // (t, p) -- rows 16t..16t+15, k = 128p..128p+127 -- is stored contiguously at
 // tile index t * n_pairs + p, as 64 lane slots of 16 bytes (W4) or two
 // 1 KB halves of 64 x 16 bytes (W8).  Lane slot l = 16 j + r holds row
-// 16t + r, k = 128p + 64 (j >> 1) + 32 (j & 1) + [0, 32): exactly the bytes
-// the MFMA B operand of lane l needs; within each 32-bit word (k-slots 0..7)
-// the W4 codes are reordered so that unpacking is one mask per output
-// register (see unpack_w4).  A wave therefore reads 1 KB per load
-// instruction and streams a contiguous region.  Scales and biases become one
-// 32-bit word per (row, group): fp16 scale in the low half, fp16 bias in the
-// high half, stored as [t][p / 2][h * 16 + r][p % 2] for group g = 2p + h, so
-// one 8-byte load gives a lane the words of two pairs.  Rows past N and
-// groups past K/64 are zero, so they contribute exactly nothing.
+// 16t + r, k = 128p + 32 j + [0, 32) (W8 half v: k = 128p + 32 j + 16 v +
+// [0, 16)), the codes in their original order: exactly the bytes the MFMA B
+// operand of lane l needs.  A wave therefore reads 1 KB per load
+// instruction and streams a contiguous region.  Scales and biases become
+// one 32-bit word per (row, group): fp16 scale in the low half, fp16 bias in
+// the high half, stored as [t][p / 2][h * 16 + r][p % 2] for group
+// g = 2p + h, so one 8-byte load gives a lane the words of two pairs.  Rows
+// past N and groups past K/64 are zero, so they contribute exactly nothing.
 // ---------------------------------------------------------------------------
 
 // With a second matrix (w2, scales2, biases2 non-null: the up projection
@@ -148,24 +209,10 @@ __global__ __launch_bounds__(256) void pack_kernel(
         const int r = lane & 15, j = lane >> 4;
         const int n = two ? 16 * (t >> 1) + r : 16 * t + r;
         const void *src = (two && (t & 1)) ? w2 : w;
-        const int k = 128 * p + 64 * (j >> 1) + 32 * (j & 1) + 16 * v;  // first k of the 16 bytes
+        const int k = 128 * p + 32 * j + 16 * v;   // first k of the 16 bytes
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (n < N && k < K) {
-            if (BITS == 4) {
-                val = reinterpret_cast<const u32x4 *>(src)[((size_t)n * K + k) >> 5];
-                // k-slot e of each word moves to nibble (e & 1) * 4 + (e >> 1)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    unsigned out = 0;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        out |= ((val[c] >> (4 * e)) & 0xFu) << (16 * (e & 1) + 4 * (e >> 1));
-                    val[c] = out;
-                }
-            } else {
-                val = reinterpret_cast<const u32x4 *>(src)[((size_t)n * K + k) >> 4];
-            }
-        }
+        if (n < N && k < K)
+            val = reinterpret_cast<const u32x4 *>(src)[((size_t)n * K + k) / (BITS == 4 ? 32 : 16)];
         wp[i] = val;
     }
     // scale/bias words: [t][p / 2][h * 16 + r][p % 2] for the group g = 2p + h
@@ -190,10 +237,24 @@ __global__ __launch_bounds__(256) void pack_kernel(
     }
 }
 
+// Kernel arguments.  Packed layout: w = tiles, sb = scale/bias words,
+// biases unused.  Interchange layout: w = codes [N][K*BITS/8], sb = scales
+// [N][K/64], biases [N][K/64] (fp16 bit patterns).
+struct QmvArgs {
+    const void *w;
+    const void *sb;
+    const uint16_t *biases;
+    const uint16_t *x;
+    void *out;
+    int M, N, K, n_out;
+};
+
+// RM: the interchange (row-major) layout instead of packed tiles.
+//
 // XH: 16-byte x loads per lane and pair -- 1 when M <= 4 (rows 0..3),
-// 2 when M <= 8, 4 when M <= 16.  Rows a launch does not stage are never
-// read (their MFMA operand lanes read zeros), so the M <= 4 and M <= 8
-// variants compute bitwise the same.
+// 2 when M <= 8, 4 when M <= 16.  Rows a launch does not stage hold zeros
+// (their MFMA operand rows are zero), so the M <= 4 and M <= 8 variants
+// compute bitwise the same.
 //
 // XH = 4 is the wide form for 9..16 rows: every A row is an x row, so the
 // two groups of a pair can no longer share an MFMA through the row split.
@@ -208,31 +269,31 @@ __global__ __launch_bounds__(256) void pack_kernel(
 // activation h[m][f] = silu(g) * u as bf16 [M][n_out], g and u being the
 // outputs of tiles 2i and 2i + 1 for f = 16i + r.  g and u are reduced
 // exactly as a plain launch reduces them.
-template <int BITS, int WAVES, int T, int U, int S, int XH, bool GLU = false>
-__global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
-    const u32x4 *__restrict__ wp, const uint32_t *__restrict__ sbp,
-    const uint16_t *__restrict__ x, void *__restrict__ out, int M, int N, int K,
-    int n_out) {
-    static_assert(U == 1 || U == 2, "a stage is one or two pairs");
+//
+// MR: C rows of a lane's 4-row block that can hold an x row (M itself when
+// M <= 4, else 4); the per-group affine epilogue skips the others.
+template <int BITS, bool RM, int WAVES, int T, int S, int XH, bool GLU = false, int MR = 4>
+__global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
     static_assert(XH == 1 || XH == 2 || XH == 4, "x loads per lane and pair");
-    static_assert(!GLU || T % 2 == 0, "a gated launch pairs gate and up tiles");
+    static_assert(!GLU || (T % 2 == 0 && !RM), "a gated launch pairs packed gate and up tiles");
+    static_assert(RM || S % 2 == 0, "packed scale/bias blocks hand over between stage slots");
+    static_assert(MR >= 1 && MR <= 4 && (XH == 1 || MR == 4), "rows per lane block");
     constexpr bool WIDE = XH == 4;  // 9..16 rows: one MFMA per group
-    constexpr int XR = WIDE ? 16 : 8;   // staged x rows
     constexpr int NG = WIDE ? 2 : 1;    // groups (accumulators) per lane
-    constexpr int L = BITS / 4;     // 1 KB loads per pair, tile and wave
-    constexpr int kPitch = 136;     // bf16 per staged x row: 256 B + 16 B against bank conflicts
-    // Each wave stages its x rows in its own slot; the cross-wave reduction
+    constexpr int L = BITS / 4;     // 16-byte code loads per pair, tile and lane
+    // Each wave stages x in its own 16 x 128 slot; the cross-wave reduction
     // reuses the same memory after the main loop.
     union Shared {
-        uint16_t xs[WAVES][U][XR][kPitch];
+        uint16_t xs[WAVES][16][128];
         f32x4 red[WAVES][T][64];
     };
     __shared__ __attribute__((aligned(16))) Shared sh;
     __shared__ __attribute__((aligned(16))) uint16_t xzero[8];
 
+    const int M = a.M, N = a.N, K = a.K;
     const int ng = K >> 6;                   // groups per row
     const int n_pairs = (ng + 1) >> 1;       // 128-wide K steps
-    const int npp = (n_pairs + 1) >> 1;      // scale/bias blocks of two pairs
+    const int npp = (n_pairs + 1) >> 1;      // packed scale/bias blocks of two pairs
     const int n_tiles = (N + 15) >> 4;
     const int lane = threadIdx.x & 63;
     // readfirstlane makes the wave index (and all that derives from it)
@@ -243,53 +304,80 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     const int h = j >> 1;      // which group of the pair this lane's k slots hold
     const int sub = j & 1;     // which 32-k half of that group
 
-    // This wave's contiguous share of the pairs (an even count, so a stage
-    // of two pairs never straddles a scale/bias block).
+    // This wave's contiguous share of the pairs (an even count, so a wave's
+    // range starts at an even pair, as the packed scale/bias blocks need).
     const int ppw = ((n_pairs + WAVES - 1) / WAVES + 1) & ~1;
     const int p_lo = min(n_pairs, wave * ppw);
     const int p_hi = min(n_pairs, p_lo + ppw);
 
     // Buffer resources: lane-dependent offsets are fixed, per-pair offsets
-    // are wave-uniform (scalar registers).  A tile past the last one gets an
-    // empty resource, so its loads return zeros.
-    __amdgpu_buffer_rsrc_t wres[T], sbres[T];
+    // are wave-uniform (scalar registers).  A tile past the last one (or
+    // rows past N) gets an empty range, so its loads return zeros.
+    constexpr int kRowBytesPerK = BITS;          // row bytes = K * BITS / 8
+    const unsigned row_bytes = (unsigned)(K / 8) * kRowBytesPerK;
+    __amdgpu_buffer_rsrc_t wres[T], sres[T], bres[T];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
         const int t = blockIdx.x * T + tt;
-        const bool there = t < n_tiles;
-        wres[tt] = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(wp + (size_t)min(t, n_tiles - 1) * n_pairs * 64 * L), (short)0,
-            there ? n_pairs * 1024 * L : 0, kBufferFlags);
-        sbres[tt] = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(sbp + (size_t)min(t, n_tiles - 1) * npp * 64), (short)0,
-            there ? npp * 256 : 0, kBufferFlags);
+        const int tc = min(t, n_tiles - 1);
+        if (!RM) {
+            const bool there = t < n_tiles;
+            wres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const u32x4 *)a.w + (size_t)tc * n_pairs * 64 * L), (short)0,
+                there ? n_pairs * 1024 * L : 0, kBufferFlags);
+            sres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const uint32_t *)a.sb + (size_t)tc * npp * 64), (short)0,
+                there ? npp * 256 : 0, kBufferFlags);
+        } else {
+            const int rows = max(0, min(16, N - 16 * t));
+            wres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const char *)a.w + (size_t)16 * tc * row_bytes), (short)0,
+                rows * row_bytes, kBufferFlags);
+            sres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const uint16_t *)a.sb + (size_t)16 * tc * ng), (short)0,
+                rows * ng * 2, kBufferFlags);
+            bres[tt] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.biases + (size_t)16 * tc * ng), (short)0, rows * ng * 2, kBufferFlags);
+        }
     }
     const __amdgpu_buffer_rsrc_t xres =
-        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, M * K * 2, kBufferFlags);
-    const unsigned woff = (unsigned)lane * 16u;
-    // pair form: this lane's group h; wide form: both groups of row r
+        __builtin_amdgcn_make_buffer_rsrc((void *)a.x, (short)0, M * K * 2, kBufferFlags);
+    // Packed: lane slot l of a tile's pair; interchange: row r, bytes
+    // 32 j * BITS / 8 of the pair's k.
+    const unsigned woff = RM ? (unsigned)r * row_bytes + (unsigned)j * (4 * BITS) : (unsigned)lane * 16u;
+    // Scale/bias offsets.  Pair form: this lane's group h; wide form: both
+    // groups of row r.  Packed: the word of (row, group) in a 2-pair block;
+    // interchange: the fp16 of (row, group) relative to the pair's first.
     unsigned sboff[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-        sboff[g] = (unsigned)((WIDE ? g : h) * 16 + r) * 8u;
+        sboff[g] = RM ? (unsigned)(r * ng + (WIDE ? g : h)) * 2u
+                      : (unsigned)((WIDE ? g : h) * 16 + r) * 8u;
     // x is loaded compactly: lane -> row (lane >> 4) + 4 i, 16-byte chunk
     // (lane & 15) of the pair's 128 k; rows >= M read zeros.
     const int xrow0 = lane >> 4, xch = lane & 15;
-    // MFMA A operand.  Pair form: row r carries x row (r & 7) for group
-    // half (r >> 3) and is zero on the other half's k slots (and for rows
-    // >= M).  Wide form: row r is x row r, masked to group g's k slots for
-    // the group-g MFMA.
-    const int a_row = WIDE ? r : (r & 7);
+    // Wide form: lanes read their A row only for the MFMA of their own group.
     bool a_act[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-        a_act[g] = (h == (WIDE ? g : (r >> 3))) && (a_row < M);
+        a_act[g] = h == g;
+    // Zero this wave's staged A matrix once: in the pair form, the halves of
+    // each row that belong to the other group, and the rows no x row maps
+    // to, are never written again.
+    {
+        u32x4 *slot = reinterpret_cast<u32x4 *>(&sh.xs[wave][0][0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            slot[lane + 64 * i] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (threadIdx.x < 8)
         xzero[threadIdx.x] = 0;
     __syncthreads();
 
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    const unsigned w4base = w4_base_vgpr();
+    const bf16x8 ones = __builtin_bit_cast(
+        bf16x8, u32x4{vgpr_const(0x3F803F80u), vgpr_const(0x3F803F80u), vgpr_const(0x3F803F80u),
+                      vgpr_const(0x3F803F80u)});
+    const unsigned w4base = vgpr_const(0x41804180u);
     f32x4 acc[T][NG];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
@@ -297,139 +385,141 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         for (int g = 0; g < NG; ++g)
             acc[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // A stage is U pairs: the T tiles' codes and scale/bias words, and the
+    // A stage is one pair: the T tiles' codes and scale/bias words, and the
     // compact x rows, all issued together.  Pairs outside this wave's range
     // load through an out-of-range offset (zeros, no memory traffic), so no
     // load sits under a branch and the compiler counts outstanding loads
-    // exactly.  With one pair per stage the scale/bias words still come two
-    // pairs per load: the stage of an even pair (stage slot 0, since a wave's
-    // range starts at an even pair) loads the 8-byte block holding both
-    // pairs' words, and its compute hands the odd pair's word on to the next
-    // stage (sb_next); the odd stage loads none.  Half the load instructions
-    // and requests for these words, measured 2-5% faster; same arithmetic.
-    static_assert(U == 2 || S % 2 == 0, "one-pair stages alternate even and odd pairs");
+    // exactly.  Packed scale/bias words come two pairs per load: the stage
+    // of an even pair (an even stage slot, since a wave's range starts at an
+    // even pair and S is even) loads the 8-byte block holding both pairs'
+    // words, and its compute hands the odd pair's word on to the next stage
+    // (sb_next); the odd stage loads none.  Interchange scales and biases
+    // are two 2-byte loads per pair and group.
     struct Stage {
-        u32x4 raw[U][T][L];
-        uint32_t sb[U][T][NG];
-        uint32_t sb_odd[T][NG];   // one-pair stages: the odd pair's words
-        u32x4 xc[U][XH];
+        u32x4 raw[T][L];
+        uint32_t sb[T][NG];
+        uint32_t sb_odd[T][NG];   // packed: the odd pair's words
+        u32x4 xc[XH];
     };
     uint32_t sb_next[T][NG];
-    auto issue = [&](Stage &st, int p0, int slot) {
-        const bool in0 = p0 >= p_lo && p0 < p_hi;
+    auto issue = [&](Stage &st, int p, int slot) {
+        const bool in = p >= p_lo && p < p_hi;
+        const int pc = in ? p : 0;
+        // interchange: the odd last group of a row has no codes or scales
+        const bool gin = !RM || 2 * pc + h < ng;
+        const unsigned wv = (in && gin) ? woff : kOutOfRange;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + u;
-            const bool in = p >= p_lo && p < p_hi;
-            const int pc = in ? p : 0;
-            const unsigned wv = in ? woff : kOutOfRange;
+        for (int tt = 0; tt < T; ++tt)
 #pragma unroll
-            for (int tt = 0; tt < T; ++tt)
-#pragma unroll
-                for (int v = 0; v < L; ++v)
-                    st.raw[u][tt][v] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[tt], wv, (pc * L + v) * 1024, kStreamOnce));
-        }
-        // one load gives this lane's scale/bias words of both pairs of a block
-        const int pc0 = in0 ? p0 : 0;
+            for (int v = 0; v < L; ++v)
+                st.raw[tt][v] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               wres[tt], wv, RM ? pc * 16 * BITS + 16 * v : (pc * L + v) * 1024,
+                               RM ? kRowHalfLine : kStreamOnce));
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const unsigned sv = in0 ? sboff[g] : kOutOfRange;
-                if (U == 2 || slot % 2 == 0) {
-                    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sbres[tt], sv, (pc0 >> 1) * 256, 0);
-                    st.sb[0][tt][g] = v2[0];
-                    if (U == 2)
-                        st.sb[U - 1][tt][g] = v2[1];
-                    else
-                        st.sb_odd[tt][g] = v2[1];
+                if (RM) {
+                    const bool gg = in && 2 * pc + (WIDE ? g : h) < ng;
+                    const unsigned sv = gg ? sboff[g] : kOutOfRange;
+                    const uint32_t s16 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sres[tt], sv, pc * 4, 0);
+                    const uint32_t b16 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bres[tt], sv, pc * 4, 0);
+                    st.sb[tt][g] = s16 | (b16 << 16);
+                } else if (slot % 2 == 0) {
+                    // one load gives this lane's words of both pairs of a block
+                    const unsigned sv = in ? sboff[g] : kOutOfRange;
+                    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sres[tt], sv, (pc >> 1) * 256, 0);
+                    st.sb[tt][g] = v2[0];
+                    st.sb_odd[tt][g] = v2[1];
                 }
             }
         }
+        // the odd last group of a row has no partner: its chunks read zeros
+        const bool xgin = 2 * pc + (xch >> 3) < ng;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + u;
-            const bool in = p >= p_lo && p < p_hi;
-            const int pc = in ? p : 0;
-            // the odd last group of a row has no partner: its chunks read zeros
-            const bool gin = 2 * pc + (xch >> 3) < ng;
-#pragma unroll
-            for (int i = 0; i < XH; ++i) {
-                const int row = xrow0 + 4 * i;
-                const unsigned off = (in && gin && row < M) ? (unsigned)((row * K + 8 * xch) * 2) : kOutOfRange;
-                st.xc[u][i] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, pc * 256, 0));
-            }
+        for (int i = 0; i < XH; ++i) {
+            const int row = xrow0 + 4 * i;
+            const unsigned off = (in && xgin && row < M) ? (unsigned)((row * K + 8 * xch) * 2) : kOutOfRange;
+            st.xc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, pc * 256, 0));
         }
     };
-    auto compute = [&](const Stage &st, int p0, int slot) {
-        // Stage x through this wave's LDS slot, then read the MFMA A
+    auto compute = [&](const Stage &st, int p, int slot) {
+        if (p >= p_hi)
+            return;
+        // Stage x through this wave's LDS matrix, then read the MFMA A
         // fragments back.  LDS operations of one wave complete in order, so
-        // the slot can be rewritten by the next stage right away.
+        // the matrix can be rewritten by the next stage right away.  Pair
+        // form: x row m's chunk c goes to A row m (c < 8, group 0) or m + 8
+        // (group 1); wide form: A row m.
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int i = 0; i < XH; ++i) {
+            const int m = xrow0 + 4 * i;
+            const int arow = WIDE ? m : m + 8 * (xch >> 3);
+            const u32x4 v = BITS == 4 ? stage_w4_order(st.xc[i]) : st.xc[i];
+            *reinterpret_cast<u32x4 *>(&sh.xs[wave][arow][8 * (xch ^ swz(arow))]) = v;
+        }
+        f32x4 c[T][NG];
+        f32x4 cx[NG];
 #pragma unroll
-            for (int i = 0; i < XH; ++i)
-                *reinterpret_cast<u32x4 *>(&sh.xs[wave][u][xrow0 + 4 * i][8 * xch]) = st.xc[u][i];
+        for (int g = 0; g < NG; ++g) {
+            cx[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (p0 + u >= p_hi)
-                break;
-            f32x4 c[T][NG];
-            f32x4 cx[NG];
+            for (int tt = 0; tt < T; ++tt)
+                c[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const int rsw = swz(r);
+        bf16x8 bw4[T][2];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                cx[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s4 = 0; s4 < 4; ++s4) {
+            if (BITS == 4 && s4 % 2 == 0) {
 #pragma unroll
                 for (int tt = 0; tt < T; ++tt)
-                    c[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    unpack_w4(st.raw[tt][0], s4 / 2, w4base, bw4[tt]);
             }
+            bf16x8 av[NG];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                bf16x8 av[NG];
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const uint16_t *src = a_act[g] ? &sh.xs[wave][u][a_row][64 * h + 32 * sub + 8 * s4] : xzero;
-                    av[g] = *reinterpret_cast<const bf16x8 *>(src);
-                    cx[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], ones, cx[g], 0, 0, 0);
-                }
-#pragma unroll
-                for (int tt = 0; tt < T; ++tt) {
-                    bf16x8 bv;
-                    if (BITS == 4) {
-                        bv = unpack_w4(st.raw[u][tt][0][s4], w4base);
-                    } else {
-                        const u32x4 &lo = st.raw[u][tt][s4 >> 1];
-                        bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
-                    }
-#pragma unroll
-                    for (int g = 0; g < NG; ++g)
-                        c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], bv, c[tt][g], 0, 0, 0);
-                }
+            for (int g = 0; g < NG; ++g) {
+                const uint16_t *src = (!WIDE || a_act[g]) ? &sh.xs[wave][r][8 * ((4 * j + s4) ^ rsw)] : xzero;
+                av[g] = *reinterpret_cast<const bf16x8 *>(src);
+                cx[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], ones, cx[g], 0, 0, 0);
             }
-            // Pair form: C row 4*j + i is x row m = 4*sub + i of half h.
-            // Wide form: C row 4*j + i is x row 4*j + i, one accumulator per
-            // group.  cx holds the same rows' sums of x over the group.
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
+                bf16x8 bv;
+                if (BITS == 4) {
+                    bv = bw4[tt][s4 % 2];
+                } else {
+                    const u32x4 &lo = st.raw[tt][s4 >> 1];
+                    bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
+                }
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    uint32_t sbw = st.sb[u][tt][g];
-                    if (U == 1) {
-                        if (slot % 2 == 0)
-                            sb_next[tt][g] = st.sb_odd[tt][g];
-                        else
-                            sbw = sb_next[tt][g];
-                    }
-                    const float s = half_bits_to_float((uint16_t)(sbw & 0xFFFFu));
-                    const float bias = half_bits_to_float((uint16_t)(sbw >> 16));
-                    const float bb = (BITS == 4) ? fmaf(-128.0f, s, bias) : bias;
+                for (int g = 0; g < NG; ++g)
+                    c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], bv, c[tt][g], 0, 0, 0);
+            }
+        }
+        // Pair form: C row 4*j + i is x row m = 4*sub + i of half h.
+        // Wide form: C row 4*j + i is x row 4*j + i, one accumulator per
+        // group.  cx holds the same rows' sums of x over the group.
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[tt][g][i] = fmaf(s, c[tt][g][i], acc[tt][g][i]);
-                        acc[tt][g][i] = fmaf(bb, cx[g][i], acc[tt][g][i]);
-                    }
+        for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                uint32_t sbw = st.sb[tt][g];
+                if (!RM) {
+                    if (slot % 2 == 0)
+                        sb_next[tt][g] = st.sb_odd[tt][g];
+                    else
+                        sbw = sb_next[tt][g];
+                }
+                const float s = half_bits_to_float((uint16_t)(sbw & 0xFFFFu));
+                const float bias = half_bits_to_float((uint16_t)(sbw >> 16));
+                const float bb = BITS == 4 ? fmaf(-16.0f, s, bias) : bias;
+                // rows i >= MR of this lane's C block hold no x row
+#pragma unroll
+                for (int i = 0; i < MR; ++i) {
+                    acc[tt][g][i] = fmaf(s, c[tt][g][i], acc[tt][g][i]);
+                    acc[tt][g][i] = fmaf(bb, cx[g][i], acc[tt][g][i]);
                 }
             }
         }
@@ -440,13 +530,13 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     // loop header sees are always the previous round's, in issue order, and
     // each compute waits only for its own stage.
     Stage st[S];
-    for (int base = p_lo - S * U; base < p_hi; base += S * U) {
+    for (int base = p_lo - S; base < p_hi; base += S) {
 #pragma unroll
         for (int q = 0; q < S; ++q) {
-            if (base + q * U >= p_lo)
-                compute(st[q], base + q * U, q);
+            if (base + q >= p_lo)
+                compute(st[q], base + q, q);
             __builtin_amdgcn_sched_barrier(0);
-            issue(st[q], base + (q + S) * U, q);
+            issue(st[q], base + q + S, q);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -454,7 +544,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
     // Fixed-order reduction: the two groups of a pair (pair form: lanes l,
     // l ^ 32; wide form: the two accumulators of a lane), then the waves in
     // index order.  Neither depends on M.
-    __syncthreads();   // every wave is done with its x slot
+    __syncthreads();   // every wave is done with its x matrix
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
         sh.red[wave][tt][lane] = WIDE ? acc[tt][0] + acc[tt][NG - 1] : acc[tt][0];
@@ -469,7 +559,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
         }
         const int m0 = WIDE ? 4 * j : 4 * sub;
         if (!GLU) {
-            float *y = static_cast<float *>(out);
+            float *y = static_cast<float *>(a.out);
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
                 const int n = (blockIdx.x * T + tt) * 16 + r;
@@ -481,11 +571,11 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
                         y[(size_t)(m0 + i) * N + n] = tot[tt][i];
             }
         } else {
-            uint16_t *h = static_cast<uint16_t *>(out);
+            uint16_t *hout = static_cast<uint16_t *>(a.out);
 #pragma unroll
             for (int tt = 0; tt < T; tt += 2) {
                 const int f = ((blockIdx.x * T + tt) >> 1) * 16 + r;
-                if (f >= n_out)
+                if (f >= a.n_out)
                     continue;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -498,7 +588,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(
                     const unsigned bits = __float_as_uint(v);
                     const unsigned rnd = (v != v) ? 0x7FC00000u
                                                   : bits + 0x7FFFu + ((bits >> 16) & 1u);
-                    h[(size_t)(m0 + i) * n_out + f] = (uint16_t)(rnd >> 16);
+                    hout[(size_t)(m0 + i) * a.n_out + f] = (uint16_t)(rnd >> 16);
                 }
             }
         }
@@ -566,6 +656,32 @@ __global__ void fill_zero_kernel(V *__restrict__ y, size_t count) {
         y[i] = V(0);
 }
 
+template <typename V>
+hipError_t fill_zero(V *y, size_t count, hipStream_t stream) {
+    const int blocks = (int)std::min<size_t>((count + 255) / 256, 4096);
+    fill_zero_kernel<<<blocks, 256, 0, stream>>>(y, count);
+    return hipGetLastError();
+}
+
+// Launches qmv_kernel for one (bits, layout) at the plan's shape; the x-row
+// variant (XH) follows M.
+template <int B, bool RM, int W, int TT, int SS, bool GLU>
+hipError_t launch_shape(const QmvArgs &a, int blocks, hipStream_t stream) {
+    if (a.M == 1)
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 1><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M == 2)
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 2><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M == 3)
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 3><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M == 4)
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 4><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M <= 8)
+        qmv_kernel<B, RM, W, TT, SS, 2, GLU><<<blocks, W * 64, 0, stream>>>(a);
+    else
+        qmv_kernel<B, RM, W, TT, SS, 4, GLU><<<blocks, W * 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 } // namespace
 
 QmvPlan qmv_plan(int bits, int N, int K) {
@@ -581,7 +697,7 @@ QmvPlan qmv_plan(int bits, int N, int K) {
     //   tall (MLP gate/up, >= 1024 tiles):    2 tiles, 4 waves (W8: 1 tile, 8 waves)
     //   long K (MLP down, >= 96 pairs):       2 tiles, 8 waves
     //   the rest (attention q/k/v/o):         1 tile, 8 waves
-    p.pairs_per_stage = 1;
+    p.stages = 2;
     if (p.n_tiles >= 4096) {
         p.tiles_per_wave = bits == 4 ? 4 : 2;
         p.waves = bits == 4 ? 4 : 8;
@@ -636,34 +752,23 @@ hipError_t launch_requantize_w4(const uint16_t *w, int N, int K, uint32_t *w4,
     return hipGetLastError();
 }
 
-hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
-                      const uint16_t *x, float *y, int M, int N, int K,
-                      hipStream_t stream) {
+hipError_t launch_qmv(int bits, bool interchange, const void *w, const void *sb,
+                      const uint16_t *biases, const uint16_t *x, float *y, int M, int N,
+                      int K, hipStream_t stream) {
     if (M == 0 || N == 0)
         return hipSuccess;
-    if (K == 0) {
-        const size_t count = (size_t)M * N;
-        const int blocks = (int)std::min<size_t>((count + 255) / 256, 4096);
-        fill_zero_kernel<<<blocks, 256, 0, stream>>>(y, count);
-        return hipGetLastError();
-    }
+    if (K == 0)
+        return fill_zero(y, (size_t)M * N, stream);
     const QmvPlan plan = qmv_plan(bits, N, K);
-    const u32x4 *wp = (const u32x4 *)w_packed;
-    const uint32_t *sbp = (const uint32_t *)sb_packed;
-    const dim3 grid((plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave);
-#define SPEC_QMV_LAUNCH(B, W, TT, UU)                                                       \
-    if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.pairs_per_stage == UU) { \
-        if (M <= 4)                                                                         \
-            qmv_kernel<B, W, TT, UU, 2, 1><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
-        else if (M <= 8)                                                                    \
-            qmv_kernel<B, W, TT, UU, 2, 2><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
-        else                                                                                \
-            qmv_kernel<B, W, TT, UU, 2, 4><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, y, M, N, K, 0); \
-        return hipGetLastError();                                                           \
-    }
+    const QmvArgs a{w, sb, biases, x, y, M, N, K, 0};
+    const int blocks = (plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave;
+#define SPEC_QMV_LAUNCH(B, W, TT, SS)                                                    \
+    if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.stages == SS) \
+        return interchange ? launch_shape<B, true, W, TT, SS, false>(a, blocks, stream)  \
+                           : launch_shape<B, false, W, TT, SS, false>(a, blocks, stream);
 #define SPEC_QMV_SHAPES(B) \
-    SPEC_QMV_LAUNCH(B, 4, 4, 1) SPEC_QMV_LAUNCH(B, 4, 2, 1) SPEC_QMV_LAUNCH(B, 8, 2, 1) \
-    SPEC_QMV_LAUNCH(B, 8, 1, 1)
+    SPEC_QMV_LAUNCH(B, 4, 4, 2) SPEC_QMV_LAUNCH(B, 4, 2, 2) SPEC_QMV_LAUNCH(B, 8, 2, 2) \
+    SPEC_QMV_LAUNCH(B, 8, 1, 2)
     SPEC_QMV_SHAPES(4)
     SPEC_QMV_SHAPES(8)
 #undef SPEC_QMV_SHAPES
@@ -676,33 +781,21 @@ hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *s
                                    hipStream_t stream) {
     if (M == 0 || F == 0)
         return hipSuccess;
-    if (K == 0) {   // g = u = 0, so h = silu(0) * 0 = +0
-        const size_t count = (size_t)M * F;
-        const int blocks = (int)std::min<size_t>((count + 255) / 256, 4096);
-        fill_zero_kernel<<<blocks, 256, 0, stream>>>(h, count);
-        return hipGetLastError();
-    }
+    if (K == 0)   // g = u = 0, so h = silu(0) * 0 = +0
+        return fill_zero(h, (size_t)M * F, stream);
     const int N = gate_up_rows(F);
     const QmvPlan plan = qmv_plan(bits, N, K);
     // The plain launch shape with at least one gate/up tile pair per
     // workgroup: the waves (hence every output's reduction order) are the
     // plain launch's, only the tiles per workgroup may double.
     const int T = std::max(plan.tiles_per_wave, 2);
-    const u32x4 *wp = (const u32x4 *)w_packed;
-    const uint32_t *sbp = (const uint32_t *)sb_packed;
+    const QmvArgs a{w_packed, sb_packed, nullptr, x, h, M, N, K, F};
     // n_tiles is even, so no workgroup splits a gate/up pair; tiles past the
     // end (T = 4) read zeros and write nothing.
-    const dim3 grid((plan.n_tiles + T - 1) / T);
-#define SPEC_QMV_GLU_LAUNCH(B, W, TT)                                                      \
-    if (bits == B && plan.waves == W && T == TT && plan.pairs_per_stage == 1) {            \
-        if (M <= 4)                                                                         \
-            qmv_kernel<B, W, TT, 1, 2, 1, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
-        else if (M <= 8)                                                                    \
-            qmv_kernel<B, W, TT, 1, 2, 2, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
-        else                                                                                \
-            qmv_kernel<B, W, TT, 1, 2, 4, true><<<grid, (W) * 64, 0, stream>>>(wp, sbp, x, h, M, N, K, F); \
-        return hipGetLastError();                                                           \
-    }
+    const int blocks = (plan.n_tiles + T - 1) / T;
+#define SPEC_QMV_GLU_LAUNCH(B, W, TT)                                          \
+    if (bits == B && plan.waves == W && T == TT && plan.stages == 2)           \
+        return launch_shape<B, false, W, TT, 2, true>(a, blocks, stream);
     SPEC_QMV_GLU_LAUNCH(4, 4, 4) SPEC_QMV_GLU_LAUNCH(4, 4, 2) SPEC_QMV_GLU_LAUNCH(4, 8, 2)
     SPEC_QMV_GLU_LAUNCH(8, 8, 2)
 #undef SPEC_QMV_GLU_LAUNCH

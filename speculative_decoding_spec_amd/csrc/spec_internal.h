@@ -17,7 +17,7 @@ struct QmvPlan {
     int n_pairs;          // 128-wide K steps (pairs of 64-groups)
     int waves;            // waves per workgroup (K split inside the workgroup)
     int tiles_per_wave;   // tiles each workgroup (and each of its waves) serves
-    int pairs_per_stage;  // pairs per in-flight load stage (1 or 2)
+    int stages;           // pairs in flight per wave (one pair per load stage)
 };
 
 QmvPlan qmv_plan(int bits, int N, int K);
@@ -33,9 +33,12 @@ int gate_up_rows(int F);
 // Draft-only 4-bit copy (G = 64) of a bf16 [N][K] matrix, interchange layout.
 hipError_t launch_requantize_w4(const uint16_t *w, int N, int K, uint32_t *w4,
                                 uint16_t *scales, uint16_t *biases, hipStream_t stream);
-hipError_t launch_qmv(int bits, const void *w_packed, const void *sb_packed,
-                      const uint16_t *x, float *y, int M, int N, int K,
-                      hipStream_t stream);
+// interchange = false: w / sb are the packed tiles and scale/bias words of
+// launch_pack (biases unused); true: w is the caller's row-major codes,
+// sb the fp16 scales and biases the fp16 biases, each [N][K/64].
+hipError_t launch_qmv(int bits, bool interchange, const void *w, const void *sb,
+                      const uint16_t *biases, const uint16_t *x, float *y, int M, int N,
+                      int K, hipStream_t stream);
 // h (bf16 [M][F]) = silu(x G^T) * (x U^T) from a gate/up pair packed with
 // alternating tiles.
 hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,

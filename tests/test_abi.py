@@ -47,15 +47,18 @@ def test_status_strings(L):
     assert L.spec_version() >= 100
 
 
-def qmv(L, fn="spec_qmv_w4", w=P, sb=P, x=P, y=P, M=4, N=64, K=128, G=64):
-    return getattr(L, fn)(w, sb, x, y, M, N, K, G, None)
+def qmv(L, fn="spec_qmv_w4_packed", w=P, sb=P, x=P, y=P, M=4, N=64, K=128, G=64, b=P2):
+    if fn.endswith("_packed"):
+        return getattr(L, fn)(w, sb, x, y, M, N, K, G, None)
+    return getattr(L, fn)(w, sb, b, x, y, M, N, K, G, None)
 
 
 def pack(L, fn="spec_pack_w4", w=P, s=P, b=P, N=64, K=128, G=64, wp=P, sbp=P2):
     return getattr(L, fn)(w, s, b, N, K, G, wp, sbp, None)
 
 
-@pytest.mark.parametrize("fn", ["spec_qmv_w4", "spec_qmv_w8"])
+@pytest.mark.parametrize("fn", ["spec_qmv_w4", "spec_qmv_w8", "spec_qmv_w4_packed",
+                                "spec_qmv_w8_packed"])
 def test_qmv_validation(L, fn):
     assert qmv(L, fn, M=-1) == INVALID
     assert qmv(L, fn, K=100) == INVALID            # K % G != 0
@@ -70,6 +73,13 @@ def test_qmv_validation(L, fn):
     assert qmv(L, fn, x=MIS) == UNSUPPORTED
     assert qmv(L, fn, M=0) == OK                   # no-op, nothing enqueued
     assert qmv(L, fn, N=0) == OK
+    # 32-bit buffer ranges and offsets in the kernel: K below 2^24, N at most 2^28
+    assert qmv(L, fn, K=1 << 24) == UNSUPPORTED
+    assert qmv(L, fn, N=(1 << 28) + 1) == UNSUPPORTED
+    if not fn.endswith("_packed"):
+        assert qmv(L, fn, b=None) == INVALID
+        assert qmv(L, fn, b=ctypes.c_void_p(0x20001)) == INVALID    # fp16 biases, odd address
+        assert qmv(L, fn, sb=ctypes.c_void_p(0x10001)) == INVALID   # fp16 scales, odd address
 
 
 @pytest.mark.parametrize("fn", ["spec_pack_w4", "spec_pack_w8"])

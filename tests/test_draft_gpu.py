@@ -69,13 +69,18 @@ def test_draft_head_product(dev):
     wb = weights(5, N, K)
     x = synth.activations(5, 1, K)
     w = torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16)
-    packed = spec.spec_pack_w4(*spec.spec_requantize_w4(w))
-    y = spec.spec_qmv_w4(packed, parity.dev_x(x, dev)).cpu().numpy()
+    q4 = spec.spec_requantize_w4(w)
+    xt = parity.dev_x(x, dev)
+    y = spec.spec_qmv_w4_packed(spec.spec_pack_w4(*q4), xt).cpu().numpy()
+    # the requantized codes are in the interchange layout: read as stored
+    yi = spec.spec_qmv_w4(*q4, xt).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), yi.view(np.uint32))
     q, s, b = oracle.requantize_w4(wb, 64)
     ref, mag = parity.oracle_qmv_threaded(4, q, s, b, x, 64)
     nf, nabs, worst = parity.check_qmv(y, ref, mag)
     print(f"draft head N={N}: fail={nf} abs-only={nabs} worst_rel={worst:.2e}", flush=True)
     assert nf == 0
+    assert nabs <= parity.abs_only_limit(y.size), nabs
 
 
 def test_full_head_sampled_rows(dev):

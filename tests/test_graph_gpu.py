@@ -25,7 +25,7 @@ def test_qmv_and_acceptance_replay_from_a_graph():
     u = synth.uniforms(9, synth.U_ACCEPT, (B, D + 1))
     tt, dd = torch.from_numpy(t).to(dev), torch.from_numpy(d).to(dev)
     tk, uu = torch.from_numpy(dt).to(dev), torch.from_numpy(u).to(dev)
-    y_ref = spec.spec_qmv_w4(pk, x)
+    y_ref = spec.spec_qmv_w4_packed(pk, x)
     a_ref, n_ref = spec.spec_verify_accept(tt, dd, tk, uu, T)
     torch.cuda.synchronize()
 
@@ -36,7 +36,7 @@ def test_qmv_and_acceptance_replay_from_a_graph():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):      # warm up allocations outside the capture
-        spec.spec_qmv_w4(pk, x, y=y)
+        spec.spec_qmv_w4_packed(pk, x, y=y)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -52,7 +52,7 @@ def test_qmv_and_acceptance_replay_from_a_graph():
         assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), rep
         assert torch.equal(acc, a_ref) and torch.equal(nxt, n_ref), rep
         # eager work between replays, on other data
-        spec.spec_qmv_w4(pk, torch.flip(x, [0]).contiguous())
+        spec.spec_qmv_w4_packed(pk, torch.flip(x, [0]).contiguous())
         spec.spec_verify_accept(tt[:4].contiguous(), dd[:4].contiguous(), tk[:4].contiguous(),
                                 uu[:4].contiguous(), 1.0)
         torch.cuda.synchronize()

@@ -118,11 +118,12 @@ def test_mlp_block_chain(dev):
     gate, up, x, hg, hb = check_h(4, M, F, H, dev, cfg=40)
     down = synth.qweights(40, 4, H, F, 64, salt=3)
     pk = spec.spec_pack_w4(*parity.dev_qweights(*down, dev))
-    y = spec.spec_qmv_w4(pk, hg).cpu().numpy()
+    y = spec.spec_qmv_w4_packed(pk, hg).cpu().numpy()
     ref, mag = parity.oracle_qmv_threaded(4, *down, hb, 64)
     nf, nabs, worst = parity.check_qmv(y, ref, mag)
     print(f"MLP block M={M}: fail={nf} abs-only={nabs} worst_rel={worst:.2e}", flush=True)
     assert nf == 0
+    assert nabs <= parity.abs_only_limit(y.size), nabs
 
 
 def test_degenerate_shapes(dev):

@@ -25,23 +25,34 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run(bits, w, s, b, x, dev, G=64):
+def run(bits, w, s, b, x, dev, G=64, layout="packed"):
+    """y from the weights as stored (spec_qmv_w*, layout="interchange") or
+    from the repacked copy (spec_qmv_w*_packed)."""
     import speculative_decoding_spec_amd as spec
     wt, st, bt = parity.dev_qweights(w, s, b, dev)
-    pack = spec.spec_pack_w4 if bits == 4 else spec.spec_pack_w8
-    fn = spec.spec_qmv_w4 if bits == 4 else spec.spec_qmv_w8
-    y = fn(pack(wt, st, bt, G=G), parity.dev_x(x, dev))
+    xt = parity.dev_x(x, dev)
+    if layout == "interchange":
+        fn = spec.spec_qmv_w4 if bits == 4 else spec.spec_qmv_w8
+        y = fn(wt, st, bt, xt, G=G)
+    else:
+        pack = spec.spec_pack_w4 if bits == 4 else spec.spec_pack_w8
+        fn = spec.spec_qmv_w4_packed if bits == 4 else spec.spec_qmv_w8_packed
+        y = fn(pack(wt, st, bt, G=G), xt)
     return y.cpu().numpy()
 
 
 def full_check(bits, M, N, K, dev, cfg, salt=0):
+    """Every output against the oracle; both layouts, bitwise equal."""
     w, s, b = synth.qweights(cfg, bits, N, K, 64, salt=salt)
     x = synth.activations(cfg, M, K, salt=salt)
     got = run(bits, w, s, b, x, dev)
+    inter = run(bits, w, s, b, x, dev, layout="interchange")
+    assert np.array_equal(got.view(np.uint32), inter.view(np.uint32)), "layouts differ"
     ref, mag = parity.oracle_qmv_threaded(bits, w, s, b, x, 64)
     nf, nabs, worst = parity.check_qmv(got, ref, mag)
     print(f"W{bits} M={M} N={N} K={K}: fail={nf} abs-only={nabs} worst_rel={worst:.2e}", flush=True)
     assert nf == 0
+    assert nabs <= parity.abs_only_limit(got.size), nabs
     return got
 
 
@@ -69,6 +80,8 @@ def test_lm_head_sampled(dev, bits, M):
     w, s, b = synth.qweights(2 if bits == 4 else 4, bits, N, K, 64)
     x = synth.activations(2 if bits == 4 else 4, M, K)
     got = run(bits, w, s, b, x, dev)
+    inter = run(bits, w, s, b, x, dev, layout="interchange")
+    assert np.array_equal(got.view(np.uint32), inter.view(np.uint32)), "layouts differ"
     rng = np.random.default_rng(17)
     n_idx = np.concatenate([np.arange(64), np.arange(N - 64, N), rng.integers(0, N, 1500)])
     m_idx = rng.integers(0, M, n_idx.shape[0])
@@ -76,7 +89,16 @@ def test_lm_head_sampled(dev, bits, M):
     nf, nabs, worst = parity.check_qmv(got[m_idx, n_idx], ref, mag)
     print(f"LM head W{bits} M={M}: fail={nf} abs-only={nabs} worst_rel={worst:.2e}", flush=True)
     assert nf == 0
+    assert nabs <= parity.abs_only_limit(n_idx.shape[0]), nabs
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 6), (8, 8)])
+def test_lm_head_launch_shape_full(dev, bits, M):
+    """The launch shape of heads of 4096 tiles or more (W4: 4 tiles x 4 waves,
+    W8: 2 tiles x 8 waves) on every output, at a K the oracle finishes fast:
+    65600 rows (4100 tiles, a ragged last workgroup) x 256."""
+    full_check(bits, M, 65600, 256, dev, cfg=2, salt=65600 + M)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -100,13 +122,13 @@ def test_degenerate_shapes(dev):
                            torch.zeros((16, 0), dtype=torch.float16, device=dev),
                            torch.zeros((16, 0), dtype=torch.float16, device=dev))
     y = torch.full((3, 16), 7.0, device=dev)
-    spec.spec_qmv_w4(pk, torch.zeros((3, 0), dtype=torch.bfloat16, device=dev), y=y)
+    spec.spec_qmv_w4_packed(pk, torch.zeros((3, 0), dtype=torch.bfloat16, device=dev), y=y)
     assert torch.all(y == 0)
     # M = 0 is a no-op.
     pk = spec.spec_pack_w4(torch.zeros((16, 8), dtype=torch.int32, device=dev),
                            torch.zeros((16, 1), dtype=torch.float16, device=dev),
                            torch.zeros((16, 1), dtype=torch.float16, device=dev))
-    spec.spec_qmv_w4(pk, torch.zeros((0, 64), dtype=torch.bfloat16, device=dev))
+    spec.spec_qmv_w4_packed(pk, torch.zeros((0, 64), dtype=torch.bfloat16, device=dev))
     torch.cuda.synchronize()
 
 
@@ -143,7 +165,7 @@ def test_bound_call_matches_plain_call(dev):
     call()
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), first.view(torch.int32))
-    assert torch.equal(spec.spec_qmv_w4(pk, xt).view(torch.int32), y.view(torch.int32))
+    assert torch.equal(spec.spec_qmv_w4_packed(pk, xt).view(torch.int32), y.view(torch.int32))
 
 
 def test_fused_gate_up_matches_separate_launches(dev):
@@ -159,9 +181,9 @@ def test_fused_gate_up_matches_separate_launches(dev):
     u = spec.spec_pack_w4(*parity.dev_qweights(*up, dev))
     cat = [np.concatenate([a, b], axis=0) for a, b in zip(gate, up)]
     gu = spec.spec_pack_w4(*parity.dev_qweights(*cat, dev))
-    y = spec.spec_qmv_w4(gu, x)
-    assert torch.equal(y[:, :N].view(torch.int32), spec.spec_qmv_w4(g, x).view(torch.int32))
-    assert torch.equal(y[:, N:].view(torch.int32), spec.spec_qmv_w4(u, x).view(torch.int32))
+    y = spec.spec_qmv_w4_packed(gu, x)
+    assert torch.equal(y[:, :N].view(torch.int32), spec.spec_qmv_w4_packed(g, x).view(torch.int32))
+    assert torch.equal(y[:, N:].view(torch.int32), spec.spec_qmv_w4_packed(u, x).view(torch.int32))
 
 
 @pytest.mark.parametrize("M", [3, 6])
@@ -176,11 +198,11 @@ def test_fused_qkv_matches_separate_launches(dev, M):
     xa = synth.activations(9, M, K)
     x = parity.dev_x(xa, dev)
     cat = [np.concatenate(list(t), axis=0) for t in zip(*parts)]
-    y = spec.spec_qmv_w4(spec.spec_pack_w4(*parity.dev_qweights(*cat, dev)), x)
+    y = spec.spec_qmv_w4_packed(spec.spec_pack_w4(*parity.dev_qweights(*cat, dev)), x)
     lo = 0
     for p in parts:
         n = p[0].shape[0]
-        ys = spec.spec_qmv_w4(spec.spec_pack_w4(*parity.dev_qweights(*p, dev)), x)
+        ys = spec.spec_qmv_w4_packed(spec.spec_pack_w4(*parity.dev_qweights(*p, dev)), x)
         assert torch.equal(y[:, lo:lo + n].view(torch.int32), ys.view(torch.int32))
         lo += n
     rng = np.random.default_rng(M)
