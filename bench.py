@@ -16,50 +16,47 @@ One step = one pass of the whole hot path over resident synthetic inputs:
 
 Launches go through pre-marshalled calls (`bind_qmv_gate_up_silu`,
 `bind_qmv`, `bind_verify_accept`), so the host queues them far faster than
-the GPU runs them.  Under `variants`: the same weights streamed with gate/up
-as one launch writing fp32 outputs (no activation), and gate, up and down as
-24 separate launches.  (Replaying the step from a HIP graph measured slower than
-these eager launches on this system -- 359 vs 322 us for the qmv part -- so
-graphs are not used here; the library's calls are capture-safe all the same.)
-
-Greedy verification (`bind_verify_greedy`: match the greedy draft's tokens
-against the target's argmax, reading only the target logits) of the same
-block is timed on its own after the steps and reported under
-`accept_greedy`; it is not part of the step.
+the GPU runs them.  HIP events on the launch stream bracket the qmv part and
+the acceptance call of every timed step; `value` and the acceptance figures
+come from the median step, with p10 and p90 beside them.
 
 Printed: one JSON line.  `value` is the verify qmv throughput in HBM GB/s
-(algorithmic bytes / time of the qmv part of the steps); the acceptance
-throughput (verify positions per second) and per-M figures ride along, and
-`stream_read` gives the rate of a plain streaming read of 2 GiB
-(`spec_stream_read`), of which `qmv_frac_of_stream` and
-`accept.frac_of_stream` are the two parts' shares.
+(algorithmic bytes of the 16 launches / the median time of the qmv part).
+Beside it, after the timed steps (none of it inside the steps):
+  * `variants`: the same MLP weights read as stored (spec_qmv_w4 on the
+    interchange layout, gate/up fused into one fp32 launch), as one plain
+    gate/up launch from the packed copy, and as 24 separate launches;
+  * `per_M`: the step's time split by M (events around each launch);
+  * `configs`: every other workload of the verify hot path --
+      pr1_reference   W4 g64 qmv M=4 K=1024 N=4096 and acceptance B=1 D=3
+                      V=32768 T=0.6 (latency, us);
+      lm_head_accept  the W4 LM head 5120->151936 at M=6, then acceptance of
+                      its logits with top-k 20 / top-p 0.95 (B=1, D=5);
+      w8_lm_head      the W8 g64 LM head at M=8;
+      verify_pass_64_layers  the projections of a 64-layer 5120-hidden
+                      decoder (12.3 GB of W4 weights) at M=3..6, four
+                      launches per layer as the model runs them;
+  * `accept_greedy`: greedy verification of the step's block (target logits
+    only);
+  * `stream_read`: a plain streaming read of 2 GiB (`spec_stream_read`), of
+    which `qmv_frac_of_stream` and `accept.frac_of_stream` are the shares;
+  * `cpu_baseline`: the fp64 oracle on the host, all threads and one.
 
 `roofline` covers qmv_kernel, the kernel with the most time per step (16
 launches): algorithmic bytes per launch over the average launch duration,
-the qmv part of the timed steps (HIP events on the launch stream around the
-16 back-to-back launches) divided by 16.  A second set of timed steps with
-events around every launch splits the time by shape and M.  `traffic` is the HBM bytes per
-launch from the committed counter summary under profiles/ (FETCH_SIZE +
-WRITE_SIZE scaled by a plain-copy calibration), and null when qmv.hip or the
-step's launches have changed since those counters were taken.
+i.e. the median qmv part of a step divided by 16.  `traffic` is the HBM
+bytes per launch from the committed counter summary under profiles/
+(FETCH_SIZE + WRITE_SIZE scaled by a plain-copy calibration), and null when
+qmv.hip or the step's launches have changed since those counters were taken.
 
-`--step-only` times the steps alone (no variants, no greedy verification, no
-CPU baseline): the form the counter runs use.
+`--step-only` times the steps alone (no variants, configs or CPU baseline):
+the form the counter runs use.
 `--copy-probe` runs only a plain read-once / write-once elementwise kernel
 over 1 GiB (the calibration kernel for those counters) and exits.
-`--lmhead` times the end of one sequence's verify pass: the W4 LM head at
-M = 6 and the acceptance with top-k 20 / top-p 0.95 on its logits.
-`--depth` times the projections of a whole 64-layer verify pass (12.3 GB
-of weights) at M = 3..6, fused as the model runs them and as separate
-launches.
-`--draft` times the draft step: the LM head at M = 1 (a 4-bit copy built by
-`spec_requantize_w4`, and an 8-bit head for comparison) and one draw.
-`--gdn` times the recurrent-state capture and commit of one verify cycle
-over 36 layers, as two calls and as the one-pass cycle boundary (one JSON
-line), and exits.
-`--shapes` times qmv alone per layer shape and M (rotating >= 1.1 GB of
-weight copies) plus an N sweep that splits a launch's time into a fixed
-cost and an incremental bandwidth, prints one JSON line each, and exits.
+`--lmhead`, `--depth` (also as 7 separate launches per layer), `--draft`,
+`--gdn` and `--shapes` time one part each and print one JSON line (per
+shape for `--shapes`, with an N sweep that splits a launch's time into a
+fixed cost and an incremental bandwidth), and exit.
 """
 from __future__ import annotations
 
@@ -81,20 +78,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmv_kernel_w4_mlp_block_hbm_traffic.txt")
 QMV_SOURCE = os.path.join(ROOT, "speculative_decoding_spec_amd", "csrc", "qmv.hip")
 COPY_BYTES = 1 << 30
+PEAK_GBS = 8000.0
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of each oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel used to calibrate HBM counters")
     ap.add_argument("--step-only", action="store_true",
-                    help="time the steps only (no variants, greedy pass or CPU baseline)")
+                    help="time the steps only (no variants, configs or CPU baseline)")
     ap.add_argument("--lmhead", action="store_true",
                     help="only time the LM head at M=6 plus acceptance with top-k/top-p (B=1) and exit")
     ap.add_argument("--depth", action="store_true",
@@ -127,7 +125,76 @@ SHAPES = {
 SWEEP_N = [2176, 4352, 8704, 17408, 34816, 69632]
 
 
-def lmhead(dev, steps):
+def pct(values):
+    """(median, p10, p90) of a list."""
+    import numpy as np
+    a = np.asarray(values, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def spread_us(values_us):
+    med, p10, p90 = pct(values_us)
+    return {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2)}
+
+
+def rate(nbytes, us):
+    gbs = nbytes / us / 1e3
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4)}
+
+
+def timed_each(calls, reps, stream):
+    """Microseconds of each of `reps` back-to-back calls (cycling through
+    `calls`), with HIP events on `stream` around every call."""
+    import torch
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        calls[i % len(calls)]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def pr1_reference(dev, steps):
+    """The smallest workload: W4 g64 qmv at M=4, K=1024, N=4096 (read as
+    stored and from the packed copy) and acceptance of B=1, D=3 over a
+    32768-token vocabulary at T=0.6.  Latency-bound, so reported in us."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    stream = torch.cuda.current_stream(dev)
+    M, N, K = 4, 4096, 1024
+    raw = [synth.torch_qweights(4, N, K, GROUP, 8600 + c, dev) for c in range(64)]
+    x = synth.torch_activations(M, K, 8690, dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # 64 weight copies (155 MB) so the launches do not stream from cache
+    packed = [spec.bind_qmv(spec.spec_pack_w4(*r, G=GROUP), x, y) for r in raw]
+    inter = [spec.bind_qmv(spec.QWeights(4, *r, G=GROUP), x, y) for r in raw]
+    B, D, V = 1, 3, 32768
+    t, d = synth.torch_logits_pair(B, D, V, 8691, dev)
+    toks = spec.spec_sample_tokens(d.view(B * D, V), synth.torch_uniforms((B * D,), 8692, dev),
+                                   ACC_T).view(B, D).contiguous()
+    u = synth.torch_uniforms((B, D + 1), 8693, dev)
+    out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+           None, None)
+    accept = spec.bind_verify_accept(t, d, toks, u, ACC_T, out=out)
+    qb = roofline.qmv_bytes(4, M, N, K)
+    ab = roofline.accept_bytes(B, D, V)
+    pk = spread_us(timed_each(packed, steps, stream))
+    it = spread_us(timed_each(inter, steps, stream))
+    ac = spread_us(timed_each([accept], steps, stream))
+    return {"workload": "W4 g64 qmv M=4 K=1024 N=4096; acceptance B=1 D=3 V=32768 T=0.6",
+            "qmv_packed": {**pk, **rate(qb, pk["us"])},
+            "qmv_interchange": {**it, **rate(qb, it["us"])},
+            "accept": {**ac, **rate(ab, ac["us"]), "positions_per_s": round(B * (D + 1) / ac["us"] * 1e6, 1)},
+            "algorithmic_bytes": {"qmv": qb, "accept": ab}}
+
+
+def lmhead_accept(dev, steps):
     """The end of a verify pass for one sequence at depth D = 5: the W4 LM
     head at M = 6 writes the target logits, and the acceptance (T = 0.6,
     top-k 20, top-p 0.95) runs on them; the draft logits are the target's
@@ -136,6 +203,7 @@ def lmhead(dev, steps):
     import torch
     import speculative_decoding_spec_amd as spec
     from speculative_decoding_spec_amd import roofline, synth
+    stream = torch.cuda.current_stream(dev)
     V, K, D = 151936, HIDDEN, 5
     heads = [spec.spec_pack_w4(*synth.torch_qweights(4, V, K, GROUP, 8400 + c, dev), G=GROUP)
              for c in range(3)]
@@ -148,50 +216,54 @@ def lmhead(dev, steps):
     ud = synth.torch_uniforms((D,), 8412, dev)
     toks = spec.spec_sample_tokens(draft, ud, ACC_T, 20, 0.95).view(1, D).contiguous()
     u = synth.torch_uniforms((1, D + 1), 8413, dev)
-    t3 = logits.view(1, D + 1, V)
-    d3 = draft.view(1, D, V)
     out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
            None, None)
-    accept = spec.bind_verify_accept(t3, d3, toks, u, ACC_T, 20, 0.95, out=out)
+    accept = spec.bind_verify_accept(logits.view(1, D + 1, V), draft.view(1, D, V), toks, u, ACC_T,
+                                     20, 0.95, out=out)
     calls = [spec.bind_qmv(h, x, logits) for h in heads]
-    for c in calls:
-        c()
-        accept()
-    torch.cuda.synchronize()
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-    for i, (a, b_, c_) in enumerate(ev):
-        a.record()
-        calls[i % len(calls)]()
-        b_.record()
-        accept()
-        c_.record()
-    torch.cuda.synchronize()
-    head = sum(a.elapsed_time(b_) for a, b_, _ in ev) / steps * 1e3
-    acc = sum(b_.elapsed_time(c_) for _, b_, c_ in ev) / steps * 1e3
+    head = spread_us(timed_each(calls, steps, stream))
+    acc = spread_us(timed_each([accept], steps, stream))
     nb = roofline.qmv_bytes(4, D + 1, V, K)
-    print(json.dumps({"lmhead": ("W4 g64 LM head 5120->151936 at M=6, then acceptance of D=5 drafts "
-                                 "(T=0.6, top-k 20, top-p 0.95) for one sequence"),
-                      "head_us": round(head, 2), "head_GB/s": round(nb / head / 1e3, 1),
-                      "head_frac": round(nb / head / 1e3 / 8000.0, 4), "accept_us": round(acc, 2),
-                      "accepted_len": int(out[0].item()), "next_token": int(out[1].item())}),
-          flush=True)
+    return {"workload": ("W4 g64 LM head 5120->151936 at M=6, then acceptance of D=5 drafts "
+                         "(T=0.6, top-k 20, top-p 0.95) for one sequence"),
+            "head": {**head, **rate(nb, head["us"]), "algorithmic_bytes": nb},
+            "accept": acc,
+            "accepted_len": int(out[0].item()), "next_token": int(out[1].item())}
+
+
+def w8_lm_head(dev, steps):
+    """The W8 g64 LM head 5120->151936 at M=8 (two copies, 1.66 GB)."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline, synth
+    stream = torch.cuda.current_stream(dev)
+    V, K, M = 151936, HIDDEN, 8
+    heads = [spec.spec_pack_w8(*synth.torch_qweights(8, V, K, GROUP, 8500 + c, dev), G=GROUP)
+             for c in range(2)]
+    x = synth.torch_activations(M, K, 8510, dev)
+    y = torch.empty((M, V), dtype=torch.float32, device=dev)
+    t = spread_us(timed_each([spec.bind_qmv(h, x, y) for h in heads], steps, stream))
+    nb = roofline.qmv_bytes(8, M, V, K)
+    return {"workload": "W8 g64 LM head 5120->151936 at M=8", **t, **rate(nb, t["us"]),
+            "algorithmic_bytes": nb}
 
 
 DEPTH_LAYERS, Q_N, KV_N, O_K = 64, 6144, 1024, 6144
 
 
-def depth(dev, steps):
+def verify_pass(dev, steps, Ms=(3, 4, 5, 6), separate=False):
     """The linear projections of a whole verify pass: 64 decoder layers of
     q 5120->6144, k and v 5120->1024, o 6144->5120, gate and up
     5120->17408, down 17408->5120, all W4 g64 with each layer's own weights
     (12.3 GB), at M = 3..6 (depths D2..D5).  Streamed as the model runs it:
     q, k and v as one launch (they share x), o, gate/up with the gated
-    activation, and down on that activation, 4 launches per layer; and, for
-    comparison, the same weights as 7 separate launches per layer."""
+    activation, and down on that activation, 4 launches per layer; with
+    `separate`, also the same weights as 7 separate launches per layer."""
     import torch
     import speculative_decoding_spec_amd as spec
     from speculative_decoding_spec_amd import roofline, synth
-    fused, separate = [], []
+    stream = torch.cuda.current_stream(dev)
+    fused, sep = [], []
     for li in range(DEPTH_LAYERS):
         sd = 9000 + 10 * li
         q = synth.torch_qweights(4, Q_N, HIDDEN, GROUP, sd, dev)
@@ -204,59 +276,62 @@ def depth(dev, steps):
         qkv = spec.spec_pack_w4(*[torch.cat(t) for t in zip(q, k, v)], G=GROUP)
         po, pd = spec.spec_pack_w4(*o, G=GROUP), spec.spec_pack_w4(*d, G=GROUP)
         fused.append((qkv, po, spec.spec_pack_gate_up(4, g, u, G=GROUP), pd))
-        separate.append(tuple(spec.spec_pack_w4(*t, G=GROUP) for t in (q, k, v, o, g, u, d)))
+        if separate:
+            sep.append(tuple(spec.spec_pack_w4(*t, G=GROUP) for t in (q, k, v, o, g, u, d)))
         del q, k, v, o, g, u, d
     torch.cuda.synchronize()
     res = {}
-    for M in (3, 4, 5, 6):
+    for M in Ms:
         x = synth.torch_activations(M, HIDDEN, 9500 + M, dev)
         a = synth.torch_activations(M, O_K, 9510 + M, dev)          # attention output
         yqkv = torch.empty((M, Q_N + 2 * KV_N), device=dev)
         yo = torch.empty((M, HIDDEN), device=dev)
         h = torch.empty((M, FFN), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((M, HIDDEN), device=dev)
-        yq = torch.empty((M, Q_N), device=dev)
-        ykv = torch.empty((M, KV_N), device=dev)
-        yg = torch.empty((M, FFN), device=dev)
-        f_calls, s_calls = [], []
-        f_bytes = s_bytes = 0
-        for (qkv, po, glu, pd), (q, k, v, o, g, u, d) in zip(fused, separate):
+        f_calls, f_bytes = [], 0
+        for (qkv, po, glu, pd) in fused:
             f_calls += [spec.bind_qmv(qkv, x, yqkv), spec.bind_qmv(po, a, yo),
                         spec.bind_qmv_gate_up_silu(glu, x, h), spec.bind_qmv(pd, h, yd)]
             f_bytes += (roofline.qmv_bytes(4, M, Q_N + 2 * KV_N, HIDDEN)
                         + roofline.qmv_bytes(4, M, HIDDEN, O_K)
                         + roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN)
                         + roofline.qmv_bytes(4, M, HIDDEN, FFN))
-            s_calls += [spec.bind_qmv(q, x, yq), spec.bind_qmv(k, x, ykv), spec.bind_qmv(v, x, ykv),
-                        spec.bind_qmv(o, a, yo), spec.bind_qmv(g, x, yg), spec.bind_qmv(u, x, yg),
-                        spec.bind_qmv(d, h, yd)]
-            s_bytes += (roofline.qmv_bytes(4, M, Q_N, HIDDEN) + 2 * roofline.qmv_bytes(4, M, KV_N, HIDDEN)
-                        + roofline.qmv_bytes(4, M, HIDDEN, O_K) + 2 * roofline.qmv_bytes(4, M, FFN, HIDDEN)
-                        + roofline.qmv_bytes(4, M, HIDDEN, FFN))
 
-        def cycle_us(calls):
+        def pass_us(calls):
+            """Microseconds of each of `steps` whole passes (events around each)."""
             for c in calls:
                 c()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record(stream)
                 for c in calls:
                     c()
-            e1.record()
+                e1.record(stream)
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / steps
+            return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
 
-        fu, su = cycle_us(f_calls), cycle_us(s_calls)
-        res[str(M)] = {"fused_4_launches_per_layer": {"us": round(fu, 1), "bytes": f_bytes,
-                                                      "GB/s": round(f_bytes / fu / 1e3, 1),
-                                                      "frac": round(f_bytes / fu / 1e3 / 8000.0, 4)},
-                       "separate_7_launches_per_layer": {"us": round(su, 1), "bytes": s_bytes,
-                                                         "GB/s": round(s_bytes / su / 1e3, 1),
-                                                         "frac": round(s_bytes / su / 1e3 / 8000.0, 4)}}
-    print(json.dumps({"depth": (f"verify-pass projections of a {DEPTH_LAYERS}-layer 5120-hidden "
-                                "decoder, W4 g64, each layer its own weights, per M"),
-                      "per_M": res}), flush=True)
+        fu = spread_us(pass_us(f_calls))
+        res[str(M)] = {"fused_4_launches_per_layer": {**fu, "bytes": f_bytes, **rate(f_bytes, fu["us"])}}
+        if separate:
+            yq = torch.empty((M, Q_N), device=dev)
+            ykv = torch.empty((M, KV_N), device=dev)
+            yg = torch.empty((M, FFN), device=dev)
+            s_calls, s_bytes = [], 0
+            for (q, k, v, o, g, u, d) in sep:
+                s_calls += [spec.bind_qmv(q, x, yq), spec.bind_qmv(k, x, ykv), spec.bind_qmv(v, x, ykv),
+                            spec.bind_qmv(o, a, yo), spec.bind_qmv(g, x, yg), spec.bind_qmv(u, x, yg),
+                            spec.bind_qmv(d, h, yd)]
+                s_bytes += (roofline.qmv_bytes(4, M, Q_N, HIDDEN) + 2 * roofline.qmv_bytes(4, M, KV_N, HIDDEN)
+                            + roofline.qmv_bytes(4, M, HIDDEN, O_K) + 2 * roofline.qmv_bytes(4, M, FFN, HIDDEN)
+                            + roofline.qmv_bytes(4, M, HIDDEN, FFN))
+            su = spread_us(pass_us(s_calls))
+            res[str(M)]["separate_7_launches_per_layer"] = {**su, "bytes": s_bytes, **rate(s_bytes, su["us"])}
+    del fused, sep
+    torch.cuda.empty_cache()
+    return {"workload": (f"verify-pass projections of a {DEPTH_LAYERS}-layer 5120-hidden decoder, "
+                         "W4 g64, each layer its own weights, per M"), "per_M": res}
 
 
 def draft(dev, steps):
@@ -532,38 +607,6 @@ def measured_traffic(bytes_per_launch):
         return None, "no counter summary"
 
 
-def build_inputs(dev, variants=True):
-    """Packed W4 weights (packing is a load-time step, outside the timing):
-    per M, gate/up packed for the gated launch, the down matrix, and (for
-    the variants) gate/up packed as one plain matrix and gate and up packed
-    separately."""
-    import torch
-    import speculative_decoding_spec_amd as spec
-    from speculative_decoding_spec_amd import synth
-
-    blocks = []
-    for i, M in enumerate(MS):
-        g = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1000 + 10 * i, dev)
-        u = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1001 + 10 * i, dev)
-        d = synth.torch_qweights(4, HIDDEN, FFN, GROUP, 1002 + 10 * i, dev)
-        glu = spec.spec_pack_gate_up(4, g, u, G=GROUP)
-        down = spec.spec_pack_w4(*d, G=GROUP)
-        blk = dict(M=M, glu=glu, down=down)
-        if variants:
-            blk["gate_up"] = spec.spec_pack_w4(*[torch.cat([a, b]) for a, b in zip(g, u)], G=GROUP)
-            blk["gate"], blk["up"] = spec.spec_pack_w4(*g, G=GROUP), spec.spec_pack_w4(*u, G=GROUP)
-        del g, u, d
-        blk["x"] = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
-        blk["h"] = torch.empty((M, FFN), dtype=torch.bfloat16, device=dev)
-        blk["ygu"] = torch.empty((M, 2 * FFN), dtype=torch.float32, device=dev)
-        blk["yg"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
-        blk["yu"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
-        blk["yd"] = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
-        blocks.append(blk)
-    torch.cuda.synchronize()
-    return blocks
-
-
 def build_accept(dev):
     import torch
     import speculative_decoding_spec_amd as spec
@@ -580,68 +623,122 @@ def build_accept(dev):
     return dict(t=t, d=d, toks=toks.contiguous(), u=u, acc=acc, nxt=nxt)
 
 
-def run_accept(a):
+
+def build_inputs(dev, variants=True):
+    """W4 weights per M: gate/up packed for the gated launch and the down
+    matrix (packing is a load-time step, outside the timing); for the
+    variants also the weights as stored (read by spec_qmv_w4 directly, gate
+    and up concatenated) and gate/up packed as one plain matrix and as two."""
+    import torch
     import speculative_decoding_spec_amd as spec
-    spec.spec_verify_accept(a["t"], a["d"], a["toks"], a["u"], ACC_T,
-                            out=(a["acc"], a["nxt"], None, None))
+    from speculative_decoding_spec_amd import synth
+
+    blocks = []
+    for i, M in enumerate(MS):
+        g = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1000 + 10 * i, dev)
+        u = synth.torch_qweights(4, FFN, HIDDEN, GROUP, 1001 + 10 * i, dev)
+        d = synth.torch_qweights(4, HIDDEN, FFN, GROUP, 1002 + 10 * i, dev)
+        glu = spec.spec_pack_gate_up(4, g, u, G=GROUP)
+        down = spec.spec_pack_w4(*d, G=GROUP)
+        blk = dict(M=M, glu=glu, down=down)
+        if variants:
+            gu = [torch.cat([a, b]) for a, b in zip(g, u)]
+            blk["gate_up"] = spec.spec_pack_w4(*gu, G=GROUP)
+            blk["gate"], blk["up"] = spec.spec_pack_w4(*g, G=GROUP), spec.spec_pack_w4(*u, G=GROUP)
+            blk["gate_up_as_stored"] = spec.QWeights(4, *gu, G=GROUP)
+            blk["down_as_stored"] = spec.QWeights(4, *d, G=GROUP)
+        del g, u, d
+        blk["x"] = synth.torch_activations(M, HIDDEN, 1003 + 10 * i, dev)
+        blk["h"] = torch.empty((M, FFN), dtype=torch.bfloat16, device=dev)
+        blk["ygu"] = torch.empty((M, 2 * FFN), dtype=torch.float32, device=dev)
+        blk["yg"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
+        blk["yu"] = torch.empty((M, FFN), dtype=torch.float32, device=dev)
+        blk["yd"] = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
+        blocks.append(blk)
+    torch.cuda.synchronize()
+    return blocks
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(seconds):
-    """The fp64 oracle, as it stands, on a bounded sample of the step.
+    """The fp64 oracle, as it stands, on a bounded sample of the step, with
+    all host threads (16 at most: the box's share) and with one.
 
     qmv: the step's MLP chain at M = 1..8 (the gated gate/up activation,
     then down on the oracle's own bf16 h) with one seeded weight set per
-    shape, rows split over the host threads, stopping once `seconds` have
-    passed; acceptance: the 256-sequence batch, drafts drawn from the draft
-    rows as on the GPU, likewise bounded.  Rates use the GPU figure's
-    algorithmic bytes (GB/s) and verify positions per second."""
+    shape, rows split over the threads, stopping once `seconds` have passed;
+    acceptance: the 256-sequence batch, drafts drawn from the draft rows as
+    on the GPU, likewise bounded.  Rates use the GPU figure's algorithmic
+    bytes (GB/s) and verify positions per second."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     from speculative_decoding_spec_amd import roofline, synth
-    threads = min(16, os.cpu_count() or 1)
     gate = synth.qweights(1, 4, FFN, HIDDEN, GROUP, salt=1)
     up = synth.qweights(1, 4, FFN, HIDDEN, GROUP, salt=2)
     down = synth.qweights(1, 4, HIDDEN, FFN, GROUP, salt=3)
-    chunk = 256
-    done_bytes, launches, t0 = 0, 0, time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        for M in MS:
-            if time.perf_counter() - t0 >= seconds:
-                break
-            x = synth.activations(1, M, HIDDEN, salt=M)
-            spans = [(r, min(FFN, r + chunk)) for r in range(0, FFN, chunk)]
-            parts = list(ex.map(lambda sp: oracle.gate_up_silu(4, gate, up, x, GROUP, rows=sp), spans))
-            hb = np.ascontiguousarray(np.concatenate([p[1] for p in parts], axis=1))
-            done_bytes += roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN, GROUP)
-            launches += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-            spans = [(r, min(HIDDEN, r + chunk)) for r in range(0, HIDDEN, chunk)]
-            list(ex.map(lambda sp: oracle.qmv(4, *down, hb, GROUP, rows=sp), spans))
-            done_bytes += roofline.qmv_bytes(4, M, HIDDEN, FFN, GROUP)
-            launches += 1
-    dt = time.perf_counter() - t0
     tl, dl = synth.logits_pair(4, ACC_B, ACC_D, ACC_V)
     ud = synth.uniforms(4, synth.U_DRAFT, ACC_B * ACC_D)
     toks = oracle.sample_rows(dl.reshape(ACC_B * ACC_D, ACC_V), ACC_T, 0, 1.0, ud).reshape(ACC_B, ACC_D)
     u = synth.uniforms(4, synth.U_ACCEPT, (ACC_B, ACC_D + 1))
-    nseq, t1 = 0, time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        while nseq < ACC_B and time.perf_counter() - t1 < seconds:
-            idx = range(nseq, min(ACC_B, nseq + threads))
-            list(ex.map(lambda i: oracle.accept(tl[i:i + 1], dl[i:i + 1], toks[i:i + 1],
-                                                u[i:i + 1], ACC_T), idx))
-            nseq = idx[-1] + 1
-    at = time.perf_counter() - t1
+
+    def run(threads, budget):
+        chunk = 256
+        done_bytes, launches, t0 = 0, 0, time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            for M in MS:
+                if time.perf_counter() - t0 >= budget:
+                    break
+                x = synth.activations(1, M, HIDDEN, salt=M)
+                spans = [(r, min(FFN, r + chunk)) for r in range(0, FFN, chunk)]
+                parts = list(ex.map(lambda sp: oracle.gate_up_silu(4, gate, up, x, GROUP, rows=sp), spans))
+                hb = np.ascontiguousarray(np.concatenate([p[1] for p in parts], axis=1))
+                done_bytes += roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN, GROUP)
+                launches += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+                spans = [(r, min(HIDDEN, r + chunk)) for r in range(0, HIDDEN, chunk)]
+                list(ex.map(lambda sp: oracle.qmv(4, *down, hb, GROUP, rows=sp), spans))
+                done_bytes += roofline.qmv_bytes(4, M, HIDDEN, FFN, GROUP)
+                launches += 1
+        dt = time.perf_counter() - t0
+        nseq, t1 = 0, time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            while nseq < ACC_B and time.perf_counter() - t1 < budget:
+                idx = range(nseq, min(ACC_B, nseq + threads))
+                list(ex.map(lambda i: oracle.accept(tl[i:i + 1], dl[i:i + 1], toks[i:i + 1],
+                                                    u[i:i + 1], ACC_T), idx))
+                nseq = idx[-1] + 1
+        at = time.perf_counter() - t1
+        return {"GB/s": round(done_bytes / dt / 1e9, 4), "launches": launches,
+                "MB": round(done_bytes / 1e6), "qmv_s": round(dt, 2),
+                "accept_positions_per_s": round(nseq * (ACC_D + 1) / at, 1), "sequences": nseq,
+                "accept_s": round(at, 2)}
+
+    threads = min(16, os.cpu_count() or 1)
+    allc = run(threads, seconds)
+    one = run(1, seconds / 2)
     return {
-        "value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": (f"W4 g64 MLP chain: {launches} of the step's 16 launches (gated gate/up "
-                   f"5120->2x17408, down 17408->5120, M=1..8), {done_bytes / 1e6:.0f} MB "
-                   f"algorithmic in {dt:.1f} s; acceptance: {nseq} of 256 sequences (D=5, "
-                   f"V=151936, T=0.6) in {at:.2f} s"),
-        "accept_positions_per_s": round(nseq * (ACC_D + 1) / at, 1),
-        "cpu": platform.processor() or platform.machine(),
+        "value": allc["GB/s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"W4 g64 MLP chain: {allc['launches']} of the step's 16 launches (gated gate/up "
+                   f"5120->2x17408, down 17408->5120, M=1..8), {allc['MB']} MB algorithmic in "
+                   f"{allc['qmv_s']} s; acceptance: {allc['sequences']} of 256 sequences (D=5, "
+                   f"V=151936, T=0.6) in {allc['accept_s']} s"),
+        "accept_positions_per_s": allc["accept_positions_per_s"],
+        "single_thread": {"GB/s": one["GB/s"], "accept_positions_per_s": one["accept_positions_per_s"],
+                          "sample": (f"{one['launches']} launches, {one['MB']} MB in {one['qmv_s']} s; "
+                                     f"{one['sequences']} sequences in {one['accept_s']} s")},
+        "cpu": cpu_model(), "host_threads": os.cpu_count(),
     }
 
 
@@ -672,53 +769,47 @@ def main():
         draft(dev, args.steps)
         return
     if args.depth:
-        depth(dev, args.steps)
+        print(json.dumps({"depth": verify_pass(dev, min(args.steps, 20), separate=True)}), flush=True)
         return
     if args.lmhead:
-        lmhead(dev, args.steps)
+        print(json.dumps({"lmhead": lmhead_accept(dev, args.steps)}), flush=True)
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)
     acc = build_accept(dev)
     stream = torch.cuda.current_stream(dev)
-
     acc_bytes = roofline.accept_bytes(ACC_B, ACC_D, ACC_V)
 
     def pair():
         return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
-    def chain_launches():
-        """(bound call, shape name, algorithmic bytes) of the step's 16
-        launches: the gated gate/up launch, then down reading its h."""
+    def mlp_launches(kind):
+        """(bound call, shape name, algorithmic bytes) per launch of the MLP
+        blocks: 'chain' = gated gate/up then down on its h (the step);
+        'plain' = gate/up as one fp32 launch, then down; 'separate' = gate,
+        up and down; 'as_stored' = 'plain' read from the interchange layout."""
         out = []
         for b in blocks:
-            out.append((spec.bind_qmv_gate_up_silu(b["glu"], b["x"], b["h"]), "gate_up_silu",
-                        roofline.gate_up_silu_bytes(4, b["M"], FFN, HIDDEN)))
-            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
-                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
+            M = b["M"]
+            if kind == "chain":
+                out.append((spec.bind_qmv_gate_up_silu(b["glu"], b["x"], b["h"]), "gate_up_silu",
+                            roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN)))
+            elif kind == "plain":
+                out.append((spec.bind_qmv(b["gate_up"], b["x"], b["ygu"]), "gate_up",
+                            roofline.qmv_bytes(4, M, 2 * FFN, HIDDEN)))
+            elif kind == "as_stored":
+                out.append((spec.bind_qmv(b["gate_up_as_stored"], b["x"], b["ygu"]), "gate_up",
+                            roofline.qmv_bytes(4, M, 2 * FFN, HIDDEN)))
+            else:
+                out.append((spec.bind_qmv(b["gate"], b["x"], b["yg"]), "gate",
+                            roofline.qmv_bytes(4, M, FFN, HIDDEN)))
+                out.append((spec.bind_qmv(b["up"], b["x"], b["yu"]), "up",
+                            roofline.qmv_bytes(4, M, FFN, HIDDEN)))
+            down = b["down_as_stored"] if kind == "as_stored" else b["down"]
+            out.append((spec.bind_qmv(down, b["h"], b["yd"]), "down", roofline.qmv_bytes(4, M, HIDDEN, FFN)))
         return out
 
-    def plain_fused_launches():
-        out = []
-        for b in blocks:
-            out.append((spec.bind_qmv(b["gate_up"], b["x"], b["ygu"]), "gate_up",
-                        roofline.qmv_bytes(4, b["M"], 2 * FFN, HIDDEN)))
-            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
-                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
-        return out
-
-    def unfused_launches():
-        out = []
-        for b in blocks:
-            out.append((spec.bind_qmv(b["gate"], b["x"], b["yg"]), "gate",
-                        roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
-            out.append((spec.bind_qmv(b["up"], b["x"], b["yu"]), "up",
-                        roofline.qmv_bytes(4, b["M"], FFN, HIDDEN)))
-            out.append((spec.bind_qmv(b["down"], b["h"], b["yd"]), "down",
-                        roofline.qmv_bytes(4, b["M"], HIDDEN, FFN)))
-        return out
-
-    launches = chain_launches()
+    launches = mlp_launches("chain")
     accept_call = spec.bind_verify_accept(acc["t"], acc["d"], acc["toks"], acc["u"], ACC_T,
                                           out=(acc["acc"], acc["nxt"], None, None))
     qmv_bytes_step = sum(l[2] for l in launches)
@@ -740,7 +831,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed steps: events around the qmv part and the acceptance call.
+    # Timed steps: events around the qmv part and the acceptance call of each.
     ev = [{"q": pair(), "a": pair()} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -748,29 +839,31 @@ def main():
         step(ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    qspan_ms = sum(e["q"][0].elapsed_time(e["q"][1]) for e in ev) / args.steps
-    acc_ms = sum(e["a"][0].elapsed_time(e["a"][1]) for e in ev) / args.steps
-    qmv_gbs = qmv_bytes_step / (qspan_ms * 1e-3) / 1e9
+    q_us = [e["q"][0].elapsed_time(e["q"][1]) * 1e3 for e in ev]
+    a_us = [e["a"][0].elapsed_time(e["a"][1]) * 1e3 for e in ev]
+    qmed, qp10, qp90 = pct(q_us)
+    amed, ap10, ap90 = pct(a_us)
+    qmv_gbs = qmv_bytes_step / qmed / 1e3
     positions = ACC_B * (ACC_D + 1)
-    acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
-    accept = {"positions_per_s": round(positions / (acc_ms * 1e-3), 1), "us": round(acc_ms * 1e3, 2),
-              "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4),
+    acc_gbs = acc_bytes / amed / 1e3
+    accept = {"positions_per_s": round(positions / amed * 1e6, 1),
+              "us": round(amed, 2), "p10_us": round(ap10, 2), "p90_us": round(ap90, 2),
+              "positions_per_s_p10_p90": [round(positions / ap90 * 1e6, 1), round(positions / ap10 * 1e6, 1)],
+              "GB/s": round(acc_gbs, 1), "frac": round(acc_gbs / PEAK_GBS, 4),
               "algorithmic_bytes": acc_bytes,
               "mean_accepted": float(acc["acc"].float().mean().item())}
 
     # Roofline of qmv_kernel: algorithmic bytes per launch over the average
-    # launch duration, i.e. the qmv part of a step (16 launches back to back,
-    # no events between them) divided by 16.  The per-launch events of the
-    # variants add about 2 us of marker time to each launch, so they only
-    # split the time by shape.
+    # launch duration, i.e. the median qmv part of a step (16 launches back
+    # to back, no events between them) divided by 16.
     bytes_per_launch = qmv_bytes_step / len(launches)
-    launch_us = qspan_ms / len(launches) * 1e3
-    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
+    launch_us = qmed / len(launches)
+    achieved = bytes_per_launch / launch_us / 1e3
     traffic, tinfo = measured_traffic(bytes_per_launch)
     roof = {"kernel": ("qmv_kernel (W4; 16 launches per step: gate/up with the gated activation, "
                        "and down, at M=1..8)"),
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-            "frac": round(achieved / 8000.0, 4),
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
             "algorithmic_bytes_per_launch": round(bytes_per_launch),
             "avg_launch_us": round(launch_us, 2),
@@ -786,12 +879,74 @@ def main():
                                 "M=1..8 on distinct weight copies + batched acceptance B=256 D=5 "
                                 "V=151936 T=0.6"),
                    "qmv_bytes_per_step": qmv_bytes_step, "accept_bytes_per_step": acc_bytes},
-        "qmv_frac_of_peak": round(qmv_gbs / 8000.0, 4),
-        "qmv_us_per_step": round(qspan_ms * 1e3, 2), "accept": accept, "roofline": roof,
+        "qmv_frac_of_peak": round(qmv_gbs / PEAK_GBS, 4),
+        "qmv_us_per_step": round(qmed, 2), "qmv_us_p10": round(qp10, 2), "qmv_us_p90": round(qp90, 2),
+        "value_p10_p90": [round(qmv_bytes_step / qp90 / 1e3, 1), round(qmv_bytes_step / qp10 / 1e3, 1)],
+        "accept": accept, "roofline": roof,
     }
     if not full:
         print(json.dumps(out), flush=True)
         return
+
+    steps = args.steps
+
+    def span_us(calls):
+        """Median (p10, p90) microseconds of `steps` passes over `calls`."""
+        for c, _, _ in calls:
+            c()
+        accept_call()          # untimed: the queue is busy at the first event
+        evs = [pair() for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            for c, _, _ in calls:
+                c()
+            e1.record(stream)
+            accept_call()
+        torch.cuda.synchronize()
+        return spread_us([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+
+    variants = {}
+    for kind, label in (("chain", "chained MLP: gate/up with the gated activation, then down on its h (value)"),
+                        ("as_stored", ("weights read as stored (spec_qmv_w4, interchange layout): gate/up as "
+                                       "one fp32 launch, then down")),
+                        ("plain", "packed: gate/up as one launch with fp32 outputs, no activation; down"),
+                        ("separate", "packed: separate gate, up and down launches (24)")):
+        calls = launches if kind == "chain" else mlp_launches(kind)
+        t = span_us(calls)
+        nb = sum(l[2] for l in calls)
+        variants[label] = {"qmv_us_per_step": t["us"], "p10_us": t["p10_us"], "p90_us": t["p90_us"],
+                           **rate(nb, t["us"])}
+    out["variants"] = variants
+
+    # Per M and per shape: events around every launch (about 2 us of marker
+    # time each, so these only split the step).
+    evs = [[pair() for _ in launches] for _ in range(steps)]
+    accept_call()
+    for each in evs:
+        for i, (call, _, _) in enumerate(launches):
+            each[i][0].record(stream)
+            call()
+            each[i][1].record(stream)
+        accept_call()
+    torch.cuda.synchronize()
+    l_us = [pct([e[i][0].elapsed_time(e[i][1]) * 1e3 for e in evs])[0] for i in range(len(launches))]
+    per_m = {}
+    for j, b in enumerate(blocks):
+        us = l_us[2 * j] + l_us[2 * j + 1]
+        nb = launches[2 * j][2] + launches[2 * j + 1][2]
+        per_m[str(b["M"])] = {"us": round(us, 2), **rate(nb, us)}
+    per_shape = {}
+    for name in ("gate_up_silu", "down"):
+        idx = [i for i, l in enumerate(launches) if l[1] == name]
+        us = sum(l_us[i] for i in idx) / len(idx)
+        nb = sum(launches[i][2] for i in idx) / len(idx)
+        per_shape[name] = {"us_per_launch": round(us, 2), **rate(nb, us)}
+    out["per_M (per-launch events, median)"] = per_m
+    out["roofline_parts"] = {
+        "qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / PEAK_GBS, 4),
+                       "per_shape (per-launch events)": per_shape},
+        "accept (row statistics pass + fused decide/sum/draw)": {
+            "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / PEAK_GBS, 4), "us_per_call": round(amed, 2)}}
 
     # Greedy verification of the same block (target logits only), drafts
     # from the greedy draft (argmax of each draft row).
@@ -799,81 +954,20 @@ def main():
     g_out = (torch.empty(ACC_B, dtype=torch.int32, device=dev),
              torch.empty(ACC_B, dtype=torch.int32, device=dev))
     greedy_call = spec.bind_verify_greedy(acc["t"], g_toks, out=g_out)
-    for _ in range(args.warmup):
-        greedy_call()
-    g_ev = [pair() for _ in range(args.steps)]
-    for e in g_ev:
-        e[0].record(stream)
-        greedy_call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    g_ms = sum(e[0].elapsed_time(e[1]) for e in g_ev) / args.steps
+    g = spread_us(timed_each([greedy_call], steps, stream))
     g_bytes = roofline.greedy_bytes(ACC_B, ACC_D, ACC_V)
-
-    def eager(calls, per_launch):
-        """K eager steps of `calls`: the span of each step and, if asked, the
-        duration of every launch (events around it)."""
-        evs = [(pair(), [pair() for _ in calls]) for _ in range(args.steps)]
-        accept_call()          # untimed: the queue is busy at the first event
-        for span, each in evs:
-            span[0].record(stream)
-            for i, (call, _, _) in enumerate(calls):
-                if per_launch:
-                    each[i][0].record(stream)
-                call()
-                if per_launch:
-                    each[i][1].record(stream)
-            span[1].record(stream)
-            accept_call()
-        torch.cuda.synchronize()
-        span_ms = sum(s[0].elapsed_time(s[1]) for s, _ in evs) / args.steps
-        each_ms = ([sum(e[i][0].elapsed_time(e[i][1]) for _, e in evs) / args.steps
-                    for i in range(len(calls))] if per_launch else None)
-        return span_ms, each_ms
-
-    plain = plain_fused_launches()
-    unfused = unfused_launches()
-    plain_ms, _ = eager(plain, False)
-    unfused_ms, _ = eager(unfused, False)
-    _, q_ms = eager(launches, True)
-    per_m = {}
-    for j, b in enumerate(blocks):
-        ms = sum(q_ms[2 * j:2 * j + 2])
-        nb = sum(l[2] for l in launches[2 * j:2 * j + 2])
-        per_m[str(b["M"])] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                              "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
-    per_shape = {}
-    for name in ("gate_up_silu", "down"):
-        idx = [i for i, l in enumerate(launches) if l[1] == name]
-        ms = sum(q_ms[i] for i in idx) / len(idx)
-        nb = sum(launches[i][2] for i in idx) / len(idx)
-        per_shape[name] = {"us_per_launch": round(ms * 1e3, 2),
-                           "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                           "frac": round(nb / (ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
-    plain_bytes = sum(l[2] for l in plain)
-    unfused_bytes = sum(l[2] for l in unfused)
-    out["variants"] = {
-        "chained MLP: gate/up with the gated activation, then down on its h (value)": {
-            "qmv_us_per_step": round(qspan_ms * 1e3, 2), "GB/s": round(qmv_gbs, 1)},
-        "gate/up as one launch with fp32 outputs, no activation; down on a separate h": {
-            "qmv_us_per_step": round(plain_ms * 1e3, 2),
-            "GB/s": round(plain_bytes / (plain_ms * 1e-3) / 1e9, 1)},
-        "separate gate, up and down launches (24)": {
-            "qmv_us_per_step": round(unfused_ms * 1e3, 2),
-            "GB/s": round(unfused_bytes / (unfused_ms * 1e-3) / 1e9, 1)},
-    }
-    out["per_M (per-launch events)"] = per_m
     out["accept_greedy (same block, target logits only; not part of the step)"] = {
-        "positions_per_s": round(positions / (g_ms * 1e-3), 1), "us": round(g_ms * 1e3, 2),
-        "GB/s": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
-        "frac": round(g_bytes / (g_ms * 1e-3) / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        "positions_per_s": round(positions / g["us"] * 1e6, 1), **g, **rate(g_bytes, g["us"]),
         "algorithmic_bytes": g_bytes, "mean_accepted": float(g_out[0].float().mean().item())}
-    out["roofline_parts"] = {
-        "qmv_kernel": {"achieved": round(achieved, 1), "frac": round(achieved / 8000.0, 4),
-                       "per_shape (per-launch events)": per_shape},
-        "accept (row statistics pass + fused decide/sum/draw)": {
-            "achieved": round(acc_gbs, 1), "frac": round(acc_gbs / 8000.0, 4),
-            "us_per_call": round(acc_ms * 1e3, 2)}}
+    del blocks, launches
+    torch.cuda.empty_cache()
+
+    # The other workloads of the verify hot path.
+    out["configs"] = {"pr1_reference": pr1_reference(dev, steps),
+                      "lm_head_accept": lmhead_accept(dev, steps),
+                      "w8_lm_head": w8_lm_head(dev, steps),
+                      "verify_pass_64_layers": verify_pass(dev, min(steps, 20))}
+
     # The attainable read rate beside the published peak: a plain streaming
     # read of 2 GiB (spec_stream_read), and each part's share of it.
     sr = stream_read_rate(dev)

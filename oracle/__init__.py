@@ -19,18 +19,27 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# Address- and undefined-behaviour-sanitized build, loaded instead when
+# SPEC_ORACLE_SANITIZE=1 (the process must preload gcc's libasan).
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+_SANITIZE = os.environ.get("SPEC_ORACLE_SANITIZE") == "1"
 
 _c_long_p = ctypes.POINTER(ctypes.c_long)
 
 
-def build() -> str:
-    """Compile oracle.c with gcc into liboracle.so (always recompiles)."""
-    tmp = _LIB + ".tmp"
+def build(sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (always recompiles); with
+    sanitize, into liboracle_san.so with AddressSanitizer and
+    UndefinedBehaviorSanitizer (any report aborts)."""
+    out = _LIB_SAN if sanitize else _LIB
+    tmp = out + ".tmp"
+    extra = (["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fno-omit-frame-pointer", "-g"] if sanitize else [])
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-Wall", *extra, "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -39,9 +48,10 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        path = _LIB_SAN if _SANITIZE else _LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(sanitize=_SANITIZE)
+        L = ctypes.CDLL(path)
         vp, lg, i, f = ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_float
         L.oracle_qmv.argtypes = [i, vp, vp, vp, vp, lg, lg, lg, lg, lg, lg, vp, vp]
         L.oracle_qmv.restype = i

@@ -39,7 +39,9 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspec.so")
+# SPEC_LIB_PATH selects another build of the same library (the host-side
+# sanitizer build of the CPU test run); the default is the in-tree build.
+LIB_PATH = os.environ.get("SPEC_LIB_PATH") or os.path.join(_HERE, "libspec.so")
 
 STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID", 2: "SPEC_ERR_UNSUPPORTED",
           3: "SPEC_ERR_WORKSPACE", 4: "SPEC_ERR_DEVICE"}
@@ -155,24 +157,38 @@ def _require(t, dtype, name, device=None):
     return t
 
 
-# ---- workspaces: device buffers cached per (device, purpose) ----
+# ---- workspaces: device buffers cached per (device, stream, purpose) ----
 _ws_cache: dict = {}
 
 
-def get_workspace(nbytes: int, device, key: str = "default"):
-    """A 256-byte aligned device buffer of at least nbytes.
+def _cached_buffer(cache: dict, slot, nbytes: int, alloc):
+    """The cached buffer of `slot`, replaced by alloc(n) when missing or
+    smaller than nbytes (n = max(nbytes, 4096))."""
+    buf = cache.get(slot)
+    if buf is None or buf.numel() < nbytes:
+        buf = alloc(max(nbytes, 4096))
+        cache[slot] = buf
+    return buf
+
+
+def get_workspace(nbytes: int, device, key: str = "default", stream=None):
+    """A 256-byte aligned device buffer of at least nbytes for calls issued
+    on `stream` (torch's current stream of `device` when None).
 
     Workspaces need no initialization and hold nothing between calls, so one
-    buffer serves every later call ordered on the same stream."""
+    buffer serves every later call ordered on the same stream.  Buffers are
+    cached per stream: calls on two streams never share one, and a buffer
+    that grows is replaced only for its own stream, where the torch
+    allocator orders its reuse after that stream's earlier work."""
     import torch
     if nbytes == 0:
         return None
-    slot = (str(device), key)
-    buf = _ws_cache.get(slot)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
-        assert buf.data_ptr() % 256 == 0
-        _ws_cache[slot] = buf
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    slot = (str(device), int(stream.cuda_stream), key)
+    buf = _cached_buffer(_ws_cache, slot, nbytes,
+                         lambda n: torch.empty(n, dtype=torch.uint8, device=device))
+    assert buf.data_ptr() % 256 == 0
     return buf
 
 

@@ -116,8 +116,18 @@ def draw_tie(w, u, x_gpu, x_ref):
 def compare_accept(gpu, ref, t, d, toks, u, T, k=0, p=1.0):
     """Compares a GPU verification with the oracle's.
 
-    Returns dict(exact, ties, bad=[...], prob_err) where prob_err is the worst
-    |p_draft / q_draft difference| over sequences without top-p ties."""
+    Bit-exact apart from counted ties, and a tie excuses only a mismatch
+    that depends on it:
+      - accepted_len differs at position i = min(L_gpu, L_oracle): a ratio
+        tie at i, or a top-p tie on target row i or draft row i (the rows
+        P_i(d_i) and Q_i(d_i) come from);
+      - same accepted_len, different token: a draw tie, or a top-p tie on
+        the rows of the draw (target row L, and draft row L below D).
+    A validity mismatch (one side -1, the other not) is always a failure.
+    p_draft / q_draft are checked at every position whose two rows have no
+    top-p tie.
+
+    Returns dict(exact, ties, bad=[...], prob_err)."""
     acc_g, nxt_g = gpu["accepted_len"], gpu["next_token"]
     acc_o, nxt_o = ref["accepted_len"], ref["next_token"]
     B = acc_o.shape[0]
@@ -125,34 +135,35 @@ def compare_accept(gpu, ref, t, d, toks, u, T, k=0, p=1.0):
     exact, ties, bad = 0, 0, []
     prob_err = 0.0
     for b in range(B):
-        tp_tie = False
-        if p < 1.0:
-            rows = [t[b, i] for i in range(D + 1)] + [d[b, i] for i in range(D)]
-            tp_tie = any(top_p_tie(z, T, k, p) for z in rows)
-        if D > 0 and acc_o[b] >= 0 and not tp_tie and "p_draft" in gpu:
-            e = max(np.abs(gpu["p_draft"][b] - ref["p_draft"][b]).max(),
-                    np.abs(gpu["q_draft"][b] - ref["q_draft"][b]).max())
-            prob_err = max(prob_err, float(e))
+        tt = [p < 1.0 and top_p_tie(t[b, i], T, k, p) for i in range(D + 1)]
+        dt = [p < 1.0 and top_p_tie(d[b, i], T, k, p) for i in range(D)]
+        if (acc_o[b] < 0) != (acc_g[b] < 0):
+            bad.append((b, "validity", int(acc_g[b]), int(acc_o[b])))
+            continue
+        if D > 0 and acc_o[b] >= 0 and "p_draft" in gpu:
+            for i in range(D):
+                if tt[i] or dt[i]:
+                    continue
+                e = max(abs(float(gpu["p_draft"][b, i]) - float(ref["p_draft"][b, i])),
+                        abs(float(gpu["q_draft"][b, i]) - float(ref["q_draft"][b, i])))
+                prob_err = max(prob_err, e)
         if acc_g[b] == acc_o[b] and nxt_g[b] == nxt_o[b]:
             exact += 1
-            continue
-        if tp_tie:
-            ties += 1
-            continue
-        if acc_o[b] < 0 or acc_g[b] < 0:
-            bad.append((b, "validity", int(acc_g[b]), int(acc_o[b])))
             continue
         if acc_g[b] != acc_o[b]:
             i = int(min(acc_g[b], acc_o[b]))
             pf = np.float32(ref["p_draft"][b, i])
             qf = np.float32(ref["q_draft"][b, i])
             a = np.float32(0) if pf == 0 else np.float32(pf / qf)
-            if abs(float(u[b, i]) - float(a)) < TIE:
+            if abs(float(u[b, i]) - float(a)) < TIE or tt[i] or dt[i]:
                 ties += 1
             else:
                 bad.append((b, "decision", i, int(acc_g[b]), int(acc_o[b]), float(u[b, i]), float(a)))
             continue
         L = int(acc_o[b])
+        if tt[L] or (L < D and dt[L]):
+            ties += 1
+            continue
         P = oracle.probs(t[b, L], T, k, p)
         if L < D:
             Q = oracle.probs(d[b, L], T, k, p)

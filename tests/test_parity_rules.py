@@ -1,0 +1,67 @@
+"""The GPU-vs-oracle comparison rules themselves (host only): planted
+mismatches in a copy of an oracle result must be classified correctly --
+a validity mismatch is always a failure, a tie excuses only the mismatch
+that depends on it."""
+import numpy as np
+
+import oracle
+from speculative_decoding_spec_amd import synth
+from tests import parity
+
+
+def case(B=6, D=3, V=16, seed=3):
+    t, d = synth.logits_pair(seed, B, D, V)
+    u = synth.uniforms(seed, synth.U_ACCEPT, (B, D + 1))
+    toks = oracle.sample_rows(d.reshape(B * D, V), 0.8, 0, 1.0,
+                              synth.uniforms(seed, synth.U_DRAFT, B * D)).reshape(B, D)
+    ref = oracle.accept(t, d, toks, u, 0.8)
+    return t, d, toks, u, ref
+
+
+def copy(ref):
+    return {k: np.array(v, copy=True) for k, v in ref.items()}
+
+
+def test_identical_result_is_exact():
+    t, d, toks, u, ref = case()
+    res = parity.compare_accept(copy(ref), ref, t, d, toks, u, 0.8)
+    assert res["exact"] == t.shape[0] and res["ties"] == 0 and not res["bad"]
+    assert res["prob_err"] == 0.0
+
+
+def test_validity_mismatch_is_a_failure():
+    t, d, toks, u, ref = case()
+    g = copy(ref)
+    g["accepted_len"][1] = -1
+    g["next_token"][1] = -1
+    res = parity.compare_accept(g, ref, t, d, toks, u, 0.8)
+    assert [x[1] for x in res["bad"]] == ["validity"]
+
+
+def test_far_decision_and_draw_mismatches_are_failures():
+    t, d, toks, u, ref = case(B=32)
+    D = t.shape[1] - 1
+    # a sequence that rejected at L with the uniform far from the ratio there
+    cands = []
+    for b in range(t.shape[0]):
+        L = int(ref["accepted_len"][b])
+        if 0 <= L < D:
+            pf, qf = np.float32(ref["p_draft"][b, L]), np.float32(ref["q_draft"][b, L])
+            a = np.float32(0) if pf == 0 else np.float32(pf / qf)
+            if abs(float(u[b, L]) - float(a)) > 1e-2:
+                cands.append(b)
+    assert len(cands) >= 2
+    g = copy(ref)
+    g["accepted_len"][cands[0]] += 1
+    g["next_token"][cands[1]] = (ref["next_token"][cands[1]] + 7) % t.shape[2]
+    res = parity.compare_accept(g, ref, t, d, toks, u, 0.8)
+    assert res["ties"] == 0
+    assert sorted(x[1] for x in res["bad"]) == ["decision", "draw"]
+
+
+def test_probability_error_is_reported():
+    t, d, toks, u, ref = case()
+    g = copy(ref)
+    g["p_draft"][3, 1] += 1e-3
+    res = parity.compare_accept(g, ref, t, d, toks, u, 0.8)
+    assert abs(res["prob_err"] - 1e-3) < 1e-6
