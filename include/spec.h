@@ -20,9 +20,11 @@
  *    never allocates, frees or retains them.  Layouts are row-major and
  *    contiguous.
  *  - Calls are asynchronous and stream ordered on `stream` (NULL = the
- *    default stream).  The library keeps no mutable global state; calls on
- *    different streams may run concurrently as long as they do not share a
- *    workspace.
+ *    default stream).  The library keeps no mutable global state beyond the
+ *    per-GPU address of the fixed workspace of spec_verify_accept_noalloc;
+ *    calls on different streams may run concurrently as long as they do not
+ *    share a workspace (which all spec_verify_accept_noalloc calls on one GPU
+ *    do).
  *  - Arguments are validated on the host first.  On failure the call returns
  *    SPEC_ERR_INVALID / SPEC_ERR_UNSUPPORTED / SPEC_ERR_WORKSPACE and
  *    enqueues nothing.  SPEC_ERR_DEVICE means a HIP call failed.
@@ -263,6 +265,34 @@ spec_status spec_verify_accept(const float *target_logits,
                                int32_t *accepted_len, int32_t *next_token,
                                float *p_draft, float *q_draft, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify_accept_noalloc: the same call for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument, and no allocation.  Its
+ * workspace is a fixed array of SPEC_NOALLOC_SCRATCH_BYTES in device memory
+ * that the library holds on each GPU it runs on until the process ends (its
+ * device address is looked up once per GPU, on the first call there).
+ *  - Arguments, results and errors as spec_verify_accept; a call whose
+ *    workspace (spec_verify_accept_workspace for its B, D, V, top_k is an
+ *    upper bound) would exceed SPEC_NOALLOC_SCRATCH_BYTES returns
+ *    SPEC_ERR_WORKSPACE and enqueues nothing.
+ *  - `stream` must belong to the current device (SPEC_ERR_INVALID
+ *    otherwise); NULL is the current device's default stream.
+ *  - Every call on one GPU uses the same array: calls that overlap on one
+ *    GPU (on different streams, or from several host threads) race and give
+ *    wrong results.  Calls ordered on one stream are safe; the array keeps
+ *    the last call's contents, which no call reads.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+spec_status spec_verify_accept_noalloc(const float *target_logits,
+                                       const float *draft_logits,
+                                       const int32_t *draft_tokens,
+                                       const float *uniforms, int B, int D, int V,
+                                       float temperature, int top_k, float top_p,
+                                       int32_t *accepted_len, int32_t *next_token,
+                                       float *p_draft, float *q_draft, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* Greedy verification: match the drafts against the target's argmax   */

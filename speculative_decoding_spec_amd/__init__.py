@@ -18,6 +18,8 @@ Names follow the C ABI:
     spec_pack_gate_up /              gate and up projections as one launch with
     spec_qmv_gate_up_silu            the SiLU-gated activation applied (bf16 out)
     spec_verify_accept               ratio acceptance + residual / bonus draw
+    spec_verify_accept_noalloc       the same with the library's fixed device
+                                     scratch instead of a workspace
     spec_sample_probs                filtered sampling distribution
     spec_sample_tokens               inverse-CDF draw from that distribution
     spec_verify_greedy               greedy verification (match the target argmax)
@@ -97,6 +99,9 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_accept.argtypes = [vp, vp, vp, vp, i, i, i, f, i, f, vp, vp,
                                          vp, vp, vp, sz, vp]
         L.spec_verify_accept.restype = i
+        L.spec_verify_accept_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, f, i, f, vp, vp,
+                                                 vp, vp, vp]
+        L.spec_verify_accept_noalloc.restype = i
         L.spec_sample_workspace_size.argtypes = [i, i, i]
         L.spec_sample_workspace_size.restype = sz
         L.spec_sample_probs.argtypes = [vp, i, i, f, i, f, vp, vp, sz, vp]
@@ -418,11 +423,13 @@ def spec_verify_accept_workspace(B: int, D: int, V: int, top_k: int) -> int:
 
 def spec_verify_accept(target_logits, draft_logits, draft_tokens, uniforms,
                        temperature: float, top_k: int = 0, top_p: float = 1.0,
-                       with_probs: bool = False, out=None, workspace=None):
+                       with_probs: bool = False, out=None, workspace=None, noalloc=False):
     """Acceptance for B sequences.  target_logits fp32 [B][D+1][V],
     draft_logits fp32 [B][D][V], draft_tokens int32 [B][D], uniforms fp32
     [B][D+1].  Returns (accepted_len, next_token) int32 [B], plus
-    (p_draft, q_draft) fp32 [B][D] when with_probs."""
+    (p_draft, q_draft) fp32 [B][D] when with_probs.  With noalloc (and `out`
+    given) the call goes to spec_verify_accept_noalloc: no workspace, nothing
+    allocated."""
     import torch
     dev = target_logits.device
     _require(target_logits, torch.float32, "target_logits", dev)
@@ -443,6 +450,14 @@ def spec_verify_accept(target_logits, draft_logits, draft_tokens, uniforms,
         qd = torch.empty((B, D), dtype=torch.float32, device=dev) if with_probs else None
     else:
         acc, nxt, pd, qd = out
+    if noalloc:
+        st = lib().spec_verify_accept_noalloc(
+            _ptr(target_logits), _ptr(draft_logits if D > 0 else None),
+            _ptr(draft_tokens if D > 0 else None), _ptr(uniforms), B, D, V,
+            float(temperature), int(top_k), float(top_p), _ptr(acc), _ptr(nxt),
+            _ptr(pd), _ptr(qd), _stream(dev))
+        _check("spec_verify_accept_noalloc", st)
+        return (acc, nxt, pd, qd) if with_probs else (acc, nxt)
     need = spec_verify_accept_workspace(B, D, V, top_k)
     if workspace is None:
         workspace = get_workspace(need, dev, "accept")

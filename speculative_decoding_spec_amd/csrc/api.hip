@@ -6,6 +6,7 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -103,6 +104,88 @@ spec_status check_sampling(int V, float temperature, int top_k, float top_p) {
 
 bool ws_ok(const void *ws, size_t have, size_t need) {
     return need == 0 || (ws && have >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0);
+}
+
+// Workspace of spec_verify_accept_noalloc: a fixed array in device memory,
+// one copy per GPU (each GPU that loads the library holds it until the
+// process ends), shared by every such call on that GPU.  Host code never
+// passes the name itself to a kernel or a copy: the per-device address from
+// hipGetSymbolAddress is used instead.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the stream's device, looked up once per
+// device (with that device current) and kept.
+spec_status scratch_ptr(hipStream_t stream, void **out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess)
+            return SPEC_ERR_DEVICE;
+        if (sdev != cur)
+            return SPEC_ERR_INVALID;     // the stream must belong to the current device
+    }
+    if (cur < 0 || cur >= kMaxDevices)
+        return SPEC_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[cur]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return SPEC_ERR_DEVICE;
+        g_scratch_ptr[cur] = p;
+    }
+    *out = g_scratch_ptr[cur];
+    return SPEC_OK;
+}
+
+// spec_verify_accept with a caller workspace, or (fixed_scratch) with the
+// library's scratch array.
+spec_status verify_accept_common(const float *target_logits, const float *draft_logits,
+                                 const int32_t *draft_tokens, const float *uniforms, int B,
+                                 int D, int V, float temperature, int top_k, float top_p,
+                                 int32_t *accepted_len, int32_t *next_token, float *p_draft,
+                                 float *q_draft, void *workspace, size_t workspace_bytes,
+                                 bool fixed_scratch, hipStream_t stream) {
+    if (B < 0 || D < 0)
+        return SPEC_ERR_INVALID;
+    if (D > kMaxD)
+        return SPEC_ERR_UNSUPPORTED;
+    const spec_status s = check_sampling(V, temperature, top_k, top_p);
+    if (s != SPEC_OK)
+        return s;
+    if (B == 0)
+        return SPEC_OK;
+    if (!target_logits || !uniforms || !accepted_len || !next_token)
+        return SPEC_ERR_INVALID;
+    if (D > 0 && (!draft_logits || !draft_tokens))
+        return SPEC_ERR_INVALID;
+    if (!aligned4(target_logits) || (D > 0 && !aligned4(draft_logits)))
+        return SPEC_ERR_INVALID;
+    if (((V & 3) == 0) && (!aligned16(target_logits) || (D > 0 && !aligned16(draft_logits))))
+        return SPEC_ERR_UNSUPPORTED;
+    if ((size_t)B * (2 * D + 1) > kMaxRows)
+        return SPEC_ERR_UNSUPPORTED;
+    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
+    const spec::AcceptPlan plan = spec::accept_plan(B, D, V, sp.k_eff, sp.candidates);
+    if (fixed_scratch) {
+        if (plan.ws_bytes > SPEC_NOALLOC_SCRATCH_BYTES)
+            return SPEC_ERR_WORKSPACE;
+        const spec_status ps = scratch_ptr(stream, &workspace);
+        if (ps != SPEC_OK)
+            return ps;
+    } else if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes)) {
+        return SPEC_ERR_WORKSPACE;
+    }
+    if (spec::launch_accept(target_logits, draft_logits, draft_tokens, uniforms,
+                            plan, sp, accepted_len, next_token, p_draft,
+                            q_draft, workspace, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
 }
 
 } // namespace
@@ -273,34 +356,21 @@ spec_status spec_verify_accept(const float *target_logits,
                                int32_t *accepted_len, int32_t *next_token,
                                float *p_draft, float *q_draft, void *workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-    if (B < 0 || D < 0)
-        return SPEC_ERR_INVALID;
-    if (D > kMaxD)
-        return SPEC_ERR_UNSUPPORTED;
-    const spec_status s = check_sampling(V, temperature, top_k, top_p);
-    if (s != SPEC_OK)
-        return s;
-    if (B == 0)
-        return SPEC_OK;
-    if (!target_logits || !uniforms || !accepted_len || !next_token)
-        return SPEC_ERR_INVALID;
-    if (D > 0 && (!draft_logits || !draft_tokens))
-        return SPEC_ERR_INVALID;
-    if (!aligned4(target_logits) || (D > 0 && !aligned4(draft_logits)))
-        return SPEC_ERR_INVALID;
-    if (((V & 3) == 0) && (!aligned16(target_logits) || (D > 0 && !aligned16(draft_logits))))
-        return SPEC_ERR_UNSUPPORTED;
-    if ((size_t)B * (2 * D + 1) > kMaxRows)
-        return SPEC_ERR_UNSUPPORTED;
-    const spec::SamplingParams sp = spec::sampling_params(temperature, top_k, top_p, V);
-    const spec::AcceptPlan plan = spec::accept_plan(B, D, V, sp.k_eff, sp.candidates);
-    if (!ws_ok(workspace, workspace_bytes, plan.ws_bytes))
-        return SPEC_ERR_WORKSPACE;
-    if (spec::launch_accept(target_logits, draft_logits, draft_tokens, uniforms,
-                            plan, sp, accepted_len, next_token, p_draft,
-                            q_draft, workspace, stream) != hipSuccess)
-        return SPEC_ERR_DEVICE;
-    return SPEC_OK;
+    return verify_accept_common(target_logits, draft_logits, draft_tokens, uniforms, B, D, V,
+                                temperature, top_k, top_p, accepted_len, next_token, p_draft,
+                                q_draft, workspace, workspace_bytes, false, stream);
+}
+
+spec_status spec_verify_accept_noalloc(const float *target_logits,
+                                       const float *draft_logits,
+                                       const int32_t *draft_tokens,
+                                       const float *uniforms, int B, int D, int V,
+                                       float temperature, int top_k, float top_p,
+                                       int32_t *accepted_len, int32_t *next_token,
+                                       float *p_draft, float *q_draft, hipStream_t stream) {
+    return verify_accept_common(target_logits, draft_logits, draft_tokens, uniforms, B, D, V,
+                                temperature, top_k, top_p, accepted_len, next_token, p_draft,
+                                q_draft, nullptr, 0, true, stream);
 }
 
 size_t spec_sample_workspace_size(int R, int V, int top_k) {

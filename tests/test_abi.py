@@ -259,3 +259,18 @@ def test_requantize_validation(L):
     assert f(MIS, 4, 128, 64, P, P, P, None) == UNSUPPORTED
     assert f(P, 4, 128, 64, P, ctypes.c_void_p(0x10001), P, None) == INVALID
     assert f(P, 0, 128, 64, P, P, P, None) == OK
+
+
+def test_noalloc_rejects_workspace_beyond_its_scratch(L):
+    """spec_verify_accept_noalloc refuses, before touching a device, a call
+    whose workspace exceeds its fixed scratch (8192 sequences of D = 5 over
+    151936 tokens need about 39 MB of block sums), and validates like
+    spec_verify_accept otherwise."""
+    f = L.spec_verify_accept_noalloc
+    args = lambda B, D, V, T=0.6, k=0, p=1.0: (P, P2, P, P, B, D, V, T, k, p, P, P2, None, None, None)
+    assert f(*args(8192, 5, 151936)) == WORKSPACE
+    assert f(*args(-1, 5, 1000)) == INVALID
+    assert f(*args(4, 16, 1000)) == UNSUPPORTED
+    assert f(*args(4, 5, 1)) == INVALID
+    assert f(*args(0, 5, 1000)) == OK
+    assert f(P, None, P, P, 4, 3, 1000, 0.6, 0, 1.0, P, P2, None, None, None) == INVALID
