@@ -84,36 +84,41 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 // the k order (k0, k4, k1, k5, k2, k6, k3, k7); the x operand is staged in
 // the same order (stage_w4_order).  The shifts are 64-bit, each serving two
 // words at once: the bits a 64-bit shift carries across the word boundary
-// land outside the mask.  Six VALU operations per 8 codes.
-__device__ __forceinline__ uint64_t shr64(uint64_t v, int s) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(s), "v"(v));
-    return r;
-}
-__device__ __forceinline__ uint64_t shl64(uint64_t v, int s) {
-    uint64_t r;
-    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(s), "v"(v));
-    return r;
-}
+// land outside the mask.  Six VALU operations per 8 codes.  The shift counts
+// arrive in scalar registers the compiler cannot see through (opaque_sgpr):
+// with constant counts it would prove the carried bits unused and split each
+// 64-bit shift back into two 32-bit ones.
+struct W4Shifts {
+    unsigned l3, r1, r5, r9;
+};
 
-// Two 32-bit words of codes (words 2 half and 2 half + 1 of the 16 bytes a
-// lane holds per tile and pair) -> the MFMA B operands of 32-k steps
-// 2 half and 2 half + 1.
-__device__ __forceinline__ void unpack_w4(u32x4 raw, int half, unsigned base, bf16x8 b[2]) {
+// The two 32-bit words 2 half and 2 half + 1 of the 16 bytes of codes a lane
+// holds per tile and pair -> the MFMA B operands of 32-k steps 2 half and
+// 2 half + 1.
+__device__ __forceinline__ void unpack_w4(u32x4 raw, int half, unsigned base, W4Shifts sh,
+                                          bf16x8 b[2]) {
     constexpr unsigned kMask = 0x00780078u;
     typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
     const uint64_t w = __builtin_bit_cast(u64x2, raw)[half];
-    const uint64_t l3 = shl64(w, 3), r1 = shr64(w, 1), r5 = shr64(w, 5), r9 = shr64(w, 9);
+    const uint64_t l3 = w << sh.l3, r1 = w >> sh.r1, r5 = w >> sh.r5, r9 = w >> sh.r9;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int sh = 32 * e;
+        const int hi = 32 * e;
         u32x4 o;
-        o.x = ((unsigned)(l3 >> sh) & kMask) | base;
-        o.y = ((unsigned)(r1 >> sh) & kMask) | base;
-        o.z = ((unsigned)(r5 >> sh) & kMask) | base;
-        o.w = ((unsigned)(r9 >> sh) & kMask) | base;
+        o.x = ((unsigned)(l3 >> hi) & kMask) | base;
+        o.y = ((unsigned)(r1 >> hi) & kMask) | base;
+        o.z = ((unsigned)(r5 >> hi) & kMask) | base;
+        o.w = ((unsigned)(r9 >> hi) & kMask) | base;
         b[e] = __builtin_bit_cast(bf16x8, o);
     }
+}
+
+// A wave-uniform constant in a scalar register, opaque to the optimizer
+// (set once, before the main loop; a scalar move, no vector-register write).
+__device__ __forceinline__ unsigned opaque_sgpr(unsigned c) {
+    unsigned v;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(v) : "i"(c));
+    return v;
 }
 
 // A value in a vector register the compiler cannot rematerialize: constants
@@ -272,11 +277,18 @@ struct QmvArgs {
 //
 // MR: C rows of a lane's 4-row block that can hold an x row (M itself when
 // M <= 4, else 4); the per-group affine epilogue skips the others.
-template <int BITS, bool RM, int WAVES, int T, int S, int XH, bool GLU = false, int MR = 4>
+//
+// SB2 (interchange only): the scales and biases of two pairs come in one
+// 8-byte load each (rows of a multiple of 4 groups, 8-byte aligned arrays);
+// otherwise two 2-byte loads per pair and group.
+template <int BITS, bool RM, int WAVES, int T, int S, int XH, bool GLU = false, int MR = 4,
+          bool SB2 = true>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
     static_assert(XH == 1 || XH == 2 || XH == 4, "x loads per lane and pair");
     static_assert(!GLU || (T % 2 == 0 && !RM), "a gated launch pairs packed gate and up tiles");
-    static_assert(RM || S % 2 == 0, "packed scale/bias blocks hand over between stage slots");
+    // packed, or SB2: a two-pair scale/bias block hands over between stage slots
+    constexpr bool HANDOFF = !RM || SB2;
+    static_assert(!HANDOFF || S % 2 == 0, "scale/bias blocks of two pairs need an even stage count");
     static_assert(MR >= 1 && MR <= 4 && (XH == 1 || MR == 4), "rows per lane block");
     constexpr bool WIDE = XH == 4;  // 9..16 rows: one MFMA per group
     constexpr int NG = WIDE ? 2 : 1;    // groups (accumulators) per lane
@@ -378,6 +390,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
         bf16x8, u32x4{vgpr_const(0x3F803F80u), vgpr_const(0x3F803F80u), vgpr_const(0x3F803F80u),
                       vgpr_const(0x3F803F80u)});
     const unsigned w4base = vgpr_const(0x41804180u);
+    const W4Shifts w4sh{opaque_sgpr(3), opaque_sgpr(1), opaque_sgpr(5), opaque_sgpr(9)};
     f32x4 acc[T][NG];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
@@ -420,13 +433,25 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
         for (int tt = 0; tt < T; ++tt) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                if (RM) {
+                if (RM && !SB2) {
                     const bool gg = in && 2 * pc + (WIDE ? g : h) < ng;
                     const unsigned sv = gg ? sboff[g] : kOutOfRange;
                     const uint32_t s16 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sres[tt], sv, pc * 4, 0);
                     const uint32_t b16 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bres[tt], sv, pc * 4, 0);
                     st.sb[tt][g] = s16 | (b16 << 16);
-                } else if (slot % 2 == 0) {
+                } else if (RM && slot % 2 == 0) {
+                    // groups 4q .. 4q + 3 of this lane's row: pair 2q holds
+                    // 4q + grp, pair 2q + 1 holds 4q + 2 + grp
+                    const int grp = WIDE ? g : h;
+                    const unsigned sv = in ? (unsigned)(r * ng) * 2u : kOutOfRange;
+                    const auto s4 = __builtin_amdgcn_raw_buffer_load_b64(sres[tt], sv, (pc >> 1) * 8, 0);
+                    const auto b4 = __builtin_amdgcn_raw_buffer_load_b64(bres[tt], sv, (pc >> 1) * 8, 0);
+                    const unsigned sh16 = 16u * (unsigned)(grp & 1);
+                    const unsigned se = (s4[grp >> 1] >> sh16) & 0xFFFFu, so = (s4[1 + (grp >> 1)] >> sh16) & 0xFFFFu;
+                    const unsigned be = (b4[grp >> 1] >> sh16) & 0xFFFFu, bo = (b4[1 + (grp >> 1)] >> sh16) & 0xFFFFu;
+                    st.sb[tt][g] = se | (be << 16);
+                    st.sb_odd[tt][g] = so | (bo << 16);
+                } else if (!RM && slot % 2 == 0) {
                     // one load gives this lane's words of both pairs of a block
                     const unsigned sv = in ? sboff[g] : kOutOfRange;
                     const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(sres[tt], sv, (pc >> 1) * 256, 0);
@@ -469,33 +494,42 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
                 c[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         const int rsw = swz(r);
-        bf16x8 bw4[T][2];
+        // Two 32-k steps at a time: both A fragments, then per tile the two B
+        // operands (unpacked right before their MFMAs, so only one tile's are
+        // live) -- the same MFMA order per accumulator as step by step.
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            if (BITS == 4 && s4 % 2 == 0) {
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 av[2][NG];
 #pragma unroll
-                for (int tt = 0; tt < T; ++tt)
-                    unpack_w4(st.raw[tt][0], s4 / 2, w4base, bw4[tt]);
-            }
-            bf16x8 av[NG];
+            for (int e = 0; e < 2; ++e) {
+                const int s4 = 2 * half + e;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const uint16_t *src = (!WIDE || a_act[g]) ? &sh.xs[wave][r][8 * ((4 * j + s4) ^ rsw)] : xzero;
-                av[g] = *reinterpret_cast<const bf16x8 *>(src);
-                cx[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], ones, cx[g], 0, 0, 0);
-            }
-#pragma unroll
-            for (int tt = 0; tt < T; ++tt) {
-                bf16x8 bv;
-                if (BITS == 4) {
-                    bv = bw4[tt][s4 % 2];
-                } else {
-                    const u32x4 &lo = st.raw[tt][s4 >> 1];
-                    bv = unpack_w8(lo[(s4 * 2) & 3], lo[(s4 * 2 + 1) & 3]);
+                for (int g = 0; g < NG; ++g) {
+                    const uint16_t *src =
+                        (!WIDE || a_act[g]) ? &sh.xs[wave][r][8 * ((4 * j + s4) ^ rsw)] : xzero;
+                    av[e][g] = *reinterpret_cast<const bf16x8 *>(src);
                 }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
-                    c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[g], bv, c[tt][g], 0, 0, 0);
+                    cx[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[e][g], ones, cx[g], 0, 0, 0);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt) {
+                bf16x8 bv[2];
+                if (BITS == 4) {
+                    unpack_w4(st.raw[tt][0], half, w4base, w4sh, bv);
+                } else {
+                    const u32x4 &lo = st.raw[tt][half];
+                    bv[0] = unpack_w8(lo[0], lo[1]);
+                    bv[1] = unpack_w8(lo[2], lo[3]);
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[e][g], bv[e], c[tt][g], 0, 0, 0);
             }
         }
         // Pair form: C row 4*j + i is x row m = 4*sub + i of half h.
@@ -506,7 +540,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 uint32_t sbw = st.sb[tt][g];
-                if (!RM) {
+                if (HANDOFF) {
                     if (slot % 2 == 0)
                         sb_next[tt][g] = st.sb_odd[tt][g];
                     else
@@ -664,21 +698,21 @@ hipError_t fill_zero(V *y, size_t count, hipStream_t stream) {
 }
 
 // Launches qmv_kernel for one (bits, layout) at the plan's shape; the x-row
-// variant (XH) follows M.
-template <int B, bool RM, int W, int TT, int SS, bool GLU>
+// variant (XH, MR) follows M.
+template <int B, bool RM, int W, int TT, int SS, bool GLU, bool SB2 = true>
 hipError_t launch_shape(const QmvArgs &a, int blocks, hipStream_t stream) {
     if (a.M == 1)
-        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 1><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 1, SB2><<<blocks, W * 64, 0, stream>>>(a);
     else if (a.M == 2)
-        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 2><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 2, SB2><<<blocks, W * 64, 0, stream>>>(a);
     else if (a.M == 3)
-        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 3><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 3, SB2><<<blocks, W * 64, 0, stream>>>(a);
     else if (a.M == 4)
-        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 4><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 1, GLU, 4, SB2><<<blocks, W * 64, 0, stream>>>(a);
     else if (a.M <= 8)
-        qmv_kernel<B, RM, W, TT, SS, 2, GLU><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 2, GLU, 4, SB2><<<blocks, W * 64, 0, stream>>>(a);
     else
-        qmv_kernel<B, RM, W, TT, SS, 4, GLU><<<blocks, W * 64, 0, stream>>>(a);
+        qmv_kernel<B, RM, W, TT, SS, 4, GLU, 4, SB2><<<blocks, W * 64, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -762,10 +796,15 @@ hipError_t launch_qmv(int bits, bool interchange, const void *w, const void *sb,
     const QmvPlan plan = qmv_plan(bits, N, K);
     const QmvArgs a{w, sb, biases, x, y, M, N, K, 0};
     const int blocks = (plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave;
+    // Interchange scales and biases load two pairs' worth (8 bytes) at a time
+    // when every row starts 8-byte aligned.
+    const bool sb2 = (K / 64) % 4 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(sb) | reinterpret_cast<uintptr_t>(biases)) & 7u) == 0;
 #define SPEC_QMV_LAUNCH(B, W, TT, SS)                                                    \
     if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.stages == SS) \
-        return interchange ? launch_shape<B, true, W, TT, SS, false>(a, blocks, stream)  \
-                           : launch_shape<B, false, W, TT, SS, false>(a, blocks, stream);
+        return !interchange ? launch_shape<B, false, W, TT, SS, false>(a, blocks, stream) \
+               : sb2        ? launch_shape<B, true, W, TT, SS, false, true>(a, blocks, stream) \
+                            : launch_shape<B, true, W, TT, SS, false, false>(a, blocks, stream);
 #define SPEC_QMV_SHAPES(B) \
     SPEC_QMV_LAUNCH(B, 4, 4, 2) SPEC_QMV_LAUNCH(B, 4, 2, 2) SPEC_QMV_LAUNCH(B, 8, 2, 2) \
     SPEC_QMV_LAUNCH(B, 8, 1, 2)

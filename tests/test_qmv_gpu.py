@@ -216,3 +216,28 @@ def test_fused_qkv_matches_separate_launches(dev, M):
 def test_long_k(dev, bits):
     """K = 131072 (1024 pairs per row, 64-128 per wave) on two ragged tiles."""
     full_check(bits, 8, 30, 131072, dev, cfg=10, salt=bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_interchange_scales_not_8_byte_aligned(dev, bits):
+    """Scales and biases on odd 2-byte offsets (rows of 80 groups, a multiple
+    of 4, so only the alignment rules out the 8-byte scale/bias loads): the
+    2-byte-load form, bitwise equal to the packed copy."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    N, K, M = 1000, 5120, 5
+    w, s, b = synth.qweights(11, bits, N, K, 64)
+    x = parity.dev_x(synth.activations(11, M, K), dev)
+    wt, st, bt = parity.dev_qweights(w, s, b, dev)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=torch.float16, device=dev)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 8 != 0
+        return v
+    fn = spec.spec_qmv_w4 if bits == 4 else spec.spec_qmv_w8
+    pack = spec.spec_pack_w4 if bits == 4 else spec.spec_pack_w8
+    yi = fn(wt, shifted(st), shifted(bt), x).cpu().numpy()
+    yp = (spec.spec_qmv_w4_packed if bits == 4 else spec.spec_qmv_w8_packed)(pack(wt, st, bt), x).cpu().numpy()
+    assert np.array_equal(yi.view(np.uint32), yp.view(np.uint32))
