@@ -340,7 +340,7 @@ def test_two_token_vocabulary(dev):
     check(t, d, toks, u, 0.8, 0, 1.0, dev)
 
 
-@pytest.mark.parametrize("B,D,V", [(200, 5, 151936), (130, 3, 1001)])
+@pytest.mark.parametrize("B,D,V", [(200, 5, 151936), (130, 3, 1001), (300, 2, 2048)])
 def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
     """From 128 sequences on, each sequence is decided, summed and drawn by
     one fused workgroup; below, by separate block-sum and draw launches.
