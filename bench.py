@@ -103,6 +103,8 @@ def parse():
                     help="only time the recurrent-state capture and commit and exit")
     ap.add_argument("--shapes", action="store_true",
                     help="only time qmv per layer shape and M (one JSON line each) and exit")
+    ap.add_argument("--valu", action="store_true",
+                    help="only time the chained MLP block at M=1..4 on the vector ALU against MFMA and exit")
     return ap.parse_args()
 
 
@@ -607,6 +609,39 @@ def measured_traffic(bytes_per_launch):
         return None, "no counter summary"
 
 
+def valu_compare(blocks, stream, steps):
+    """The chained MLP block at M = 1..4 with the products on the vector ALU
+    (spec_qmv_gate_up_silu_w4_valu, spec_qmv_w4_packed_valu) and on the
+    matrix cores: median (p10, p90) of each M's two launches back to back."""
+    import torch
+    import speculative_decoding_spec_amd as spec
+    from speculative_decoding_spec_amd import roofline
+    res = {}
+    for b in blocks:
+        M = b["M"]
+        if M > 4:
+            continue
+        nb = roofline.gate_up_silu_bytes(4, M, FFN, HIDDEN) + roofline.qmv_bytes(4, M, HIDDEN, FFN)
+        row = {}
+        for path, valu in (("mfma", False), ("valu", True)):
+            calls = [spec.bind_qmv_gate_up_silu(b["glu"], b["x"], b["h"], valu=valu),
+                     spec.bind_qmv(b["down"], b["h"], b["yd"], valu=valu)]
+            for c in calls:
+                c()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                for c in calls:
+                    c()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            t = spread_us([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            row[path] = {"us": t["us"], "p10_us": t["p10_us"], "p90_us": t["p90_us"], **rate(nb, t["us"])}
+        res[str(M)] = row
+    return res
+
+
 def build_accept(dev):
     import torch
     import speculative_decoding_spec_amd as spec
@@ -776,6 +811,10 @@ def main():
         return
     full = not args.step_only
     blocks = build_inputs(dev, variants=full)
+    if args.valu:
+        print(json.dumps({"mfma_vs_valu": valu_compare(blocks, torch.cuda.current_stream(dev),
+                                                       args.steps)}), flush=True)
+        return
     acc = build_accept(dev)
     stream = torch.cuda.current_stream(dev)
     acc_bytes = roofline.accept_bytes(ACC_B, ACC_D, ACC_V)
@@ -917,6 +956,8 @@ def main():
         variants[label] = {"qmv_us_per_step": t["us"], "p10_us": t["p10_us"], "p90_us": t["p90_us"],
                            **rate(nb, t["us"])}
     out["variants"] = variants
+
+    out["mfma_vs_valu (chained MLP block at M=1..4, us per block)"] = valu_compare(blocks, stream, steps)
 
     # Per M and per shape: events around every launch (about 2 us of marker
     # time each, so these only split the step).

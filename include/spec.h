@@ -194,6 +194,31 @@ spec_status spec_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb
                                   int G, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Vector-ALU comparison variants (W4, M = 1..4)                        */
+/* ------------------------------------------------------------------ */
+/*
+ * The small-M product of spec_qmv_w4_packed and of spec_qmv_gate_up_silu
+ * (bits 4) with the multiply-accumulate on the vector ALU
+ * (v_dot2c_f32_bf16, two bf16 products per instruction) instead of the
+ * matrix cores: the same packed weights, loads, x staging, affine fold and
+ * reduction order over waves, kept to measure the one against the other at
+ * the small M where most of each MFMA's A rows are zero (the MTPLX
+ * announcement, "Layer 0: MLX Runtime", fixes its stock small-M kernel with
+ * wider SIMD groups and unrolling, i.e. on the vector units).  Results obey
+ * the same parity bound as spec_qmv_*, but are not bitwise equal to them
+ * (the products are summed in another order).  Arguments, layouts and
+ * errors as for spec_qmv_w4_packed and spec_qmv_gate_up_silu, except:
+ *  M  0..4 (SPEC_ERR_UNSUPPORTED above)
+ */
+spec_status spec_qmv_w4_packed_valu(const void *w_packed, const void *sb_packed,
+                                    const uint16_t *x, float *y, int M, int N, int K,
+                                    int G, hipStream_t stream);
+
+spec_status spec_qmv_gate_up_silu_w4_valu(const void *w_packed, const void *sb_packed,
+                                          const uint16_t *x, uint16_t *h, int M, int F,
+                                          int K, int G, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Sampling distribution                                                */
 /* ------------------------------------------------------------------ */
 /*

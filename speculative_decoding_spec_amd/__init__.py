@@ -17,6 +17,9 @@ Names follow the C ABI:
     spec_requantize_w4               draft-only 4-bit copy of a bf16 matrix
     spec_pack_gate_up /              gate and up projections as one launch with
     spec_qmv_gate_up_silu            the SiLU-gated activation applied (bf16 out)
+    spec_qmv_w4_packed_valu /        the W4 products with the multiply-accumulate
+    spec_qmv_gate_up_silu_w4_valu    on the vector ALU instead of the matrix
+                                     cores (M <= 4; the comparison variant)
     spec_verify_accept               ratio acceptance + residual / bonus draw
     spec_verify_accept_noalloc       the same with the library's fixed device
                                      scratch instead of a workspace
@@ -90,7 +93,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
             fn.restype = i
-        for name in ("spec_qmv_w4_packed", "spec_qmv_w8_packed"):
+        for name in ("spec_qmv_w4_packed", "spec_qmv_w8_packed", "spec_qmv_w4_packed_valu"):
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
             fn.restype = i
@@ -115,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.spec_pack_gate_up.restype = i
         L.spec_qmv_gate_up_silu.argtypes = [i, vp, vp, vp, vp, i, i, i, i, vp]
         L.spec_qmv_gate_up_silu.restype = i
+        L.spec_qmv_gate_up_silu_w4_valu.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        L.spec_qmv_gate_up_silu_w4_valu.restype = i
         L.spec_gdn_record.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
         L.spec_gdn_record.restype = i
         L.spec_gdn_commit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -284,33 +289,52 @@ def spec_pack_gate_up(bits: int, gate, up, G: int = 64) -> PackedGateUp:
     return PackedGateUp(bits, F, K, G, wp, sbp)
 
 
-def spec_qmv_gate_up_silu(packed: PackedGateUp, x, h=None):
-    """h[M][F] bf16 = silu(x G^T) * (x U^T) for a pair packed by spec_pack_gate_up."""
+def _gate_up_args(packed: PackedGateUp, x, h, valu):
+    """(C function name, argument tuple) of one gated gate/up call, checked."""
     import torch
     dev = x.device
     _require(x, torch.bfloat16, "x", dev)
     M, K = x.shape
     if K != packed.K:
         raise ValueError(f"x has K={K}, weights have K={packed.K}")
-    if h is None:
-        h = torch.empty((M, packed.F), dtype=torch.bfloat16, device=dev)
     _require(h, torch.bfloat16, "h", dev)
     if tuple(h.shape) != (M, packed.F):
         raise ValueError(f"h must be [{M}][{packed.F}]")
-    st = lib().spec_qmv_gate_up_silu(packed.bits, _ptr(packed.w), _ptr(packed.sb), _ptr(x),
-                                     _ptr(h), M, packed.F, K, packed.G, _stream(dev))
-    _check("spec_qmv_gate_up_silu", st)
+    if valu:
+        if packed.bits != 4:
+            raise ValueError("the vector-ALU variant takes W4 weights")
+        return "spec_qmv_gate_up_silu_w4_valu", (_ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(h),
+                                                 M, packed.F, K, packed.G, _stream(dev))
+    return "spec_qmv_gate_up_silu", (packed.bits, _ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(h),
+                                     M, packed.F, K, packed.G, _stream(dev))
+
+
+def spec_qmv_gate_up_silu(packed: PackedGateUp, x, h=None):
+    """h[M][F] bf16 = silu(x G^T) * (x U^T) for a pair packed by spec_pack_gate_up."""
+    import torch
+    if h is None:
+        h = torch.empty((x.shape[0], packed.F), dtype=torch.bfloat16, device=x.device)
+    name, args = _gate_up_args(packed, x, h, False)
+    _check(name, getattr(lib(), name)(*args))
     return h
 
 
-def bind_qmv_gate_up_silu(packed: PackedGateUp, x, h) -> "_Bound":
-    """spec_qmv_gate_up_silu on fixed tensors, marshalled once (first call
-    checked)."""
-    spec_qmv_gate_up_silu(packed, x, h)
-    M, K = x.shape
-    args = (packed.bits, _ptr(packed.w), _ptr(packed.sb), _ptr(x), _ptr(h), M, packed.F, K,
-            packed.G, _stream(x.device))
-    return _Bound("spec_qmv_gate_up_silu", lib().spec_qmv_gate_up_silu, args, (packed, x, h))
+def spec_qmv_gate_up_silu_w4_valu(packed: PackedGateUp, x, h=None):
+    """spec_qmv_gate_up_silu (W4, M <= 4) with the products on the vector ALU."""
+    import torch
+    if h is None:
+        h = torch.empty((x.shape[0], packed.F), dtype=torch.bfloat16, device=x.device)
+    name, args = _gate_up_args(packed, x, h, True)
+    _check(name, getattr(lib(), name)(*args))
+    return h
+
+
+def bind_qmv_gate_up_silu(packed: PackedGateUp, x, h, valu: bool = False) -> "_Bound":
+    """spec_qmv_gate_up_silu (or, with valu, spec_qmv_gate_up_silu_w4_valu)
+    on fixed tensors, marshalled once (first call checked)."""
+    name, args = _gate_up_args(packed, x, h, valu)
+    _check(name, getattr(lib(), name)(*args))
+    return _Bound(name, getattr(lib(), name), args, (packed, x, h))
 
 
 class QWeights:
@@ -335,7 +359,7 @@ class QWeights:
         self.w, self.scales, self.biases = w, scales, biases
 
 
-def _qmv_args(weights, x, y):
+def _qmv_args(weights, x, y, valu=False):
     """(C function name, argument tuple) of one qmv call, checked."""
     import torch
     dev = x.device
@@ -346,8 +370,10 @@ def _qmv_args(weights, x, y):
     _require(y, torch.float32, "y", dev)
     if tuple(y.shape) != (M, weights.N):
         raise ValueError(f"y must be [{M}][{weights.N}]")
+    if valu and not (isinstance(weights, PackedWeights) and weights.bits == 4):
+        raise ValueError("the vector-ALU variant takes W4 packed weights")
     if isinstance(weights, PackedWeights):
-        name = f"spec_qmv_w{weights.bits}_packed"
+        name = f"spec_qmv_w{weights.bits}_packed" + ("_valu" if valu else "")
         args = (_ptr(weights.w), _ptr(weights.sb), _ptr(x), _ptr(y), M, weights.N, K, weights.G,
                 _stream(dev))
     elif isinstance(weights, QWeights):
@@ -386,6 +412,16 @@ def spec_qmv_w4_packed(packed: PackedWeights, x, y=None):
     return _qmv(packed, x, y)
 
 
+def spec_qmv_w4_packed_valu(packed: PackedWeights, x, y=None):
+    """spec_qmv_w4_packed (M <= 4) with the products on the vector ALU."""
+    import torch
+    if y is None:
+        y = torch.empty((x.shape[0], packed.N), dtype=torch.float32, device=x.device)
+    name, args = _qmv_args(packed, x, y, valu=True)
+    _check(name, getattr(lib(), name)(*args))
+    return y
+
+
 def spec_qmv_w8_packed(packed: PackedWeights, x, y=None):
     """spec_qmv_w8 from weights repacked by spec_pack_w8."""
     if packed.bits != 8:
@@ -408,11 +444,12 @@ class _Bound:
             raise SpecError(self.name, st)
 
 
-def bind_qmv(weights, x, y) -> _Bound:
+def bind_qmv(weights, x, y, valu: bool = False) -> _Bound:
     """A qmv on fixed tensors, marshalled once: weights are PackedWeights
-    (spec_qmv_w*_packed) or QWeights (spec_qmv_w*, interchange layout).  The
-    first call is checked like the unbound functions."""
-    name, args = _qmv_args(weights, x, y)
+    (spec_qmv_w*_packed, or with valu spec_qmv_w4_packed_valu) or QWeights
+    (spec_qmv_w*, interchange layout).  The first call is checked like the
+    unbound functions."""
+    name, args = _qmv_args(weights, x, y, valu)
     _check(name, getattr(lib(), name)(*args))
     return _Bound(name, getattr(lib(), name), args, (weights, x, y))
 

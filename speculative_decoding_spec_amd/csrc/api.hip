@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int kMaxM = 16;
+constexpr int kMaxValuM = 4;     // rows of the vector-ALU comparison variant
 constexpr int kMaxD = 15;
 constexpr int kMaxCand = 256;
 constexpr int kMaxV = (1 << 24) - 1;
@@ -253,6 +254,55 @@ spec_status spec_qmv_w8_packed(const void *w_packed, const void *sb_packed,
                                const uint16_t *x, float *y, int M, int N, int K, int G,
                                hipStream_t stream) {
     return qmv_common(8, false, w_packed, sb_packed, nullptr, x, y, M, N, K, G, stream);
+}
+
+spec_status spec_qmv_w4_packed_valu(const void *w_packed, const void *sb_packed,
+                                    const uint16_t *x, float *y, int M, int N, int K, int G,
+                                    hipStream_t stream) {
+    if (M < 0)
+        return SPEC_ERR_INVALID;
+    const spec_status s = qmv_shape_ok(N, K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (M > kMaxValuM)
+        return SPEC_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return SPEC_OK;
+    if (!y || (K > 0 && (!w_packed || !sb_packed || !x)))
+        return SPEC_ERR_INVALID;
+    if (K > 0 && (!aligned16(w_packed) || !aligned16(x) || !aligned4(sb_packed)))
+        return SPEC_ERR_UNSUPPORTED;
+    if (!aligned4(y))
+        return SPEC_ERR_INVALID;
+    if (spec::launch_qmv_valu(w_packed, sb_packed, x, y, M, N, K, 0, stream) != hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
+}
+
+spec_status spec_qmv_gate_up_silu_w4_valu(const void *w_packed, const void *sb_packed,
+                                          const uint16_t *x, uint16_t *h, int M, int F, int K,
+                                          int G, hipStream_t stream) {
+    if (M < 0 || F < 0)
+        return SPEC_ERR_INVALID;
+    if (F > (1 << 27))
+        return SPEC_ERR_UNSUPPORTED;
+    const spec_status s = qmv_shape_ok(spec::gate_up_rows(F), K, G);
+    if (s != SPEC_OK)
+        return s;
+    if (M > kMaxValuM)
+        return SPEC_ERR_UNSUPPORTED;
+    if (M == 0 || F == 0)
+        return SPEC_OK;
+    if (!h || (K > 0 && (!w_packed || !sb_packed || !x)))
+        return SPEC_ERR_INVALID;
+    if (K > 0 && (!aligned16(w_packed) || !aligned16(x) || !aligned4(sb_packed)))
+        return SPEC_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(h) & 1u)
+        return SPEC_ERR_INVALID;
+    if (spec::launch_qmv_valu(w_packed, sb_packed, x, h, M, spec::gate_up_rows(F), K, F, stream) !=
+        hipSuccess)
+        return SPEC_ERR_DEVICE;
+    return SPEC_OK;
 }
 
 spec_status spec_requantize_w4(const uint16_t *w_bf16, int N, int K, int G, uint32_t *w4,

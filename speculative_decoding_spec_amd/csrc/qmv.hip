@@ -281,10 +281,18 @@ struct QmvArgs {
 // SB2 (interchange only): the scales and biases of two pairs come in one
 // 8-byte load each (rows of a multiple of 4 groups, 8-byte aligned arrays);
 // otherwise two 2-byte loads per pair and group.
+//
+// VALU (W4, M <= 4): the same loads, staging and fold, with the products on
+// the vector ALU instead of the matrix cores -- the comparison variant.
+// Lane 16 j + r takes its 32 codes of row r (k slots 32 j ..) against the
+// same k of each x row m < MR, two products per v_dot2c_f32_bf16, and the
+// x sums over those k the same way; lanes j and j ^ 1 (the two halves of
+// one group) are added before the usual reduction.
 template <int BITS, bool RM, int WAVES, int T, int S, int XH, bool GLU = false, int MR = 4,
-          bool SB2 = true>
+          bool SB2 = true, bool VALU = false>
 __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
     static_assert(XH == 1 || XH == 2 || XH == 4, "x loads per lane and pair");
+    static_assert(!VALU || (BITS == 4 && XH == 1), "the vector-ALU variant serves W4 at M <= 4");
     static_assert(!GLU || (T % 2 == 0 && !RM), "a gated launch pairs packed gate and up tiles");
     // packed, or SB2: a two-pair scale/bias block hands over between stage slots
     constexpr bool HANDOFF = !RM || SB2;
@@ -494,6 +502,59 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
                 c[tt][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         const int rsw = swz(r);
+        if constexpr (VALU) {
+            // c[tt][0][m] and cx[0][m]: this lane's 32 k of x row m against
+            // the codes of tile tt, and against ones.  x row m of this
+            // lane's group h is A row m + 8 h; its 32 k are chunks 4 j ..
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                bf16x8 xv[2][MR];
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const int ar = m + 8 * h;
+                        xv[e][m] = *reinterpret_cast<const bf16x8 *>(
+                            &sh.xs[wave][ar][8 * ((4 * j + 2 * half + e) ^ swz(ar))]);
+                    }
+                // (Words go through named scalars: a bit_cast applied to a
+                // vector element directly read element 0 for every index.)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const u32x4 xw = __builtin_bit_cast(u32x4, xv[e][m]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const unsigned xq = xw[q];
+                            cx[0][m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq),
+                                                                      one2, cx[0][m], false);
+                        }
+                    }
+#pragma unroll
+                for (int tt = 0; tt < T; ++tt) {
+                    bf16x8 bv[2];
+                    unpack_w4(st.raw[tt][0], half, w4base, w4sh, bv);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const u32x4 bw = __builtin_bit_cast(u32x4, bv[e]);
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            const u32x4 xw = __builtin_bit_cast(u32x4, xv[e][m]);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const unsigned xq = xw[q], bq = bw[q];
+                                c[tt][0][m] = __builtin_amdgcn_fdot2_f32_bf16(
+                                    __builtin_bit_cast(bf16x2, xq), __builtin_bit_cast(bf16x2, bq),
+                                    c[tt][0][m], false);
+                            }
+                        }
+                    }
+                }
+            }
+        } else {
         // Two 32-k steps at a time: both A fragments, then per tile the two B
         // operands (unpacked right before their MFMAs, so only one tile's are
         // live) -- the same MFMA order per accumulator as step by step.
@@ -531,6 +592,7 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
                     for (int g = 0; g < NG; ++g)
                         c[tt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[e][g], bv[e], c[tt][g], 0, 0, 0);
             }
+        }
         }
         // Pair form: C row 4*j + i is x row m = 4*sub + i of half h.
         // Wide form: C row 4*j + i is x row 4*j + i, one accumulator per
@@ -578,6 +640,22 @@ __global__ __launch_bounds__(WAVES * 64) void qmv_kernel(QmvArgs a) {
     // Fixed-order reduction: the two groups of a pair (pair form: lanes l,
     // l ^ 32; wide form: the two accumulators of a lane), then the waves in
     // index order.  Neither depends on M.
+    if constexpr (VALU) {
+        // the two halves of a group (lanes l, l ^ 16) into the even one; the
+        // odd lanes stand for x rows 4..7, which a call of M <= 4 lacks
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // (the element goes through a named scalar: a bit_cast applied
+                // to a vector element directly read element 0 for every i)
+                const float ai = acc[tt][0][i];
+                o[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, ai), 0x401F));
+            }
+            acc[tt][0] = sub ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[tt][0] + o;
+        }
+    }
     __syncthreads();   // every wave is done with its x matrix
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
@@ -716,6 +794,20 @@ hipError_t launch_shape(const QmvArgs &a, int blocks, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The vector-ALU variant (W4, M = 1..4) at the plan's shape.
+template <int W, int TT, bool GLU>
+hipError_t launch_valu_shape(const QmvArgs &a, int blocks, hipStream_t stream) {
+    if (a.M == 1)
+        qmv_kernel<4, false, W, TT, 2, 1, GLU, 1, true, true><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M == 2)
+        qmv_kernel<4, false, W, TT, 2, 1, GLU, 2, true, true><<<blocks, W * 64, 0, stream>>>(a);
+    else if (a.M == 3)
+        qmv_kernel<4, false, W, TT, 2, 1, GLU, 3, true, true><<<blocks, W * 64, 0, stream>>>(a);
+    else
+        qmv_kernel<4, false, W, TT, 2, 1, GLU, 4, true, true><<<blocks, W * 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 } // namespace
 
 QmvPlan qmv_plan(int bits, int N, int K) {
@@ -838,6 +930,29 @@ hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *s
     SPEC_QMV_GLU_LAUNCH(4, 4, 4) SPEC_QMV_GLU_LAUNCH(4, 4, 2) SPEC_QMV_GLU_LAUNCH(4, 8, 2)
     SPEC_QMV_GLU_LAUNCH(8, 8, 2)
 #undef SPEC_QMV_GLU_LAUNCH
+    return hipErrorInvalidConfiguration;   // no kernel for this plan (unreachable)
+}
+
+hipError_t launch_qmv_valu(const void *w_packed, const void *sb_packed, const uint16_t *x,
+                           void *out, int M, int N, int K, int F, hipStream_t stream) {
+    const bool gated = F > 0;
+    if (M == 0 || N == 0)
+        return hipSuccess;
+    if (K == 0)
+        return gated ? fill_zero(static_cast<uint16_t *>(out), (size_t)M * F, stream)
+                     : fill_zero(static_cast<float *>(out), (size_t)M * N, stream);
+    const QmvPlan plan = qmv_plan(4, N, K);
+    const int T = gated ? std::max(plan.tiles_per_wave, 2) : plan.tiles_per_wave;
+    const QmvArgs a{w_packed, sb_packed, nullptr, x, out, M, N, K, gated ? F : 0};
+    const int blocks = (plan.n_tiles + T - 1) / T;
+#define SPEC_QMV_VALU_LAUNCH(W, TT)                                                     \
+    if (plan.waves == W && T == TT)                                                     \
+        return gated ? launch_valu_shape<W, TT, true>(a, blocks, stream)                \
+                     : launch_valu_shape<W, TT, false>(a, blocks, stream);
+    SPEC_QMV_VALU_LAUNCH(4, 4) SPEC_QMV_VALU_LAUNCH(4, 2) SPEC_QMV_VALU_LAUNCH(8, 2)
+#undef SPEC_QMV_VALU_LAUNCH
+    if (!gated && plan.waves == 8 && T == 1)
+        return launch_valu_shape<8, 1, false>(a, blocks, stream);
     return hipErrorInvalidConfiguration;   // no kernel for this plan (unreachable)
 }
 

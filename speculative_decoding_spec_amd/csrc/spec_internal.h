@@ -44,6 +44,11 @@ hipError_t launch_qmv(int bits, bool interchange, const void *w, const void *sb,
 hipError_t launch_qmv_gate_up_silu(int bits, const void *w_packed, const void *sb_packed,
                                    const uint16_t *x, uint16_t *h, int M, int F, int K,
                                    hipStream_t stream);
+// The vector-ALU comparison variant on packed W4 weights, M = 1..4: y fp32
+// [M][N] (F == 0), or the gated activation h bf16 [M][F] of a gate/up pair
+// packed as N = gate_up_rows(F) rows (F > 0).
+hipError_t launch_qmv_valu(const void *w_packed, const void *sb_packed, const uint16_t *x,
+                           void *out, int M, int N, int K, int F, hipStream_t stream);
 
 // ------------------------------------------------------------ sampling ----
 struct SamplingParams {

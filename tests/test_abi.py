@@ -48,7 +48,7 @@ def test_status_strings(L):
 
 
 def qmv(L, fn="spec_qmv_w4_packed", w=P, sb=P, x=P, y=P, M=4, N=64, K=128, G=64, b=P2):
-    if fn.endswith("_packed"):
+    if fn.endswith("_packed") or fn.endswith("_valu"):
         return getattr(L, fn)(w, sb, x, y, M, N, K, G, None)
     return getattr(L, fn)(w, sb, b, x, y, M, N, K, G, None)
 
@@ -80,6 +80,24 @@ def test_qmv_validation(L, fn):
         assert qmv(L, fn, b=None) == INVALID
         assert qmv(L, fn, b=ctypes.c_void_p(0x20001)) == INVALID    # fp16 biases, odd address
         assert qmv(L, fn, sb=ctypes.c_void_p(0x10001)) == INVALID   # fp16 scales, odd address
+
+
+def test_valu_variant_validation(L):
+    fn = "spec_qmv_w4_packed_valu"
+    assert qmv(L, fn, M=-1) == INVALID
+    assert qmv(L, fn, K=100) == INVALID
+    assert qmv(L, fn, G=32, K=128) == UNSUPPORTED
+    assert qmv(L, fn, M=5) == UNSUPPORTED           # the vector-ALU variant serves M <= 4
+    assert qmv(L, fn, M=0) == OK
+    assert qmv(L, fn, w=None) == INVALID
+    assert qmv(L, fn, x=MIS) == UNSUPPORTED
+    assert qmv(L, fn, K=1 << 24) == UNSUPPORTED
+    g = L.spec_qmv_gate_up_silu_w4_valu
+    assert g(P, P, P, P, 5, 64, 128, 64, None) == UNSUPPORTED
+    assert g(P, P, P, P, -1, 64, 128, 64, None) == INVALID
+    assert g(P, P, P, ctypes.c_void_p(0x20001), 2, 64, 128, 64, None) == INVALID   # bf16 h, odd
+    assert g(P, P, MIS, P, 2, 64, 128, 64, None) == UNSUPPORTED
+    assert g(P, P, P, P, 0, 64, 128, 64, None) == OK
 
 
 @pytest.mark.parametrize("fn", ["spec_pack_w4", "spec_pack_w8"])

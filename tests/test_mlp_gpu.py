@@ -43,12 +43,12 @@ def oracle_h_threaded(bits, gate, up, x, G=64):
             np.concatenate([p[1] for p in parts], axis=1))
 
 
-def gpu_h(bits, gate, up, x, dev, G=64):
+def gpu_h(bits, gate, up, x, dev, G=64, valu=False):
     import speculative_decoding_spec_amd as spec
     pk = spec.spec_pack_gate_up(bits, parity.dev_qweights(*gate, dev),
                                 parity.dev_qweights(*up, dev), G=G)
-    h = spec.spec_qmv_gate_up_silu(pk, parity.dev_x(x, dev))
-    return h
+    fn = spec.spec_qmv_gate_up_silu_w4_valu if valu else spec.spec_qmv_gate_up_silu
+    return fn(pk, parity.dev_x(x, dev))
 
 
 def bf16_midpoints(h):
@@ -64,12 +64,12 @@ def bf16_midpoints(h):
     return (lo + f(dn)) / 2, (lo + f(up)) / 2
 
 
-def check_h(bits, M, F, K, dev, cfg):
+def check_h(bits, M, F, K, dev, cfg, valu=False):
     import torch
     gate = synth.qweights(cfg, bits, F, K, 64, salt=1)
     up = synth.qweights(cfg, bits, F, K, 64, salt=2)
     x = synth.activations(cfg, M, K)
-    hg = gpu_h(bits, gate, up, x, dev)
+    hg = gpu_h(bits, gate, up, x, dev, valu=valu)
     got_bits = hg.view(torch.int16).cpu().numpy().view(np.uint16)
     got = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
     h, hb = oracle_h_threaded(bits, gate, up, x)
@@ -84,7 +84,7 @@ def check_h(bits, M, F, K, dev, cfg):
     tie = (np.abs(h - m_lo) <= tol_in) | (np.abs(h - m_hi) <= tol_in)
     far = int((np.abs(got - h) > tol).sum())
     wrong_bits = int(((got_bits != hb) & ~tie).sum())
-    print(f"W{bits} M={M} F={F} K={K}: outside_bound={far} wrong_bits={wrong_bits} "
+    print(f"W{bits}{' valu' if valu else ''} M={M} F={F} K={K}: outside_bound={far} wrong_bits={wrong_bits} "
           f"ties={int(tie.sum())} bits_differ={int((got_bits != hb).sum())} of {h.size}",
           flush=True)
     assert far == 0
