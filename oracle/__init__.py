@@ -65,8 +65,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_sample_rows.argtypes = [vp, lg, lg, f, i, f, vp, vp]
         L.oracle_sample_rows.restype = i
         L.oracle_accept.argtypes = [vp, vp, vp, vp, lg, lg, lg, f, i, f, vp, vp, vp,
-                                    vp, vp]
+                                    vp, vp, vp]
         L.oracle_accept.restype = i
+        L.oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.oracle_splitmix64.restype = ctypes.c_uint64
+        L.oracle_stream_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.oracle_stream_uniform.restype = ctypes.c_float
         L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         L.oracle_double_to_bf16.restype = ctypes.c_uint16
         L.oracle_gate_up_silu.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, lg, lg, lg, lg,
@@ -230,13 +234,24 @@ def accept(target_logits: np.ndarray, draft_logits: np.ndarray | None,
     pd = np.empty((B, max(D, 1)), np.float64)
     qd = np.empty((B, max(D, 1)), np.float64)
     row = np.empty(B, np.int32)
+    margin = np.empty(B, np.float64)
     rc = lib().oracle_accept(_ptr(tl), _ptr(dl), _ptr(dt), _ptr(u), B, D, V,
                              temperature, top_k, top_p, _ptr(acc), _ptr(nxt),
-                             _ptr(pd), _ptr(qd), _ptr(row))
+                             _ptr(pd), _ptr(qd), _ptr(row), _ptr(margin))
     if rc != 0:
         raise ValueError(f"oracle_accept failed (rc={rc})")
     return {"accepted_len": acc, "next_token": nxt, "p_draft": pd[:, :D],
-            "q_draft": qd[:, :D], "draw_row": row}
+            "q_draft": qd[:, :D], "draw_row": row, "draw_margin": margin}
+
+
+def splitmix64(seed: int, i: int) -> int:
+    """Output i of the SplitMix64 stream with the given seed."""
+    return int(lib().oracle_splitmix64(seed, i))
+
+
+def stream_uniform(seed: int, i: int) -> float:
+    """Output i of the stream as an exact fp32 uniform on [0, 1)."""
+    return float(lib().oracle_stream_uniform(seed, i))
 
 
 def verify_greedy(target_logits: np.ndarray, draft_tokens: np.ndarray | None) -> dict:

@@ -384,24 +384,60 @@ int oracle_probs(const float *z, long V, float T, int top_k, float top_p,
 
 /* Inverse CDF in vocabulary order: c_x = sum_{y <= x} w_y (fp64), and the
  * draw is the first x with c_x > u * c_{V-1}.  The strict comparison means a
- * zero-weight token is never drawn.  Returns -1 if the weights sum to zero. */
-static long inv_cdf(const double *wts, long V, float u)
+ * zero-weight token is never drawn.  Returns -1 if the weights sum to zero.
+ * margin (nullable) receives the distance of u * c_{V-1} to the nearer
+ * boundary of the drawn token's interval, relative to c_{V-1}: a draw whose
+ * margin is below a rounding tolerance may come out as a neighbour under
+ * another summation order. */
+static long inv_cdf_margin(const double *wts, long V, float u, double *margin)
 {
     double total = 0.0;
     for (long x = 0; x < V; ++x)
         total += wts[x];
+    if (margin)
+        *margin = INFINITY;
     if (!(total > 0.0))
         return -1;
     double target = (double)u * total, c = 0.0;
     long last_pos = -1;
     for (long x = 0; x < V; ++x) {
+        const double before = c;
         c += wts[x];
         if (wts[x] > 0.0)
             last_pos = x;
-        if (c > target)
+        if (c > target) {
+            if (margin)
+                *margin = fmin(c - target, target - before) / total;
             return x;
+        }
     }
+    if (margin)
+        *margin = 0.0;
     return last_pos; /* unreachable for u < 1; guards rounding at the end */
+}
+
+static long inv_cdf(const double *wts, long V, float u)
+{
+    return inv_cdf_margin(wts, V, u, NULL);
+}
+
+/* SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast splittable pseudorandom
+ * number generators", OOPSLA 2014), used as a counter-based generator:
+ * output i of the stream with seed s is the finalizer applied to
+ * s + (i + 1) * 0x9E3779B97F4A7C15 (mod 2^64). */
+uint64_t oracle_splitmix64(uint64_t seed, uint64_t i)
+{
+    uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Output i of the stream as a uniform on [0, 1): its top 24 bits times 2^-24,
+ * an exact fp32 value. */
+float oracle_stream_uniform(uint64_t seed, uint64_t i)
+{
+    return (float)(oracle_splitmix64(seed, i) >> 40) * 0x1p-24f;
 }
 
 /* One token drawn from the filtered distribution of a row with uniform u. */
@@ -441,25 +477,52 @@ int oracle_sample_rows(const float *z, long R, long V, float T, int top_k,
  *             P_i(d_i) = 0, +inf when only Q_i(d_i) = 0;
  *       accept d_i iff u_i < a_i (fp32 compare), i.e. with probability
  *             min(1, P_i(d_i) / Q_i(d_i));
- *       on the first rejection: r = max(0, P_i - Q_i) (fp64; r = P_i if it
- *             sums to zero), next = InvCDF(r, u_D), accepted = i, stop;
+ *       on the first rejection: next is drawn from r = max(0, P_i - Q_i)
+ *             (fp64; r = P_i if it sums to zero), accepted = i, stop;
  *   if all D are accepted: next = InvCDF(P_D, u_D), accepted = D (bonus).
  * The emitted tokens are d_0..d_{accepted-1} followed by next.
  *
+ * How next is drawn from r (a reading; the pages name the residual, not
+ * the way it is sampled):
+ *   - with top-k or top-p active (and for greedy sampling), r's support is
+ *     a few kept tokens: next = InvCDF(r, u_D);
+ *   - over the full vocabulary, by rejection from P_i, which never needs r
+ *     in full: candidate k = 0, 1, ... is j_k = InvCDF(P_i, v_k), kept iff
+ *     a_k < (P - Q) / P at j_k, with P, Q rounded to fp32 and the quotient
+ *     taken in fp32 (as the ratio test); the first kept candidate is next.
+ *     A candidate j is kept with probability max(0, 1 - Q(j)/P(j)), so next
+ *     has exactly the distribution r / sum(r).  v_k and a_k are outputs 2k
+ *     and 2k + 1 of the SplitMix64 stream seeded with u_D's bit pattern;
+ *     after kCandidates candidates none of which is kept, next =
+ *     InvCDF(r, output 2 * kCandidates).
+ *
  * Uniform layout (a reading): u[b][0..D-1] are the D tests, u[b][D] is the
- * single final draw.  Any row that is invalid, or a draft token outside
- * [0, V), makes the whole sequence invalid: accepted = next = -1.
+ * single final draw (or the seed of its stream).  Any row that is invalid,
+ * or a draft token outside [0, V), makes the whole sequence invalid:
+ * accepted = next = -1.
  *
  * p_draft / q_draft (nullable) receive P_i(d_i), Q_i(d_i) in fp64 for every
  * i (NaN for an invalid sequence).  draw_row (nullable) receives, per
  * sequence, the position whose distribution the final draw used (i for a
- * residual at i, D for the bonus, -1 if invalid). */
+ * residual at i, D for the bonus, -1 if invalid).  draw_margin (nullable)
+ * receives, per sequence, the smallest relative distance to a decision
+ * boundary met while drawing next: over every inverse-CDF draw made, the
+ * target's distance to its interval's boundaries over the total, and over
+ * every candidate test up to the kept one, |a_k - (P - Q)/P|.  A draw whose
+ * margin is below a rounding tolerance may come out differently under
+ * another (correct) summation order. */
+enum { kCandidates = 64 };
+
 int oracle_accept(const float *target_logits, const float *draft_logits,
                   const int32_t *draft_tokens, const float *uniforms, long B,
                   long D, long V, float T, int top_k, float top_p,
                   int32_t *accepted_len, int32_t *next_token, double *p_draft,
-                  double *q_draft, int32_t *draw_row)
+                  double *q_draft, int32_t *draw_row, double *draw_margin)
 {
+    /* filtered (candidate) mode, as the sampling settings define it */
+    const int greedy = !(T > 0.0f) || top_k == 1;
+    const int k_eff = greedy ? 1 : ((top_k >= 1 && top_k < V) ? top_k : (int)V);
+    const int filtered = k_eff < V || (!greedy && top_p < 1.0f);
     if (B < 0 || D < 0 || V < 1)
         return -1;
     double *P = (double *)malloc(sizeof(double) * (size_t)((D + 1) * V));
@@ -485,6 +548,8 @@ int oracle_accept(const float *target_logits, const float *draft_logits,
             accepted_len[b] = next_token[b] = -1;
             if (draw_row)
                 draw_row[b] = -1;
+            if (draw_margin)
+                draw_margin[b] = INFINITY;
             for (long i = 0; i < D; ++i) {
                 if (p_draft) p_draft[b * D + i] = NAN;
                 if (q_draft) q_draft[b * D + i] = NAN;
@@ -503,24 +568,49 @@ int oracle_accept(const float *target_logits, const float *draft_logits,
             if (!(u[i] < a))
                 break;
         }
-        long tok;
+        long tok = -1;
+        double margin = INFINITY, mk;
         if (i < D) {
+            const double *Pi = P + i * V, *Qi = Q + i * V;
             double tot = 0.0;
             for (long x = 0; x < V; ++x) {
-                double d = P[i * V + x] - Q[i * V + x];
+                double d = Pi[x] - Qi[x];
                 r[x] = d > 0.0 ? d : 0.0;
                 tot += r[x];
             }
             if (!(tot > 0.0))
-                memcpy(r, P + i * V, sizeof(double) * (size_t)V);
-            tok = inv_cdf(r, V, u[D]);
+                memcpy(r, Pi, sizeof(double) * (size_t)V);
+            if (filtered) {
+                tok = inv_cdf_margin(r, V, u[D], &margin);
+            } else {
+                uint32_t ubits;
+                memcpy(&ubits, &u[D], sizeof ubits);
+                const uint64_t seed = ubits;
+                for (long c = 0; c < kCandidates && tok < 0; ++c) {
+                    const float v = oracle_stream_uniform(seed, 2 * (uint64_t)c);
+                    const float a = oracle_stream_uniform(seed, 2 * (uint64_t)c + 1);
+                    const long j = inv_cdf_margin(Pi, V, v, &mk);
+                    margin = fmin(margin, mk);
+                    const float pf = (float)Pi[j], qf = (float)Qi[j];
+                    const float thr = (pf - qf) / pf;
+                    margin = fmin(margin, fabs((double)a - (double)thr));
+                    if (a < thr)
+                        tok = j;
+                }
+                if (tok < 0) {
+                    tok = inv_cdf_margin(r, V, oracle_stream_uniform(seed, 2 * (uint64_t)kCandidates), &mk);
+                    margin = fmin(margin, mk);
+                }
+            }
         } else {
-            tok = inv_cdf(P + D * V, V, u[D]);
+            tok = inv_cdf_margin(P + D * V, V, u[D], &margin);
         }
         accepted_len[b] = (int32_t)i;
         next_token[b] = (int32_t)tok;
         if (draw_row)
             draw_row[b] = (int32_t)i;
+        if (draw_margin)
+            draw_margin[b] = margin;
     }
     free(P); free(Q); free(r);
     return 0;

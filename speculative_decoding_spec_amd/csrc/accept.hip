@@ -932,6 +932,16 @@ __device__ DrawRows draw_rows(const Rows &rows, const Ws &ws, const SamplingPara
     return d;
 }
 
+// The target-row view of a draw: block sums over it are (p, p).
+__device__ __forceinline__ DrawRows target_only(const DrawRows &d) {
+    DrawRows t = d;
+    t.residual = false;
+    t.fd = RowFinal{0.0f, 1.0f, 0, 0};
+    t.zd = t.zt;
+    t.kd = t.kt;
+    return t;
+}
+
 // Weights of token x: (residual max(0, p - q) or p, and p), full vocabulary.
 // p and q are each rounded before the subtraction (contraction into a fused
 // multiply-add is off here): where the two distributions agree, p - q is then
@@ -957,8 +967,8 @@ __device__ void block_draw_sums(const DrawRows &d, const SamplingParams &sp, int
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if ((V & 3) == 0) {
         // kAhead blocks per wave in flight: their loads are all issued
-        // before the first is reduced.  (A bonus draw has no draft row: both
-        // pointers name the target row, and the second load hits the cache.)
+        // before the first is reduced.  (Without a residual only the target
+        // row is read.)
         constexpr int kAhead = 4;
         const float4 *zt4 = reinterpret_cast<const float4 *>(d.zt);
         const float4 *zd4 = reinterpret_cast<const float4 *>(d.zd);
@@ -969,7 +979,7 @@ __device__ void block_draw_sums(const DrawRows &d, const SamplingParams &sp, int
                 const int blk = min(blk0 + k * kW, blk_hi - 1);
                 const int e4 = min(blk * kBlock + 4 * lane, V - 4) >> 2;
                 t[k] = load_once(&zt4[e4]);
-                q[k] = load_once(&zd4[e4]);
+                q[k] = d.residual ? load_once(&zd4[e4]) : t[k];
             }
 #pragma unroll
             for (int k = 0; k < kAhead; ++k) {
@@ -1002,7 +1012,7 @@ __device__ void block_draw_sums(const DrawRows &d, const SamplingParams &sp, int
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             zt4[q] = d.zt[min(e + q, V - 1)];
-            zd4[q] = d.zd[min(e + q, V - 1)];
+            zd4[q] = d.residual ? d.zd[min(e + q, V - 1)] : zt4[q];
         }
         float wr = 0.0f, wp = 0.0f;
 #pragma unroll
@@ -1038,7 +1048,10 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const DrawRows d = draw_rows(rows, ws, sp, s_rf, b, L);
     const int blk_lo = c * blocks_per_chunk;
     const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
-    block_draw_sums<kWaves>(d, sp, V, blk_lo, blk_hi, ws.block_sums + (size_t)b * nblocks);
+    // the target row's block masses: the bonus draws from them, a residual
+    // draws candidates from them
+    block_draw_sums<kWaves>(target_only(d), sp, V, blk_lo, blk_hi,
+                            ws.block_sums + (size_t)b * nblocks);
 }
 
 template <int NW>
@@ -1046,6 +1059,10 @@ struct FinalSharedT {
     RowFinal rf[2 * kMaxDepth + 1];   // the sequence's row statistics
     float fsh[NW];
     int ish[NW];
+    // rejection draw: inclusive prefix of the target mass per block run,
+    // and each wave's candidate of a round
+    float run_incl[kThreads];
+    int cand[NW];
     int found;
     int L;
     float before, target;
@@ -1206,6 +1223,172 @@ __device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, cons
     }
 }
 
+// The residual draw over the full vocabulary, by rejection from the
+// target distribution P of the stop row (MTPLX announcement, "Layer 2":
+// the residual (p - q)+ replaces a rejected draft; the way it is sampled is
+// this library's reading): candidate k is the inverse-CDF draw from P with
+// uniform v_k, kept iff a_k < (P - Q) / P at it (P and Q in fp32, the
+// quotient in fp32).  A candidate j is kept with probability
+// max(0, 1 - Q(j)/P(j)), so the first kept one has exactly the residual's
+// distribution -- and needs P's block masses (one pass over the target row)
+// and one 256-token block per candidate, not the residual over both rows.
+// v_k and a_k are outputs 2k and 2k + 1 of the SplitMix64 stream (Steele,
+// Lea and Flood, "Fast splittable pseudorandom number generators", OOPSLA
+// 2014) seeded with the bit pattern of the sequence's final uniform; after
+// kCandidates candidates none of which is kept, the inverse CDF of the
+// residual with output 2 kCandidates decides.
+constexpr int kCandidates = 64;
+
+__device__ __forceinline__ float stream_uniform(uint64_t seed, uint64_t i) {
+    uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (float)(uint32_t)(z >> 40) * 0x1p-24f;
+}
+
+// Inclusive wave scan (lane order) of one float per lane.
+__device__ __forceinline__ float wave_incl_scan_f(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(v, o);
+        if (lane >= o)
+            v += t;
+    }
+    return v;
+}
+
+// One candidate, by one wave (every lane returns it): the first token x in
+// vocabulary order whose cumulative target mass exceeds `target`, from the
+// block masses bs[k].y (runs of `per` blocks per logical thread, their
+// inclusive prefixes in run_incl) and the block's own tokens.  Where rounding
+// leaves no crossing, the last position with positive mass is taken, as in
+// the single draw.
+__device__ int wave_candidate(const DrawRows &d, float scale, int V, const float2 *bs,
+                              const float *run_incl, int per, float target) {
+    const int lane = threadIdx.x & 63;
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    // the run holding the target
+    int t = -1;
+    for (int c = 0; c < kThreads && t < 0; c += 64) {
+        const unsigned long long m = __ballot(run_incl[c + lane] > target);
+        if (m)
+            t = c + __ffsll((long long)m) - 1;
+    }
+    if (t < 0) {   // past the end: the last run with positive mass
+        for (int c = kThreads - 64; c >= 0 && t < 0; c -= 64) {
+            const int tt = c + lane;
+            const float ex = tt > 0 ? run_incl[tt - 1] : 0.0f;
+            const unsigned long long m = __ballot(run_incl[tt] > ex);
+            if (m)
+                t = c + 63 - __clzll(m);
+        }
+        t = max(t, 0);
+    }
+    // the block within the run
+    const int lo = min(nblocks, t * per), hi = min(nblocks, lo + per);
+    float carry = t > 0 ? run_incl[t - 1] : 0.0f;
+    int blk = -1, last_blk = -1;
+    float before = carry, last_before = carry;
+    for (int c0 = lo; c0 < hi && blk < 0; c0 += 64) {
+        const int k = c0 + lane;
+        const float m = k < hi ? bs[k].y : 0.0f;
+        const float incl = wave_incl_scan_f(m) + carry;
+        const unsigned long long hit = __ballot(m > 0.0f && incl > target);
+        const unsigned long long pos = __ballot(m > 0.0f);
+        if (hit) {
+            const int f = __ffsll((long long)hit) - 1;
+            blk = c0 + f;
+            before = __shfl(incl - m, f);
+        } else if (pos) {
+            const int f = 63 - __clzll(pos);
+            last_blk = c0 + f;
+            last_before = __shfl(incl - m, f);
+        }
+        carry = __shfl(incl, 63);
+    }
+    if (blk < 0) {
+        blk = max(last_blk, lo);
+        before = last_blk >= 0 ? last_before : carry;
+    }
+    // the token within the block
+    const int e = blk * kBlock + 4 * lane;
+    float w4[4];
+    float lane_sum = 0.0f;
+    int last_local = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int x = e + q;
+        const float w = x < V ? weight(d.zt[x], d.ft.m, scale) * d.ft.inv : 0.0f;
+        w4[q] = w;
+        lane_sum += w;
+        if (w > 0.0f)
+            last_local = x;
+    }
+    const float incl_l = wave_incl_scan_f(lane_sum);
+    const float tgt = target - before;
+    int pick = -1;
+    {
+        float cum = incl_l - lane_sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            cum += w4[q];
+            if (pick < 0 && w4[q] > 0.0f && cum > tgt)
+                pick = e + q;
+        }
+    }
+    const unsigned long long hit = __ballot(pick >= 0);
+    if (hit)
+        return __shfl(pick, __ffsll((long long)hit) - 1);
+    const unsigned long long pos = __ballot(last_local >= 0);
+    return pos ? __shfl(last_local, 63 - __clzll(pos)) : blk * kBlock;
+}
+
+// The rejection draw of one sequence (d: a residual draw; bs: the block
+// masses of its target row, (p, p) per block).  Called by all threads;
+// returns the kept token to every thread, or -1 if no candidate was kept.
+template <int NW>
+__device__ int rejection_draw(const Rows &rows, const SamplingParams &sp, const float2 *bs,
+                              const DrawRows &d, uint64_t seed, FinalSharedT<NW> &sh) {
+#pragma clang fp contract(off)
+    const int V = rows.V;
+    const float scale = sp.scale;
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    // runs of blocks per logical thread (kThreads of them, as the single
+    // draw has), their target masses summed in order, then scanned
+    const int per = (nblocks + kThreads - 1) / kThreads;
+    const int b_lo = min(nblocks, (int)threadIdx.x * per);
+    const int b_hi = min(nblocks, b_lo + per);
+    float mine = 0.0f;
+    for (int k = b_lo; k < b_hi; ++k)
+        mine += bs[k].y;
+    const float incl = block_incl_scan_f(mine, sh.fsh);
+    if (threadIdx.x < kThreads)
+        sh.run_incl[threadIdx.x] = incl;
+    __syncthreads();
+    const float total = sh.run_incl[kThreads - 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int k0 = 0; k0 < kCandidates; k0 += NW) {
+        const uint64_t k = (uint64_t)(k0 + wave);
+        const float v = stream_uniform(seed, 2 * k), a = stream_uniform(seed, 2 * k + 1);
+        const int j = wave_candidate(d, scale, V, bs, sh.run_incl, per, v * total);
+        const float pf = weight(d.zt[j], d.ft.m, scale) * d.ft.inv;
+        const float qf = weight(d.zd[j], d.fd.m, scale) * d.fd.inv;
+        const float thr = (pf - qf) / pf;
+        if (lane == 0)
+            sh.cand[wave] = (k0 + wave < kCandidates && a < thr) ? j : -1;
+        __syncthreads();
+        int tok = -1;
+        for (int w = 0; w < NW && tok < 0; ++w)
+            tok = sh.cand[w];
+        __syncthreads();
+        if (tok >= 0)
+            return tok;
+    }
+    return -1;
+}
+
 // Kernel 4: decisions, then the inverse-CDF draw.
 __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
@@ -1286,8 +1469,26 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         }
         return;
     }
-    draw_full_vocab(rows, sp, ws.block_sums + (size_t)b * ((rows.V + kBlock - 1) / kBlock), d, b, L, u,
-                    sh, accepted_len, next_token);
+    const int nblocks = (rows.V + kBlock - 1) / kBlock;
+    float2 *bs = ws.block_sums + (size_t)b * nblocks;   // the target row's (p, p) sums
+    if (d.residual) {
+        const uint32_t ubits = __float_as_uint(u);
+        const int tok = rejection_draw(rows, sp, bs, d, (uint64_t)ubits, sh);
+        if (tok >= 0) {
+            if (threadIdx.x == 0) {
+                if (accepted_len) accepted_len[b] = L;
+                next_token[b] = tok;
+            }
+            return;
+        }
+        // no candidate kept: the residual's own sums, then its inverse CDF
+        block_draw_sums<kWaves>(d, sp, rows.V, 0, nblocks, bs);
+        __syncthreads();
+        draw_full_vocab(rows, sp, bs, d, b, L, stream_uniform(ubits, 2 * kCandidates), sh,
+                        accepted_len, next_token);
+        return;
+    }
+    draw_full_vocab(rows, sp, bs, d, b, L, u, sh, accepted_len, next_token);
 }
 
 // Kernels 3 and 4 as one, for large batches (full vocabulary, verification):
@@ -1325,8 +1526,26 @@ __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
     const DrawRows d = draw_rows(rows, ws, sp, sh.rf, b, L);
     const int nblocks = (V + kBlock - 1) / kBlock;
     float2 *bs = nblocks <= kFusedLdsBlocks ? sh.bsum : ws.block_sums + (size_t)b * nblocks;
-    block_draw_sums<NW>(d, sp, V, 0, nblocks, bs);
+    // the target row's block masses: the bonus draws from them, a residual
+    // draws candidates from them
+    block_draw_sums<NW>(target_only(d), sp, V, 0, nblocks, bs);
     __syncthreads();   // the block sums, written above, are read by other waves below
+    if (d.residual) {
+        const uint32_t ubits = __float_as_uint(u);
+        const int tok = rejection_draw(rows, sp, bs, d, (uint64_t)ubits, sh);
+        if (tok >= 0) {
+            if (threadIdx.x == 0) {
+                if (accepted_len) accepted_len[b] = L;
+                next_token[b] = tok;
+            }
+            return;
+        }
+        block_draw_sums<NW>(d, sp, V, 0, nblocks, bs);
+        __syncthreads();
+        draw_full_vocab(rows, sp, bs, d, b, L, stream_uniform(ubits, 2 * kCandidates), sh,
+                        accepted_len, next_token);
+        return;
+    }
     draw_full_vocab(rows, sp, bs, d, b, L, u, sh, accepted_len, next_token);
 }
 

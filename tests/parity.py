@@ -121,8 +121,10 @@ def compare_accept(gpu, ref, t, d, toks, u, T, k=0, p=1.0):
       - accepted_len differs at position i = min(L_gpu, L_oracle): a ratio
         tie at i, or a top-p tie on target row i or draft row i (the rows
         P_i(d_i) and Q_i(d_i) come from);
-      - same accepted_len, different token: a draw tie, or a top-p tie on
-        the rows of the draw (target row L, and draft row L below D).
+      - same accepted_len, different token: a draw tie (the oracle's
+        draw_margin below TIE: some inverse-CDF draw or candidate test on the
+        way to its token lay within TIE of a boundary), or a top-p tie on the
+        rows of the draw (target row L, and draft row L below D).
     A validity mismatch (one side -1, the other not) is always a failure.
     p_draft / q_draft are checked at every position whose two rows have no
     top-p tie.
@@ -164,16 +166,8 @@ def compare_accept(gpu, ref, t, d, toks, u, T, k=0, p=1.0):
         if tt[L] or (L < D and dt[L]):
             ties += 1
             continue
-        P = oracle.probs(t[b, L], T, k, p)
-        if L < D:
-            Q = oracle.probs(d[b, L], T, k, p)
-            w = np.maximum(P - Q, 0.0)
-            if not (w.sum() > 0):
-                w = P
-        else:
-            w = P
-        if draw_tie(w, u[b, D], int(nxt_g[b]), int(nxt_o[b])):
+        if float(ref["draw_margin"][b]) < TIE:
             ties += 1
         else:
-            bad.append((b, "draw", L, int(nxt_g[b]), int(nxt_o[b])))
+            bad.append((b, "draw", L, int(nxt_g[b]), int(nxt_o[b]), float(ref["draw_margin"][b])))
     return {"exact": exact, "ties": ties, "bad": bad, "prob_err": prob_err}

@@ -4,8 +4,11 @@ The pages give no worked numeric example of acceptance, so the pins are the
 facts the rule itself fixes: identical distributions accept everything, the
 greedy limit is the sample-and-match loop, the emitted tokens are
 distributed as the target (chi-square over 10^6 trials on vocab 8), the
-acceptance rates have closed forms, residual draws only land where p > q, and
-an exact midpoint-grid integration on vocab 3 reproduces the target masses.
+acceptance rates have closed forms, residual draws only land where p > q, an
+exact midpoint-grid integration on vocab 3 reproduces the target masses (the
+filtered draw), the full-vocabulary draw by rejection follows the residual
+distribution (chi-square) and falls back to the inverse CDF, and the stream
+generator reproduces SplitMix64's published outputs.
 """
 import json
 import math
@@ -244,7 +247,11 @@ def test_exact_midpoint_grid_vocab3():
     # Every boundary of the piecewise-constant output map (draft CDF at 0.2,
     # 0.4; acceptance ratio 0.5 for token 2; residual CDF at 0.5) lies on the
     # 1/100 grid, so a 100^3 midpoint grid integrates the first emitted token's
-    # distribution exactly: counts must be 0.35, 0.35, 0.3 of 10^6.
+    # distribution exactly: counts must be 0.35, 0.35, 0.3 of 10^6.  top_p
+    # just below 1 keeps every token of both rows (so the distributions are
+    # unchanged) and selects the filtered draw, the inverse CDF of the
+    # residual with u_D; the full-vocabulary draw (rejection from P_0, seeded
+    # by u_D) is pinned in distribution below.
     n = 100
     g = (np.arange(n, dtype=np.float64) + 0.5) / n
     ud, u0, u1 = np.meshgrid(g, g, g, indexing="ij")
@@ -254,10 +261,87 @@ def test_exact_midpoint_grid_vocab3():
     pd = np.log(np.array([[0.2, 0.2, 0.6]])).astype(np.float32)
     dl = _replicate(pd, B)
     toks = oracle.sample_rows(dl[:, 0], 1.0, 0, 1.0, ud).reshape(B, 1)
-    out = oracle.accept(_replicate(pt, B), dl, toks, np.stack([u0, u1], axis=1), 1.0)
+    out = oracle.accept(_replicate(pt, B), dl, toks, np.stack([u0, u1], axis=1), 1.0,
+                        top_p=0.9999)
     L, nxt = out["accepted_len"], out["next_token"]
     first = np.where(L > 0, toks[:, 0], nxt)
     assert np.bincount(first, minlength=3).tolist() == [350000, 350000, 300000]
+
+
+def test_splitmix64_known_answers():
+    # SplitMix64 (Steele, Lea, Flood, OOPSLA 2014) seeded with 0: the first
+    # outputs of the reference generator.
+    assert [oracle.splitmix64(0, i) for i in range(3)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    # the uniform is the top 24 bits over 2^24
+    assert oracle.stream_uniform(0, 0) == (0xE220A8397B1DCDAF >> 40) / 2.0**24
+    # counter-based: output i depends on seed + (i + 1) * gamma only
+    gamma = 0x9E3779B97F4A7C15
+    assert oracle.splitmix64(gamma, 4) == oracle.splitmix64(0, 5)
+
+
+def _rejected_at_zero(P0, Q0, n, seed):
+    """n sequences of D = 1 whose draft token is always rejected (P < Q there
+    and u_0 just below 1), with random u_1: every next token is the residual
+    draw over the full vocabulary."""
+    V = P0.shape[0]
+    d_tok = int(np.argmax(Q0 - P0))
+    assert P0[d_tok] < Q0[d_tok]
+    t = np.log(np.stack([P0, np.full(V, 1.0 / V)]))[None].astype(np.float32)
+    d = np.log(Q0)[None, None].astype(np.float32)
+    u = np.empty((n, 2), np.float32)
+    u[:, 0] = np.float32(1.0 - 2.0**-24)
+    u[:, 1] = synth.uniforms(seed, synth.U_ACCEPT, (n,))
+    out = oracle.accept(_replicate(t[0], n), _replicate(d[0], n),
+                        np.full((n, 1), d_tok, np.int32), u, 1.0)
+    assert np.all(out["accepted_len"] == 0)
+    return out, u
+
+
+def test_rejection_draw_has_the_residual_distribution():
+    # Rejection from P_0 keeps candidate j with probability (P - Q)+ / P, so
+    # the kept token follows the normalized residual: chi-square over 10^6
+    # draws, on a vocabulary where the residual has four nonzero entries.
+    P0 = np.array([0.30, 0.05, 0.25, 0.10, 0.20, 0.10])
+    Q0 = np.array([0.10, 0.30, 0.05, 0.30, 0.05, 0.20])
+    out, _ = _rejected_at_zero(P0, Q0, 1_000_000, 61)
+    r = np.maximum(P0 - Q0, 0.0)
+    r /= r.sum()
+    obs = np.bincount(out["next_token"], minlength=P0.shape[0])
+    assert np.all(obs[r == 0] == 0)
+    exp = r[r > 0] * obs.sum()
+    chi2 = float(((obs[r > 0] - exp) ** 2 / exp).sum())
+    assert chi2 < scipy.stats.chi2.ppf(0.999, int((r > 0).sum()) - 1), (chi2, obs, exp)
+
+
+def test_rejection_falls_back_to_the_inverse_cdf():
+    # P_0 = Q_0 with the draft token at probability 0 (ratio 0: rejected):
+    # the residual is zero (drawn from P_0 instead, R11), and no candidate
+    # can be kept ((P - Q)/P = 0), so after every candidate the inverse CDF
+    # of P_0 with stream output 128 decides.
+    P0 = np.array([0.1, 0.4, 0.2, 0.3, 0.0])
+    with np.errstate(divide="ignore"):
+        lp = np.log(P0)
+    t = np.stack([lp, lp])[None].astype(np.float32)
+    d = lp[None, None].astype(np.float32)
+    Pf = oracle.probs(t[0, 0], 1.0)
+    for ud in (0.0, 0.125, 0.5, 0.7311, 1.0 - 2.0**-24):
+        u = np.array([[np.float32(0.5), np.float32(ud)]], np.float32)
+        out = oracle.accept(t, d, np.array([[4]], np.int32), u, 1.0)
+        assert out["accepted_len"][0] == 0
+        seed = int(np.float32(ud).view(np.uint32))
+        v = oracle.stream_uniform(seed, 128)
+        c = np.cumsum(Pf)
+        assert out["next_token"][0] == int(np.argmax(c > v * c[-1]))
+
+
+def test_draw_margin_is_the_distance_to_a_boundary():
+    # Bonus draw from (0.5, 0.5): u = 0.5 sits on the boundary (margin 0),
+    # u = 0.25 a quarter of the mass away from both.
+    t = np.zeros((1, 1, 2), np.float32)
+    for u, m in ((0.5, 0.0), (0.25, 0.25)):
+        out = oracle.accept(t, None, None, np.array([[u]], np.float32), 1.0)
+        assert abs(out["draw_margin"][0] - m) < 1e-12
 
 
 def test_invalid_sequences_report_minus_one():

@@ -50,10 +50,11 @@ def test_far_decision_and_draw_mismatches_are_failures():
             a = np.float32(0) if pf == 0 else np.float32(pf / qf)
             if abs(float(u[b, L]) - float(a)) > 1e-2:
                 cands.append(b)
-    assert len(cands) >= 2
+    far_draw = [b for b in cands if ref["draw_margin"][b] > 1e-2]
+    assert len(cands) >= 2 and far_draw and far_draw[0] != cands[0]
     g = copy(ref)
     g["accepted_len"][cands[0]] += 1
-    g["next_token"][cands[1]] = (ref["next_token"][cands[1]] + 7) % t.shape[2]
+    g["next_token"][far_draw[0]] = (ref["next_token"][far_draw[0]] + 7) % t.shape[2]
     res = parity.compare_accept(g, ref, t, d, toks, u, 0.8)
     assert res["ties"] == 0
     assert sorted(x[1] for x in res["bad"]) == ["decision", "draw"]
@@ -65,3 +66,15 @@ def test_probability_error_is_reported():
     g["p_draft"][3, 1] += 1e-3
     res = parity.compare_accept(g, ref, t, d, toks, u, 0.8)
     assert abs(res["prob_err"] - 1e-3) < 1e-6
+
+
+def test_draw_on_a_boundary_is_a_tie():
+    # A bonus draw from (0.5, 0.5) with u_D = 0.5 lies on the boundary of the
+    # two tokens' intervals (draw_margin 0): either token is a correct result.
+    t = np.zeros((1, 1, 2), np.float32)
+    u = np.array([[0.5]], np.float32)
+    ref = oracle.accept(t, None, None, u, 1.0)
+    g = copy(ref)
+    g["next_token"][0] = 1 - ref["next_token"][0]
+    res = parity.compare_accept(g, ref, t, None, None, u, 1.0)
+    assert res["ties"] == 1 and not res["bad"]
