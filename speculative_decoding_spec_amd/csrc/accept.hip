@@ -56,6 +56,11 @@ constexpr int kFusedMinB = 128;     // batches drawn by the fused kernel (half t
 constexpr int kStatsThreads = 256;
 constexpr int kStatsLoads = 8;
 constexpr int kBlock = 256;         // tokens per draw block (64 lanes x 4)
+// Block statistics of one statistics chunk are gathered in LDS and written
+// out once, contiguously (single-lane scattered 8-byte stores measured 20 us
+// slower over 1536 rows of 151936 logits); full-vocabulary chunks hold at
+// most this many blocks.
+constexpr int kStatsLdsBlocks = 1024;
 
 constexpr int kInvalid = 1;         // row flag: NaN / +inf / no finite logit
 constexpr int kMaxDepth = 15;       // drafts per sequence at most (the ABI's limit)
@@ -110,6 +115,8 @@ struct Ws {
     RowFinal *row_final;        // [rows]
     uint64_t *row_keys;         // [rows][k]          (candidate mode)
     float2 *block_sums;         // [B][nblocks]  (draw mass, target mass)
+    float *block_stats;         // [B][D + 1][nblocks]  target blocks' sums of
+                                // exponentials relative to their chunk's max
 };
 
 // ---------------------------------------------------------------- keys ----
@@ -144,7 +151,7 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 template <class Op>
-__device__ __forceinline__ float wave_reduce(float v, Op op, float identity) {
+__device__ __forceinline__ float wave_reduce_tree(float v, Op op, float identity) {
     v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
     v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
     v = op(v, dpp_f<0x141>(v));   // row_half_mirror
@@ -155,7 +162,23 @@ __device__ __forceinline__ float wave_reduce(float v, Op op, float identity) {
                   __float_as_int(identity), __float_as_int(v), 0x142, 0xA, 0xF, false)));
     v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(
                   __float_as_int(identity), __float_as_int(v), 0x143, 0xC, 0xF, false)));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    return v;   // the total in lane 63
+}
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op, float identity) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_reduce_tree(v, op, identity)), 63));
+}
+// The wave's sum in lane 63 only (other lanes hold partial sums).
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    return wave_reduce_tree(v, [](float a, float b) { return a + b; }, 0.0f);
+}
+// Orders one wave's LDS writes before its following LDS reads (and reads
+// before later writes): a wave's LDS operations run in program order, so
+// only the compiler must not move them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 __device__ __forceinline__ float wave_sum(float v) {
     return wave_reduce(v, [](float a, float b) { return a + b; }, 0.0f);
@@ -436,67 +459,14 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
     if (!CAND) {
         // ---- running max and normalizer over the chunk ----
         float m = -INFINITY, S = 0.0f;
-        if (sp.block_stats) {
-            // Plain sampling: the same pass also leaves, per 256-token block
-            // (one wave's 64 lanes x 4 logits for each u), the block's max
-            // and its sum of exp2((z - max) * scale).  The loop bound is the
-            // same for every thread, so each wave reduces whole blocks.
-            const float4 *z4 = reinterpret_cast<const float4 *>(z);
-            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-            const int nblocks = (V + kBlock - 1) / kBlock;
-            float2 *bsum = ws.block_sums + (size_t)r * nblocks;
-            for (int base_w = lo; base_w < hi; base_w += kThreads * 16) {
-                float v[16];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = base_w + 4 * threadIdx.x + u * kThreads * 4;
-                    const float4 t = load_once(&z4[min(e, hi - 4) >> 2]);
-                    const bool in = e < hi;
-                    v[4 * u + 0] = in ? t.x : -INFINITY;
-                    v[4 * u + 1] = in ? t.y : -INFINITY;
-                    v[4 * u + 2] = in ? t.z : -INFINITY;
-                    v[4 * u + 3] = in ? t.w : -INFINITY;
-                }
-                float bm = m;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    bad |= !(v[q] < INFINITY);   // NaN or +inf
-                    bm = fmaxf(bm, v[q]);
-                }
-                if (bm > -INFINITY) {
-                    float s = (m == bm) ? S : S * weight(m, bm, scale);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        s += weight(v[q], bm, scale);
-                    S = s;
-                    m = bm;
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int blk = (base_w + u * kThreads * 4) / kBlock + wave;
-                    float lm = fmaxf(fmaxf(v[4 * u], v[4 * u + 1]), fmaxf(v[4 * u + 2], v[4 * u + 3]));
-                    const float mb = wave_max(lm);
-                    float sb = 0.0f;
-                    if (mb > -INFINITY && mb < INFINITY) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            sb += weight(v[4 * u + q], mb, scale);
-                    }
-                    sb = wave_sum(sb);
-                    if (lane == 0 && blk * kBlock < hi)
-                        bsum[blk] = make_float2(mb, sb);
-                }
-            }
-        } else {
-            // rows not 16-byte aligned (aligned rows go to row_stats_kernel)
-            for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
-                const float v = load_once(&z[e]);
-                bad |= !(v < INFINITY);   // NaN or +inf
-                const float bm = fmaxf(m, v);
-                if (bm > -INFINITY) {
-                    S = ((m == bm) ? S : S * weight(m, bm, scale)) + weight(v, bm, scale);
-                    m = bm;
-                }
+        // rows not 16-byte aligned (aligned rows go to row_stats_kernel)
+        for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
+            const float v = load_once(&z[e]);
+            bad |= !(v < INFINITY);   // NaN or +inf
+            const float bm = fmaxf(m, v);
+            if (bm > -INFINITY) {
+                S = ((m == bm) ? S : S * weight(m, bm, scale)) + weight(v, bm, scale);
+                m = bm;
             }
         }
         // A finite logit was seen iff the running max left -inf (a +inf
@@ -614,6 +584,8 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     constexpr int NW = NT / 64;
     __shared__ float s_m[NW], s_S[NW];
     __shared__ int s_flags[NW];
+    __shared__ __align__(16) float s_red[NW][NV][64];
+    __shared__ float2 s_bst[kStatsLdsBlocks];
     const int r = blockIdx.x;
     const int c = blockIdx.y;
     const int V = rows.V;
@@ -621,12 +593,20 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     const int lo = c * chunk_len;
     const int hi = min(V, lo + chunk_len);
     const float scale = sp.scale;
+    // Target rows of a full-vocabulary draw also leave, per 256-token block,
+    // the block's sum of exp2((z - M) * scale) with M the chunk's max, so the
+    // draw needs no second pass over the row.  For each u, the 64 lanes of a
+    // wave hold one whole block (chunks start on 1024-token boundaries).
+    const int per_seq = 2 * rows.D + 1;
+    const int seq = r / per_seq, pos = r - seq * per_seq;
+    const bool emit = sp.block_stats && pos <= rows.D;
+    const int nblocks = (V + kBlock - 1) / kBlock;
+    float *bstat = ws.block_stats + ((size_t)seq * (rows.D + 1) + pos) * nblocks;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float m = -INFINITY, S = 0.0f;
-    int bad = 0;
-    for (int base = lo + threadIdx.x * 4; base < hi; base += NT * 4 * NV) {
-        // Branch-free: clamp each load into the chunk and mask the lanes
-        // past its end to -inf (which adds nothing below).
-        float v[4 * NV];
+    // Loads are clamped into the chunk and lanes past its end masked to
+    // -inf, which adds nothing below.
+    auto load = [&](int base, float *v) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int e = base + u * NT * 4;
@@ -637,21 +617,67 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
             v[4 * u + 2] = in ? t.z : -INFINITY;
             v[4 * u + 3] = in ? t.w : -INFINITY;
         }
-        float bm = m;
+    };
+    // Invalid logits (NaN, +inf) are not tested one by one: either enters
+    // the sum of exponentials as NaN (a NaN's weight is NaN; a +inf makes
+    // the running max +inf and its own weight exp2(NaN)), which stays NaN
+    // through every rescale and merge.  Only a NaN among values that are
+    // otherwise all -inf skips the sum, and is looked for there.
+    int hidden_nan = 0;
+    // The running max is kept per wave, so one set of exponentials serves
+    // the normalizer and, on target rows, the block sums: block u of an
+    // iteration is stored as (the wave's running max M, its sum of
+    // exp2((z - M) * scale)).  The lanes' four-token partial sums of the
+    // wave's NV blocks pass through LDS (transposed: eight lanes per block),
+    // then eight-lane DPP folds finish them.  Target and draft rows are
+    // summed alike, so identical rows get identical statistics.  The loop
+    // bound is the same for every thread, so each wave reduces whole blocks.
+    float(*red)[64] = s_red[wave];
+    for (int base0 = lo; base0 < hi; base0 += NT * 4 * NV) {
+        float v[4 * NV];
+        load(base0 + threadIdx.x * 4, v);
+        float lm = m;
 #pragma unroll
-        for (int q = 0; q < 4 * NV; ++q) {
-            bad |= !(v[q] < INFINITY);   // NaN or +inf
-            bm = fmaxf(bm, v[q]);
-        }
+        for (int q = 0; q < 4 * NV; ++q)
+            lm = fmaxf(lm, v[q]);
+        const float bm = wave_max(lm);
+        float t = 0.0f;
         if (bm > -INFINITY) {
             float s = (m == bm) ? S : S * weight(m, bm, scale);
 #pragma unroll
-            for (int q = 0; q < 4 * NV; ++q)
-                s += weight(v[q], bm, scale);
+            for (int u = 0; u < NV; ++u) {
+                float sb = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sb += weight(v[4 * u + q], bm, scale);
+                s += sb;
+                if (emit)
+                    red[u][lane] = sb;
+            }
             S = s;
             m = bm;
+            if (emit) {
+                wave_lds_sync();
+                const float4 *rp = reinterpret_cast<const float4 *>(&red[lane >> 3][(lane & 7) * 8]);
+                const float4 a = rp[0], c = rp[1];
+                t = ((a.x + a.y) + (a.z + a.w)) + ((c.x + c.y) + (c.z + c.w));
+                t += dpp_f<0xB1>(t);    // quad_perm [1,0,3,2]
+                t += dpp_f<0x4E>(t);    // quad_perm [2,3,0,1]
+                t += dpp_f<0x141>(t);   // row_half_mirror: the other quad
+                wave_lds_sync();        // the reads above precede the next writes
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4 * NV; ++q)
+                hidden_nan |= v[q] != v[q];
+        }
+        if (emit) {
+            const int lblk = (base0 - lo) / kBlock + wave + (lane >> 3) * (NT * 4 / kBlock);
+            if ((lane & 7) == 0 && lo + lblk * kBlock < hi)
+                s_bst[lblk] = make_float2(bm, t);
         }
     }
+    const int bad = hidden_nan | !(S == S);
     // a finite logit was seen iff the running max left -inf
     int flags = bad | ((m > -INFINITY) ? 2 : 0);
     wave_merge_ms(m, S, scale);
@@ -674,6 +700,19 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
             ws.row_final[r] = RowFinal{mm, 1.0f / SS, 0, (rbad || !rfin) ? kInvalid : 0};
         else
             ws.chunk_stats[(size_t)r * chunks + c] = ChunkStat{mm, SS, rbad, rfin};
+        s_m[0] = mm;
+    }
+    if (emit) {
+        // The block sums, rescaled to the chunk's max, written out once and
+        // contiguously: 4 bytes per block (HBM writes measured costly while
+        // the pass streams: about 2 us per MB written).
+        __syncthreads();
+        const float mm = s_m[0];
+        const int nb = (hi - lo + kBlock - 1) / kBlock;
+        for (int k = threadIdx.x; k < nb; k += NT) {
+            const float2 st = s_bst[k];
+            bstat[lo / kBlock + k] = st.y > 0.0f ? st.y * weight(st.x, mm, scale) : 0.0f;
+        }
     }
 }
 
@@ -942,6 +981,22 @@ __device__ __forceinline__ DrawRows target_only(const DrawRows &d) {
     return t;
 }
 
+// The stop row's block statistics (each block's sum of exp2((z - M) *
+// scale), M its statistics chunk's max) to its block masses (p, p).
+__device__ void stats_to_masses(const Rows &rows, const Ws &ws, const SamplingParams &sp,
+                                const DrawRows &d, int b, int L, float2 *dst) {
+#pragma clang fp contract(off)
+    const int nblocks = (rows.V + kBlock - 1) / kBlock;
+    const float *src = ws.block_stats + ((size_t)b * (rows.D + 1) + L) * nblocks;
+    const int chunks = max(1, sp.merge_chunks);
+    const ChunkStat *cs = ws.chunk_stats + (size_t)rows.target_row(b, L) * chunks;
+    for (int k = threadIdx.x; k < nblocks; k += blockDim.x) {
+        const float mc = chunks > 1 ? cs[k / sp.chunk_blocks].m : d.ft.m;
+        const float mass = src[k] * weight(mc, d.ft.m, sp.scale) * d.ft.inv;
+        dst[k] = make_float2(mass, mass);
+    }
+}
+
 // Weights of token x: (residual max(0, p - q) or p, and p), full vocabulary.
 // p and q are each rounded before the subtraction (contraction into a fused
 // multiply-add is off here): where the two distributions agree, p - q is then
@@ -1050,8 +1105,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const int blk_hi = min(nblocks, blk_lo + blocks_per_chunk);
     // the target row's block masses: the bonus draws from them, a residual
     // draws candidates from them
-    block_draw_sums<kWaves>(target_only(d), sp, V, blk_lo, blk_hi,
-                            ws.block_sums + (size_t)b * nblocks);
+    block_draw_sums<kWaves>(target_only(d), sp, V, blk_lo, blk_hi, ws.block_sums + (size_t)b * nblocks);
 }
 
 template <int NW>
@@ -1087,12 +1141,9 @@ __device__ void draw_full_vocab(const Rows &rows, const SamplingParams &sp, cons
     const float scale = sp.scale;
     // ---- full vocabulary: find the block holding u * total ----
     const int nblocks = (V + kBlock - 1) / kBlock;
-    // Block masses: from the draw pass (residual mass, target mass), or, for
-    // plain sampling, from the statistics pass's (block max, block sum).
+    // Block masses: (residual mass, target mass), or (p, p) without a residual.
     auto mass = [&](int k, bool target_mass) -> float {
         const float2 v = bs[k];
-        if (sp.block_stats)
-            return v.y * weight(v.x, d.ft.m, scale) * d.ft.inv;
         return target_mass ? v.y : v.x;
     };
     // thread t owns a contiguous run of blocks
@@ -1470,7 +1521,13 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         return;
     }
     const int nblocks = (rows.V + kBlock - 1) / kBlock;
-    float2 *bs = ws.block_sums + (size_t)b * nblocks;   // the target row's (p, p) sums
+    // the target row's (p, p) block masses: from its statistics, or as the
+    // block-sum launch left them
+    float2 *bs = ws.block_sums + (size_t)b * nblocks;
+    if (sp.block_stats) {
+        stats_to_masses(rows, ws, sp, d, b, L, bs);
+        __syncthreads();
+    }
     if (d.residual) {
         const uint32_t ubits = __float_as_uint(u);
         const int tok = rejection_draw(rows, sp, bs, d, (uint64_t)ubits, sh);
@@ -1526,10 +1583,14 @@ __global__ __launch_bounds__(kFusedThreads) void draw_fused_kernel(
     const DrawRows d = draw_rows(rows, ws, sp, sh.rf, b, L);
     const int nblocks = (V + kBlock - 1) / kBlock;
     float2 *bs = nblocks <= kFusedLdsBlocks ? sh.bsum : ws.block_sums + (size_t)b * nblocks;
-    // the target row's block masses: the bonus draws from them, a residual
-    // draws candidates from them
-    block_draw_sums<NW>(target_only(d), sp, V, 0, nblocks, bs);
-    __syncthreads();   // the block sums, written above, are read by other waves below
+    // the target row's block masses (the bonus draws from them, a residual
+    // draws candidates from them): from the row's block statistics, or summed
+    // here over the row
+    if (sp.block_stats)
+        stats_to_masses(rows, ws, sp, d, b, L, bs);
+    else
+        block_draw_sums<NW>(target_only(d), sp, V, 0, nblocks, bs);
+    __syncthreads();   // the block masses, written above, are read by other waves below
     if (d.residual) {
         const uint32_t ubits = __float_as_uint(u);
         const int tok = rejection_draw(rows, sp, bs, d, (uint64_t)ubits, sh);
@@ -1574,6 +1635,7 @@ Ws carve(const AcceptPlan &p, void *base) {
     w.row_final = reinterpret_cast<RowFinal *>(b + p.off_row_final);
     w.row_keys = reinterpret_cast<uint64_t *>(b + p.off_row_keys);
     w.block_sums = reinterpret_cast<float2 *>(b + p.off_block_sums);
+    w.block_stats = reinterpret_cast<float *>(b + p.off_block_stats);
     return w;
 }
 
@@ -1586,7 +1648,7 @@ hipError_t launch_row_stats(const Rows &rows, const AcceptPlan &plan,
     if (sp.candidates)
         row_chunk_kernel<true><<<dim3(plan.rows, plan.chunks), kThreads, 0, stream>>>(
             rows, plan.chunks, plan.chunk_len, sp, w);
-    else if (!sp.block_stats && (rows.V & 3) == 0)
+    else if ((rows.V & 3) == 0)
         row_stats_kernel<kStatsThreads, kStatsLoads><<<dim3(plan.rows, plan.chunks), kStatsThreads, 0, stream>>>(
             rows, plan.chunks, plan.chunk_len, sp, w);
     else
@@ -1631,6 +1693,7 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
     } else {
         int C = (kTargetBlocks + std::max(p.rows, 1) - 1) / std::max(p.rows, 1);
         C = std::max(1, std::min(C, (V + 2047) / 2048));
+        C = std::max(C, (V + kStatsLdsBlocks * kBlock - 1) / (kStatsLdsBlocks * kBlock));
         int len = (V + C - 1) / C;
         p.chunk_len = ((len + 1023) / 1024) * 1024;
     }
@@ -1651,7 +1714,11 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
     p.off_chunk_keys = off;  off += align256((size_t)p.rows * p.chunks * k * sizeof(uint64_t));
     p.off_row_final = off;   off += align256((size_t)p.rows * sizeof(RowFinal));
     p.off_row_keys = off;    off += align256((size_t)p.rows * k * sizeof(uint64_t));
+    // full vocabulary: per sequence the draw's block masses, and (rows
+    // 16-byte aligned) per target row the block statistics
+    const size_t stat_rows = (candidates || V % 4 != 0) ? 0 : (size_t)B * (D + 1);
     p.off_block_sums = off;  off += align256(candidates ? 0 : (size_t)B * p.nblocks * sizeof(float2));
+    p.off_block_stats = off; off += align256(stat_rows * p.nblocks * sizeof(float));
     p.ws_bytes = off;
     return p;
 }
@@ -1667,17 +1734,18 @@ hipError_t launch_accept(const float *target, const float *draft,
     Rows rows{target, draft, plan.D, plan.V};
     Ws w = carve(plan, ws);
     SamplingParams spl = sp;
-    spl.block_stats = plan.D == 0 && !sp.candidates && (plan.V & 3) == 0;
+    spl.block_stats = !sp.candidates && (plan.V & 3) == 0;
     spl.merge_chunks = (!sp.candidates && plan.chunks > 1) ? plan.chunks : 0;
+    spl.chunk_blocks = plan.chunk_len / kBlock;
     hipError_t e = launch_row_stats(rows, plan, spl, w, false, stream);
     if (e != hipSuccess)
         return e;
+    if (!sp.candidates && plan.fused_draw) {
+        draw_fused_kernel<<<plan.B, kFusedThreads, 0, stream>>>(
+            rows, spl, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
+        return hipGetLastError();
+    }
     if (!sp.candidates && !spl.block_stats) {
-        if (plan.fused_draw) {
-            draw_fused_kernel<<<plan.B, kFusedThreads, 0, stream>>>(
-                rows, spl, draft_tokens, uniforms, accepted_len, next_token, p_draft, q_draft, w);
-            return hipGetLastError();
-        }
         draw_sums_kernel<<<dim3(plan.B, plan.chunks3), kThreads, 0, stream>>>(
             rows, spl, draft_tokens, uniforms, plan.blocks_per_chunk3, w);
         e = hipGetLastError();

@@ -57,11 +57,12 @@ struct SamplingParams {
     float top_p;     // applied when use_p
     bool use_p;
     bool candidates; // true: distributions live on <= 256 sorted candidates
-    bool block_stats; // plain sampling (D = 0, full vocabulary, V % 4 == 0): the
-                      // statistics pass also leaves each 256-token block's
-                      // (max, sum of exponentials), so no re-read is needed
+    bool block_stats; // full vocabulary, V % 4 == 0: the statistics pass also
+                      // leaves each target row's 256-token block (max, sum of
+                      // exponentials), so the draw need not re-read the row
     int merge_chunks; // > 0: full-vocabulary rows span this many chunks and the
                       // draw kernels merge their statistics themselves
+    int chunk_blocks; // 256-token blocks per statistics chunk (block_stats)
 };
 
 struct AcceptPlan {
@@ -75,7 +76,8 @@ struct AcceptPlan {
     int blocks_per_chunk3;
     size_t ws_bytes;
     // workspace offsets
-    size_t off_chunk_stats, off_chunk_keys, off_row_final, off_row_keys, off_block_sums;
+    size_t off_chunk_stats, off_chunk_keys, off_row_final, off_row_keys, off_block_sums,
+        off_block_stats;
 };
 
 AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates);

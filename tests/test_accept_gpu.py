@@ -237,6 +237,34 @@ def test_invalid_sequences(dev):
     assert got["next_token"][0] == ref["next_token"][0]
 
 
+@pytest.mark.parametrize("B", [8, 130])
+def test_invalid_logits_among_minus_inf(dev, B):
+    """A NaN or +inf logit makes its row, and so its sequence, invalid, also
+    where every other logit of the row (or of a statistics thread's share
+    of it) is -inf, on target rows (whose statistics pass also leaves block
+    statistics) and on draft rows; a row of -inf with one finite logit stays
+    valid.  Several chunks per row (B=8) and one (B=130)."""
+    D, V = 2, 4096
+    t, d = synth.logits_pair(780 + B, B, D, V)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 780 + B)
+
+    def lone(row, x, val):
+        row[:] = -np.inf
+        row[x] = val
+
+    lone(t[1, 0], 100, np.nan)         # target row, NaN alone among -inf
+    lone(d[2, 1], V - 1, np.nan)       # draft row, NaN in the last slot
+    lone(t[3, 2], 7, np.inf)           # bonus row, +inf alone
+    lone(d[4, 0], 0, np.inf)           # draft row, +inf in the first slot
+    t[5, 1, 2048] = np.nan             # NaN among finite logits
+    lone(t[6, 0], 17, 0.0)             # one finite logit: valid
+    u = synth.uniforms(780 + B, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert ref["accepted_len"][1:6].tolist() == [-1] * 5
+    assert got["next_token"][1:6].tolist() == [-1] * 5
+    assert np.all(ref["accepted_len"][[0, 6, 7]] >= 0)
+
+
 def test_determinism(dev):
     B, D, V = 64, 5, 151936
     t, d = synth.logits_pair(600, B, D, V)
