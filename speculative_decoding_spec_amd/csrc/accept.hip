@@ -584,6 +584,7 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     constexpr int NW = NT / 64;
     __shared__ float s_m[NW], s_S[NW];
     __shared__ int s_flags[NW];
+    static_assert(NV == 8, "the block-sum transpose reads two float4 per lane: 8 blocks");
     __shared__ __align__(16) float s_red[NW][NV][64];
     __shared__ float2 s_bst[kStatsLdsBlocks];
     const int r = blockIdx.x;
@@ -628,8 +629,8 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
     // the normalizer and, on target rows, the block sums: block u of an
     // iteration is stored as (the wave's running max M, its sum of
     // exp2((z - M) * scale)).  The lanes' four-token partial sums of the
-    // wave's NV blocks pass through LDS (transposed: eight lanes per block),
-    // then eight-lane DPP folds finish them.  Target and draft rows are
+    // wave's NV blocks pass through LDS (transposed: each lane picks up four
+    // partials of two blocks), then 16-lane DPP folds finish them.  Target and draft rows are
     // summed alike, so identical rows get identical statistics.  The loop
     // bound is the same for every thread, so each wave reduces whole blocks.
     float(*red)[64] = s_red[wave];
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
         for (int q = 0; q < 4 * NV; ++q)
             lm = fmaxf(lm, v[q]);
         const float bm = wave_max(lm);
-        float t = 0.0f;
+        float t0 = 0.0f, t1 = 0.0f;
         if (bm > -INFINITY) {
             float s = (m == bm) ? S : S * weight(m, bm, scale);
 #pragma unroll
@@ -657,13 +658,18 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
             S = s;
             m = bm;
             if (emit) {
+                // Lane l reads 16 consecutive bytes at l and at 64 + l (no
+                // bank conflicts): four partials of block l / 16 and four of
+                // block 4 + l / 16; each row of 16 lanes then folds its two.
                 wave_lds_sync();
-                const float4 *rp = reinterpret_cast<const float4 *>(&red[lane >> 3][(lane & 7) * 8]);
-                const float4 a = rp[0], c = rp[1];
-                t = ((a.x + a.y) + (a.z + a.w)) + ((c.x + c.y) + (c.z + c.w));
-                t += dpp_f<0xB1>(t);    // quad_perm [1,0,3,2]
-                t += dpp_f<0x4E>(t);    // quad_perm [2,3,0,1]
-                t += dpp_f<0x141>(t);   // row_half_mirror: the other quad
+                const float4 *rp = reinterpret_cast<const float4 *>(&red[0][0]);
+                const float4 a = rp[lane], c = rp[64 + lane];
+                t0 = (a.x + a.y) + (a.z + a.w);
+                t1 = (c.x + c.y) + (c.z + c.w);
+                t0 += dpp_f<0xB1>(t0);  t1 += dpp_f<0xB1>(t1);    // quad_perm [1,0,3,2]
+                t0 += dpp_f<0x4E>(t0);  t1 += dpp_f<0x4E>(t1);    // quad_perm [2,3,0,1]
+                t0 += dpp_f<0x141>(t0); t1 += dpp_f<0x141>(t1);   // row_half_mirror
+                t0 += dpp_f<0x140>(t0); t1 += dpp_f<0x140>(t1);   // row_mirror
                 wave_lds_sync();        // the reads above precede the next writes
             }
         } else {
@@ -671,10 +677,11 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
             for (int q = 0; q < 4 * NV; ++q)
                 hidden_nan |= v[q] != v[q];
         }
-        if (emit) {
-            const int lblk = (base0 - lo) / kBlock + wave + (lane >> 3) * (NT * 4 / kBlock);
-            if ((lane & 7) == 0 && lo + lblk * kBlock < hi)
-                s_bst[lblk] = make_float2(bm, t);
+        if (emit && (lane & 15) < 2) {
+            const int u = (lane >> 4) + 4 * (lane & 1);
+            const int lblk = (base0 - lo) / kBlock + wave + u * (NT * 4 / kBlock);
+            if (lo + lblk * kBlock < hi)
+                s_bst[lblk] = make_float2(bm, (lane & 1) ? t1 : t0);
         }
     }
     const int bad = hidden_nan | !(S == S);
