@@ -887,13 +887,20 @@ hipError_t launch_qmv(int bits, bool interchange, const void *w, const void *sb,
         return fill_zero(y, (size_t)M * N, stream);
     const QmvPlan plan = qmv_plan(bits, N, K);
     const QmvArgs a{w, sb, biases, x, y, M, N, K, 0};
-    const int blocks = (plan.n_tiles + plan.tiles_per_wave - 1) / plan.tiles_per_wave;
+    // Very tall launches (LM heads) at one or two rows take half the tiles
+    // per workgroup: x is a small share of their bytes there, and smaller
+    // workgroups drain sooner at the end of the launch (W4 M = 1: 65.8
+    // against 68.5 us).  The waves, and so every output's arithmetic, are
+    // the plan's: results do not depend on the tile count.
+    const int T = (plan.n_tiles >= 4096 && M <= 2) ? std::max(1, plan.tiles_per_wave / 2)
+                                                   : plan.tiles_per_wave;
+    const int blocks = (plan.n_tiles + T - 1) / T;
     // Interchange scales and biases load two pairs' worth (8 bytes) at a time
     // when every row starts 8-byte aligned.
     const bool sb2 = (K / 64) % 4 == 0 &&
                      ((reinterpret_cast<uintptr_t>(sb) | reinterpret_cast<uintptr_t>(biases)) & 7u) == 0;
 #define SPEC_QMV_LAUNCH(B, W, TT, SS)                                                    \
-    if (bits == B && plan.waves == W && plan.tiles_per_wave == TT && plan.stages == SS) \
+    if (bits == B && plan.waves == W && T == TT && plan.stages == SS) \
         return !interchange ? launch_shape<B, false, W, TT, SS, false>(a, blocks, stream) \
                : sb2        ? launch_shape<B, true, W, TT, SS, false, true>(a, blocks, stream) \
                             : launch_shape<B, true, W, TT, SS, false, false>(a, blocks, stream);

@@ -93,12 +93,28 @@ def test_lm_head_sampled(dev, bits, M):
     assert np.all(np.isfinite(got))
 
 
-@pytest.mark.parametrize("bits,M", [(4, 1), (4, 6), (8, 8)])
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 6), (8, 1), (8, 8)])
 def test_lm_head_launch_shape_full(dev, bits, M):
-    """The launch shape of heads of 4096 tiles or more (W4: 4 tiles x 4 waves,
-    W8: 2 tiles x 8 waves) on every output, at a K the oracle finishes fast:
-    65600 rows (4100 tiles, a ragged last workgroup) x 256."""
-    full_check(bits, M, 65600, 256, dev, cfg=2, salt=65600 + M)
+    """The launch shapes of heads of 4096 tiles or more (W4: 4 tiles x 4 waves,
+    2 tiles at M <= 2; W8: 2 tiles x 8 waves, 1 tile at M <= 2) on every
+    output, at a K the oracle finishes fast: 65621 rows (4102 tiles, the last
+    one of 5 rows; a ragged last workgroup of 4 tiles) x 256."""
+    full_check(bits, M, 65621, 256, dev, cfg=2, salt=65600 + M)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_lm_head_rows_do_not_depend_on_tiles_per_workgroup(dev, bits):
+    """At M <= 2 a head launch takes half the tiles per workgroup; the waves
+    and so every output's arithmetic are unchanged: rows of a 6-row call
+    equal the one- and two-row calls bitwise."""
+    w, s, b = synth.qweights(8, bits, 65621, 256, 64)
+    x = synth.activations(8, 6, 256)
+    full = run(bits, w, s, b, x, dev)
+    for m in range(6):
+        one = run(bits, w, s, b, np.ascontiguousarray(x[m:m + 1]), dev)
+        assert np.array_equal(one[0].view(np.uint32), full[m].view(np.uint32)), m
+    two = run(bits, w, s, b, np.ascontiguousarray(x[2:4]), dev)
+    assert np.array_equal(two.view(np.uint32), full[2:4].view(np.uint32))
 
 
 @pytest.mark.parametrize("bits", [4, 8])
