@@ -452,6 +452,31 @@ def test_zero_residual_draws_from_target(dev, B):
     assert np.all(ref["accepted_len"] == 0) and np.all(got["accepted_len"] == 0)
 
 
+@pytest.mark.parametrize("B", [24, 130])
+def test_residual_fallback_after_rejected_candidates(dev, B):
+    """R22's fallback on both draw paths: target and draft rows close
+    (target = draft + N(0, 0.03)), so at a rejected position the residual
+    holds about 2% of the mass and each of the 64 rejection candidates is
+    kept with that probability; when none is, the residual's own inverse CDF
+    decides with stream output 128.  Position 0 is rejected (a uniform just
+    below 1) wherever P < Q at the draft token.  The expected number of
+    sequences drawn by the fallback, the sum of (1 - TV)^64, is checked to
+    be at least 2."""
+    D, V = 2, 32768
+    t, d = synth.logits_pair(790 + B, B, D, V, noise_sd=0.03)
+    toks = draft_tokens(d, 0.6, 0, 1.0, 790 + B)
+    u = synth.uniforms(790 + B, synth.U_ACCEPT, (B, D + 1))
+    u[:, 0] = np.float32(0.99999994)
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    rej = np.nonzero(ref["accepted_len"] == 0)[0]
+    tv = np.array([0.5 * np.abs(oracle.probs(t[b, 0], 0.6, 0, 1.0) -
+                                oracle.probs(d[b, 0], 0.6, 0, 1.0)).sum() for b in rej])
+    expected = float(np.sum((1.0 - tv) ** 64))
+    print(f"B={B}: rejected at 0: {len(rej)}, mean TV {tv.mean():.4f}, "
+          f"expected fallbacks {expected:.1f}", flush=True)
+    assert expected >= 2.0
+
+
 @pytest.mark.parametrize("B", [3, 130])
 def test_zero_draft_probability_is_accepted(dev, B):
     """The R12 reading: a draft token the draft gives probability zero (its
