@@ -710,15 +710,16 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(
         s_m[0] = mm;
     }
     if (emit) {
-        // The block sums, rescaled to the chunk's max, written out once and
-        // contiguously: 4 bytes per block (HBM writes measured costly while
-        // the pass streams: about 2 us per MB written).
+        // The block sums, rescaled to the chunk's max, written out once,
+        // contiguously and non-temporally: 4 bytes per block (HBM writes
+        // measured costly while the pass streams: about 2 us per MB).
         __syncthreads();
         const float mm = s_m[0];
         const int nb = (hi - lo + kBlock - 1) / kBlock;
         for (int k = threadIdx.x; k < nb; k += NT) {
             const float2 st = s_bst[k];
-            bstat[lo / kBlock + k] = st.y > 0.0f ? st.y * weight(st.x, mm, scale) : 0.0f;
+            __builtin_nontemporal_store(st.y > 0.0f ? st.y * weight(st.x, mm, scale) : 0.0f,
+                                        &bstat[lo / kBlock + k]);
         }
     }
 }
