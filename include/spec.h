@@ -263,15 +263,29 @@ spec_status spec_sample_tokens(const float *logits, int R, int V,
  *   P_i = distribution of target row i (i = 0..D), Q_i = of draft row i
  *   (i < D), both with the same temperature / top_k / top_p;
  *   for i = 0..D-1: a_i = P_i(d_i) / Q_i(d_i) in fp32; accept d_i iff
- *   u_i < a_i; at the first rejection draw the next token from
- *   max(0, P_i - Q_i) with u_D (from P_i if that residual is all zero);
+ *   u_i < a_i; at the first rejection draw the next token from the
+ *   residual max(0, P_i - Q_i) (from P_i if that residual is all zero);
  *   if all D are accepted draw the bonus token from P_D with u_D.
+ * Draws are inverse-CDF draws in vocabulary order (the first token whose
+ * cumulative weight exceeds u times the total).  The residual (the pages
+ * name it, not its sampler) is drawn:
+ *   - with top-k / top-p / greedy filters, by inverse CDF with u_D;
+ *   - over the full vocabulary, by rejection from P_i: candidate k =
+ *     0, 1, ... is the inverse-CDF draw from P_i with v_k and is kept iff
+ *     a_k < (P_i - Q_i) / P_i at it (fp32); v_k, a_k are outputs 2k, 2k + 1
+ *     of the SplitMix64 stream seeded with u_D's bit pattern (z = seed +
+ *     (i + 1) * 0x9E3779B97F4A7C15, then the published mix; uniform = the
+ *     top 24 bits * 2^-24); after 64 candidates none of which is kept, the
+ *     residual's inverse CDF with output 128.  This has exactly the
+ *     residual's distribution and reads one block of each row per
+ *     candidate instead of the rows again.
  * The sequence emits draft_tokens[b][0..accepted_len-1] then next_token.
  *
  *  target_logits  fp32 [B][D+1][V]
  *  draft_logits   fp32 [B][D][V] (may be NULL when D == 0)
  *  draft_tokens   int32 [B][D]   (may be NULL when D == 0)
- *  uniforms       fp32 [B][D+1] in [0, 1): tests u_0..u_{D-1}, final draw u_D
+ *  uniforms       fp32 [B][D+1] in [0, 1): tests u_0..u_{D-1}, final draw
+ *                 (or the residual's stream seed) u_D
  *  B >= 0, 0 <= D <= 15, 2 <= V < 2^24
  *  accepted_len   int32 [B] out: 0..D
  *  next_token     int32 [B] out
