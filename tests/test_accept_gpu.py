@@ -477,6 +477,24 @@ def test_residual_fallback_after_rejected_candidates(dev, B):
     assert expected >= 2.0
 
 
+@pytest.mark.parametrize("B,V", [(24, 32768), (130, 32768), (130, 4099)])
+def test_residual_never_draws_a_token_the_target_rules_out(dev, B, V):
+    """Every odd token has target logit -inf (P = 0) while the draft gives it
+    weight, so drafts often land there and are rejected (ratio 0); the
+    residual max(0, P - Q) is then zero at every odd token, and neither the
+    rejection candidates (drawn from P) nor the fallback may return one.
+    Both draw paths, and the scalar-load path (V = 4099), against the oracle."""
+    D = 2
+    t, d = synth.logits_pair(800 + B + V, B, D, V)
+    t[:, :, 1::2] = -np.inf
+    toks = draft_tokens(d, 0.6, 0, 1.0, 800 + B + V)
+    u = synth.uniforms(800 + B + V, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    L = got["accepted_len"]
+    assert (L < D).sum() >= B // 4
+    assert np.all(got["next_token"] % 2 == 0)
+
+
 @pytest.mark.parametrize("B", [3, 130])
 def test_zero_draft_probability_is_accepted(dev, B):
     """The R12 reading: a draft token the draft gives probability zero (its
