@@ -478,8 +478,11 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
             sh.fsh[threadIdx.x >> 6] = m;
             sh.fsh2[threadIdx.x >> 6] = S;
         }
-        bad = block_or(bad, sh.ish);
-        finite = block_or(finite, sh.ish);
+        {
+            const int f = block_or((bad ? 1 : 0) | (finite ? 2 : 0), sh.ish);
+            bad = f & 1;
+            finite = (f >> 1) & 1;
+        }
         if (threadIdx.x == 0) {
             float mm = sh.fsh[0], SS = sh.fsh2[0];
             for (int w = 1; w < kWaves; ++w)
@@ -561,8 +564,11 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
     // the chunks' lists from their heads
     if (!sorted)
         block_sort_desc(sh.keys, got);
-    bad = block_or(bad, sh.ish);
-    finite = block_or(finite, sh.ish);
+    {
+        const int f = block_or((bad ? 1 : 0) | (finite ? 2 : 0), sh.ish);
+        bad = f & 1;
+        finite = (f >> 1) & 1;
+    }
     if (chunks == 1) {
         finalize_candidates(sh.keys, got, (bad || !finite) ? kInvalid : 0, sp, r, ws);
         return;
