@@ -220,6 +220,42 @@ def test_emitted_tokens_follow_the_target_chi_square(dev):
         assert chi2 < 24.32, (i, chi2)
 
 
+@pytest.mark.parametrize("noise", [0.5, 0.02])
+def test_residual_draws_follow_the_residual_chi_square(dev, noise):
+    """10^6 sequences of vocab 16, D = 1, one target and draft row pair, the
+    draft token fixed where P < Q and u_0 just below 1, so every sequence
+    rejects it and draws from the residual max(0, P - Q) through the GPU's
+    rejection sampler (R22) with its own stream per sequence.  The drawn
+    tokens must follow the normalized residual (chi-square over its support,
+    alpha = 0.001).  With noise 0.02 the residual holds about 1% of the mass
+    and most sequences fall back to the residual's inverse CDF."""
+    B, D, V = 1_000_000, 1, 16
+    t1, d1 = synth.logits_pair(43, 1, D, V, noise_sd=noise)
+    P, Q = oracle.probs(t1[0, 0], 0.6), oracle.probs(d1[0, 0], 0.6)
+    x = int(np.argmax(Q - P))                   # the draft token: P < Q there
+    assert P[x] < Q[x]
+    r = np.maximum(P - Q, 0.0)
+    r /= r.sum()
+    t = np.ascontiguousarray(np.broadcast_to(t1, (B, D + 1, V)))
+    d = np.ascontiguousarray(np.broadcast_to(d1, (B, D, V)))
+    toks = np.full((B, D), x, np.int32)
+    u = synth.uniforms(43, synth.U_ACCEPT, (B, D + 1))
+    u[:, 0] = np.float32(0.99999994)
+    got = gpu_accept(t, d, toks, u, 0.6, 0, 1.0, dev)
+    assert np.all(got["accepted_len"] == 0)
+    obs = np.bincount(got["next_token"], minlength=V)
+    support = r > 0
+    assert obs[~support].sum() == 0
+    exp = r[support] * B
+    chi2 = float(((obs[support] - exp) ** 2 / exp).sum())
+    dof = int(support.sum()) - 1
+    limit = {1: 10.83, 2: 13.82, 3: 16.27, 4: 18.47, 5: 20.52, 6: 22.46, 7: 24.32, 8: 26.12,
+             9: 27.88, 10: 29.59, 11: 31.26, 12: 32.91, 13: 34.53, 14: 36.12, 15: 37.70}[dof]
+    print(f"noise {noise}: residual mass {np.maximum(P - Q, 0).sum():.4f}, support {dof + 1}, "
+          f"chi2 {chi2:.2f} (limit {limit})", flush=True)
+    assert chi2 < limit
+
+
 def test_invalid_sequences(dev):
     B, D, V = 6, 2, 4096
     t, d = synth.logits_pair(500, B, D, V)
