@@ -388,6 +388,20 @@ def test_deepest_block(dev):
     assert ref["accepted_len"].max() >= 10
 
 
+def test_deepest_block_fused_draw(dev):
+    """D = 15 (31 rows per sequence) on the large-batch path (130 sequences:
+    the statistics pass, then one fused draw workgroup per sequence),
+    against the oracle."""
+    B, D, V = 130, 15, 8192
+    t, d = synth.logits_pair(704, B, D, V)
+    d[:, :8] = t[:, :8]
+    toks = draft_tokens(d, 0.6, 0, 1.0, 704)
+    u = synth.uniforms(704, synth.U_ACCEPT, (B, D + 1))
+    got, ref = check(t, d, toks, u, 0.6, 0, 1.0, dev)
+    L = ref["accepted_len"]
+    assert L.max() >= 8 and (L < D).sum() > 0
+
+
 def test_many_sequences_small_vocabulary(dev):
     B, D, V = 4096, 2, 256
     t, d = synth.logits_pair(702, B, D, V)
@@ -406,12 +420,13 @@ def test_two_token_vocabulary(dev):
 
 @pytest.mark.parametrize("B,D,V", [(200, 5, 151936), (130, 3, 1001), (300, 2, 2048)])
 def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
-    """From 128 sequences on, each sequence is decided, summed and drawn by
-    one fused workgroup; below, by separate block-sum and draw launches.
-    Sequences are independent, and both halves here keep one statistics chunk
-    per row (as the whole batch does), so the whole batch must give, bit for
-    bit, what its two halves give: residual and bonus draws, invalid
-    sequences, and an odd vocabulary on the scalar-load path."""
+    """From 128 sequences on, each sequence is decided and drawn by one fused
+    workgroup; below, by the draw launch (after a block-sum launch for rows
+    that are not 16-byte aligned).  Sequences are independent, and both
+    halves here keep one statistics chunk per row (as the whole batch does),
+    so the whole batch must give, bit for bit, what its two halves give:
+    residual and bonus draws, invalid sequences, and an odd vocabulary on the
+    scalar-load path."""
     t, d = synth.logits_pair(720 + D, B, D, V)
     d[: B // 4] = t[: B // 4, :D]            # some sequences accept every draft
     toks = draft_tokens(d, 0.6, 0, 1.0, 720 + D)
