@@ -14,24 +14,29 @@
 // Kernels (no workgroup ever waits for, or signals, another: each step's
 // results reach the next through the kernel boundary, so there are no
 // fences, counters or spin waits):
-//  1. row_chunk  -- grid (row, chunk).  One streaming pass over every fp32
-//     logit.  Full-vocabulary mode: per-chunk running max and sum of
-//     exp2((z - max) * log2(e)/T) (row_stats_kernel when the rows are
-//     16-byte aligned and no per-block output is wanted).  Candidate mode
-//     (top-k active, top-p, or greedy): the chunk's top-k (logit, index) keys
-//     by radix select.  A row that is a single chunk is finalized right here.
-//  2. row_merge  -- grid (row), only when rows span several chunks: merges
-//     the chunks in chunk order into the row's final statistics.
-//  3. draw_sums  -- grid (sequence, chunk), full-vocabulary mode: recomputes
-//     the D ratio tests from the row statistics (a handful of gathers) and
-//     sums the draw distribution -- residual max(0, p - q) at the rejected
-//     position, or the bonus row -- over every 256-token block.
-//  4. draw_final -- grid (sequence): decisions, then the inverse-CDF draw:
-//     scan the block sums for the block holding u * total, re-read that one
-//     block and scan it in vocabulary order.  In candidate mode the draw runs
-//     over the <= 256 kept candidates instead.
-//     draw_fused    -- 3 and 4 in one 1024-thread workgroup per sequence, for
-//     batches of 128 sequences or more (same sums, same draw).
+//  1. row_stats / row_chunk -- grid (row, chunk).  One streaming pass over
+//     every fp32 logit.  Full-vocabulary mode (row_stats_kernel; rows that
+//     are not 16-byte aligned go to row_chunk_kernel<false>): per-chunk
+//     running max and sum of exp2((z - max) * log2(e)/T), and on target rows
+//     every 256-token block's sum relative to the chunk's max.  Candidate
+//     mode (top-k active, top-p, or greedy; row_chunk_kernel<true>): the
+//     chunk's top-k (logit, index) keys.  A row that is a single chunk is
+//     finalized right here.
+//  2. row_merge  -- grid (row), candidate rows that span several chunks (and
+//     every such row for the dense probabilities): merges the chunks into
+//     the row's final statistics.  The draw kernels merge full-vocabulary
+//     rows of their own sequence themselves.
+//  3. draw_sums  -- grid (sequence, chunk), full-vocabulary rows without
+//     block sums (not 16-byte aligned): recomputes the D ratio tests and sums
+//     the target row's mass over every 256-token block.
+//  4. draw_final -- grid (sequence): decisions, then the draw.  Bonus: the
+//     inverse CDF over the target row's block masses, then one block scanned
+//     in vocabulary order.  Residual: candidates drawn from the target row
+//     and kept with probability (p - q)/p (falling back to the residual's
+//     inverse CDF).  In candidate mode the draw runs over the <= 256 kept
+//     candidates instead.
+//     draw_fused    -- the same in one 1024-thread workgroup per sequence,
+//     for batches of 128 sequences or more (same masses, same draw).
 //  5. probs      -- dense write of the distributions (spec_sample_probs).
 //
 // Every reduction runs in a fixed order, so results are deterministic.
@@ -67,8 +72,9 @@ constexpr int kMaxDepth = 15;       // drafts per sequence at most (the ABI's li
 
 // Logit loads of the statistics pass are non-temporal: every logit is read
 // once there, and keeping it out of the caches measured 12% faster for the
-// pass plus the draw that follows (which re-reads one or two rows per
-// sequence with ordinary loads).
+// pass plus the draw that follows (which then re-read one or two rows per
+// sequence with ordinary loads; it now reads one 256-token block per
+// candidate, and whole rows only on the residual's fallback).
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 load_once(const float4 *p) {
     const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
@@ -1098,8 +1104,9 @@ __device__ void block_draw_sums(const DrawRows &d, const SamplingParams &sp, int
     }
 }
 
-// Kernel 3: per 256-token block, the sums of the draw weights, for small
-// batches (several workgroups per sequence).
+// Kernel 3: per 256-token block, the target row's mass, for rows the
+// statistics pass left no block sums for (not 16-byte aligned) in batches
+// below the fused draw (several workgroups per sequence).
 __global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     Rows rows, SamplingParams sp, const int32_t *__restrict__ draft_tokens,
     const float *__restrict__ uniforms, int blocks_per_chunk, Ws ws) {
