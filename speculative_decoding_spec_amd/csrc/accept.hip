@@ -386,10 +386,34 @@ __device__ int block_select_topk(Each each, int n, int k, uint64_t *out, int cap
     return min(want, min(sh.out_n, cap));
 }
 
+// Gathers the nonzero keys at or above theta among those `each` visits
+// (a functor calling f(key) for every key this thread owns) into out[], in
+// thread order, and returns how many there are (only the first cap are
+// stored).  Positions come from one block-wide scan of the per-thread
+// counts, so no two threads contend for a counter.  sh: kWaves ints.
+template <class Each>
+__device__ int block_gather_ge(Each each, uint64_t theta, uint64_t *out, int cap, int *sh) {
+    int cnt = 0;
+    each([&](uint64_t key) { cnt += (key != 0 && key >= theta) ? 1 : 0; });
+    int pos = block_incl_scan(cnt, sh) - cnt;
+    int total = 0;
+    for (int w = 0; w < kWaves; ++w)
+        total += sh[w];
+    each([&](uint64_t key) {
+        if (key != 0 && key >= theta) {
+            if (pos < cap)
+                out[pos] = key;
+            ++pos;
+        }
+    });
+    return total;
+}
+
 // Sorts keys[0..n) in LDS (n <= kThreads, keys unique) into descending
 // order, in place, by rank: thread t's key moves to the number of keys
-// greater than it.  n broadcast reads per thread and two barriers -- far
-// fewer steps than a sorting network for the short lists sorted here.
+// greater than it.  n broadcast reads per thread (issued eight at a time, so
+// their latencies overlap) and two barriers -- far fewer steps than a
+// sorting network for the short lists sorted here.
 __device__ void block_sort_desc(uint64_t *keys, int n) {
     __syncthreads();   // the caller's writes to keys
     const int t = threadIdx.x;
@@ -397,7 +421,17 @@ __device__ void block_sort_desc(uint64_t *keys, int n) {
     int rank = 0;
     if (t < n) {
         mine = keys[t];
-        for (int j = 0; j < n; ++j)
+        int j = 0;
+        for (; j + 8 <= n; j += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = keys[j + q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                rank += v[q] > mine;
+        }
+        for (; j < n; ++j)
             rank += keys[j] > mine;
     }
     __syncthreads();
@@ -416,30 +450,59 @@ struct StatsShared {
     int ish[kWaves];
 };
 
+// Reads lane l's value of v (l uniform).
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Sorted candidates -> the row's final statistics (top-p cut, normalizer).
-// keys[0..got) sorted by rank, in LDS; called by all threads.
+// keys[0..got) sorted by rank, in LDS; called by all threads.  Wave 0 does
+// the work: lane l computes the weights of candidates l, l + 64, ..., then
+// the cumulative sums run in rank order, one addition at a time (the order
+// fixes their rounding), each lane keeping the sums at its own candidates;
+// the top-p cut is the first candidate whose cumulative share reaches
+// top_p, found by one division per lane and a ballot.
 __device__ void finalize_candidates(const uint64_t *keys, int got, int flags,
                                     const SamplingParams &sp, int r, Ws &ws) {
-    if (threadIdx.x == 0) {
+    constexpr int Q = kMaxCand / 64;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
         const float m = key_logit(keys[0]);
+        float w[Q], cs[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int i = lane + 64 * q;
+            w[q] = i < got ? weight(key_logit(keys[i]), m, sp.scale) : 0.0f;
+            cs[q] = 0.0f;
+        }
         float cum = 0.0f;
-        for (int i = 0; i < got; ++i)
-            cum += weight(key_logit(keys[i]), m, sp.scale);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int cnt = min(64, got - 64 * q);
+            for (int l = 0; l < cnt; ++l) {
+                cum += lane_value(w[q], l);
+                cs[q] = lane == l ? cum : cs[q];
+            }
+        }
         const float S_all = cum;
         int kept = got;
         float S_kept = S_all;
         if (sp.use_p) {
-            cum = 0.0f;
-            for (int i = 0; i < got; ++i) {
-                cum += weight(key_logit(keys[i]), m, sp.scale);
-                if (cum / S_all >= sp.top_p) {
-                    kept = i + 1;
-                    break;
+#pragma unroll
+            for (int q = Q - 1; q >= 0; --q) {
+                const int i = lane + 64 * q;
+                const unsigned long long hit = __ballot(i < got && cs[q] / S_all >= sp.top_p);
+                if (hit) {
+                    const int l = __ffsll((long long)hit) - 1;
+                    kept = 64 * q + l + 1;
+                    S_kept = lane_value(cs[q], l);
                 }
             }
-            S_kept = (kept == got) ? S_all : cum;
+            if (kept == got)
+                S_kept = S_all;
         }
-        ws.row_final[r] = RowFinal{m, 1.0f / S_kept, kept, flags};
+        if (lane == 0)
+            ws.row_final[r] = RowFinal{m, 1.0f / S_kept, kept, flags};
     }
     uint64_t *rk = ws.row_keys + (size_t)r * sp.k_eff;
     for (int i = threadIdx.x; i < sp.k_eff; i += kThreads)
@@ -538,23 +601,14 @@ __global__ __launch_bounds__(kThreads) void row_chunk_kernel(
         const uint64_t kth = wave_kth_largest(tmax, (want + kWaves - 1) / kWaves);
         if ((threadIdx.x & 63) == 0)
             sh.kth[threadIdx.x >> 6] = kth;
-        if (threadIdx.x == 0)
-            sh.sel.out_n = 0;
         __syncthreads();
         uint64_t theta = sh.kth[0];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
             theta = min(theta, sh.kth[w]);
         uint64_t *cand = sh.keys + kMaxCand;   // second half; the result goes to the first
-        each([&](uint64_t key) {
-            if (key >= theta) {
-                const int slot = atomicAdd(&sh.sel.out_n, 1);
-                if (slot < kMaxCand)
-                    cand[slot] = key;
-            }
-        });
+        const int C = block_gather_ge(each, theta, cand, kMaxCand, sh.sel.scan);
         __syncthreads();
-        const int C = sh.sel.out_n;
         if (C <= kMaxCand) {   // else (many equal-valued... or spread keys): the general select
             block_sort_desc(cand, C);
             for (int i = threadIdx.x; i < want; i += kThreads)
@@ -807,10 +861,48 @@ __global__ __launch_bounds__(kThreads) void row_merge_kernel(
         n_real += min(k, min(V, (cc + 1) * chunk_len) - cc * chunk_len);
     int got;
     if (walk) {
+        got = min(k, n_real);
+        // The row's top-k lie at or above a bound found as in the chunk
+        // pass: each wave takes the ceil(got / 4)-th largest of its threads'
+        // largest staged keys, and the smallest of the four is at most the
+        // got-th largest key.  The keys at or above it are gathered and
+        // sorted by rank: the same keys in the same order as the walk below,
+        // which runs only when more than kMaxCand keys reach the bound.
+        {
+            uint64_t tmax = 0;
+#pragma unroll
+            for (int q = 0; q < kMergeWalkMax / kThreads; ++q)
+                tmax = max(tmax, staged[q]);
+            const uint64_t kth = wave_kth_largest(tmax, (got + kWaves - 1) / kWaves);
+            if ((threadIdx.x & 63) == 0)
+                sh.kth[threadIdx.x >> 6] = kth;
+            __syncthreads();
+            uint64_t theta = sh.kth[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                theta = min(theta, sh.kth[w]);
+            auto each_s = [&](auto f) {
+#pragma unroll
+                for (int q = 0; q < kMergeWalkMax / kThreads; ++q)
+                    f(staged[q]);
+            };
+            uint64_t *cand = sh.keys + kMaxCand;
+            const int C = block_gather_ge(each_s, theta, cand, kMaxCand, sh.sel.scan);
+            if (C <= kMaxCand) {
+                block_sort_desc(cand, C);
+                for (int i = threadIdx.x; i < got; i += kThreads)
+                    sh.keys[i] = cand[i];
+                __syncthreads();
+                finalize_candidates(sh.keys, got, flags, sp, r, ws);
+                return;
+            }
+        }
         // The chunks' lists arrive sorted, so the row's top-k is a k-way
         // merge.  The lists are staged in LDS; wave 0 keeps list c's head in
         // lane c and k times takes the largest head (keys are unique) and
-        // advances that list.
+        // advances that list.  Each lane also holds the key after its head,
+        // so an advance takes the held key and its LDS read (for the key
+        // after that) has a whole step to arrive.
         uint64_t *lists = sh.walk;
 #pragma unroll
         for (int q = 0; q < kMergeWalkMax / kThreads; ++q) {
@@ -819,18 +911,19 @@ __global__ __launch_bounds__(kThreads) void row_merge_kernel(
                 lists[i] = staged[q];
         }
         __syncthreads();
-        got = min(k, n_real);
         if (threadIdx.x < 64) {
             const int lane = threadIdx.x;
             int pos = 0;
             uint64_t head = lane < chunks ? lists[lane * k] : 0;
+            uint64_t next = (lane < chunks && k > 1) ? lists[lane * k + 1] : 0;
             for (int i = 0; i < got; ++i) {
                 const uint64_t top = wave_max_u64(head);
                 if (lane == 0)
                     sh.keys[i] = top;
                 if (head == top) {   // the one list holding it
                     ++pos;
-                    head = pos < k ? lists[lane * k + pos] : 0;
+                    head = next;
+                    next = pos + 1 < k ? lists[lane * k + pos + 1] : 0;
                 }
             }
         }
@@ -1509,35 +1602,72 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         }
         __syncthreads();
         block_sort_desc(sh.ckey, n);   // entries n.. are zero and stay last
-        if (threadIdx.x == 0) {
+        if (threadIdx.x < 64) {
+            // Wave 0: lane l holds the candidates l, l + 64, ... in
+            // vocabulary order (token, residual weight, target probability);
+            // the totals and the running sum go one addition at a time in
+            // that order, each lane keeping the sums at its own candidates;
+            // the token is the first whose running sum passes u * total (else
+            // the last with positive weight).
+            constexpr int Q = kMaxCand / 64;
+            const int lane = threadIdx.x;
+            int xs[Q];
+            float wr[Q], wp[Q], cs[Q];
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int i = lane + 64 * q;
+                const uint64_t key = i < n ? ~sh.ckey[i] : 0;
+                const int slot = (int)(uint32_t)key;
+                xs[q] = (int)(key >> 32);
+                wr[q] = i < n ? sh.cw[slot] : 0.0f;
+                wp[q] = i < n ? sh.cp[slot] : 0.0f;
+                cs[q] = 0.0f;
+            }
             float tot = 0.0f;
-            for (int i = 0; i < n; ++i)
-                tot += sh.cw[(uint32_t)~sh.ckey[i]];
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                for (int l = 0; l < min(64, n - 64 * q); ++l)
+                    tot += lane_value(wr[q], l);
             const bool use_p = !(tot > 0.0f);
             if (use_p) {
                 tot = 0.0f;
-                for (int i = 0; i < n; ++i)
-                    tot += sh.cp[(uint32_t)~sh.ckey[i]];
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    for (int l = 0; l < min(64, n - 64 * q); ++l)
+                        tot += lane_value(wp[q], l);
             }
             const float target = u * tot;
             float cum = 0.0f;
-            int pick = -1, last_pos = -1;
-            for (int i = 0; i < n; ++i) {
-                const int slot = (int)(uint32_t)~sh.ckey[i];
-                const float w = use_p ? sh.cp[slot] : sh.cw[slot];
-                const int x = (int)((~sh.ckey[i]) >> 32);
-                cum += w;
-                if (w > 0.0f)
-                    last_pos = x;
-                if (cum > target) {
-                    pick = x;
-                    break;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const float wq = use_p ? wp[q] : wr[q];
+                for (int l = 0; l < min(64, n - 64 * q); ++l) {
+                    cum += lane_value(wq, l);
+                    cs[q] = lane == l ? cum : cs[q];
                 }
+            }
+            int pick = -1, last_pos = -1;
+#pragma unroll
+            for (int q = Q - 1; q >= 0; --q) {
+                const int i = lane + 64 * q;
+                const unsigned long long pass = __ballot(i < n && cs[q] > target);
+                if (pass)
+                    pick = __shfl(xs[q], __ffsll((long long)pass) - 1);
+            }
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int i = lane + 64 * q;
+                const float wq = use_p ? wp[q] : wr[q];
+                const unsigned long long pos = __ballot(i < n && wq > 0.0f);
+                if (pos)
+                    last_pos = __shfl(xs[q], 63 - __clzll((long long)pos));
             }
             if (pick < 0)
                 pick = last_pos;
-            if (accepted_len) accepted_len[b] = L;
-            next_token[b] = pick;
+            if (lane == 0) {
+                if (accepted_len) accepted_len[b] = L;
+                next_token[b] = pick;
+            }
         }
         return;
     }
