@@ -465,8 +465,9 @@ def test_fused_draw_long_rows_parity(dev):
 
 
 @pytest.mark.parametrize("V,k,p", [
-    (151936, 64, 1.0),      # largest k of the head-walk merge (38 chunk lists)
-    (151936, 1, 1.0),       # greedy through the walk
+    (151936, 64, 1.0),      # 38 chunk lists of 64: about 460 keys reach the bound, so the walk runs
+    (151936, 1, 1.0),       # greedy: bound-and-gather over the 38 lists
+    (151936, 20, 1.0),      # bound-and-gather (about 40 keys reach the bound)
     (32768, 100, 0.9),      # radix merge over register-held keys (800 keys)
     (32768, 200, 1.0),      # radix merge re-reading keys (1600 keys)
     (300000, 20, 0.95),     # 74 chunks: more lists than lanes, radix merge
