@@ -36,7 +36,8 @@
 //     inverse CDF).  In candidate mode the draw runs over the <= 256 kept
 //     candidates instead.
 //     draw_fused    -- the same in one 1024-thread workgroup per sequence,
-//     for batches of 128 sequences or more (same masses, same draw).
+//     for every full-vocabulary batch whose rows have block sums, and for
+//     the others from 128 sequences on (same masses, same draw).
 //  5. probs      -- dense write of the distributions (spec_sample_probs).
 //
 // Every reduction runs in a fixed order, so results are deterministic.
@@ -54,7 +55,10 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxCand = 256;       // top-k cap in candidate mode
 constexpr int kCandChunk = 4096;    // logits per workgroup in candidate mode
 constexpr int kTargetBlocks = 1024;
-constexpr int kFusedMinB = 128;     // batches drawn by the fused kernel (half the CUs)
+// Batches whose rows lack block sums (not 16-byte aligned) are drawn by the
+// fused kernel from this many sequences on (half the CUs busy); below, the
+// block sums are spread over a launch of their own first.
+constexpr int kFusedMinB = 128;
 // Statistics pass over 16-byte aligned rows: workgroup size and 16-byte
 // loads per thread in flight (measured: 256 x 8 slightly ahead of 256 x 4
 // and 512 x 4; 128-thread workgroups 4-5% slower).
@@ -1672,13 +1676,9 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
         return;
     }
     const int nblocks = (rows.V + kBlock - 1) / kBlock;
-    // the target row's (p, p) block masses: from its statistics, or as the
-    // block-sum launch left them
+    // the target row's (p, p) block masses, as the block-sum launch left
+    // them (rows with block statistics are drawn by draw_fused_kernel)
     float2 *bs = ws.block_sums + (size_t)b * nblocks;
-    if (sp.block_stats) {
-        stats_to_masses(rows, ws, sp, d, b, L, bs);
-        __syncthreads();
-    }
     if (d.residual) {
         const uint32_t ubits = __float_as_uint(u);
         const int tok = rejection_draw(rows, sp, bs, d, (uint64_t)ubits, sh);
@@ -1699,10 +1699,11 @@ __global__ __launch_bounds__(kThreads) void draw_final_kernel(
     draw_full_vocab(rows, sp, bs, d, b, L, u, sh, accepted_len, next_token);
 }
 
-// Kernels 3 and 4 as one, for large batches (full vocabulary, verification):
-// one 1024-thread workgroup per sequence decides, sums the draw blocks with
-// 16 waves, then draws.  Same block sums and draw as the two-kernel path, one
-// launch and one decision pass fewer.
+// Kernels 3 and 4 as one (full vocabulary): one 1024-thread workgroup per
+// sequence decides (16 waves merge its rows' statistics in parallel), turns
+// the target row's block sums into masses in LDS (or sums the blocks itself
+// for rows without them), then draws.  Same masses and draw as the
+// two-kernel path, one launch and one decision pass fewer.
 constexpr int kFusedThreads = 1024;
 // Block sums of rows up to this many 256-token blocks (262144 tokens) stay
 // in LDS; longer rows use the workspace.
@@ -1850,11 +1851,12 @@ AcceptPlan accept_plan(int B, int D, int V, int k_eff, bool candidates) {
     }
     p.chunks = std::max(1, (V + p.chunk_len - 1) / p.chunk_len);
     p.nblocks = (V + kBlock - 1) / kBlock;
-    // The draw: from kFusedMinB sequences on, one fused 1024-thread
-    // workgroup per sequence (half the CUs or more busy); below, draw-sum
-    // workgroups of whole 256-token blocks, about kTargetBlocks in total,
-    // then one draw workgroup per sequence.
-    p.fused_draw = B >= kFusedMinB;
+    // The draw: one fused 1024-thread workgroup per sequence whenever the
+    // statistics pass leaves the target rows' block sums (16-byte aligned
+    // rows), and for rows without them from kFusedMinB sequences on; below
+    // that, draw-sum workgroups of whole 256-token blocks (about
+    // kTargetBlocks in total), then one draw workgroup per sequence.
+    p.fused_draw = B >= kFusedMinB || (!candidates && V % 4 == 0);
     int C3 = (kTargetBlocks + std::max(B, 1) - 1) / std::max(B, 1);
     C3 = std::max(1, std::min(C3, (p.nblocks + 31) / 32));
     p.blocks_per_chunk3 = (p.nblocks + C3 - 1) / C3;

@@ -420,13 +420,15 @@ def test_two_token_vocabulary(dev):
 
 @pytest.mark.parametrize("B,D,V", [(200, 5, 151936), (130, 3, 1001), (300, 2, 2048)])
 def test_fused_draw_equals_two_launch_draw(dev, B, D, V):
-    """From 128 sequences on, each sequence is decided and drawn by one fused
-    workgroup; below, by the draw launch (after a block-sum launch for rows
-    that are not 16-byte aligned).  Sequences are independent, and both
-    halves here keep one statistics chunk per row (as the whole batch does),
-    so the whole batch must give, bit for bit, what its two halves give:
-    residual and bonus draws, invalid sequences, and an odd vocabulary on the
-    scalar-load path."""
+    """Sequences are independent, and both halves here keep one statistics
+    chunk per row (as the whole batch does), so the whole batch must give,
+    bit for bit, what its two halves give: residual and bonus draws, invalid
+    sequences.  Rows with block sums (V = 151936, 2048) are drawn by the
+    fused workgroup per sequence in the batch and in its halves alike; the
+    odd vocabulary (scalar-load path, no block sums) is drawn by the fused
+    kernel in the 130-sequence batch and by the block-sum and draw launches
+    in its 65-sequence halves, so that case also checks the two draw paths
+    against each other."""
     t, d = synth.logits_pair(720 + D, B, D, V)
     d[: B // 4] = t[: B // 4, :D]            # some sequences accept every draft
     toks = draft_tokens(d, 0.6, 0, 1.0, 720 + D)
@@ -482,15 +484,16 @@ def test_candidate_merge_paths(dev, V, k, p):
     check(t, d, toks, u, 0.7, k, p, dev)
 
 
-@pytest.mark.parametrize("B", [3, 130])
-def test_zero_residual_draws_from_target(dev, B):
+@pytest.mark.parametrize("B,V", [(3, 40000), (3, 40001), (130, 40000)])
+def test_zero_residual_draws_from_target(dev, B, V):
     """The R11 reading: target and draft rows identical, and every position-0
     draft token has probability zero under both (its logit far below the
     rest, so its weight underflows).  The ratio p/q is then taken as 0, the
     draft is rejected, and the residual max(0, p - q) is zero everywhere, so
-    the token is drawn from the target row itself.  Small batches and the
-    fused large-batch draw both."""
-    D, V = 2, 40000
+    the token is drawn from the target row itself.  Both draw paths: the
+    fused draw (rows with block sums, any batch) and the block-sum and draw
+    launches (a small batch of rows that are not 16-byte aligned)."""
+    D = 2
     t, _ = synth.logits_pair(740 + B, B, D, V)
     d = np.ascontiguousarray(t[:, :D]).copy()
     toks = np.zeros((B, D), np.int32)
@@ -504,8 +507,8 @@ def test_zero_residual_draws_from_target(dev, B):
     assert np.all(ref["accepted_len"] == 0) and np.all(got["accepted_len"] == 0)
 
 
-@pytest.mark.parametrize("B", [24, 130])
-def test_residual_fallback_after_rejected_candidates(dev, B):
+@pytest.mark.parametrize("B,V", [(24, 32768), (24, 32769), (130, 32768)])
+def test_residual_fallback_after_rejected_candidates(dev, B, V):
     """R22's fallback on both draw paths: target and draft rows close
     (target = draft + N(0, 0.03)), so at a rejected position the residual
     holds about 2% of the mass and each of the 64 rejection candidates is
@@ -513,8 +516,10 @@ def test_residual_fallback_after_rejected_candidates(dev, B):
     decides with stream output 128.  Position 0 is rejected (a uniform just
     below 1) wherever P < Q at the draft token.  The expected number of
     sequences drawn by the fallback, the sum of (1 - TV)^64, is checked to
-    be at least 2."""
-    D, V = 2, 32768
+    be at least 2.  V = 32769 (a small batch of rows that are not 16-byte
+    aligned) takes the block-sum and draw launches, the others the fused
+    draw."""
+    D = 2
     t, d = synth.logits_pair(790 + B, B, D, V, noise_sd=0.03)
     toks = draft_tokens(d, 0.6, 0, 1.0, 790 + B)
     u = synth.uniforms(790 + B, synth.U_ACCEPT, (B, D + 1))
@@ -529,13 +534,15 @@ def test_residual_fallback_after_rejected_candidates(dev, B):
     assert expected >= 2.0
 
 
-@pytest.mark.parametrize("B,V", [(24, 32768), (130, 32768), (130, 4099)])
+@pytest.mark.parametrize("B,V", [(24, 32768), (130, 32768), (24, 4099), (130, 4099)])
 def test_residual_never_draws_a_token_the_target_rules_out(dev, B, V):
     """Every odd token has target logit -inf (P = 0) while the draft gives it
     weight, so drafts often land there and are rejected (ratio 0); the
     residual max(0, P - Q) is then zero at every odd token, and neither the
     rejection candidates (drawn from P) nor the fallback may return one.
-    Both draw paths, and the scalar-load path (V = 4099), against the oracle."""
+    The fused draw, and the scalar-load path (V = 4099) through the fused
+    kernel (130 sequences) and through the block-sum and draw launches (24),
+    against the oracle."""
     D = 2
     t, d = synth.logits_pair(800 + B + V, B, D, V)
     t[:, :, 1::2] = -np.inf
@@ -547,12 +554,13 @@ def test_residual_never_draws_a_token_the_target_rules_out(dev, B, V):
     assert np.all(got["next_token"] % 2 == 0)
 
 
-@pytest.mark.parametrize("B", [3, 130])
-def test_zero_draft_probability_is_accepted(dev, B):
+@pytest.mark.parametrize("B,V", [(3, 40000), (3, 40001), (130, 40000)])
+def test_zero_draft_probability_is_accepted(dev, B, V):
     """The R12 reading: a draft token the draft gives probability zero (its
     draft logit far below the rest, weight underflowing) but the target does
-    not has ratio +inf, so it is accepted whatever the uniform."""
-    D, V = 3, 40000
+    not has ratio +inf, so it is accepted whatever the uniform.  Both draw
+    paths, as in the R11 test."""
+    D = 3
     t, d = synth.logits_pair(750 + B, B, D, V)
     toks = draft_tokens(d, 0.6, 0, 1.0, 750 + B)
     for b in range(B):
