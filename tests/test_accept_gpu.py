@@ -105,7 +105,8 @@ def test_sample_probs_ties_and_invalid_rows(dev):
     (1, 151936, 0.6, 0, 1.0),       # one row of 75 chunks (the draft step)
     (300, 1000, 0.8, 0, 1.0),       # a partial last block
     (512, 151936, 0.6, 20, 0.95),   # candidates
-    (512, 999, 1.0, 0, 1.0),        # odd vocabulary: the draw pass re-reads
+    (512, 999, 1.0, 0, 1.0),        # odd vocabulary: the fused draw sums the blocks
+    (3, 999, 1.0, 0, 1.0),          # odd vocabulary, few rows: block-sum and draw launches
 ])
 def test_sample_tokens(dev, R, V, T, k, p):
     import speculative_decoding_spec_amd as spec
